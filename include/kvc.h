@@ -1,0 +1,187 @@
+/*
+ * kvc — attention-score-guided KV-cache token selection and compaction on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three policies share one library:
+ *   - SnapKV prompt compression: the abeam.tech summary of "SnapKV: LLM Knows
+ *     What You are Looking for Before Generation", section 技術の仕組み (how it
+ *     works), subsection 処理の流れ (processing flow), steps 1-4.
+ *   - H2O heavy-hitter + recent eviction during decoding: the abeam.tech summary
+ *     of "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of Large
+ *     Language Models", section 技術の仕組み, subsections 何を残すのか (what is
+ *     kept) and 処理の流れ (processing flow).
+ *   - StreamingLLM attention sinks + recent window: the abeam.tech summary of
+ *     "Efficient Streaming Language Models with Attention Sinks", section
+ *     技術の仕組み, subsections キャッシュ構造 (cache structure) and 推論の流れ
+ *     (inference flow).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers; the caller owns every buffer,
+ *     including workspaces (size them with the *_workspace_bytes queries). The
+ *     library never allocates or frees device memory.
+ *   - Work is enqueued on `stream` and runs asynchronously; no entry point
+ *     synchronises the host. A device-side fault surfaces as a HIP error at the
+ *     caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is enqueued. A bad
+ *     argument returns a non-OK status, leaves every output untouched and sets
+ *     a message readable with kvc_last_error(). No C++ exception crosses the ABI.
+ *   - Element types: KVC_BF16 (bfloat16 stored as 16-bit patterns) or KVC_F32.
+ *     Arithmetic is float32 with fp32 accumulation in every case.
+ *   - head_dim D must be 64 or 128 and is the contiguous (innermost) axis.
+ *     Device pointers and the byte size of every row stride must be multiples
+ *     of 16.
+ *   - Calls on one stream are ordered; concurrent calls that share a workspace
+ *     or a cache race.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = 1, /* a pointer, size or policy value is out of range      */
+  KVC_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels handle (D, w)     */
+  KVC_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query     */
+  KVC_ERR_HIP = 4          /* a kernel launch failed; message holds the HIP error  */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Element strides of a [B, H, T, D] tensor whose D axis is contiguous. */
+typedef struct {
+  int64_t b, h, t;
+} kvc_strides;
+
+/* Message describing the last non-OK status returned on the calling thread
+ * ("" if none). The pointer stays valid until the next call on that thread. */
+const char* kvc_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kvc_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* SnapKV prompt-KV compression (one attention layer, every head).            */
+/* ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace kvc_snapkv_compress needs for these sizes
+ * (0 if the sizes are invalid). */
+size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
+                                  int pool_kernel, kvc_dtype dt);
+
+/* Compress the prompt cache of one layer to `budget` rows per head.
+ *
+ * For every (b, h), independently (SnapKV page, processing flow):
+ *   1. the last `window` prompt queries attend to the prompt keys with scores
+ *      q.k / sqrt(D); query i of the window sits at position L-window+i and sees
+ *      keys 0 .. L-window+i (causal inside the window); each row's softmax runs
+ *      over every key it sees;
+ *   2. vote[j] = sum over the window rows of their softmax weight on prefix
+ *      position j, j < L-window;
+ *   3. pooled = 1D max-pool of vote, odd width pool_kernel, stride 1, neighbours
+ *      beyond either end ignored;
+ *   4. the budget-window prefix positions with the largest pooled score are kept
+ *      (equal scores: lower position first), in ascending order, and their K/V
+ *      rows are concatenated with the window's own K/V rows.
+ *
+ * q        [B, H, q_len, D] queries with strides qs; rows q_len-window .. q_len-1
+ *          are the observation window (the rest is not read).
+ * k, v     [B, H, L, D] prompt keys and values, both with strides kvs.
+ * k_out,   [B, H, budget, D] contiguous outputs: kept prefix rows in ascending
+ * v_out    position order, then the window rows L-window .. L-1.
+ * idx_out  [B, H, budget-window] int32 kept prefix positions, ascending.
+ * pooled_out, vote_out  optional float [B, H, L-window] (NULL = not written).
+ * workspace  device buffer of at least kvc_snapkv_workspace_bytes(...) bytes;
+ *          its contents on entry do not matter.
+ *
+ * Requires 1 <= window <= 32, window < budget < L (when L <= budget there is
+ * nothing to compress: INVALID_ARG), pool_kernel odd in [1, 65], q_len >= window,
+ * D in {64, 128}. Outputs must not overlap the inputs. */
+kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
+                               const void* k, const void* v, kvc_strides kvs,
+                               int B, int H, int L, int D, int window, int budget,
+                               int pool_kernel, kvc_dtype dt,
+                               void* k_out, void* v_out, int32_t* idx_out,
+                               float* pooled_out, float* vote_out,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Instrumentation (not part of the method): while set, every
+ * kvc_snapkv_compress call on the calling thread records events[i] on its
+ * stream at phase boundary i, for i < n_events (at most 8): 0 before the
+ * first kernel, then after the workspace clear (1), the row-statistics pass
+ * (2), the vote pass (3), pooling + histogram (4), classification (5), the
+ * final selection (6) and the gather (7). The events are created and owned
+ * by the caller; pass NULL or 0 to stop recording. */
+void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events);
+
+/* ------------------------------------------------------------------------- */
+/* H2O heavy-hitter + recent cache, one decode step.                          */
+/* ------------------------------------------------------------------------- */
+
+/* Cache of one layer. Device arrays are caller-owned; n and len live on the
+ * host and are advanced by the library (deterministically, no readback).
+ * Every head holds the same number n of valid slots (0 .. n-1); slot order is
+ * arbitrary (eviction moves the last slots into the freed ones). */
+typedef struct {
+  void* k;        /* [B, H, cap, D] cached keys, contiguous                  */
+  void* v;        /* [B, H, cap, D] cached values, contiguous                */
+  int32_t* pos;   /* [B, H, cap] absolute position of each cached token       */
+  float* acc;     /* [B, H, cap] cumulative attention score of each token     */
+  int B, H, D, cap;
+  int n;          /* valid slots per head                                     */
+  int64_t len;    /* tokens seen so far (positions 0 .. len-1)                */
+  kvc_dtype dt;
+} kvc_h2o_cache;
+
+/* One decode step for every head (H2O page, processing flow and what is kept):
+ *   - the new token (position len) is appended with score 0;
+ *   - the new query attends, scores q.k / sqrt(D), softmax over all n+1 cached
+ *     tokens; each token's probability is added to its score; if attn_out is
+ *     not NULL, attn_out = sum_j p_j v_j (float32, [B, H, D], contiguous);
+ *   - with length = len+1, tokens at positions >= length - n_recent are recent;
+ *     when n+1 > n_heavy + n_recent, every recent token is kept and the rest
+ *     of the budget n_heavy + n_recent goes to the other tokens with the
+ *     largest score (equal scores: newer position kept).
+ * On return c->len has grown by one and c->n = min(n+1, n_heavy + n_recent).
+ * q, k_new, v_new: [B, H, D] contiguous, element type c->dt.
+ * Requires n+1 <= cap, cap <= 8192, n_heavy >= 0, n_recent >= 0. */
+kvc_status kvc_h2o_step(kvc_h2o_cache* c, const void* q, const void* k_new,
+                        const void* v_new, int n_heavy, int n_recent,
+                        float* attn_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* StreamingLLM sink + recent ring, one new token.                            */
+/* ------------------------------------------------------------------------- */
+
+/* Write the new token's key/value into the cache and report what it holds
+ * (StreamingLLM page, cache structure and inference flow).
+ *
+ * The cache has n_sink sink slots followed by a ring of n_recent slots; the
+ * token at position p lives in slot p if p < n_sink, else in slot
+ * n_sink + (p - n_sink) mod n_recent. `len` counts tokens including the new
+ * one, whose position is len-1.
+ * ring_k, ring_v  [B, H, n_sink+n_recent, D] contiguous.
+ * k_new, v_new    [B, H, D] contiguous.
+ * slot_pos        [n_sink+n_recent] int32, shared by all heads: the position
+ *                 now held by each slot is updated for the new token's slot.
+ * kept_idx_out    optional [min(len, n_sink+n_recent)] int32: the held
+ *                 positions, ascending (sinks 0 .. min(n_sink,len)-1, then
+ *                 max(n_sink, len-n_recent) .. len-1).
+ * Requires len >= 1, n_sink >= 0, n_recent >= 1. */
+kvc_status kvc_sink_recent(void* ring_k, void* ring_v, int32_t* slot_pos,
+                           const void* k_new, const void* v_new, int64_t len,
+                           int n_sink, int n_recent, int B, int H, int D,
+                           kvc_dtype dt, int32_t* kept_idx_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,225 @@
+"""kvc: attention-score-guided KV-cache selection and compaction on AMD MI355X.
+
+Python binding of ``libkvc.so`` (the HIP kernels behind the C ABI declared in
+``include/kvc.h``). This module only marshals arguments: it takes torch device
+tensors, passes their pointers, strides and the current HIP stream to the
+library, and allocates outputs and workspaces with torch. Every step of the
+computation runs in the library's kernels. There is no CPU fallback: when the
+library is missing or a call fails, an exception is raised.
+
+Entry points (same names as the C ABI, without the ``kvc_`` prefix):
+  snapkv_compress     SnapKV prompt compression of one layer
+  snapkv_workspace_bytes
+  H2OCache.step       H2O decode step (kvc_h2o_step)
+  SinkCache.append    StreamingLLM sink + recent ring (kvc_sink_recent)
+"""
+import ctypes
+import os
+from collections import namedtuple
+
+import torch
+
+__all__ = [
+    "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
+    "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS",
+]
+
+KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
+KVC_F32, KVC_BF16 = 0, 1
+_STATUS_NAMES = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
+
+EXPORTED_SYMBOLS = (
+    "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
+    "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.path.join(_HERE, "libkvc.so")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"kvc {_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("t", ctypes.c_int64)]
+
+
+class _H2OCacheC(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+        ("acc", ctypes.c_void_p), ("B", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int),
+        ("cap", ctypes.c_int), ("n", ctypes.c_int), ("len", ctypes.c_int64), ("dt", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def library():
+    """Load libkvc.so (built in-tree by ``python -m kv_cache_compression_02_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with python -m kv_cache_compression_02_amd.build")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.kvc_last_error.restype = ctypes.c_char_p
+    L.kvc_last_error.argtypes = []
+    L.kvc_version.restype = i32
+    L.kvc_version.argtypes = []
+    L.kvc_snapkv_workspace_bytes.restype = sz
+    L.kvc_snapkv_workspace_bytes.argtypes = [i32] * 7 + [i32]
+    L.kvc_snapkv_compress.restype = i32
+    L.kvc_snapkv_compress.argtypes = [
+        vp, i32, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kvc_h2o_step.restype = i32
+    L.kvc_h2o_step.argtypes = [ctypes.POINTER(_H2OCacheC), vp, vp, vp, i32, i32, vp, vp]
+    L.kvc_snapkv_set_phase_events.restype = None
+    L.kvc_snapkv_set_phase_events.argtypes = [vp, i32]
+    L.kvc_sink_recent.restype = i32
+    L.kvc_sink_recent.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != KVC_OK:
+        raise KvcError(status, library().kvc_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last (head_dim) axis must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _strides4(t):
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, dtype):
+    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    return int(library().kvc_snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, code))
+
+
+SnapKVResult = namedtuple("SnapKVResult", "k v idx pooled vote")
+
+
+def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,
+                    workspace=None, out=None):
+    """SnapKV compression of one layer (kvc_snapkv_compress).
+
+    q: [B, H, q_len, D] (last ``window`` rows used); k, v: [B, H, L, D] with the same
+    strides; bf16 or fp32 on the GPU. Returns SnapKVResult(k [B,H,budget,D],
+    v [B,H,budget,D], idx int32 [B,H,budget-window], pooled, vote) where pooled/vote
+    are float32 [B,H,L-window] or None. ``workspace`` (uint8 tensor) and ``out``
+    (a SnapKVResult of preallocated tensors) may be passed to avoid allocations.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be 4-D [B, H, T, D]")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, L, D = k.shape
+    dt = _dtype_code(k)
+    dev = k.device
+    if out is None:
+        k_out = torch.empty((B, H, budget, D), dtype=k.dtype, device=dev)
+        v_out = torch.empty_like(k_out)
+        idx = torch.empty((B, H, max(budget - window, 0)), dtype=torch.int32, device=dev)
+        pooled = torch.empty((B, H, L - window), dtype=torch.float32, device=dev) if want_pooled else None
+        vote = torch.empty((B, H, L - window), dtype=torch.float32, device=dev) if want_vote else None
+    else:
+        k_out, v_out, idx, pooled, vote = out
+    if workspace is None:
+        nbytes = snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, k.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(library().kvc_snapkv_compress(
+        _ptr(q), q.shape[2], _strides4(q), _ptr(k), _ptr(v), _strides4(k), B, H, L, D,
+        window, budget, pool_kernel, dt, _ptr(k_out), _ptr(v_out), _ptr(idx), _ptr(pooled),
+        _ptr(vote), _ptr(workspace), workspace.numel(), _stream()))
+    return SnapKVResult(k_out, v_out, idx, pooled, vote)
+
+
+class H2OCache:
+    """Device-resident H2O cache of one layer (kvc_h2o_cache) and its step call."""
+
+    def __init__(self, B, H, D, cap, dtype=torch.bfloat16, device="cuda"):
+        self.k = torch.zeros((B, H, cap, D), dtype=dtype, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.pos = torch.full((B, H, cap), -1, dtype=torch.int32, device=device)
+        self.acc = torch.zeros((B, H, cap), dtype=torch.float32, device=device)
+        self._c = _H2OCacheC(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(),
+                             self.acc.data_ptr(), B, H, D, cap, 0, 0, _dtype_code(self.k))
+
+    @property
+    def n(self):
+        return self._c.n
+
+    @property
+    def length(self):
+        return self._c.len
+
+    def step(self, q, k_new, v_new, n_heavy, n_recent, attn_out=None):
+        """One decode step for every head; q, k_new, v_new: [B, H, D] contiguous."""
+        for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+            _dev(t, n)
+            if not t.is_contiguous() or t.dtype != self.k.dtype:
+                raise ValueError(f"{n} must be contiguous with the cache's dtype")
+        _check(library().kvc_h2o_step(ctypes.byref(self._c), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                      n_heavy, n_recent, _ptr(attn_out), _stream()))
+        return attn_out
+
+
+class SinkCache:
+    """StreamingLLM sink + recent ring of one layer (kvc_sink_recent)."""
+
+    def __init__(self, B, H, D, n_sink, n_recent, dtype=torch.bfloat16, device="cuda"):
+        self.B, self.H, self.D = B, H, D
+        self.n_sink, self.n_recent = n_sink, n_recent
+        slots = n_sink + n_recent
+        self.k = torch.zeros((B, H, slots, D), dtype=dtype, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.slot_pos = torch.full((slots,), -1, dtype=torch.int32, device=device)
+        self.kept = torch.empty((slots,), dtype=torch.int32, device=device)
+        self.length = 0
+
+    def append(self, k_new, v_new):
+        """Write one new token ([B, H, D] contiguous); return the held positions, ascending."""
+        self.length += 1
+        n_kept = min(self.length, self.n_sink + self.n_recent)
+        _check(library().kvc_sink_recent(
+            _ptr(self.k), _ptr(self.v), _ptr(self.slot_pos), _ptr(k_new), _ptr(v_new),
+            self.length, self.n_sink, self.n_recent, self.B, self.H, self.D,
+            _dtype_code(self.k), _ptr(self.kept), _stream()))
+        return self.kept[:n_kept]

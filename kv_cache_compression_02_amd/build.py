@@ -1,0 +1,52 @@
+"""Build libkvc.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
+
+Usage: python -m kv_cache_compression_02_amd.build
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkvc.so")
+SOURCES = ["api.hip", "snapkv.hip", "h2o.hip", "sink.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def command(out=LIB, extra=()):
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed fp32 instructions are left to the compiler's scalar forms only
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-result", "-Werror=return-type",
+        "-I", INCLUDE, "-I", CSRC,
+        *[os.path.join(CSRC, s) for s in SOURCES], *extra,
+        "-o", out,
+    ]
+
+
+def build(verbose=True):
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,788 @@
+// SnapKV prompt-KV selection and compaction on gfx950.
+//
+// The method (abeam.tech summary of "SnapKV: LLM Knows What You are Looking
+// for Before Generation", section 技術の仕組み › 処理の流れ, steps 1-4): the last
+// `w` prompt queries attend to the prompt; for every prefix position the
+// softmax weights it receives from those queries are summed per head (the
+// vote); the votes are smoothed by a 1D max-pool; each head keeps its
+// top-scoring prefix positions and their K/V rows are concatenated with the
+// window's own rows.
+//
+// Kernel sequence per call (all on the caller's stream, no host sync):
+//   zero      clear per-head counters and histograms in the workspace
+//   stats     window scores q.k/sqrt(D) on MFMA (bf16) or VALU (fp32) for a
+//             chunk of keys; per-row running max / sum of 2^(s - m); the last
+//             workgroup of a head to finish merges the chunk partials into the
+//             row max and 1/sum (two-pass softmax, pass 1)
+//   votes     recompute the scores of the prefix keys, normalise with the merged
+//             row statistics and sum over the window rows (pass 2)
+//   pool_hist max-pool the votes of a chunk (halo from the neighbours) and
+//             histogram the top 12 bits of the pooled values per head
+//   classify  find the histogram bin that holds the k-th largest pooled score;
+//             emit positions above that bin (kept for sure) and the bin's
+//             members (candidates) to per-head lists
+//   finalize  radix-select the remaining picks among the candidates on the key
+//             (score desc, position asc); mark the kept positions in a bitmap
+//             and compact it into ascending positions
+//   gather    copy the kept K/V rows and the window rows into the outputs
+//
+// Scores live in the base-2 domain: s2 = (q.k) * log2(e)/sqrt(D), so the
+// softmax is 2^(s2 - m2) / sum; it equals exp(s - m)/sum exactly in real
+// arithmetic.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kTile = 32;            // keys per MFMA tile (the 32x32 output's N or M side)
+constexpr int kThreads = 256;        // workgroup size of the streaming kernels
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunkMfma = 1024;     // keys per workgroup, bf16 MFMA path
+constexpr int kChunkF32 = 256;       // keys per workgroup, fp32 path (a key per thread)
+constexpr int kMaxWindow = 32;
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 19;       // pooled >= 0: bits 30..19 = exponent + 4 mantissa bits
+constexpr int kPoolChunk = 4096;     // votes per workgroup in pool_hist / classify
+constexpr int kMaxPoolRadius = 32;
+constexpr int kFinThreads = 1024;
+constexpr int kCandLds = 4096;       // candidates staged in LDS by finalize
+constexpr int kBitmapLds = 16384;    // bitmap words kept in LDS (N <= 524288)
+constexpr float kNegBig = -1.0e30f;  // "no score" sentinel: 2^(kNegBig - m) == 0
+
+// ------------------------------------------------------------------ loaders
+
+// The lane's contiguous half row: elements [half*D/2, half*D/2 + D/2) as D/16
+// MFMA k-step fragments of 8 bf16. The contraction index is permuted the same
+// way for Q and K, so the dot product is unchanged while each lane reads one
+// contiguous 64/128-byte run.
+template <int D>
+__device__ __forceinline__ void load_half_row(const uint16_t* p, bf16x8_t (&f)[D / 16]) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, src[s]);
+}
+
+template <int D>
+__device__ __forceinline__ void zero_frag(bf16x8_t (&f)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+}
+
+// Row m of the 32x32 MFMA accumulator held in register r of a lane in half `half`.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// ------------------------------------------------------- row-stat merging
+
+// Called by every thread after this workgroup wrote its partial (m, l) for the
+// 32 window rows. The last workgroup of head `bh` to arrive merges all
+// partials into stat[bh][row] = (m2, 1/l) and re-arms the arrival counter.
+__device__ void merge_row_stats(int bh, int nchunk, const float2* part, float2* stat,
+                                unsigned* arrive) {
+  __shared__ unsigned s_last;
+  __shared__ float2 red[kThreads / 32][32];
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(&arrive[bh], 1u) == static_cast<unsigned>(nchunk - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int row = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const volatile float* pv = reinterpret_cast<const volatile float*>(part);
+  float m = kNegBig, l = 0.f;
+  for (int c = grp; c < nchunk; c += kThreads / 32) {
+    const int64_t o = ((static_cast<int64_t>(bh) * nchunk + c) * 32 + row) * 2;
+    lse2_merge(m, l, pv[o], pv[o + 1]);
+  }
+  red[grp][row] = make_float2(m, l);
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float mm = red[0][row].x, ll = red[0][row].y;
+#pragma unroll
+    for (int g = 1; g < kThreads / 32; ++g) lse2_merge(mm, ll, red[g][row].x, red[g][row].y);
+    stat[bh * 32 + row] = make_float2(mm, 1.f / ll);
+  }
+  if (threadIdx.x == 0) arrive[bh] = 0;
+}
+
+// ------------------------------------------------------------ zero fill
+
+__global__ void fill_u32(unsigned* p, int64_t n, unsigned value) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = value;
+}
+
+// ------------------------------------------------ pass 1: row statistics
+
+// bf16, MFMA 32x32x16. Output orientation S^T: M = keys of the tile, N = the 32
+// window queries, so each lane owns one query (lane & 31) and 16 keys, and the
+// per-query running (max, sum) stays in registers.
+template <int D>
+__global__ __launch_bounds__(kThreads) void snap_stats_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
+    int nchunk, float scale_log2, float2* __restrict__ part, float2* __restrict__ stat,
+    unsigned* __restrict__ arrive) {
+  constexpr int KS = D / 16;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 31, half = lane >> 5;
+  const int t0 = L - w;
+
+  bf16x8_t qf[KS];
+  if (col < w)
+    load_half_row<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + col) * qst + half * (D / 2), qf);
+  else
+    zero_frag<D>(qf);
+
+  const uint16_t* kb = k + b * ksb + h * ksh + half * (D / 2);
+  const int key0 = chunk * kChunkMfma;
+  const int key1 = min(L, key0 + kChunkMfma);
+  constexpr int kStep = kWaves * kTile;
+  float m_run = kNegBig, l_run = 0.f;
+
+  int tile = key0 + wave * kTile;
+  bf16x8_t kf[KS];
+  if (tile < key1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, L - 1)) * kst, kf);
+  for (; tile < key1; tile += kStep) {
+    bf16x8_t kn[KS];
+    const int nt = tile + kStep;
+    if (nt < key1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, L - 1)) * kst, kn);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+    float sv[16];
+    float tmax = kNegBig;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = tile + acc_row(r, half);
+      const bool vis = (j < L) && (j <= t0 + col);  // query col sits at position t0 + col
+      sv[r] = vis ? acc[r] * scale_log2 : kNegBig;
+      tmax = fmaxf(tmax, sv[r]);
+    }
+    const float mnew = fmaxf(m_run, tmax);
+    float add = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) add += fast_exp2(sv[r] - mnew);
+    l_run = l_run * fast_exp2(m_run - mnew) + add;
+    m_run = mnew;
+    if (nt < key1) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[s] = kn[s];
+    }
+  }
+  // lanes col and col+32 hold the same query
+  lse2_merge(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
+  __shared__ float2 wred[kWaves][32];
+  if (half == 0) wred[wave][col] = make_float2(m_run, l_run);
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float m = wred[0][threadIdx.x].x, l = wred[0][threadIdx.x].y;
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) lse2_merge(m, l, wred[i][threadIdx.x].x, wred[i][threadIdx.x].y);
+    part[(static_cast<int64_t>(bh) * nchunk + chunk) * 32 + threadIdx.x] = make_float2(m, l);
+  }
+  merge_row_stats(bh, nchunk, part, stat, arrive);
+}
+
+// fp32, VALU: one key per thread, the window rows in LDS.
+template <int D>
+__global__ __launch_bounds__(kThreads) void snap_stats_f32(
+    const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
+    int nchunk, float scale_log2, float2* __restrict__ part, float2* __restrict__ stat,
+    unsigned* __restrict__ arrive) {
+  __shared__ float qs[kMaxWindow][D];
+  __shared__ float ss[kMaxWindow][kThreads + 1];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = L - w;
+  for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
+    const int r = i / D, d = i - r * D;
+    qs[r][d] = r < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + r) * qst + d] : 0.f;
+  }
+  __syncthreads();
+  const int j = chunk * kChunkF32 + threadIdx.x;
+  const float* kr = k + b * ksb + h * ksh + static_cast<int64_t>(min(j, L - 1)) * kst;
+  float s[kMaxWindow];
+#pragma unroll
+  for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
+  for (int d = 0; d < D; d += 4) {
+    const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + d);
+#pragma unroll
+    for (int i = 0; i < kMaxWindow; ++i)
+      s[i] += qs[i][d] * kv[0] + qs[i][d + 1] * kv[1] + qs[i][d + 2] * kv[2] + qs[i][d + 3] * kv[3];
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxWindow; ++i) {
+    const bool vis = i < w && j < L && j <= t0 + i;
+    ss[i][threadIdx.x] = vis ? s[i] * scale_log2 : kNegBig;
+  }
+  __syncthreads();
+  // 32 rows x 8 segments of 32 keys; the 8 segments of a row are adjacent lanes
+  const int row = threadIdx.x >> 3, seg = threadIdx.x & 7;
+  float m = kNegBig;
+  for (int c = seg * 32; c < seg * 32 + 32; ++c) m = fmaxf(m, ss[row][c]);
+  float l = 0.f;
+  for (int c = seg * 32; c < seg * 32 + 32; ++c) l += fast_exp2(ss[row][c] - m);
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) lse2_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+  if (seg == 0) part[(static_cast<int64_t>(bh) * nchunk + chunk) * 32 + row] = make_float2(m, l);
+  merge_row_stats(bh, nchunk, part, stat, arrive);
+}
+
+// ------------------------------------------------------- pass 2: votes
+
+// bf16, MFMA 32x32x16. Output orientation S: M = the 32 window queries, N =
+// keys, so each lane owns one key (lane & 31) and 16 queries; its vote is a
+// sum over registers plus one exchange with the other half of the wave.
+template <int D>
+__global__ __launch_bounds__(kThreads) void snap_votes_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
+    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote) {
+  constexpr int KS = D / 16;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 31, half = lane >> 5;
+  const int t0 = L - w;
+
+  bf16x8_t qf[KS];
+  if (col < w)
+    load_half_row<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + col) * qst + half * (D / 2), qf);
+  else
+    zero_frag<D>(qf);
+  float mr[16], il[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = acc_row(r, half);
+    if (m < w) {
+      const float2 st = stat[bh * 32 + m];
+      mr[r] = st.x;
+      il[r] = st.y;
+    } else {  // zero query row: score 0, weight 0
+      mr[r] = 0.f;
+      il[r] = 0.f;
+    }
+  }
+
+  const uint16_t* kb = k + b * ksb + h * ksh + half * (D / 2);
+  float* vb = vote + static_cast<int64_t>(bh) * t0;
+  const int key0 = chunk * kChunkMfma;
+  const int key1 = min(t0, key0 + kChunkMfma);
+  constexpr int kStep = kWaves * kTile;
+
+  int tile = key0 + wave * kTile;
+  bf16x8_t kf[KS];
+  if (tile < key1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
+  for (; tile < key1; tile += kStep) {
+    bf16x8_t kn[KS];
+    const int nt = tile + kStep;
+    if (nt < key1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v += fast_exp2(acc[r] * scale_log2 - mr[r]) * il[r];
+    v += __shfl_xor(v, 32);
+    const int j = tile + col;
+    if (half == 0 && j < key1) vb[j] = v;
+    if (nt < key1) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[s] = kn[s];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void snap_votes_f32(
+    const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
+    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote) {
+  __shared__ float qs[kMaxWindow][D];
+  __shared__ float2 st[kMaxWindow];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = L - w;
+  for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
+    const int r = i / D, d = i - r * D;
+    qs[r][d] = r < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + r) * qst + d] : 0.f;
+  }
+  if (threadIdx.x < kMaxWindow) st[threadIdx.x] = threadIdx.x < w ? stat[bh * 32 + threadIdx.x] : make_float2(0.f, 0.f);
+  __syncthreads();
+  const int j = chunk * kChunkF32 + threadIdx.x;
+  if (j >= t0) return;
+  const float* kr = k + b * ksb + h * ksh + static_cast<int64_t>(j) * kst;
+  float s[kMaxWindow];
+#pragma unroll
+  for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
+  for (int d = 0; d < D; d += 4) {
+    const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + d);
+#pragma unroll
+    for (int i = 0; i < kMaxWindow; ++i)
+      s[i] += qs[i][d] * kv[0] + qs[i][d + 1] * kv[1] + qs[i][d + 2] * kv[2] + qs[i][d + 3] * kv[3];
+  }
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxWindow; ++i)
+    if (i < w) v += fast_exp2(s[i] * scale_log2 - st[i].x) * st[i].y;
+  vote[static_cast<int64_t>(bh) * t0 + j] = v;
+}
+
+// ------------------------------------------------ pooling + histogram
+
+__global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restrict__ vote,
+                                                           float* __restrict__ pooled,
+                                                           unsigned* __restrict__ hist, int N, int r) {
+  __shared__ float sv[kPoolChunk + 2 * kMaxPoolRadius];
+  __shared__ unsigned sh[kHistBins];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
+  const int c0 = chunk * kPoolChunk, c1 = min(N, c0 + kPoolChunk);
+  const float* vb = vote + static_cast<int64_t>(bh) * N;
+  const int n_load = (c1 - c0) + 2 * r;
+  for (int i = threadIdx.x; i < n_load; i += kThreads) {
+    const int j = c0 - r + i;
+    sv[i] = (j >= 0 && j < N) ? vb[j] : -INFINITY;  // out-of-range neighbours never win
+  }
+  __syncthreads();
+  float* pb = pooled + static_cast<int64_t>(bh) * N;
+  for (int j = c0 + threadIdx.x; j < c1; j += kThreads) {
+    const float* s = sv + (j - c0);
+    float m = s[0];
+    for (int d = 1; d <= 2 * r; ++d) m = fmaxf(m, s[d]);
+    pb[j] = m;
+    atomicAdd(&sh[(__float_as_uint(m) >> kHistShift) & (kHistBins - 1)], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+    if (sh[i]) atomicAdd(&hist[static_cast<int64_t>(bh) * kHistBins + i], sh[i]);
+}
+
+// ------------------------------------------------------------ classify
+
+// The bin b* holding the k-th largest value: count(bins > b*) < k <= count(bins >= b*).
+// Every thread of the block calls it; results land in *bin / *above.
+__device__ void find_kth_bin(const unsigned* sh, unsigned kk, unsigned* scratch, unsigned* bin,
+                             unsigned* above) {
+  constexpr int kPer = kHistBins / kThreads;
+  const int t = threadIdx.x;
+  unsigned c = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) c += sh[t * kPer + i];
+  unsigned total;
+  const unsigned pre = block_excl_scan<kThreads>(c, scratch, &total);
+  const unsigned higher = total - pre - c;  // members of bins owned by higher threads
+  if (higher < kk && higher + c >= kk) {
+    unsigned run = higher;
+    for (int i = kPer - 1; i >= 0; --i) {
+      const unsigned hb = sh[t * kPer + i];
+      if (run + hb >= kk) {
+        *bin = t * kPer + i;
+        *above = run;
+        break;
+      }
+      run += hb;
+    }
+  }
+  __syncthreads();
+}
+
+// ctr[bh] = {selected count, candidate count, b*, picks left for the candidates}
+__global__ __launch_bounds__(kThreads) void snap_classify(const float* __restrict__ pooled,
+                                                          const unsigned* __restrict__ hist, int N,
+                                                          int kk, unsigned* __restrict__ ctr,
+                                                          int* __restrict__ sel,
+                                                          uint2* __restrict__ cand) {
+  __shared__ unsigned sh[kHistBins];
+  __shared__ unsigned scratch[kWaves + 1];
+  __shared__ unsigned s_bin, s_above;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = hist[static_cast<int64_t>(bh) * kHistBins + i];
+  __syncthreads();
+  find_kth_bin(sh, static_cast<unsigned>(kk), scratch, &s_bin, &s_above);
+  const unsigned bstar = s_bin;
+  if (chunk == 0 && threadIdx.x == 0) {
+    ctr[bh * 4 + 2] = bstar;
+    ctr[bh * 4 + 3] = static_cast<unsigned>(kk) - s_above;
+  }
+  const float* pb = pooled + static_cast<int64_t>(bh) * N;
+  int* sb = sel + static_cast<int64_t>(bh) * kk;
+  uint2* cb = cand + static_cast<int64_t>(bh) * N;
+  const int lane = lane_id();
+  const int c0 = chunk * kPoolChunk, c1 = min(N, c0 + kPoolChunk);
+  for (int base = c0; base < c1; base += kThreads) {
+    const int j = base + threadIdx.x;
+    const bool valid = j < c1;
+    const unsigned u = valid ? __float_as_uint(pb[j]) : 0u;
+    const unsigned bin = (u >> kHistShift) & (kHistBins - 1);
+    const bool is_sel = valid && bin > bstar;
+    const bool is_cand = valid && bin == bstar;
+    const unsigned long long ms = __ballot(is_sel);
+    if (ms) {
+      const int leader = __ffsll(static_cast<long long>(ms)) - 1;
+      unsigned at = 0;
+      if (lane == leader) at = atomicAdd(&ctr[bh * 4 + 0], static_cast<unsigned>(__popcll(ms)));
+      at = __shfl(at, leader) + popc_below(ms);
+      if (is_sel && at < static_cast<unsigned>(kk)) sb[at] = j;
+    }
+    const unsigned long long mc = __ballot(is_cand);
+    if (mc) {
+      const int leader = __ffsll(static_cast<long long>(mc)) - 1;
+      unsigned at = 0;
+      if (lane == leader) at = atomicAdd(&ctr[bh * 4 + 1], static_cast<unsigned>(__popcll(mc)));
+      at = __shfl(at, leader) + popc_below(mc);
+      if (is_cand && at < static_cast<unsigned>(N)) cb[at] = make_uint2(u, static_cast<unsigned>(j));
+    }
+  }
+}
+
+// ------------------------------------------------------------ finalize
+
+// Candidate order key: larger score first, then lower position first.
+__device__ __forceinline__ unsigned long long cand_key(uint2 c) {
+  return (static_cast<unsigned long long>(c.x) << 32) | static_cast<unsigned long long>(~c.y);
+}
+
+__device__ __forceinline__ unsigned load_word(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kFinThreads) void snap_finalize(const unsigned* __restrict__ ctr,
+                                                             const int* __restrict__ sel,
+                                                             const uint2* __restrict__ cand, int N,
+                                                             int kk, unsigned* __restrict__ bitmap_g,
+                                                             int* __restrict__ idx_out) {
+  __shared__ uint2 cl[kCandLds];
+  __shared__ unsigned bm_lds[kBitmapLds];
+  __shared__ unsigned dh[256];
+  __shared__ unsigned scratch[kFinThreads / kWave + 1];
+  __shared__ unsigned s_digit, s_above;
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const unsigned n_sel = min(ctr[bh * 4 + 0], static_cast<unsigned>(kk));
+  const unsigned n_cand = min(ctr[bh * 4 + 1], static_cast<unsigned>(N));
+  unsigned rem = ctr[bh * 4 + 3];
+  const int words = (N + 31) >> 5;
+  unsigned* bm = words <= kBitmapLds ? bm_lds : bitmap_g + static_cast<int64_t>(bh) * words;
+  for (int i = tid; i < words; i += kFinThreads) bm[i] = 0;
+
+  const uint2* cg = cand + static_cast<int64_t>(bh) * N;
+  const bool in_lds = n_cand <= static_cast<unsigned>(kCandLds);
+  if (in_lds)
+    for (unsigned i = tid; i < n_cand; i += kFinThreads) cl[i] = cg[i];
+  __syncthreads();
+  const uint2* src = in_lds ? cl : cg;
+
+  // radix select, 8 bits at a time from the top, of the rem-th largest key
+  unsigned long long prefix = 0, pmask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) dh[tid] = 0;
+    __syncthreads();
+    for (unsigned i = tid; i < n_cand; i += kFinThreads) {
+      const unsigned long long key = cand_key(src[i]);
+      if ((key & pmask) == prefix) atomicAdd(&dh[(key >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane owns digits [4*lane, 4*lane+4); suffix counts from the top digit
+      unsigned c4[4], c = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = dh[4 * tid + i];
+        c += c4[i];
+      }
+      const unsigned incl = wave_incl_scan(c);
+      const unsigned total = __shfl(incl, kWave - 1);
+      const unsigned higher = total - incl;  // digits owned by higher lanes
+      if (higher < rem && higher + c >= rem) {
+        unsigned run = higher;
+        for (int i = 3; i >= 0; --i) {
+          if (run + c4[i] >= rem) {
+            s_digit = 4 * tid + i;
+            s_above = run;
+            break;
+          }
+          run += c4[i];
+        }
+      }
+    }
+    __syncthreads();
+    rem -= s_above;
+    prefix |= static_cast<unsigned long long>(s_digit) << shift;
+    pmask |= 0xFFull << shift;
+    __syncthreads();
+  }
+  // prefix is now the exact key of the last candidate to keep
+  for (unsigned i = tid; i < n_sel; i += kFinThreads) {
+    const int j = sel[static_cast<int64_t>(bh) * kk + i];
+    if (j >= 0 && j < N) atomicOr(&bm[j >> 5], 1u << (j & 31));
+  }
+  for (unsigned i = tid; i < n_cand; i += kFinThreads) {
+    const uint2 c = src[i];
+    if (cand_key(c) >= prefix && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ordered compaction of the bitmap into ascending positions
+  const int wpt = (words + kFinThreads - 1) / kFinThreads;
+  const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
+  unsigned cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(load_word(&bm[i]));
+  unsigned total;
+  unsigned off = block_excl_scan<kFinThreads>(cnt, scratch, &total);
+  int* out = idx_out + static_cast<int64_t>(bh) * kk;
+  for (int i = w0; i < w1; ++i) {
+    unsigned wv = load_word(&bm[i]);
+    while (wv) {
+      const int bit = __ffs(wv) - 1;
+      if (off < static_cast<unsigned>(kk)) out[off] = i * 32 + bit;
+      ++off;
+      wv &= wv - 1;
+    }
+  }
+}
+
+// -------------------------------------------------------------- gather
+
+// One 16-byte piece of one output row per thread; K and V together.
+__global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__ k,
+                                                        const char* __restrict__ v, int64_t sb,
+                                                        int64_t sh, int64_t st, int H, int L, int w,
+                                                        int C, int kk, int vec_per_row,
+                                                        const int* __restrict__ idx,
+                                                        char* __restrict__ k_out,
+                                                        char* __restrict__ v_out) {
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int row = static_cast<int>(t / vec_per_row);
+  const int vc = static_cast<int>(t - static_cast<int64_t>(row) * vec_per_row);
+  if (row >= C) return;
+  int src = row < kk ? idx[static_cast<int64_t>(bh) * kk + row] : (L - w + (row - kk));
+  src = min(max(src, 0), L - 1);
+  const int64_t so = b * sb + h * sh + static_cast<int64_t>(src) * st + static_cast<int64_t>(vc) * 16;
+  const int64_t dof = (static_cast<int64_t>(bh) * C + row) * (static_cast<int64_t>(vec_per_row) * 16) +
+                      static_cast<int64_t>(vc) * 16;
+  const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(k + so);
+  const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(v + so);
+  *reinterpret_cast<u32x4_t*>(k_out + dof) = kx;
+  *reinterpret_cast<u32x4_t*>(v_out + dof) = vx;
+}
+
+// ------------------------------------------------------ workspace layout
+
+struct SnapLayout {
+  int64_t BH;
+  int N, kk, nchunk, words;
+  size_t arrive, ctr, hist, zero_bytes;
+  size_t part, stat, vote, pooled, sel, cand, bitmap, total;
+};
+
+bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, SnapLayout* o) {
+  (void)D;
+  if (B <= 0 || H <= 0 || L <= 0 || w <= 0 || budget <= w || budget >= L) return false;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  o->BH = BH;
+  o->N = L - w;
+  o->kk = budget - w;
+  const int chunk = dt == KVC_BF16 ? kChunkMfma : kChunkF32;
+  o->nchunk = (L + chunk - 1) / chunk;
+  o->words = (o->N + 31) / 32;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  // The first three regions are cleared at the start of every call.
+  o->arrive = off;
+  off += BH * 4;
+  o->ctr = off;
+  off += BH * 16;
+  o->hist = off;
+  off += BH * kHistBins * 4;
+  o->zero_bytes = off;
+  off = align_up(off, 256);
+  o->part = take(static_cast<size_t>(BH) * o->nchunk * 32 * 8);
+  o->stat = take(static_cast<size_t>(BH) * 32 * 8);
+  o->vote = take(static_cast<size_t>(BH) * o->N * 4);
+  o->pooled = take(static_cast<size_t>(BH) * o->N * 4);
+  o->sel = take(static_cast<size_t>(BH) * o->kk * 4);
+  o->cand = take(static_cast<size_t>(BH) * o->N * 8);
+  o->bitmap = take(static_cast<size_t>(BH) * o->words * 4);
+  o->total = off;
+  return true;
+}
+
+// Optional per-phase timing events (see kvc_snapkv_set_phase_events).
+thread_local hipEvent_t* g_phase_events = nullptr;
+thread_local int g_phase_count = 0;
+
+void mark_phase(int i, hipStream_t stream) {
+  if (g_phase_events && i < g_phase_count) (void)hipEventRecord(g_phase_events[i], stream);
+}
+
+template <int D>
+void launch_stats(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int qrow0, const uint16_t* k,
+                  kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
+  const dim3 g(lay.nchunk, static_cast<unsigned>(lay.BH));
+  snap_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
+                                                lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
+                                                reinterpret_cast<float2*>(ws + lay.stat),
+                                                reinterpret_cast<unsigned*>(ws + lay.arrive));
+}
+
+template <int D>
+void launch_stats(const SnapLayout& lay, const float* q, kvc_strides qs, int qrow0, const float* k,
+                  kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
+  const dim3 g(lay.nchunk, static_cast<unsigned>(lay.BH));
+  snap_stats_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
+                                               lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
+                                               reinterpret_cast<float2*>(ws + lay.stat),
+                                               reinterpret_cast<unsigned*>(ws + lay.arrive));
+}
+
+template <int D>
+void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int qrow0, const uint16_t* k,
+                  kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, float* vote,
+                  hipStream_t stream) {
+  const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
+  snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
+                                                scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote);
+}
+
+template <int D>
+void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qrow0, const float* k,
+                  kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, float* vote,
+                  hipStream_t stream) {
+  const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
+  snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
+                                               scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote);
+}
+
+// Pass 1 (row statistics) then pass 2 (votes), with phase marks 2 and 3.
+template <typename T>
+void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int qrow0, const T* k,
+                         kvc_strides kvs, int H, int L, int D, int w, float scale_log2, char* ws, float* vote,
+                         hipStream_t stream) {
+  if (D == 128)
+    launch_stats<128>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
+  else
+    launch_stats<64>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
+  mark_phase(2, stream);
+  if (D == 128)
+    launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, vote, stream);
+  else
+    launch_votes<64>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, vote, stream);
+  mark_phase(3, stream);
+}
+
+}  // namespace
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
+                                             int pool_kernel, kvc_dtype dt) {
+  (void)pool_kernel;
+  SnapLayout lay;
+  if (!snap_layout(B, H, L, D, window, budget, dt, &lay)) return 0;
+  return lay.total;
+}
+
+extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs, const void* k,
+                                          const void* v, kvc_strides kvs, int B, int H, int L, int D,
+                                          int window, int budget, int pool_kernel, kvc_dtype dt,
+                                          void* k_out, void* v_out, int32_t* idx_out,
+                                          float* pooled_out, float* vote_out, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (!q || !k || !v || !k_out || !v_out || !idx_out)
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: q, k, v, k_out, v_out and idx_out must be non-NULL");
+  if (dt != KVC_BF16 && dt != KVC_F32) return fail(KVC_ERR_INVALID_ARG, "snapkv: unknown dtype %d", (int)dt);
+  if (B <= 0 || H <= 0 || L <= 0) return fail(KVC_ERR_INVALID_ARG, "snapkv: B, H, L must be positive");
+  if (static_cast<int64_t>(B) * H > 65535) return fail(KVC_ERR_UNSUPPORTED, "snapkv: B*H must be <= 65535");
+  if (window < 1 || window >= budget || budget >= L)
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: need 1 <= window < budget < L (window=%d budget=%d L=%d)",
+                window, budget, L);
+  if (window > kMaxWindow) return fail(KVC_ERR_UNSUPPORTED, "snapkv: window %d > %d", window, kMaxWindow);
+  if (pool_kernel < 1 || pool_kernel % 2 == 0)
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: pool_kernel must be odd and >= 1 (got %d)", pool_kernel);
+  if (pool_kernel / 2 > kMaxPoolRadius)
+    return fail(KVC_ERR_UNSUPPORTED, "snapkv: pool_kernel %d > %d", pool_kernel, 2 * kMaxPoolRadius + 1);
+  if (q_len < window) return fail(KVC_ERR_INVALID_ARG, "snapkv: q_len %d < window %d", q_len, window);
+  if (D != 64 && D != 128) return fail(KVC_ERR_UNSUPPORTED, "snapkv: head_dim %d not in {64, 128}", D);
+  const int64_t es = dt == KVC_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: device pointers must be 16-byte aligned");
+  const int64_t strides[6] = {qs.b, qs.h, qs.t, kvs.b, kvs.h, kvs.t};
+  for (int64_t s : strides)
+    if (s < 0 || (s * es) % 16 != 0)
+      return fail(KVC_ERR_INVALID_ARG, "snapkv: strides must be non-negative and multiples of 16 bytes");
+  if (kvs.t < D || qs.t < D)
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: row strides must be >= head_dim (D axis contiguous)");
+  SnapLayout lay;
+  snap_layout(B, H, L, D, window, budget, dt, &lay);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(KVC_ERR_WORKSPACE, "snapkv: workspace of %zu bytes needed, got %zu", lay.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(KVC_ERR_INVALID_ARG, "snapkv: workspace must be 16-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D)));
+  float* vote = vote_out ? vote_out : reinterpret_cast<float*>(ws + lay.vote);
+  float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(ws + lay.pooled);
+  unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
+  unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
+  const int qrow0 = q_len - window;
+
+  mark_phase(0, stream);
+  fill_u32<<<64, 256, 0, stream>>>(reinterpret_cast<unsigned*>(ws + lay.arrive),
+                                   static_cast<int64_t>(lay.zero_bytes / 4), 0u);
+  mark_phase(1, stream);
+  if (dt == KVC_BF16)
+    launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0, static_cast<const uint16_t*>(k),
+                                  kvs, H, L, D, window, scale_log2, ws, vote, stream);
+  else
+    launch_score_passes<float>(lay, static_cast<const float*>(q), qs, qrow0, static_cast<const float*>(k), kvs, H,
+                               L, D, window, scale_log2, ws, vote, stream);
+  kvc_status st = check_launch("snapkv score passes");
+  if (st != KVC_OK) return st;
+
+  const dim3 gp((lay.N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(lay.BH));
+  snap_pool_hist<<<gp, kThreads, 0, stream>>>(vote, pooled, hist, lay.N, pool_kernel / 2);
+  mark_phase(4, stream);
+  snap_classify<<<gp, kThreads, 0, stream>>>(pooled, hist, lay.N, lay.kk, ctr,
+                                             reinterpret_cast<int*>(ws + lay.sel),
+                                             reinterpret_cast<uint2*>(ws + lay.cand));
+  mark_phase(5, stream);
+  snap_finalize<<<static_cast<unsigned>(lay.BH), kFinThreads, 0, stream>>>(
+      ctr, reinterpret_cast<const int*>(ws + lay.sel), reinterpret_cast<const uint2*>(ws + lay.cand), lay.N,
+      lay.kk, reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
+  mark_phase(6, stream);
+  st = check_launch("snapkv selection");
+  if (st != KVC_OK) return st;
+
+  const int vec_per_row = static_cast<int>(D * es / 16);
+  const int64_t pieces = static_cast<int64_t>(budget) * vec_per_row;
+  const dim3 gg(static_cast<unsigned>((pieces + kThreads - 1) / kThreads), static_cast<unsigned>(lay.BH));
+  snap_gather<<<gg, kThreads, 0, stream>>>(static_cast<const char*>(k), static_cast<const char*>(v),
+                                           kvs.b * es, kvs.h * es, kvs.t * es, H, L, window, budget, lay.kk,
+                                           vec_per_row, idx_out, static_cast<char*>(k_out),
+                                           static_cast<char*>(v_out));
+  mark_phase(7, stream);
+  return check_launch("snapkv gather");
+}
+
+extern "C" void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events) {
+  g_phase_events = n_events > 0 ? events : nullptr;
+  g_phase_count = n_events > 0 ? n_events : 0;
+}

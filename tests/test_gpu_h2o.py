@@ -1,0 +1,170 @@
+"""GPU parity of kvc_h2o_step (through the C ABI) against the CPU oracle.
+
+The GPU and the oracle run independent trajectories from the same seeded
+inputs. After every step the kept position set, the running scores (matched by
+position) and the attention output are compared per head. A head whose kept
+set differs is accepted only if the oracle's eviction at that step was a
+near-tie (last kept and first evicted score within REL relative) and the GPU's
+choice is valid within that tolerance; the head is then no longer compared,
+since its future legitimately depends on the tie.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_02_amd as kvc
+import synthetic as syn
+from oracle import h2o as ref
+from tests import parity as par
+
+pytestmark = pytest.mark.gpu
+
+
+def _widen(x, dtype):
+    if dtype == "bf16":
+        return (np.asarray(x, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.asarray(x, np.float32).astype(np.float64)
+
+
+def _eviction_gap(pre, p, length, hh, r):
+    """(last kept score, first evicted score) of the oracle's step, or None."""
+    pos = np.append(pre.pos, length - 1)
+    acc = np.append(pre.acc, 0.0) + p
+    n = len(pos)
+    if n <= hh + r:
+        return None
+    recent = pos >= length - r
+    cand = np.flatnonzero(~recent)
+    n_fill = hh + r - int(recent.sum())
+    order = cand[np.lexsort((-pos[cand], -acc[cand]))]
+    a_keep = acc[order[n_fill - 1]] if n_fill > 0 else np.inf
+    a_ev = acc[order[n_fill]]
+    return a_keep, a_ev, dict(zip(pos.tolist(), acc.tolist()))
+
+
+class SideBySide:
+    """Runs the GPU cache and one oracle state per compared head side by side."""
+
+    def __init__(self, B, H, D, cap, dtype, heads):
+        self.gpu = kvc.H2OCache(B, H, D, cap, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+        self.dtype = dtype
+        self.heads = heads
+        self.states = {bh: ref.HeadState(np.zeros(0, np.int64), np.zeros(0),
+                                         np.zeros((0, D), np.uint16 if dtype == "bf16" else np.float32),
+                                         np.zeros((0, D), np.uint16 if dtype == "bf16" else np.float32))
+                       for bh in heads}
+        self.live = set(heads)
+        self.diverged = {}
+        self.out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+
+    def step(self, qn, kn, vn, hh, r):
+        q, k, v = (par.to_device(x, self.dtype) for x in (qn, kn, vn))
+        self.gpu.step(q, k, v, hh, r, attn_out=self.out)
+        length = self.gpu.length
+        n = self.gpu.n
+        pos_g = self.gpu.pos[..., :n].cpu().numpy()
+        acc_g = self.gpu.acc[..., :n].cpu().numpy()
+        out_g = self.out.cpu().numpy()
+        for bh in list(self.live):
+            b, h = bh
+            pre = self.states[bh]
+            st, p, o = ref.step_head(pre, qn[b, h], kn[b, h], vn[b, h], length, hh, r, self.dtype)
+            self.states[bh] = st
+            gpos = pos_g[b, h]
+            assert len(gpos) == len(st), f"{bh} step {length}: count {len(gpos)} vs {len(st)}"
+            assert len(np.unique(gpos)) == len(gpos), f"{bh}: duplicate positions"
+            v_all = _widen(np.concatenate([pre.v, vn[b, h][None]]), self.dtype)
+            par.assert_close_votes(out_g[b, h], o, f"o{bh}@{length}", scale=p @ np.abs(v_all))
+            if set(gpos.tolist()) != set(st.pos.tolist()):
+                gap = _eviction_gap(pre, p, length, hh, r)
+                assert gap is not None, f"{bh} step {length}: sets differ without eviction"
+                a_keep, a_ev, acc_all = gap
+                assert a_keep - a_ev <= par.REL * abs(a_keep), (
+                    f"{bh} step {length}: kept sets differ across a clear gap {a_keep} vs {a_ev}")
+                for j in set(gpos.tolist()) ^ set(st.pos.tolist()):
+                    aj = acc_all[j]
+                    assert a_ev * (1 - par.REL) <= aj <= a_keep * (1 + par.REL), f"{bh}: invalid pick {j}"
+                self.diverged[bh] = length
+                self.live.discard(bh)
+                continue
+            order = np.argsort(gpos)
+            par.assert_close_votes(acc_g[b, h][order], st.acc[np.argsort(st.pos)], f"acc{bh}@{length}")
+
+
+def _stream(wl, steps_after_prompt):
+    """Token stream: the prompt tokens in order, then fresh decode tokens."""
+    B, H = wl.B, wl.H
+    prompt = [syn.h2o_prompt_head(wl, b, h) for b in range(B) for h in range(H)]
+    for t in range(wl.prompt_len):
+        q = np.stack([prompt[i][0][t] for i in range(B * H)]).reshape(B, H, wl.D)
+        k = np.stack([prompt[i][1][t] for i in range(B * H)]).reshape(B, H, wl.D)
+        v = np.stack([prompt[i][2][t] for i in range(B * H)]).reshape(B, H, wl.D)
+        yield q, k, v
+    for s in range(steps_after_prompt):
+        yield syn.h2o_step_inputs(wl, s)
+
+
+def _run(wl, steps_after_prompt, heads=None, policy=None):
+    heads = heads or [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    final = wl.prompt_len + steps_after_prompt
+    policy = policy or (lambda length: (wl.n_heavy(length), wl.n_recent(length)))
+    cap = max(policy(t)[0] + policy(t)[1] for t in range(1, final + 1)) + 1
+    print(f"[h2o] B{wl.B} H{wl.H} D{wl.D} {wl.dtype} prompt {wl.prompt_len} + {steps_after_prompt} steps, "
+          f"cap {cap}, comparing {len(heads)} heads", flush=True)
+    lf = SideBySide(wl.B, wl.H, wl.D, cap, wl.dtype, heads)
+    for t, (q, k, v) in enumerate(_stream(wl, steps_after_prompt), start=1):
+        hh, r = policy(t)
+        lf.step(q, k, v, hh, r)
+    print(f"[h2o] diverged at near-ties: {lf.diverged}", flush=True)
+    assert len(lf.diverged) <= len(heads) // 4, "too many heads hit near-ties"
+    return lf
+
+
+def test_h2o_small_bf16():
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=2, H=4, prompt_len=256)
+    _run(wl, 200)
+
+
+def test_h2o_small_fp32_d64():
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=3, D=64, prompt_len=150, dtype="fp32", seed=5)
+    _run(wl, 100)
+
+
+def test_h2o_no_heavy_is_window():
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=2, prompt_len=60)
+    lf = _run(wl, 40, policy=lambda t: (0, 9))
+    pos = lf.gpu.pos[..., :lf.gpu.n].cpu().numpy()
+    for h in range(2):
+        assert sorted(pos[0, h].tolist()) == list(range(100 - 9, 100))
+
+
+def test_h2o_budget_never_binds():
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=2, prompt_len=120)
+    lf = _run(wl, 10, policy=lambda t: (500, 500))
+    assert lf.gpu.n == 130 and not lf.diverged
+
+
+def test_h2o_many_evictions_in_one_step():
+    """A budget that drops from 150 to 12 evicts 139 tokens in a single step."""
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=4, prompt_len=150)
+    _run(wl, 30, policy=lambda t: (100, 50) if t <= 150 else (7, 5))
+
+
+def test_h2o_decode_shape_sampled_heads():
+    """The 64 x 32-head decode layer: prompt stepped token by token, then decode steps;
+    the oracle follows six sampled heads."""
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"]
+    _run(wl, 64, heads=[(0, 0), (5, 7), (17, 31), (33, 2), (50, 16), (63, 31)])
+
+
+def test_h2o_error_statuses():
+    c = kvc.H2OCache(1, 1, 128, 4)
+    x = torch.zeros((1, 1, 128), dtype=torch.bfloat16, device="cuda")
+    for _ in range(4):
+        c.step(x, x, x, 100, 100)
+    with pytest.raises(kvc.KvcError) as e:  # n + 1 > cap
+        c.step(x, x, x, 100, 100)
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+    with pytest.raises(kvc.KvcError) as e:
+        c.step(x, x, x, -1, 2)
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG

@@ -1,0 +1,56 @@
+"""GPU parity of kvc_sink_recent (through the C ABI) against the CPU oracle (exact)."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_02_amd as kvc
+import synthetic as syn
+from oracle import sink as ref
+from tests import parity as par
+
+pytestmark = pytest.mark.gpu
+
+
+def _tokens(n, B, H, D, dtype, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 2, B, H, D), dtype=np.float32)
+    return syn.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("s,r,n,dtype,D,check_every", [
+    (4, 1020, 3000, "bf16", 128, 0),
+    (0, 7, 50, "fp32", 64, 1),
+    (4, 1, 20, "bf16", 64, 1),
+    (2, 3, 12, "fp32", 128, 1),
+])
+def test_sink_ring_matches_oracle(s, r, n, dtype, D, check_every):
+    B, H = 2, 3
+    print(f"[sink] s{s} r{r} tokens {n} {dtype} D{D}", flush=True)
+    toks = _tokens(n, B, H, D, dtype, seed=s * 1000 + r)
+    cache = kvc.SinkCache(B, H, D, s, r, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    dev = par.to_device(toks, dtype)
+    samples = {1, 2, s, s + 1, s + r, s + r + 1, n // 2, n} if not check_every else set(range(1, n + 1))
+    for t in range(1, n + 1):
+        kept = cache.append(dev[t - 1, 0].contiguous(), dev[t - 1, 1].contiguous())
+        if t in samples:
+            assert kept.cpu().tolist() == ref.kept_positions(t, s, r), f"len {t}"
+    rows_k = [toks[p, 0] for p in range(n)]
+    rows_v = [toks[p, 1] for p in range(n)]
+    exp_k, exp_pos = ref.ring_after(rows_k, s, r)
+    exp_v, _ = ref.ring_after(rows_v, s, r)
+    assert cache.slot_pos.cpu().tolist() == exp_pos
+    gk, gv = par.to_host_bits(cache.k), par.to_host_bits(cache.v)
+    for slot, p in enumerate(exp_pos):
+        if p < 0:
+            continue
+        np.testing.assert_array_equal(gk[:, :, slot], exp_k[slot])
+        np.testing.assert_array_equal(gv[:, :, slot], exp_v[slot])
+
+
+def test_sink_error_statuses():
+    c = kvc.SinkCache(1, 1, 128, 4, 1)
+    c.n_recent = 0  # invalid policy passed through to the library
+    x = torch.zeros((1, 1, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kvc.KvcError) as e:
+        c.append(x, x)
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG

@@ -1,0 +1,172 @@
+"""GPU parity of kvc_snapkv_compress (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_02_amd as kvc
+import synthetic as syn
+from oracle import snapkv as ref
+from tests import parity as par
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, v, wl_window, budget, pool, dtype, **kw):
+    res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=True, want_vote=True, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def _compare(qn, kn, vn, res, window, budget, pool, dtype, heads=None):
+    """Compare GPU results with the oracle on the given (b, h) pairs (default: all)."""
+    B, H, L, D = kn.shape
+    t0 = L - window
+    idx = res.idx.cpu().numpy()
+    k_out = par.to_host_bits(res.k)
+    v_out = par.to_host_bits(res.v)
+    vote = res.vote.cpu().numpy()
+    pooled = res.pooled.cpu().numpy()
+    pairs = heads or [(b, h) for b in range(B) for h in range(H)]
+    kinds = []
+    for b, h in pairs:
+        r = ref.compress_head(qn[b, h, qn.shape[2] - window:], kn[b, h], vn[b, h], budget, pool, dtype)
+        par.assert_close_votes(vote[b, h], r["vote"], f"vote[{b},{h}]")
+        par.assert_close_votes(pooled[b, h], r["pooled"], f"pooled[{b},{h}]")
+        kinds.append(par.check_topk(r["pooled"], r["idx"], idx[b, h]))
+        par.check_gather(k_out[b, h], v_out[b, h], kn[b, h], vn[b, h], idx[b, h], t0)
+        if kinds[-1] == "exact":
+            np.testing.assert_array_equal(k_out[b, h], r["k_out"])
+            np.testing.assert_array_equal(v_out[b, h], r["v_out"])
+    return kinds
+
+
+def _workload(wl, heads=None):
+    print(f"[snapkv] workload {wl.name} B{wl.B} H{wl.H} D{wl.D} L{wl.L} w{wl.window} "
+          f"C{wl.budget} p{wl.pool_kernel} {wl.dtype}", flush=True)
+    qn, kn, vn = syn.snapkv_batch(wl)
+    q, k, v = (par.to_device(x, wl.dtype) for x in (qn, kn, vn))
+    res = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, wl.dtype)
+    kinds = _compare(qn, kn, vn, res, wl.window, wl.budget, wl.pool_kernel, wl.dtype, heads)
+    print(f"[snapkv] {wl.name}: {kinds.count('exact')} exact, {kinds.count('near-tie')} near-tie heads",
+          flush=True)
+    return kinds
+
+
+def test_tiny_fp32_full():
+    _workload(syn.SNAPKV_WORKLOADS["tiny-fp32"])
+
+
+def test_16k_shape_ragged_small():
+    # several MFMA chunks, pooling chunks and a ragged tail (L - w = 2968)
+    _workload(syn.SNAPKV_WORKLOADS["16k-bf16"].with_(L=3000, H=4))
+
+
+def test_16k_full_all_heads():
+    _workload(syn.SNAPKV_WORKLOADS["16k-bf16"])
+
+
+def test_131k_full_sampled_heads():
+    _workload(syn.SNAPKV_WORKLOADS["131k-bf16"], heads=[(0, 0), (0, 13), (0, 31)])
+
+
+def test_380k_full_sampled_heads():
+    _workload(syn.SNAPKV_WORKLOADS["380k-bf16"], heads=[(0, 5), (0, 30)])
+
+
+EDGE = [
+    # dtype, D, window, L, budget, pool
+    ("bf16", 64, 1, 100, 2, 1),
+    ("bf16", 128, 32, 70, 33, 3),        # one kept prefix position
+    ("bf16", 128, 32, 1057, 1056, 65),   # keeps all but one prefix position; widest pool
+    ("bf16", 128, 17, 5000, 300, 5),
+    ("bf16", 64, 32, 4097, 600, 7),
+    ("fp32", 128, 8, 777, 100, 9),
+    ("fp32", 64, 32, 300, 64, 3),
+    ("fp32", 64, 16, 513, 128, 5),
+]
+
+
+@pytest.mark.parametrize("dtype,D,w,L,budget,pool", EDGE)
+def test_edge_shapes(dtype, D, w, L, budget, pool):
+    wl = syn.SnapKVWorkload(name=f"edge-{dtype}-{D}-{w}-{L}", B=1, H=3, D=D, L=L, window=w, budget=budget,
+                            pool_kernel=pool, dtype=dtype, n_spans=2, span_len=3, span_boost=2.0,
+                            seed=777 + L)
+    _workload(wl)
+
+
+def test_zero_queries_exact_ties():
+    """Q = 0 makes every vote equal: the tie rule alone decides, so the kept set is 0..k-1."""
+    B, H, L, D, w, C = 1, 2, 2000, 128, 32, 300
+    rng = np.random.default_rng(0)
+    kn = syn.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32))
+    qn = np.zeros((B, H, w, D), np.uint16)
+    q, k = par.to_device(qn, "bf16"), par.to_device(kn, "bf16")
+    res = _run(q, k, k, w, C, 7, "bf16")
+    idx = res.idx.cpu().numpy()
+    for h in range(H):
+        assert idx[0, h].tolist() == list(range(C - w))
+    _compare(qn, kn, kn, res, w, C, 7, "bf16")
+
+
+def test_planted_spike_neighbourhood():
+    B, H, L, D, w, p = 1, 1, 3000, 128, 32, 7
+    rng = np.random.default_rng(1)
+    q32 = rng.standard_normal((B, H, w, D), dtype=np.float32)
+    k32 = rng.standard_normal((B, H, L, D), dtype=np.float32)
+    u = q32[0, 0].mean(0)
+    j = 1234
+    k32[0, 0, j] += 30.0 * u / np.linalg.norm(u)
+    qn, kn = syn.f32_to_bf16_bits(q32), syn.f32_to_bf16_bits(k32)
+    res = _run(par.to_device(qn, "bf16"), par.to_device(kn, "bf16"), par.to_device(kn, "bf16"), w, w + p, p,
+               "bf16")
+    assert res.idx[0, 0].cpu().tolist() == list(range(j - 3, j + 4))
+
+
+def test_strided_inputs():
+    """q_len > window and K/V row strides wider than D (views into padded buffers)."""
+    B, H, L, D, w, C, p = 2, 3, 2500, 128, 32, 256, 7
+    rng = np.random.default_rng(2)
+    qbig = syn.f32_to_bf16_bits(rng.standard_normal((B, H, 48, D), dtype=np.float32))
+    kbig = syn.f32_to_bf16_bits(rng.standard_normal((B, H, L, D + 64), dtype=np.float32))
+    vbig = syn.f32_to_bf16_bits(rng.standard_normal((B, H, L, D + 64), dtype=np.float32))
+    qd, kd, vd = (par.to_device(x, "bf16") for x in (qbig, kbig, vbig))
+    k, v = kd[..., :D], vd[..., :D]
+    assert k.stride(2) == D + 64
+    res = _run(qd, k, v, w, C, p, "bf16")
+    _compare(qbig, np.ascontiguousarray(kbig[..., :D]), np.ascontiguousarray(vbig[..., :D]), res, w, C, p,
+             "bf16")
+
+
+def test_deterministic_and_workspace_reuse():
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(L=6000, H=4)
+    qn, kn, vn = syn.snapkv_batch(wl)
+    q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
+    nbytes = kvc.snapkv_workspace_bytes(wl.B, wl.H, wl.L, wl.D, wl.window, wl.budget, wl.pool_kernel,
+                                        torch.bfloat16)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")  # garbage on entry
+    a = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", workspace=ws)
+    # a different input through the same workspace, then the first again
+    wl2 = wl.with_(seed=wl.seed + 1)
+    qn2, kn2, vn2 = syn.snapkv_batch(wl2)
+    q2, k2, v2 = (par.to_device(x, "bf16") for x in (qn2, kn2, vn2))
+    b = _run(q2, k2, v2, wl.window, wl.budget, wl.pool_kernel, "bf16", workspace=ws)
+    c = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", workspace=ws)
+    assert torch.equal(a.idx, c.idx) and torch.equal(a.vote, c.vote) and torch.equal(a.k, c.k)
+    _compare(qn2, kn2, vn2, b, wl.window, wl.budget, wl.pool_kernel, "bf16")
+
+
+def test_error_statuses():
+    B, H, L, D = 1, 2, 512, 128
+    k = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.snapkv_compress(k, k, k, 32, 512, 7)  # budget >= L
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.snapkv_compress(k, k, k, 40, 100, 7)  # window > 32
+    assert e.value.status == kvc.KVC_ERR_UNSUPPORTED
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.snapkv_compress(k, k, k, 32, 100, 7, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == kvc.KVC_ERR_WORKSPACE
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.snapkv_compress(k, k, k, 32, 100, 4)  # even pool kernel
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG
