@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
-PHASES = ["zero", "stats", "votes", "pool_hist", "classify", "finalize", "gather"]
+PHASES = ["zero", "stats", "merge", "votes", "classify", "finalize", "gather"]
 
 
 def log(msg):

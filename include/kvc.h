@@ -116,8 +116,8 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  * kvc_snapkv_compress call on the calling thread records events[i] on its
  * stream at phase boundary i, for i < n_events (at most 8): 0 before the
  * first kernel, then after the workspace clear (1), the row-statistics pass
- * (2), the vote pass (3), pooling + histogram (4), classification (5), the
- * final selection (6) and the gather (7). The events are created and owned
+ * (2), the row-statistics merge (3), the vote + pooling + histogram pass (4),
+ * classification (5), the final selection (6) and the gather (7). The events are created and owned
  * by the caller; pass NULL or 0 to stop recording. */
 void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events);
 

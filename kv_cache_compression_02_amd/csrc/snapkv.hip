@@ -11,13 +11,13 @@
 // Kernel sequence per call (all on the caller's stream, no host sync):
 //   zero      clear per-head counters and histograms in the workspace
 //   stats     window scores q.k/sqrt(D) on MFMA (bf16) or VALU (fp32) for a
-//             chunk of keys; per-row running max / sum of 2^(s - m); the last
-//             workgroup of a head to finish merges the chunk partials into the
-//             row max and 1/sum (two-pass softmax, pass 1)
+//             chunk of keys; per-row running max / sum of 2^(s - m) (two-pass
+//             softmax, pass 1)
+//   merge     combine the chunk partials into each row's max and 1/sum
 //   votes     recompute the scores of the prefix keys, normalise with the merged
-//             row statistics and sum over the window rows (pass 2)
-//   pool_hist max-pool the votes of a chunk (halo from the neighbours) and
-//             histogram the top 12 bits of the pooled values per head
+//             row statistics and sum over the window rows (pass 2); max-pool
+//             the chunk (its halo keys are recomputed) and histogram the top 12
+//             bits of the pooled values per head
 //   classify  find the histogram bin that holds the k-th largest pooled score;
 //             emit positions above that bin (kept for sure) and the bin's
 //             members (candidates) to per-head lists
@@ -76,25 +76,20 @@ __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 
 
 // ------------------------------------------------------- row-stat merging
 
-// Called by every thread after this workgroup wrote its partial (m, l) for the
-// 32 window rows. The last workgroup of head `bh` to arrive merges all
-// partials into stat[bh][row] = (m2, 1/l) and re-arms the arrival counter.
-__device__ void merge_row_stats(int bh, int nchunk, const float2* part, float2* stat,
-                                unsigned* arrive) {
-  __shared__ unsigned s_last;
+// Merge the per-chunk partials (m, l) of every window row of a head into
+// stat[bh][row] = (m2, 1/l). One workgroup per head. (A separate launch: an
+// in-kernel "last workgroup merges" scheme needs a device-scope fence per
+// workgroup, which on a multi-XCD part writes back and invalidates that XCD's
+// whole L2 and costs far more than the launch.)
+__global__ __launch_bounds__(kThreads) void snap_merge_stats(int nchunk, const float2* __restrict__ part,
+                                                             float2* __restrict__ stat) {
   __shared__ float2 red[kThreads / 32][32];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&arrive[bh], 1u) == static_cast<unsigned>(nchunk - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  const int bh = blockIdx.x;
   const int row = threadIdx.x & 31, grp = threadIdx.x >> 5;
-  const volatile float* pv = reinterpret_cast<const volatile float*>(part);
   float m = kNegBig, l = 0.f;
   for (int c = grp; c < nchunk; c += kThreads / 32) {
-    const int64_t o = ((static_cast<int64_t>(bh) * nchunk + c) * 32 + row) * 2;
-    lse2_merge(m, l, pv[o], pv[o + 1]);
+    const float2 p = part[(static_cast<int64_t>(bh) * nchunk + c) * 32 + row];
+    lse2_merge(m, l, p.x, p.y);
   }
   red[grp][row] = make_float2(m, l);
   __syncthreads();
@@ -104,7 +99,26 @@ __device__ void merge_row_stats(int bh, int nchunk, const float2* part, float2* 
     for (int g = 1; g < kThreads / 32; ++g) lse2_merge(mm, ll, red[g][row].x, red[g][row].y);
     stat[bh * 32 + row] = make_float2(mm, 1.f / ll);
   }
-  if (threadIdx.x == 0) arrive[bh] = 0;
+}
+
+// Max-pool and histogram of one chunk: sv holds the votes of prefix keys
+// [e0, e1) = [c0 - r, c1 + r) clipped to [0, t0); pooled[j] for j in [c0, c1)
+// is the max over the neighbours that exist, and each pooled value's top 12
+// bits are counted in the LDS histogram sh (merged into hist by the caller).
+__device__ void pool_and_count(const float* sv, int e0, int e1, int c0, int c1, int r, float* pooled_row,
+                               unsigned* sh) {
+  for (int j = c0 + static_cast<int>(threadIdx.x); j < c1; j += kThreads) {
+    const int lo = max(j - r, e0) - e0, hi = min(j + r, e1 - 1) - e0;
+    float m = sv[lo];
+    for (int d = lo + 1; d <= hi; ++d) m = fmaxf(m, sv[d]);
+    pooled_row[j] = m;
+    atomicAdd(&sh[(__float_as_uint(m) >> kHistShift) & (kHistBins - 1)], 1u);
+  }
+}
+
+__device__ void flush_hist(const unsigned* sh, unsigned* hist_row) {
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+    if (sh[i]) atomicAdd(&hist_row[i], sh[i]);
 }
 
 // ------------------------------------------------------------ zero fill
@@ -124,8 +138,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
-    int nchunk, float scale_log2, float2* __restrict__ part, float2* __restrict__ stat,
-    unsigned* __restrict__ arrive) {
+    int nchunk, float scale_log2, float2* __restrict__ part) {
   constexpr int KS = D / 16;
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
@@ -186,7 +199,6 @@ __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
     for (int i = 1; i < kWaves; ++i) lse2_merge(m, l, wred[i][threadIdx.x].x, wred[i][threadIdx.x].y);
     part[(static_cast<int64_t>(bh) * nchunk + chunk) * 32 + threadIdx.x] = make_float2(m, l);
   }
-  merge_row_stats(bh, nchunk, part, stat, arrive);
 }
 
 // fp32, VALU: one key per thread, the window rows in LDS.
@@ -194,8 +206,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_stats_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
-    int nchunk, float scale_log2, float2* __restrict__ part, float2* __restrict__ stat,
-    unsigned* __restrict__ arrive) {
+    int nchunk, float scale_log2, float2* __restrict__ part) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float ss[kMaxWindow][kThreads + 1];
   const int chunk = blockIdx.x, bh = blockIdx.y;
@@ -232,10 +243,14 @@ __global__ __launch_bounds__(kThreads) void snap_stats_f32(
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) lse2_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
   if (seg == 0) part[(static_cast<int64_t>(bh) * nchunk + chunk) * 32 + row] = make_float2(m, l);
-  merge_row_stats(bh, nchunk, part, stat, arrive);
 }
 
-// ------------------------------------------------------- pass 2: votes
+// ------------------------------------------- pass 2: votes, pooling, histogram
+
+// A workgroup owns prefix keys [c0, c1) and computes the votes of [e0, e1) =
+// [c0 - r, c1 + r) clipped to the prefix, so that it can max-pool its own keys
+// without a second pass (the 2r halo keys are recomputed; with 1024-key chunks
+// that is one extra partial MFMA tile).
 
 // bf16, MFMA 32x32x16. Output orientation S: M = the 32 window queries, N =
 // keys, so each lane owns one key (lane & 31) and 16 queries; its vote is a
@@ -243,14 +258,18 @@ __global__ __launch_bounds__(kThreads) void snap_stats_f32(
 template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
-    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
-    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote) {
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
+    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote, float* __restrict__ pooled,
+    unsigned* __restrict__ hist) {
   constexpr int KS = D / 16;
+  __shared__ float sv[kChunkMfma + 2 * kMaxPoolRadius];
+  __shared__ unsigned sh[kHistBins];
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int col = lane & 31, half = lane >> 5;
   const int t0 = L - w;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
 
   bf16x8_t qf[KS];
   if (col < w)
@@ -259,110 +278,99 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     zero_frag<D>(qf);
   float mr[16], il[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = acc_row(r, half);
+  for (int i = 0; i < 16; ++i) {
+    const int m = acc_row(i, half);
     if (m < w) {
       const float2 st = stat[bh * 32 + m];
-      mr[r] = st.x;
-      il[r] = st.y;
+      mr[i] = st.x;
+      il[i] = st.y;
     } else {  // zero query row: score 0, weight 0
-      mr[r] = 0.f;
-      il[r] = 0.f;
+      mr[i] = 0.f;
+      il[i] = 0.f;
     }
   }
 
   const uint16_t* kb = k + b * ksb + h * ksh + half * (D / 2);
-  float* vb = vote + static_cast<int64_t>(bh) * t0;
-  const int key0 = chunk * kChunkMfma;
-  const int key1 = min(t0, key0 + kChunkMfma);
+  const int c0 = chunk * kChunkMfma, c1 = min(t0, c0 + kChunkMfma);
+  const int e0 = max(0, c0 - r), e1 = min(t0, c1 + r);
   constexpr int kStep = kWaves * kTile;
 
-  int tile = key0 + wave * kTile;
+  int tile = e0 + wave * kTile;
   bf16x8_t kf[KS];
-  if (tile < key1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
-  for (; tile < key1; tile += kStep) {
+  if (tile < e1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
+  for (; tile < e1; tile += kStep) {
     bf16x8_t kn[KS];
     const int nt = tile + kStep;
-    if (nt < key1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
+    if (nt < e1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
     float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v += fast_exp2(acc[r] * scale_log2 - mr[r]) * il[r];
+    for (int i = 0; i < 16; ++i) v += fast_exp2(acc[i] * scale_log2 - mr[i]) * il[i];
     v += __shfl_xor(v, 32);
     const int j = tile + col;
-    if (half == 0 && j < key1) vb[j] = v;
-    if (nt < key1) {
+    if (half == 0 && j < e1) {
+      sv[j - e0] = v;
+      if (vote && j >= c0 && j < c1) vote[static_cast<int64_t>(bh) * t0 + j] = v;
+    }
+    if (nt < e1) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) kf[s] = kn[s];
     }
   }
+  __syncthreads();
+  pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
+  __syncthreads();
+  flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
 }
 
+// fp32, VALU: a key per thread, the window rows and their statistics in LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
-    const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
-    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote) {
+    const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
+    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote, float* __restrict__ pooled,
+    unsigned* __restrict__ hist) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float2 st[kMaxWindow];
+  __shared__ float sv[kChunkF32 + 2 * kMaxPoolRadius];
+  __shared__ unsigned sh[kHistBins];
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int t0 = L - w;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
   for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
-    const int r = i / D, d = i - r * D;
-    qs[r][d] = r < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + r) * qst + d] : 0.f;
+    const int rr = i / D, d = i - rr * D;
+    qs[rr][d] = rr < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rr) * qst + d] : 0.f;
   }
-  if (threadIdx.x < kMaxWindow) st[threadIdx.x] = threadIdx.x < w ? stat[bh * 32 + threadIdx.x] : make_float2(0.f, 0.f);
+  if (threadIdx.x < kMaxWindow)
+    st[threadIdx.x] = threadIdx.x < w ? stat[bh * 32 + threadIdx.x] : make_float2(0.f, 0.f);
   __syncthreads();
-  const int j = chunk * kChunkF32 + threadIdx.x;
-  if (j >= t0) return;
-  const float* kr = k + b * ksb + h * ksh + static_cast<int64_t>(j) * kst;
-  float s[kMaxWindow];
+  const int c0 = chunk * kChunkF32, c1 = min(t0, c0 + kChunkF32);
+  const int e0 = max(0, c0 - r), e1 = min(t0, c1 + r);
+  for (int j = e0 + static_cast<int>(threadIdx.x); j < e1; j += kThreads) {
+    const float* kr = k + b * ksb + h * ksh + static_cast<int64_t>(j) * kst;
+    float s[kMaxWindow];
 #pragma unroll
-  for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
-  for (int d = 0; d < D; d += 4) {
-    const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + d);
+    for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
+    for (int d = 0; d < D; d += 4) {
+      const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + d);
+#pragma unroll
+      for (int i = 0; i < kMaxWindow; ++i)
+        s[i] += qs[i][d] * kv[0] + qs[i][d + 1] * kv[1] + qs[i][d + 2] * kv[2] + qs[i][d + 3] * kv[3];
+    }
+    float v = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxWindow; ++i)
-      s[i] += qs[i][d] * kv[0] + qs[i][d + 1] * kv[1] + qs[i][d + 2] * kv[2] + qs[i][d + 3] * kv[3];
-  }
-  float v = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxWindow; ++i)
-    if (i < w) v += fast_exp2(s[i] * scale_log2 - st[i].x) * st[i].y;
-  vote[static_cast<int64_t>(bh) * t0 + j] = v;
-}
-
-// ------------------------------------------------ pooling + histogram
-
-__global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restrict__ vote,
-                                                           float* __restrict__ pooled,
-                                                           unsigned* __restrict__ hist, int N, int r) {
-  __shared__ float sv[kPoolChunk + 2 * kMaxPoolRadius];
-  __shared__ unsigned sh[kHistBins];
-  const int chunk = blockIdx.x, bh = blockIdx.y;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
-  const int c0 = chunk * kPoolChunk, c1 = min(N, c0 + kPoolChunk);
-  const float* vb = vote + static_cast<int64_t>(bh) * N;
-  const int n_load = (c1 - c0) + 2 * r;
-  for (int i = threadIdx.x; i < n_load; i += kThreads) {
-    const int j = c0 - r + i;
-    sv[i] = (j >= 0 && j < N) ? vb[j] : -INFINITY;  // out-of-range neighbours never win
+      if (i < w) v += fast_exp2(s[i] * scale_log2 - st[i].x) * st[i].y;
+    sv[j - e0] = v;
+    if (vote && j >= c0 && j < c1) vote[static_cast<int64_t>(bh) * t0 + j] = v;
   }
   __syncthreads();
-  float* pb = pooled + static_cast<int64_t>(bh) * N;
-  for (int j = c0 + threadIdx.x; j < c1; j += kThreads) {
-    const float* s = sv + (j - c0);
-    float m = s[0];
-    for (int d = 1; d <= 2 * r; ++d) m = fmaxf(m, s[d]);
-    pb[j] = m;
-    atomicAdd(&sh[(__float_as_uint(m) >> kHistShift) & (kHistBins - 1)], 1u);
-  }
+  pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads)
-    if (sh[i]) atomicAdd(&hist[static_cast<int64_t>(bh) * kHistBins + i], sh[i]);
+  flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
 }
 
 // ------------------------------------------------------------ classify
@@ -528,8 +536,7 @@ __global__ __launch_bounds__(kFinThreads) void snap_finalize(const unsigned* __r
     const uint2 c = src[i];
     if (cand_key(c) >= prefix && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
   }
-  __threadfence();
-  __syncthreads();
+  __syncthreads();  // the bitmap lives in LDS or in this XCD's L2: workgroup scope suffices
 
   // ordered compaction of the bitmap into ascending positions
   const int wpt = (words + kFinThreads - 1) / kFinThreads;
@@ -582,8 +589,8 @@ __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__
 struct SnapLayout {
   int64_t BH;
   int N, kk, nchunk, words;
-  size_t arrive, ctr, hist, zero_bytes;
-  size_t part, stat, vote, pooled, sel, cand, bitmap, total;
+  size_t ctr, hist, zero_bytes;
+  size_t part, stat, pooled, sel, cand, bitmap, total;
 };
 
 bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, SnapLayout* o) {
@@ -602,9 +609,7 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
     off = align_up(off + bytes, 256);
     return at;
   };
-  // The first three regions are cleared at the start of every call.
-  o->arrive = off;
-  off += BH * 4;
+  // The first two regions are cleared at the start of every call.
   o->ctr = off;
   off += BH * 16;
   o->hist = off;
@@ -613,7 +618,6 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
   off = align_up(off, 256);
   o->part = take(static_cast<size_t>(BH) * o->nchunk * 32 * 8);
   o->stat = take(static_cast<size_t>(BH) * 32 * 8);
-  o->vote = take(static_cast<size_t>(BH) * o->N * 4);
   o->pooled = take(static_cast<size_t>(BH) * o->N * 4);
   o->sel = take(static_cast<size_t>(BH) * o->kk * 4);
   o->cand = take(static_cast<size_t>(BH) * o->N * 8);
@@ -635,9 +639,7 @@ void launch_stats(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
                   kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
   const dim3 g(lay.nchunk, static_cast<unsigned>(lay.BH));
   snap_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
-                                                lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
-                                                reinterpret_cast<float2*>(ws + lay.stat),
-                                                reinterpret_cast<unsigned*>(ws + lay.arrive));
+                                                lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part));
 }
 
 template <int D>
@@ -645,44 +647,48 @@ void launch_stats(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
                   kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
   const dim3 g(lay.nchunk, static_cast<unsigned>(lay.BH));
   snap_stats_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
-                                               lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
-                                               reinterpret_cast<float2*>(ws + lay.stat),
-                                               reinterpret_cast<unsigned*>(ws + lay.arrive));
+                                               lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part));
 }
 
 template <int D>
 void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int qrow0, const uint16_t* k,
-                  kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, float* vote,
-                  hipStream_t stream) {
+                  kvc_strides kvs, int H, int L, int w, int r, float scale_log2, char* ws, float* vote,
+                  float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
-  snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
-                                                scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote);
+  snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
+                                                scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote,
+                                                pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
 template <int D>
 void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qrow0, const float* k,
-                  kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, float* vote,
-                  hipStream_t stream) {
+                  kvc_strides kvs, int H, int L, int w, int r, float scale_log2, char* ws, float* vote,
+                  float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
-  snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
-                                               scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote);
+  snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
+                                               scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote,
+                                               pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
-// Pass 1 (row statistics) then pass 2 (votes), with phase marks 2 and 3.
+// Pass 1 (row statistics), the merge, then pass 2 (votes, pooling and the
+// histogram), with phase marks 2, 3 and 4.
 template <typename T>
 void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int qrow0, const T* k,
-                         kvc_strides kvs, int H, int L, int D, int w, float scale_log2, char* ws, float* vote,
-                         hipStream_t stream) {
+                         kvc_strides kvs, int H, int L, int D, int w, int r, float scale_log2, char* ws,
+                         float* vote, float* pooled, hipStream_t stream) {
   if (D == 128)
     launch_stats<128>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
   else
     launch_stats<64>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
   mark_phase(2, stream);
-  if (D == 128)
-    launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, vote, stream);
-  else
-    launch_votes<64>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, vote, stream);
+  snap_merge_stats<<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
+      lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part), reinterpret_cast<float2*>(ws + lay.stat));
   mark_phase(3, stream);
+  if (D == 128)
+    launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, r, scale_log2, ws, vote, pooled, stream);
+  else
+    launch_votes<64>(lay, q, qs, qrow0, k, kvs, H, L, w, r, scale_log2, ws, vote, pooled, stream);
+  mark_phase(4, stream);
 }
 
 }  // namespace
@@ -738,28 +744,26 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
 
   char* ws = static_cast<char*>(workspace);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D)));
-  float* vote = vote_out ? vote_out : reinterpret_cast<float*>(ws + lay.vote);
-  float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(ws + lay.pooled);
+  float* vote = vote_out;  // votes are written only when asked for
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
+  float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(ws + lay.pooled);
   unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
   const int qrow0 = q_len - window;
 
   mark_phase(0, stream);
-  fill_u32<<<64, 256, 0, stream>>>(reinterpret_cast<unsigned*>(ws + lay.arrive),
+  fill_u32<<<64, 256, 0, stream>>>(reinterpret_cast<unsigned*>(ws + lay.ctr),
                                    static_cast<int64_t>(lay.zero_bytes / 4), 0u);
   mark_phase(1, stream);
   if (dt == KVC_BF16)
     launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0, static_cast<const uint16_t*>(k),
-                                  kvs, H, L, D, window, scale_log2, ws, vote, stream);
+                                  kvs, H, L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
   else
     launch_score_passes<float>(lay, static_cast<const float*>(q), qs, qrow0, static_cast<const float*>(k), kvs, H,
-                               L, D, window, scale_log2, ws, vote, stream);
+                               L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
   kvc_status st = check_launch("snapkv score passes");
   if (st != KVC_OK) return st;
 
   const dim3 gp((lay.N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(lay.BH));
-  snap_pool_hist<<<gp, kThreads, 0, stream>>>(vote, pooled, hist, lay.N, pool_kernel / 2);
-  mark_phase(4, stream);
   snap_classify<<<gp, kThreads, 0, stream>>>(pooled, hist, lay.N, lay.kk, ctr,
                                              reinterpret_cast<int*>(ws + lay.sel),
                                              reinterpret_cast<uint2*>(ws + lay.cand));
