@@ -114,7 +114,8 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
 
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its
- * stream at phase boundary i, for i < n_events (at most 8): 0 before the
+ * stream at phase boundary i, for i < n_events (at most 8) and events[i] not
+ * NULL (each recorded event costs a few microseconds of GPU time): 0 before the
  * first kernel, then after the workspace clear (1), the row-statistics pass
  * (2), the row-statistics merge (3), the vote + pooling + histogram pass (4),
  * classification (5), the final selection (6) and the gather (7). The events are created and owned

@@ -39,13 +39,14 @@ namespace {
 constexpr int kTile = 32;            // keys per MFMA tile (the 32x32 output's N or M side)
 constexpr int kThreads = 256;        // workgroup size of the streaming kernels
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunkMfma = 1024;     // keys per workgroup, bf16 MFMA path
+constexpr int kChunkMfma = 1024;     // keys per workgroup, bf16 MFMA vote pass
+constexpr int kStatChunkMfma = 2048; // keys per workgroup, bf16 MFMA statistics pass
 constexpr int kChunkF32 = 256;       // keys per workgroup, fp32 path (a key per thread)
 constexpr int kMaxWindow = 32;
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 19;       // pooled >= 0: bits 30..19 = exponent + 4 mantissa bits
-constexpr int kPoolChunk = 4096;     // votes per workgroup in pool_hist / classify
+constexpr int kClassChunk = 16384;   // pooled scores per workgroup in classify
 constexpr int kMaxPoolRadius = 32;
 constexpr int kFinThreads = 1024;
 constexpr int kCandLds = 4096;       // candidates staged in LDS by finalize
@@ -76,29 +77,42 @@ __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 
 
 // ------------------------------------------------------- row-stat merging
 
-// Merge the per-chunk partials (m, l) of every window row of a head into
-// stat[bh][row] = (m2, 1/l). One workgroup per head. (A separate launch: an
-// in-kernel "last workgroup merges" scheme needs a device-scope fence per
-// workgroup, which on a multi-XCD part writes back and invalidates that XCD's
-// whole L2 and costs far more than the launch.)
-__global__ __launch_bounds__(kThreads) void snap_merge_stats(int nchunk, const float2* __restrict__ part,
-                                                             float2* __restrict__ stat) {
-  __shared__ float2 red[kThreads / 32][32];
-  const int bh = blockIdx.x;
+// Clear one head's histogram and selection counters (run by the statistics
+// pass; the vote pass that fills them starts after it has finished).
+__device__ __forceinline__ void clear_head(unsigned* hist, unsigned* ctr, int bh) {
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
+  if (threadIdx.x < 4) ctr[bh * 4 + threadIdx.x] = 0;
+}
+
+// Merge the per-chunk partials (m, l) of the 32 window rows of head bh into
+// st[row] = (m2, 1/l) in LDS. Every thread of the block calls it; the loads
+// of a batch are in flight together.
+__device__ void merge_stats_to_lds(int bh, int nchunk, const float2* __restrict__ part, float2* st) {
+  constexpr int kGroups = kThreads / 32;
+  constexpr int kBatch = 8;
+  __shared__ float2 red[kGroups][32];
   const int row = threadIdx.x & 31, grp = threadIdx.x >> 5;
   float m = kNegBig, l = 0.f;
-  for (int c = grp; c < nchunk; c += kThreads / 32) {
-    const float2 p = part[(static_cast<int64_t>(bh) * nchunk + c) * 32 + row];
-    lse2_merge(m, l, p.x, p.y);
+  const float2* pb = part + static_cast<int64_t>(bh) * nchunk * 32;
+  for (int c0 = grp; c0 < nchunk; c0 += kBatch * kGroups) {
+    float2 pp[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kGroups;
+      pp[i] = c < nchunk ? pb[c * 32 + row] : make_float2(kNegBig, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) lse2_merge(m, l, pp[i].x, pp[i].y);
   }
   red[grp][row] = make_float2(m, l);
   __syncthreads();
   if (threadIdx.x < 32) {
     float mm = red[0][row].x, ll = red[0][row].y;
 #pragma unroll
-    for (int g = 1; g < kThreads / 32; ++g) lse2_merge(mm, ll, red[g][row].x, red[g][row].y);
-    stat[bh * 32 + row] = make_float2(mm, 1.f / ll);
+    for (int g = 1; g < kGroups; ++g) lse2_merge(mm, ll, red[g][row].x, red[g][row].y);
+    st[row] = make_float2(mm, 1.f / ll);
   }
+  __syncthreads();
 }
 
 // Max-pool and histogram of one chunk: sv holds the votes of prefix keys
@@ -121,14 +135,6 @@ __device__ void flush_hist(const unsigned* sh, unsigned* hist_row) {
     if (sh[i]) atomicAdd(&hist_row[i], sh[i]);
 }
 
-// ------------------------------------------------------------ zero fill
-
-__global__ void fill_u32(unsigned* p, int64_t n, unsigned value) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = value;
-}
-
 // ------------------------------------------------ pass 1: row statistics
 
 // bf16, MFMA 32x32x16. Output orientation S^T: M = keys of the tile, N = the 32
@@ -138,9 +144,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
-    int nchunk, float scale_log2, float2* __restrict__ part) {
+    int nchunk, float scale_log2, float2* __restrict__ part, unsigned* __restrict__ hist,
+    unsigned* __restrict__ ctr) {
   constexpr int KS = D / 16;
   const int chunk = blockIdx.x, bh = blockIdx.y;
+  if (chunk == 0) clear_head(hist, ctr, bh);
   const int b = bh / H, h = bh - b * H;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int col = lane & 31, half = lane >> 5;
@@ -153,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
     zero_frag<D>(qf);
 
   const uint16_t* kb = k + b * ksb + h * ksh + half * (D / 2);
-  const int key0 = chunk * kChunkMfma;
-  const int key1 = min(L, key0 + kChunkMfma);
+  const int key0 = chunk * kStatChunkMfma;
+  const int key1 = min(L, key0 + kStatChunkMfma);
   constexpr int kStep = kWaves * kTile;
   float m_run = kNegBig, l_run = 0.f;
 
@@ -206,10 +214,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_stats_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
-    int nchunk, float scale_log2, float2* __restrict__ part) {
+    int nchunk, float scale_log2, float2* __restrict__ part, unsigned* __restrict__ hist,
+    unsigned* __restrict__ ctr) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float ss[kMaxWindow][kThreads + 1];
   const int chunk = blockIdx.x, bh = blockIdx.y;
+  if (chunk == 0) clear_head(hist, ctr, bh);
   const int b = bh / H, h = bh - b * H;
   const int t0 = L - w;
   for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
@@ -259,12 +269,14 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
-    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote, float* __restrict__ pooled,
-    unsigned* __restrict__ hist) {
+    float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
+    float* __restrict__ pooled, unsigned* __restrict__ hist) {
   constexpr int KS = D / 16;
   __shared__ float sv[kChunkMfma + 2 * kMaxPoolRadius];
   __shared__ unsigned sh[kHistBins];
+  __shared__ float2 stat[32];
   const int chunk = blockIdx.x, bh = blockIdx.y;
+  merge_stats_to_lds(bh, nchunk, part, stat);
   const int b = bh / H, h = bh - b * H;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int col = lane & 31, half = lane >> 5;
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
   for (int i = 0; i < 16; ++i) {
     const int m = acc_row(i, half);
     if (m < w) {
-      const float2 st = stat[bh * 32 + m];
+      const float2 st = stat[m];
       mr[i] = st.x;
       il[i] = st.y;
     } else {  // zero query row: score 0, weight 0
@@ -330,8 +342,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
-    float scale_log2, const float2* __restrict__ stat, float* __restrict__ vote, float* __restrict__ pooled,
-    unsigned* __restrict__ hist) {
+    float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
+    float* __restrict__ pooled, unsigned* __restrict__ hist) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float2 st[kMaxWindow];
   __shared__ float sv[kChunkF32 + 2 * kMaxPoolRadius];
@@ -344,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const int rr = i / D, d = i - rr * D;
     qs[rr][d] = rr < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rr) * qst + d] : 0.f;
   }
-  if (threadIdx.x < kMaxWindow)
-    st[threadIdx.x] = threadIdx.x < w ? stat[bh * 32 + threadIdx.x] : make_float2(0.f, 0.f);
+  merge_stats_to_lds(bh, nchunk, part, st);
+  if (threadIdx.x < kMaxWindow && threadIdx.x >= w) st[threadIdx.x] = make_float2(0.f, 0.f);
   __syncthreads();
   const int c0 = chunk * kChunkF32, c1 = min(t0, c0 + kChunkF32);
   const int e0 = max(0, c0 - r), e1 = min(t0, c1 + r);
@@ -403,14 +415,20 @@ __device__ void find_kth_bin(const unsigned* sh, unsigned kk, unsigned* scratch,
 }
 
 // ctr[bh] = {selected count, candidate count, b*, picks left for the candidates}
+// Each thread classifies kClassChunk / kThreads positions strided by the block
+// size (coalesced loads; the order inside the lists does not matter, the
+// final selection orders positions through a bitmap). Block-wide prefix sums
+// give every thread its output slots, so a workgroup makes one atomic per
+// list (per-wave atomics on one address serialise).
 __global__ __launch_bounds__(kThreads) void snap_classify(const float* __restrict__ pooled,
                                                           const unsigned* __restrict__ hist, int N,
                                                           int kk, unsigned* __restrict__ ctr,
                                                           int* __restrict__ sel,
                                                           uint2* __restrict__ cand) {
+  constexpr int kPer = kClassChunk / kThreads;  // 16
   __shared__ unsigned sh[kHistBins];
   __shared__ unsigned scratch[kWaves + 1];
-  __shared__ unsigned s_bin, s_above;
+  __shared__ unsigned s_bin, s_above, s_base_sel, s_base_cand;
   const int chunk = blockIdx.x, bh = blockIdx.y;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = hist[static_cast<int64_t>(bh) * kHistBins + i];
   __syncthreads();
@@ -421,32 +439,40 @@ __global__ __launch_bounds__(kThreads) void snap_classify(const float* __restric
     ctr[bh * 4 + 3] = static_cast<unsigned>(kk) - s_above;
   }
   const float* pb = pooled + static_cast<int64_t>(bh) * N;
+  const int j0 = chunk * kClassChunk + static_cast<int>(threadIdx.x);
+  unsigned u[kPer];
+  unsigned ns = 0, nc = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int j = j0 + e * kThreads;
+    u[e] = j < N ? __float_as_uint(pb[j]) : 0u;
+    const unsigned bin = (u[e] >> kHistShift) & (kHistBins - 1);
+    ns += (j < N && bin > bstar);
+    nc += (j < N && bin == bstar);
+  }
+  unsigned ts, tc;
+  unsigned os = block_excl_scan<kThreads>(ns, scratch, &ts);
+  unsigned oc = block_excl_scan<kThreads>(nc, scratch, &tc);
+  if (threadIdx.x == 0) {
+    s_base_sel = ts ? atomicAdd(&ctr[bh * 4 + 0], ts) : 0u;
+    s_base_cand = tc ? atomicAdd(&ctr[bh * 4 + 1], tc) : 0u;
+  }
+  __syncthreads();
   int* sb = sel + static_cast<int64_t>(bh) * kk;
   uint2* cb = cand + static_cast<int64_t>(bh) * N;
-  const int lane = lane_id();
-  const int c0 = chunk * kPoolChunk, c1 = min(N, c0 + kPoolChunk);
-  for (int base = c0; base < c1; base += kThreads) {
-    const int j = base + threadIdx.x;
-    const bool valid = j < c1;
-    const unsigned u = valid ? __float_as_uint(pb[j]) : 0u;
-    const unsigned bin = (u >> kHistShift) & (kHistBins - 1);
-    const bool is_sel = valid && bin > bstar;
-    const bool is_cand = valid && bin == bstar;
-    const unsigned long long ms = __ballot(is_sel);
-    if (ms) {
-      const int leader = __ffsll(static_cast<long long>(ms)) - 1;
-      unsigned at = 0;
-      if (lane == leader) at = atomicAdd(&ctr[bh * 4 + 0], static_cast<unsigned>(__popcll(ms)));
-      at = __shfl(at, leader) + popc_below(ms);
-      if (is_sel && at < static_cast<unsigned>(kk)) sb[at] = j;
-    }
-    const unsigned long long mc = __ballot(is_cand);
-    if (mc) {
-      const int leader = __ffsll(static_cast<long long>(mc)) - 1;
-      unsigned at = 0;
-      if (lane == leader) at = atomicAdd(&ctr[bh * 4 + 1], static_cast<unsigned>(__popcll(mc)));
-      at = __shfl(at, leader) + popc_below(mc);
-      if (is_cand && at < static_cast<unsigned>(N)) cb[at] = make_uint2(u, static_cast<unsigned>(j));
+  os += s_base_sel;
+  oc += s_base_cand;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int j = j0 + e * kThreads;
+    if (j >= N) break;
+    const unsigned bin = (u[e] >> kHistShift) & (kHistBins - 1);
+    if (bin > bstar) {
+      if (os < static_cast<unsigned>(kk)) sb[os] = j;
+      ++os;
+    } else if (bin == bstar) {
+      if (oc < static_cast<unsigned>(N)) cb[oc] = make_uint2(u[e], static_cast<unsigned>(j));
+      ++oc;
     }
   }
 }
@@ -485,12 +511,27 @@ __global__ __launch_bounds__(kFinThreads) void snap_finalize(const unsigned* __r
   const bool in_lds = n_cand <= static_cast<unsigned>(kCandLds);
   if (in_lds)
     for (unsigned i = tid; i < n_cand; i += kFinThreads) cl[i] = cg[i];
+  __shared__ unsigned long long s_thresh;
+  if (tid == 0) s_thresh = ~0ull;  // stays "keep no candidate" if the counts were inconsistent
   __syncthreads();
   const uint2* src = in_lds ? cl : cg;
 
-  // radix select, 8 bits at a time from the top, of the rem-th largest key
+  // the rem-th largest candidate key: by direct ranking when every candidate
+  // fits one per thread (the usual case), else by radix select, 8 bits at a
+  // time from the top
   unsigned long long prefix = 0, pmask = 0;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  const bool direct = in_lds && n_cand <= static_cast<unsigned>(kFinThreads);
+  if (direct) {
+    if (static_cast<unsigned>(tid) < n_cand) {
+      const unsigned long long mine = cand_key(cl[tid]);
+      unsigned greater = 0;
+      for (unsigned i = 0; i < n_cand; ++i) greater += cand_key(cl[i]) > mine;
+      if (greater + 1 == rem) s_thresh = mine;  // keys are distinct: exactly one thread
+    }
+    __syncthreads();
+    prefix = s_thresh;
+  }
+  for (int shift = 56; shift >= 0 && !direct; shift -= 8) {
     if (tid < 256) dh[tid] = 0;
     __syncthreads();
     for (unsigned i = tid; i < n_cand; i += kFinThreads) {
@@ -559,7 +600,10 @@ __global__ __launch_bounds__(kFinThreads) void snap_finalize(const unsigned* __r
 
 // -------------------------------------------------------------- gather
 
-// One 16-byte piece of one output row per thread; K and V together.
+// kGatherPer 16-byte pieces of output rows per thread, K and V together; all
+// loads are issued before the stores.
+constexpr int kGatherPer = 4;
+
 __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__ k,
                                                         const char* __restrict__ v, int64_t sb,
                                                         int64_t sh, int64_t st, int H, int L, int w,
@@ -569,19 +613,31 @@ __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__
                                                         char* __restrict__ v_out) {
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int row = static_cast<int>(t / vec_per_row);
-  const int vc = static_cast<int>(t - static_cast<int64_t>(row) * vec_per_row);
-  if (row >= C) return;
-  int src = row < kk ? idx[static_cast<int64_t>(bh) * kk + row] : (L - w + (row - kk));
-  src = min(max(src, 0), L - 1);
-  const int64_t so = b * sb + h * sh + static_cast<int64_t>(src) * st + static_cast<int64_t>(vc) * 16;
-  const int64_t dof = (static_cast<int64_t>(bh) * C + row) * (static_cast<int64_t>(vec_per_row) * 16) +
-                      static_cast<int64_t>(vc) * 16;
-  const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(k + so);
-  const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(v + so);
-  *reinterpret_cast<u32x4_t*>(k_out + dof) = kx;
-  *reinterpret_cast<u32x4_t*>(v_out + dof) = vx;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * kThreads * kGatherPer + threadIdx.x;
+  const int64_t n_pieces = static_cast<int64_t>(C) * vec_per_row;
+  const int64_t row_bytes = static_cast<int64_t>(vec_per_row) * 16;
+  u32x4_t kx[kGatherPer], vx[kGatherPer];
+  int64_t dst[kGatherPer];
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    const int64_t t = first + static_cast<int64_t>(u) * kThreads;
+    dst[u] = -1;
+    if (t >= n_pieces) continue;
+    const int row = static_cast<int>(t / vec_per_row);
+    const int vc = static_cast<int>(t - static_cast<int64_t>(row) * vec_per_row);
+    int src = row < kk ? idx[static_cast<int64_t>(bh) * kk + row] : (L - w + (row - kk));
+    src = min(max(src, 0), L - 1);
+    const int64_t so = b * sb + h * sh + static_cast<int64_t>(src) * st + static_cast<int64_t>(vc) * 16;
+    kx[u] = *reinterpret_cast<const u32x4_t*>(k + so);
+    vx[u] = *reinterpret_cast<const u32x4_t*>(v + so);
+    dst[u] = (static_cast<int64_t>(bh) * C + row) * row_bytes + static_cast<int64_t>(vc) * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    if (dst[u] < 0) continue;
+    *reinterpret_cast<u32x4_t*>(k_out + dst[u]) = kx[u];
+    *reinterpret_cast<u32x4_t*>(v_out + dst[u]) = vx[u];
+  }
 }
 
 // ------------------------------------------------------ workspace layout
@@ -589,8 +645,8 @@ __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__
 struct SnapLayout {
   int64_t BH;
   int N, kk, nchunk, words;
-  size_t ctr, hist, zero_bytes;
-  size_t part, stat, pooled, sel, cand, bitmap, total;
+  size_t ctr, hist;
+  size_t part, pooled, sel, cand, bitmap, total;
 };
 
 bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, SnapLayout* o) {
@@ -600,7 +656,7 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
   o->BH = BH;
   o->N = L - w;
   o->kk = budget - w;
-  const int chunk = dt == KVC_BF16 ? kChunkMfma : kChunkF32;
+  const int chunk = dt == KVC_BF16 ? kStatChunkMfma : kChunkF32;
   o->nchunk = (L + chunk - 1) / chunk;
   o->words = (o->N + 31) / 32;
   size_t off = 0;
@@ -609,15 +665,9 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
     off = align_up(off + bytes, 256);
     return at;
   };
-  // The first two regions are cleared at the start of every call.
-  o->ctr = off;
-  off += BH * 16;
-  o->hist = off;
-  off += BH * kHistBins * 4;
-  o->zero_bytes = off;
-  off = align_up(off, 256);
+  o->ctr = take(static_cast<size_t>(BH) * 16);
+  o->hist = take(static_cast<size_t>(BH) * kHistBins * 4);
   o->part = take(static_cast<size_t>(BH) * o->nchunk * 32 * 8);
-  o->stat = take(static_cast<size_t>(BH) * 32 * 8);
   o->pooled = take(static_cast<size_t>(BH) * o->N * 4);
   o->sel = take(static_cast<size_t>(BH) * o->kk * 4);
   o->cand = take(static_cast<size_t>(BH) * o->N * 8);
@@ -631,7 +681,7 @@ thread_local hipEvent_t* g_phase_events = nullptr;
 thread_local int g_phase_count = 0;
 
 void mark_phase(int i, hipStream_t stream) {
-  if (g_phase_events && i < g_phase_count) (void)hipEventRecord(g_phase_events[i], stream);
+  if (g_phase_events && i < g_phase_count && g_phase_events[i]) (void)hipEventRecord(g_phase_events[i], stream);
 }
 
 template <int D>
@@ -639,7 +689,9 @@ void launch_stats(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
                   kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
   const dim3 g(lay.nchunk, static_cast<unsigned>(lay.BH));
   snap_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
-                                                lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part));
+                                                lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
+                                                reinterpret_cast<unsigned*>(ws + lay.hist),
+                                                reinterpret_cast<unsigned*>(ws + lay.ctr));
 }
 
 template <int D>
@@ -647,7 +699,9 @@ void launch_stats(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
                   kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
   const dim3 g(lay.nchunk, static_cast<unsigned>(lay.BH));
   snap_stats_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
-                                               lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part));
+                                               lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
+                                               reinterpret_cast<unsigned*>(ws + lay.hist),
+                                               reinterpret_cast<unsigned*>(ws + lay.ctr));
 }
 
 template <int D>
@@ -656,8 +710,8 @@ void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
                   float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
   snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
-                                                scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote,
-                                                pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
+                                                scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
+                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
 template <int D>
@@ -666,11 +720,12 @@ void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
                   float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
   snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
-                                               scale_log2, reinterpret_cast<const float2*>(ws + lay.stat), vote,
-                                               pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
+                                               scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
+                                               vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
-// Pass 1 (row statistics), the merge, then pass 2 (votes, pooling and the
+// Pass 1 (row statistics; it also clears the histograms and counters), then
+// pass 2 (merge of the statistics in its prologue, votes, pooling and the
 // histogram), with phase marks 2, 3 and 4.
 template <typename T>
 void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int qrow0, const T* k,
@@ -681,9 +736,7 @@ void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int 
   else
     launch_stats<64>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
   mark_phase(2, stream);
-  snap_merge_stats<<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
-      lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part), reinterpret_cast<float2*>(ws + lay.stat));
-  mark_phase(3, stream);
+  mark_phase(3, stream);  // no separate merge launch
   if (D == 128)
     launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, r, scale_log2, ws, vote, pooled, stream);
   else
@@ -751,9 +804,7 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   const int qrow0 = q_len - window;
 
   mark_phase(0, stream);
-  fill_u32<<<64, 256, 0, stream>>>(reinterpret_cast<unsigned*>(ws + lay.ctr),
-                                   static_cast<int64_t>(lay.zero_bytes / 4), 0u);
-  mark_phase(1, stream);
+  mark_phase(1, stream);  // counters and histograms are cleared by the statistics pass
   if (dt == KVC_BF16)
     launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0, static_cast<const uint16_t*>(k),
                                   kvs, H, L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
@@ -763,7 +814,7 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   kvc_status st = check_launch("snapkv score passes");
   if (st != KVC_OK) return st;
 
-  const dim3 gp((lay.N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(lay.BH));
+  const dim3 gp((lay.N + kClassChunk - 1) / kClassChunk, static_cast<unsigned>(lay.BH));
   snap_classify<<<gp, kThreads, 0, stream>>>(pooled, hist, lay.N, lay.kk, ctr,
                                              reinterpret_cast<int*>(ws + lay.sel),
                                              reinterpret_cast<uint2*>(ws + lay.cand));
@@ -775,9 +826,10 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   st = check_launch("snapkv selection");
   if (st != KVC_OK) return st;
 
-  const int vec_per_row = static_cast<int>(D * es / 16);
+  const int vec_per_row = static_cast<int>(D * es / 16);  // 16-byte pieces per row
   const int64_t pieces = static_cast<int64_t>(budget) * vec_per_row;
-  const dim3 gg(static_cast<unsigned>((pieces + kThreads - 1) / kThreads), static_cast<unsigned>(lay.BH));
+  const int64_t per_block = static_cast<int64_t>(kThreads) * kGatherPer;
+  const dim3 gg(static_cast<unsigned>((pieces + per_block - 1) / per_block), static_cast<unsigned>(lay.BH));
   snap_gather<<<gg, kThreads, 0, stream>>>(static_cast<const char*>(k), static_cast<const char*>(v),
                                            kvs.b * es, kvs.h * es, kvs.t * es, H, L, window, budget, lay.kk,
                                            vec_per_row, idx_out, static_cast<char*>(k_out),

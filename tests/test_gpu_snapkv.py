@@ -12,6 +12,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(q, k, v, wl_window, budget, pool, dtype, **kw):
+    if "workspace" not in kw:
+        B, H, L, D = k.shape
+        n = kvc.snapkv_workspace_bytes(B, H, L, D, wl_window, budget, pool, k.dtype)
+        kw["workspace"] = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")  # garbage on entry
     res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=True, want_vote=True, **kw)
     torch.cuda.synchronize()
     return res
