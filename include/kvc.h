@@ -157,6 +157,28 @@ kvc_status kvc_h2o_step(kvc_h2o_cache* c, const void* q, const void* k_new,
                         const void* v_new, int n_heavy, int n_recent,
                         float* attn_out, hipStream_t stream);
 
+/* Bytes of device workspace kvc_h2o_prefill needs (0 if the sizes are invalid). */
+size_t kvc_h2o_prefill_workspace_bytes(int B, int H, int prompt_len);
+
+/* Initial H2O state after a prompt (H2O page: the glossary's local statistics,
+ * i.e. the attention observed so far, and the what-is-kept subsection):
+ *   - the score of prompt token j is the sum, over prompt queries i >= j, of the
+ *     causal softmax weight of q_i on k_j (scores q.k / sqrt(D));
+ *   - with length = prompt_len, the eviction rule of kvc_h2o_step keeps every
+ *     recent token (position >= prompt_len - n_recent) and fills the rest of the
+ *     budget n_heavy + n_recent with the highest-scoring other tokens;
+ *   - the kept tokens are written to slots 0 .. n-1 in ascending position order
+ *     (their K/V rows, positions and scores).
+ * q [B, H, prompt_len, D] with strides qs; k, v [B, H, prompt_len, D] with
+ * strides kvs (D contiguous), element type c->dt. The cache's previous contents
+ * are replaced; on return c->n = min(prompt_len, n_heavy + n_recent) and
+ * c->len = prompt_len. Requires prompt_len <= 8192, c->n <= cap after the
+ * call, and a workspace of kvc_h2o_prefill_workspace_bytes(...) bytes. */
+kvc_status kvc_h2o_prefill(kvc_h2o_cache* c, const void* q, kvc_strides qs, const void* k,
+                           const void* v, kvc_strides kvs, int prompt_len, int n_heavy,
+                           int n_recent, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* StreamingLLM sink + recent ring, one new token.                            */
 /* ------------------------------------------------------------------------- */

@@ -10,6 +10,7 @@ library is missing or a call fails, an exception is raised.
 Entry points (same names as the C ABI, without the ``kvc_`` prefix):
   snapkv_compress     SnapKV prompt compression of one layer
   snapkv_workspace_bytes
+  H2OCache.prefill    H2O prompt scores + first eviction (kvc_h2o_prefill)
   H2OCache.step       H2O decode step (kvc_h2o_step)
   SinkCache.append    StreamingLLM sink + recent ring (kvc_sink_recent)
 """
@@ -30,7 +31,8 @@ _STATUS_NAMES = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED_SYMBOLS = (
     "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
-    "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events",
+    "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
+    "kvc_h2o_prefill_workspace_bytes",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +85,11 @@ def library():
         vp, vp, vp, vp, vp, vp, sz, vp]
     L.kvc_h2o_step.restype = i32
     L.kvc_h2o_step.argtypes = [ctypes.POINTER(_H2OCacheC), vp, vp, vp, i32, i32, vp, vp]
+    L.kvc_h2o_prefill_workspace_bytes.restype = sz
+    L.kvc_h2o_prefill_workspace_bytes.argtypes = [i32, i32, i32]
+    L.kvc_h2o_prefill.restype = i32
+    L.kvc_h2o_prefill.argtypes = [ctypes.POINTER(_H2OCacheC), vp, Strides, vp, vp, Strides, i32, i32, i32,
+                                  vp, sz, vp]
     L.kvc_snapkv_set_phase_events.restype = None
     L.kvc_snapkv_set_phase_events.argtypes = [vp, i32]
     L.kvc_sink_recent.restype = i32
@@ -189,6 +196,22 @@ class H2OCache:
     @property
     def length(self):
         return self._c.len
+
+    def prefill(self, q, k, v, n_heavy, n_recent, workspace=None):
+        """Initial state from a prompt (kvc_h2o_prefill); q, k, v: [B, H, prompt_len, D]."""
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _dev(t, n)
+            if t.dim() != 4 or t.dtype != self.k.dtype:
+                raise ValueError(f"{n} must be 4-D [B, H, T, D] with the cache's dtype")
+        if k.shape != v.shape or k.stride() != v.stride() or q.shape != k.shape:
+            raise ValueError("q, k, v must share one shape, and k, v one set of strides")
+        B, H, Lp, D = k.shape
+        if workspace is None:
+            nbytes = int(library().kvc_h2o_prefill_workspace_bytes(B, H, Lp))
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+        _check(library().kvc_h2o_prefill(ctypes.byref(self._c), _ptr(q), _strides4(q), _ptr(k), _ptr(v),
+                                         _strides4(k), Lp, n_heavy, n_recent, _ptr(workspace),
+                                         workspace.numel(), _stream()))
 
     def step(self, q, k_new, v_new, n_heavy, n_recent, attn_out=None):
         """One decode step for every head; q, k_new, v_new: [B, H, D] contiguous."""

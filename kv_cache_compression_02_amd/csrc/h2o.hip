@@ -75,6 +75,54 @@ __device__ __forceinline__ unsigned long long evict_key(float acc, int pos) {
   return (static_cast<unsigned long long>(__float_as_uint(acc)) << 32) | static_cast<unsigned>(pos);
 }
 
+// Key of the E-th smallest (score, position) among slots j < N whose position
+// is below rthr (the non-recent tokens): radix select, 8 bits at a time from the
+// top. Slots with a key <= the result are exactly the E to evict (keys are
+// distinct). dh: 256 LDS counters. Every thread of the block calls it.
+__device__ unsigned long long evict_threshold(const float* s_val, const int* s_pos, int N, int rthr,
+                                              unsigned E, unsigned* dh) {
+  __shared__ unsigned s_digit, s_below;
+  unsigned rem = E;
+  unsigned long long prefix = 0, pmask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) dh[i] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < N; j += blockDim.x) {
+      if (s_pos[j] >= rthr) continue;
+      const unsigned long long key = evict_key(s_val[j], s_pos[j]);
+      if ((key & pmask) == prefix) atomicAdd(&dh[(key >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      unsigned c4[4], c = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = dh[4 * threadIdx.x + i];
+        c += c4[i];
+      }
+      const unsigned incl = wave_incl_scan(c);
+      const unsigned lower = incl - c;  // digits owned by lower lanes
+      if (lower < rem && lower + c >= rem) {
+        unsigned run = lower;
+        for (int i = 0; i < 4; ++i) {
+          if (run + c4[i] >= rem) {
+            s_digit = 4 * threadIdx.x + i;
+            s_below = run;
+            break;
+          }
+          run += c4[i];
+        }
+      }
+    }
+    __syncthreads();
+    rem -= s_below;
+    prefix |= static_cast<unsigned long long>(s_digit) << shift;
+    pmask |= 0xFFull << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
     char* __restrict__ kc, char* __restrict__ vc, int* __restrict__ pos_g, float* __restrict__ acc_g,
@@ -93,7 +141,6 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
   __shared__ float ored[kWaves][D];
   __shared__ unsigned dh[256];
   __shared__ unsigned scratch[kWaves + 1];
-  __shared__ unsigned s_digit, s_below;
 
   const int bh = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -186,44 +233,7 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
     const int rthr = length - n_recent;  // positions >= rthr are recent
     const int E = N - budget;
     n_keep = budget;
-    unsigned rem = static_cast<unsigned>(E);
-    unsigned long long prefix = 0, pmask = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      dh[threadIdx.x] = 0;  // kThreads == 256 digits
-      __syncthreads();
-      for (int j = threadIdx.x; j < N; j += kThreads) {
-        if (s_pos[j] >= rthr) continue;
-        const unsigned long long key = evict_key(s_val[j], s_pos[j]);
-        if ((key & pmask) == prefix) atomicAdd(&dh[(key >> shift) & 255], 1u);
-      }
-      __syncthreads();
-      if (threadIdx.x < kWave) {
-        unsigned c4[4], c = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c4[i] = dh[4 * threadIdx.x + i];
-          c += c4[i];
-        }
-        const unsigned incl = wave_incl_scan(c);
-        const unsigned lower = incl - c;  // digits owned by lower lanes
-        if (lower < rem && lower + c >= rem) {
-          unsigned run = lower;
-          for (int i = 0; i < 4; ++i) {
-            if (run + c4[i] >= rem) {
-              s_digit = 4 * threadIdx.x + i;
-              s_below = run;
-              break;
-            }
-            run += c4[i];
-          }
-        }
-      }
-      __syncthreads();
-      rem -= s_below;
-      prefix |= static_cast<unsigned long long>(s_digit) << shift;
-      pmask |= 0xFFull << shift;
-      __syncthreads();
-    }
+    const unsigned long long prefix = evict_threshold(s_val, s_pos, N, rthr, static_cast<unsigned>(E), dh);
     // prefix = key of the last evicted token. Holes: evicted slots below
     // n_keep; movers: kept slots at or above n_keep. Pair them by rank.
     const int seg = (N + kThreads - 1) / kThreads;
@@ -281,6 +291,245 @@ kvc_status launch_h2o(kvc_h2o_cache* c, const void* q, const void* kn, const voi
   return check_launch("h2o step");
 }
 
+// ------------------------------------------------------------------ prefill
+//
+// Initial scores after the prompt (H2O page: local statistics are the
+// attention observed so far): score of prompt token j = sum over prompt
+// queries i >= j of the causal softmax weight P[i, j]. Pass 1 gives every
+// query row its (max, 1/sum) (a workgroup owns 32 whole rows); pass 2 sums
+// each key column over the rows that see it (a workgroup owns 32 whole
+// columns); pass 3 applies the heavy + recent eviction at length = prompt
+// length and writes the kept tokens into the cache in position order.
+
+constexpr int kPTile = 32;
+constexpr float kNegBig = -1.0e30f;
+
+template <int D>
+__device__ __forceinline__ void load_frag(const uint16_t* p, bf16x8_t (&f)[D / 16]) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, src[s]);
+}
+
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// bf16, MFMA 32x32x16, output S^T (lane = query row): per-row running max/sum.
+template <int D>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_stats_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ k,
+    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, float scale_log2, float2* __restrict__ stat) {
+  constexpr int KS = D / 16;
+  __shared__ float2 wred[kWaves][32];
+  const int qt = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 31, half = lane >> 5;
+  const int qi = qt * kPTile + col;
+  bf16x8_t qf[KS];
+  if (qi < Lp) {
+    load_frag<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qi) * qst + half * (D / 2), qf);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+  }
+  const uint16_t* kb = k + b * ksb + h * ksh + half * (D / 2);
+  float m_run = kNegBig, l_run = 0.f;
+  for (int kt = wave; kt <= qt; kt += kWaves) {
+    bf16x8_t kf[KS];
+    load_frag<D>(kb + static_cast<int64_t>(min(kt * kPTile + col, Lp - 1)) * kst, kf);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+    float sv[16], tmax = kNegBig;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = kt * kPTile + acc_row(r, half);
+      sv[r] = (j <= qi && j < Lp) ? acc[r] * scale_log2 : kNegBig;
+      tmax = fmaxf(tmax, sv[r]);
+    }
+    const float mnew = fmaxf(m_run, tmax);
+    float add = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) add += fast_exp2(sv[r] - mnew);
+    l_run = l_run * fast_exp2(m_run - mnew) + add;
+    m_run = mnew;
+  }
+  lse2_merge(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
+  if (half == 0) wred[wave][col] = make_float2(m_run, l_run);
+  __syncthreads();
+  if (threadIdx.x < 32 && qt * kPTile + static_cast<int>(threadIdx.x) < Lp) {
+    float m = wred[0][threadIdx.x].x, l = wred[0][threadIdx.x].y;
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) lse2_merge(m, l, wred[i][threadIdx.x].x, wred[i][threadIdx.x].y);
+    stat[static_cast<int64_t>(bh) * Lp + qt * kPTile + threadIdx.x] = make_float2(m, 1.f / l);
+  }
+}
+
+// bf16, MFMA, output S (lane = key column): column sums of the normalised weights.
+template <int D>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_colsum_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ k,
+    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, float scale_log2, const float2* __restrict__ stat,
+    float* __restrict__ colsum) {
+  constexpr int KS = D / 16;
+  __shared__ float wsum[kWaves][32];
+  const int kt = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 31, half = lane >> 5;
+  const int kj = kt * kPTile + col;
+  bf16x8_t kf[KS];
+  load_frag<D>(k + b * ksb + h * ksh + static_cast<int64_t>(min(kj, Lp - 1)) * kst + half * (D / 2), kf);
+  const uint16_t* qb = q + b * qsb + h * qsh + half * (D / 2);
+  const float2* sb = stat + static_cast<int64_t>(bh) * Lp;
+  const int nqt = (Lp + kPTile - 1) / kPTile;
+  float csum = 0.f;
+  for (int qt = kt + wave; qt < nqt; qt += kWaves) {
+    bf16x8_t qf[KS];
+    const int qrow = qt * kPTile + col;
+    if (qrow < Lp) {
+      load_frag<D>(qb + static_cast<int64_t>(qrow) * qst, qf);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+    }
+    f32x16_t acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = qt * kPTile + acc_row(r, half);
+      if (i < Lp && i >= kj) {
+        const float2 st = sb[i];
+        csum += fast_exp2(acc[r] * scale_log2 - st.x) * st.y;
+      }
+    }
+  }
+  csum += __shfl_xor(csum, 32);
+  if (half == 0) wsum[wave][col] = csum;
+  __syncthreads();
+  if (threadIdx.x < 32 && kt * kPTile + static_cast<int>(threadIdx.x) < Lp) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += wsum[i][threadIdx.x];
+    colsum[static_cast<int64_t>(bh) * Lp + kt * kPTile + threadIdx.x] = t;
+  }
+}
+
+// fp32, VALU: a query row (pass 1) or a key column (pass 2) per thread.
+template <int D>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_stats_f32(
+    const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const float* __restrict__ k,
+    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, float scale_log2, float2* __restrict__ stat) {
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= Lp) return;
+  const float* qr = q + b * qsb + h * qsh + static_cast<int64_t>(i) * qst;
+  const float* kb = k + b * ksb + h * ksh;
+  float m = kNegBig, l = 0.f;
+  for (int j = 0; j <= i; ++j) {
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) s += qr[d] * kb[static_cast<int64_t>(j) * kst + d];
+    s *= scale_log2;
+    const float mn = fmaxf(m, s);
+    l = l * fast_exp2(m - mn) + fast_exp2(s - mn);
+    m = mn;
+  }
+  stat[static_cast<int64_t>(bh) * Lp + i] = make_float2(m, 1.f / l);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_colsum_f32(
+    const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const float* __restrict__ k,
+    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, float scale_log2, const float2* __restrict__ stat,
+    float* __restrict__ colsum) {
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  if (j >= Lp) return;
+  const float* kr = k + b * ksb + h * ksh + static_cast<int64_t>(j) * kst;
+  const float* qb = q + b * qsb + h * qsh;
+  float c = 0.f;
+  for (int i = j; i < Lp; ++i) {
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) s += qb[static_cast<int64_t>(i) * qst + d] * kr[d];
+    const float2 st = stat[static_cast<int64_t>(bh) * Lp + i];
+    c += fast_exp2(s * scale_log2 - st.x) * st.y;
+  }
+  colsum[static_cast<int64_t>(bh) * Lp + j] = c;
+}
+
+// Pass 3: eviction at length = Lp, then the kept tokens go to slots 0..n-1 in
+// ascending position order. Dynamic LDS: scores, positions and the slot map
+// (12 bytes per prompt token).
+template <int RB>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_evict(
+    const char* __restrict__ k, const char* __restrict__ v, int64_t sb, int64_t sh, int64_t st, int H, int Lp,
+    int n_heavy, int n_recent, const float* __restrict__ colsum, char* __restrict__ kc, char* __restrict__ vc,
+    int* __restrict__ pos_g, float* __restrict__ acc_g, int cap) {
+  extern __shared__ unsigned char smem[];
+  float* s_val = reinterpret_cast<float*>(smem);
+  int* s_pos = reinterpret_cast<int*>(s_val + Lp);
+  int* s_map = s_pos + Lp;
+  __shared__ unsigned dh[256];
+  __shared__ unsigned scratch[kWaves + 1];
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  for (int j = threadIdx.x; j < Lp; j += kThreads) {
+    s_val[j] = colsum[static_cast<int64_t>(bh) * Lp + j];
+    s_pos[j] = j;
+  }
+  __syncthreads();
+  const int budget = n_heavy + n_recent;
+  const int rthr = Lp - n_recent;
+  unsigned long long prefix = 0;
+  const bool evicting = Lp > budget;
+  if (evicting) prefix = evict_threshold(s_val, s_pos, Lp, rthr, static_cast<unsigned>(Lp - budget), dh);
+  const int seg = (Lp + kThreads - 1) / kThreads;
+  const int a0 = min(Lp, static_cast<int>(threadIdx.x) * seg), a1 = min(Lp, a0 + seg);
+  unsigned cnt = 0;
+  for (int j = a0; j < a1; ++j)
+    cnt += !(evicting && j < rthr && evict_key(s_val[j], j) <= prefix);
+  unsigned total;
+  unsigned slot = block_excl_scan<kThreads>(cnt, scratch, &total);
+  for (int j = a0; j < a1; ++j)
+    if (!(evicting && j < rthr && evict_key(s_val[j], j) <= prefix)) s_map[slot++] = j;
+  __syncthreads();
+  const int n = static_cast<int>(min(total, static_cast<unsigned>(cap)));
+  const int64_t slot0 = static_cast<int64_t>(bh) * cap;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    pos_g[slot0 + i] = s_map[i];
+    acc_g[slot0 + i] = s_val[s_map[i]];
+  }
+  constexpr int kPieces = RB / 16;
+  const int64_t base = b * sb + h * sh;
+  for (int i = threadIdx.x; i < n * kPieces; i += kThreads) {
+    const int r = i / kPieces, c = i - r * kPieces;
+    const int64_t src = base + static_cast<int64_t>(s_map[r]) * st + c * 16;
+    const int64_t dst = (slot0 + r) * RB + c * 16;
+    *reinterpret_cast<u32x4_t*>(kc + dst) = *reinterpret_cast<const u32x4_t*>(k + src);
+    *reinterpret_cast<u32x4_t*>(vc + dst) = *reinterpret_cast<const u32x4_t*>(v + src);
+  }
+}
+
+template <int D>
+void launch_prefill_passes(const uint16_t* q, kvc_strides qs, const uint16_t* k, kvc_strides kvs, int H,
+                           int64_t BH, int Lp, float scale_log2, float2* stat, float* colsum, hipStream_t stream) {
+  const dim3 g((Lp + kPTile - 1) / kPTile, static_cast<unsigned>(BH));
+  h2o_prefill_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp,
+                                                       scale_log2, stat);
+  h2o_prefill_colsum_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp,
+                                                        scale_log2, stat, colsum);
+}
+
+template <int D>
+void launch_prefill_passes(const float* q, kvc_strides qs, const float* k, kvc_strides kvs, int H, int64_t BH,
+                           int Lp, float scale_log2, float2* stat, float* colsum, hipStream_t stream) {
+  const dim3 g((Lp + kThreads - 1) / kThreads, static_cast<unsigned>(BH));
+  h2o_prefill_stats_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp,
+                                                      scale_log2, stat);
+  h2o_prefill_colsum_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp,
+                                                       scale_log2, stat, colsum);
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -313,5 +562,86 @@ extern "C" kvc_status kvc_h2o_step(kvc_h2o_cache* c, const void* q, const void* 
   const int budget = n_heavy + n_recent;
   c->n = c->n + 1 > budget ? budget : c->n + 1;
   c->len += 1;
+  return KVC_OK;
+}
+
+extern "C" size_t kvc_h2o_prefill_workspace_bytes(int B, int H, int prompt_len) {
+  if (B <= 0 || H <= 0 || prompt_len <= 0) return 0;
+  return align_up(static_cast<size_t>(B) * H * prompt_len * 8, 256) +
+         align_up(static_cast<size_t>(B) * H * prompt_len * 4, 256);
+}
+
+extern "C" kvc_status kvc_h2o_prefill(kvc_h2o_cache* c, const void* q, kvc_strides qs, const void* k,
+                                      const void* v, kvc_strides kvs, int prompt_len, int n_heavy, int n_recent,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (!c) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: cache is NULL");
+  if (!c->k || !c->v || !c->pos || !c->acc || !q || !k || !v)
+    return fail(KVC_ERR_INVALID_ARG, "h2o prefill: cache arrays, q, k and v must be non-NULL");
+  if (c->dt != KVC_BF16 && c->dt != KVC_F32) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: unknown dtype");
+  if (c->B <= 0 || c->H <= 0 || c->cap <= 0) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: B, H, cap must be positive");
+  if (c->D != 64 && c->D != 128) return fail(KVC_ERR_UNSUPPORTED, "h2o prefill: head_dim %d not in {64, 128}", c->D);
+  if (static_cast<int64_t>(c->B) * c->H > 65535) return fail(KVC_ERR_UNSUPPORTED, "h2o prefill: B*H must be <= 65535");
+  if (prompt_len < 1) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: prompt_len must be >= 1");
+  if (prompt_len > kMaxCap) return fail(KVC_ERR_UNSUPPORTED, "h2o prefill: prompt_len %d > %d", prompt_len, kMaxCap);
+  if (n_heavy < 0 || n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: n_heavy and n_recent must be >= 0");
+  const int64_t budget = static_cast<int64_t>(n_heavy) + n_recent;
+  const int keep = static_cast<int>(prompt_len < budget ? prompt_len : budget);
+  if (keep > c->cap) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: %d kept tokens exceed cap %d", keep, c->cap);
+  const int64_t es = c->dt == KVC_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(c->k) || !aligned16(c->v))
+    return fail(KVC_ERR_INVALID_ARG, "h2o prefill: K/V and q/k/v pointers must be 16-byte aligned");
+  const int64_t strides[6] = {qs.b, qs.h, qs.t, kvs.b, kvs.h, kvs.t};
+  for (int64_t s : strides)
+    if (s < 0 || (s * es) % 16 != 0)
+      return fail(KVC_ERR_INVALID_ARG, "h2o prefill: strides must be non-negative and multiples of 16 bytes");
+  if (qs.t < c->D || kvs.t < c->D) return fail(KVC_ERR_INVALID_ARG, "h2o prefill: row strides must be >= head_dim");
+  const size_t need = kvc_h2o_prefill_workspace_bytes(c->B, c->H, prompt_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVC_ERR_WORKSPACE, "h2o prefill: workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const int64_t BH = static_cast<int64_t>(c->B) * c->H;
+  float2* stat = static_cast<float2*>(workspace);
+  float* colsum = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align_up(static_cast<size_t>(BH) * prompt_len * 8, 256));
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(c->D)));
+  if (c->dt == KVC_BF16) {
+    if (c->D == 128)
+      launch_prefill_passes<128>(static_cast<const uint16_t*>(q), qs, static_cast<const uint16_t*>(k), kvs, c->H, BH,
+                                 prompt_len, scale_log2, stat, colsum, stream);
+    else
+      launch_prefill_passes<64>(static_cast<const uint16_t*>(q), qs, static_cast<const uint16_t*>(k), kvs, c->H, BH,
+                                prompt_len, scale_log2, stat, colsum, stream);
+  } else {
+    if (c->D == 128)
+      launch_prefill_passes<128>(static_cast<const float*>(q), qs, static_cast<const float*>(k), kvs, c->H, BH,
+                                 prompt_len, scale_log2, stat, colsum, stream);
+    else
+      launch_prefill_passes<64>(static_cast<const float*>(q), qs, static_cast<const float*>(k), kvs, c->H, BH,
+                                prompt_len, scale_log2, stat, colsum, stream);
+  }
+  const size_t smem = static_cast<size_t>(prompt_len) * 12;
+  const int rb = static_cast<int>(c->D * es);
+  const unsigned grid = static_cast<unsigned>(BH);
+  const char* kb = static_cast<const char*>(k);
+  const char* vb = static_cast<const char*>(v);
+  char* kc = static_cast<char*>(c->k);
+  char* vc = static_cast<char*>(c->v);
+  if (rb == 128)
+    h2o_prefill_evict<128><<<grid, kThreads, smem, stream>>>(kb, vb, kvs.b * es, kvs.h * es, kvs.t * es, c->H,
+                                                            prompt_len, n_heavy, n_recent, colsum, kc, vc, c->pos,
+                                                            c->acc, c->cap);
+  else if (rb == 256)
+    h2o_prefill_evict<256><<<grid, kThreads, smem, stream>>>(kb, vb, kvs.b * es, kvs.h * es, kvs.t * es, c->H,
+                                                            prompt_len, n_heavy, n_recent, colsum, kc, vc, c->pos,
+                                                            c->acc, c->cap);
+  else
+    h2o_prefill_evict<512><<<grid, kThreads, smem, stream>>>(kb, vb, kvs.b * es, kvs.h * es, kvs.t * es, c->H,
+                                                            prompt_len, n_heavy, n_recent, colsum, kc, vc, c->pos,
+                                                            c->acc, c->cap);
+  const kvc_status st = check_launch("h2o prefill");
+  if (st != KVC_OK) return st;
+  c->n = keep;
+  c->len = prompt_len;
   return KVC_OK;
 }

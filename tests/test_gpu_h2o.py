@@ -57,6 +57,36 @@ class SideBySide:
         self.diverged = {}
         self.out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
 
+    def prefill(self, qn, kn, vn, hh, r):
+        """GPU prefill and oracle prefill from the same prompt [B,H,Lp,D]; compare the states."""
+        q, k, v = (par.to_device(x, self.dtype) for x in (qn, kn, vn))
+        self.gpu.prefill(q, k, v, hh, r)
+        Lp = kn.shape[2]
+        n = self.gpu.n
+        assert self.gpu.length == Lp and n == min(Lp, hh + r)
+        pos_g = self.gpu.pos[..., :n].cpu().numpy()
+        acc_g = self.gpu.acc[..., :n].cpu().numpy()
+        kc, vc = par.to_host_bits(self.gpu.k[..., :n, :]), par.to_host_bits(self.gpu.v[..., :n, :])
+        for bh in list(self.live):
+            b, h = bh
+            st, colsum = ref.prefill_head(qn[b, h], kn[b, h], vn[b, h], hh, r, self.dtype)
+            self.states[bh] = st
+            gpos = pos_g[b, h]
+            assert np.all(np.diff(gpos) > 0), f"{bh}: prefill slots not in ascending position order"
+            np.testing.assert_array_equal(kc[b, h], kn[b, h][gpos])
+            np.testing.assert_array_equal(vc[b, h], vn[b, h][gpos])
+            par.assert_close_votes(acc_g[b, h], colsum[gpos], f"prefill acc{bh}")
+            if set(gpos.tolist()) != set(st.pos.tolist()):
+                keep_ref = np.zeros(Lp, bool)
+                keep_ref[st.pos] = True
+                cand = np.flatnonzero(np.arange(Lp) < Lp - r)
+                order = cand[np.lexsort((-cand, -colsum[cand]))]
+                n_fill = hh + r - int((np.arange(Lp) >= Lp - r).sum())
+                a_keep, a_ev = colsum[order[n_fill - 1]], colsum[order[n_fill]]
+                assert a_keep - a_ev <= par.REL * abs(a_keep), f"{bh}: prefill sets differ across a clear gap"
+                self.diverged[bh] = Lp
+                self.live.discard(bh)
+
     def step(self, qn, kn, vn, hh, r):
         q, k, v = (par.to_device(x, self.dtype) for x in (qn, kn, vn))
         self.gpu.step(q, k, v, hh, r, attn_out=self.out)
@@ -155,6 +185,54 @@ def test_h2o_decode_shape_sampled_heads():
     the oracle follows six sampled heads."""
     wl = syn.H2O_WORKLOADS["opt6.7b-decode"]
     _run(wl, 64, heads=[(0, 0), (5, 7), (17, 31), (33, 2), (50, 16), (63, 31)])
+
+
+def _prefill_run(wl, steps, heads=None, policy=None):
+    """GPU prefill of the prompt, then decode steps; the oracle follows the sampled heads from its own
+    prefill state."""
+    heads = heads or [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    policy = policy or (lambda length: (wl.n_heavy(length), wl.n_recent(length)))
+    final = wl.prompt_len + steps
+    cap = max(sum(policy(t)) for t in range(wl.prompt_len, final + 1)) + 1
+    print(f"[h2o-prefill] B{wl.B} H{wl.H} D{wl.D} {wl.dtype} prompt {wl.prompt_len} + {steps} steps, cap {cap}",
+          flush=True)
+    lf = SideBySide(wl.B, wl.H, wl.D, cap, wl.dtype, heads)
+    dt = np.float32 if wl.dtype == "fp32" else np.uint16
+    qn = np.empty((wl.B, wl.H, wl.prompt_len, wl.D), dt)
+    kn, vn = np.empty_like(qn), np.empty_like(qn)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            qn[b, h], kn[b, h], vn[b, h], _ = syn.h2o_prompt_head(wl, b, h)
+    hh, r = policy(wl.prompt_len)
+    lf.prefill(qn, kn, vn, hh, r)
+    for s_ in range(steps):
+        hh, r = policy(wl.prompt_len + s_ + 1)
+        lf.step(*syn.h2o_step_inputs(wl, s_), hh, r)
+    print(f"[h2o-prefill] diverged at near-ties: {lf.diverged}", flush=True)
+    assert len(lf.diverged) <= max(1, len(heads) // 4)
+    return lf
+
+
+def test_h2o_prefill_small_bf16():
+    _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=2, H=3, prompt_len=200), 40)
+
+
+def test_h2o_prefill_fp32_d64():
+    _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=2, D=64, prompt_len=77, dtype="fp32", seed=9),
+                 20)
+
+
+def test_h2o_prefill_budget_never_binds():
+    """No eviction: every prompt token is kept with its full causal column sum."""
+    lf = _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=2, prompt_len=300), 0,
+                      policy=lambda t: (400, 400))
+    assert lf.gpu.n == 300
+
+
+def test_h2o_prefill_decode_shape_sampled_heads():
+    """The 64 x 32-head layer with its 2048-token prompt, then 32 decode steps."""
+    _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"], 32,
+                 heads=[(0, 0), (9, 3), (31, 31), (40, 17), (63, 0)])
 
 
 def test_h2o_error_statuses():
