@@ -27,6 +27,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 PHASES = ["zero", "stats", "merge", "votes", "classify", "finalize", "gather"]
+# the same boundaries under the single-pass schedule: counter reset, the score
+# pass, (nothing), pooling + histogram, then the shared selection phases
+PHASES_SINGLE = ["reset", "score", "none", "pool", "classify", "finalize", "gather"]
+SCHEDULES = {"auto": 0, "two-pass": 1, "single-pass": 2}
 
 
 def log(msg):
@@ -39,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="131k-bf16")
+    ap.add_argument("--schedule", choices=sorted(SCHEDULES), default="auto",
+                    help="SnapKV score schedule (auto: single pass where it can run)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-h2o", action="store_true")
@@ -107,8 +113,10 @@ def snapkv_bytes(wl):
     q_read = BH * wl.window * wl.D * es
     gather = 4 * BH * wl.budget * wl.D * es
     idx = 4 * BH * (wl.budget - wl.window)
+    votes_out = 4 * BH * (wl.L - wl.window)
     return dict(total=k_read + q_read + gather + idx, stats=k_read + q_read,
-                votes=BH * (wl.L - wl.window) * wl.D * es + q_read, gather=gather + idx)
+                votes=BH * (wl.L - wl.window) * wl.D * es + q_read,
+                score=k_read + q_read + votes_out, gather=gather + idx)
 
 
 def bench_snapkv(args, ev):
@@ -147,10 +155,15 @@ def bench_snapkv(args, ev):
         lib.kvc_snapkv_set_phase_events(ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
                                         n_ev if arr is not None else 0)
 
+    lib.kvc_snapkv_set_schedule(SCHEDULES[args.schedule])
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    # Timed region: events only around the two score passes (boundaries 1, 2 and 4;
+    single = kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
+    phases = PHASES_SINGLE if single else PHASES
+    passes = ("score", "pool") if single else ("stats", "votes")
+    log(f"schedule: {'single pass' if single else 'two passes'}")
+    # Timed region: events only around the score passes (boundaries 1, 2 and 4;
     # every recorded event costs the GPU a few microseconds).
     timed = []
     for _ in range(args.steps):
@@ -168,8 +181,8 @@ def bench_snapkv(args, ev):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     set_events(None)
-    kern_ms = {"stats": sum(ev.ms(e[0], e[1]) for e in timed) / args.steps,
-               "votes": sum(ev.ms(e[1], e[2]) for e in timed) / args.steps}
+    kern_ms = {passes[0]: sum(ev.ms(e[0], e[1]) for e in timed) / args.steps,
+               passes[1]: sum(ev.ms(e[1], e[2]) for e in timed) / args.steps}
     # Untimed instrumented pass: every phase boundary, for the breakdown only.
     events = [ev.create(n_ev) for _ in range(args.steps)]
     for i in range(args.steps):
@@ -177,16 +190,17 @@ def bench_snapkv(args, ev):
         call()
     torch.cuda.synchronize()
     set_events(None)
-    phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / args.steps for j, p in enumerate(PHASES)}
+    lib.kvc_snapkv_set_schedule(0)
+    phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / args.steps for j, p in enumerate(phases)}
     step_ms = elapsed / args.steps * 1e3
     nbytes = snapkv_bytes(wl)
-    dominant = max(("stats", "votes"), key=lambda p: kern_ms[p])
+    dominant = "score" if single else max(("stats", "votes"), key=lambda p: kern_ms[p])
     dom_bytes = nbytes[dominant]
     achieved = dom_bytes / (kern_ms[dominant] * 1e-3)
     suffix = "bf16" if wl.dtype == "bf16" else "f32"
-    kernel_name = f"snap_{dominant}_{suffix}"
+    kernel_name = "snap_coop_bf16" if single else f"snap_{dominant}_{suffix}"
     traffic = load_traffic(kernel_name, ["snapkv.hip", "common.hpp"])
-    log(f"step {step_ms:.3f} ms; phases (ms): " + ", ".join(f"{p} {phase_ms[p]:.4f}" for p in PHASES))
+    log(f"step {step_ms:.3f} ms; phases (ms): " + ", ".join(f"{p} {phase_ms[p]:.4f}" for p in phases))
     return dict(
         wl=wl, qn=qn, kn=kn, vn=vn, step_ms=step_ms, elapsed=elapsed,
         value=B * L * args.steps / elapsed,
@@ -195,7 +209,7 @@ def bench_snapkv(args, ev):
                   "frac": achieved / PEAK_HBM, "traffic": traffic, "kernel": kernel_name,
                   "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": kern_ms[dominant],
                   "score_pass_ms": kern_ms},
-        phase_ms=phase_ms, alg_bytes=nbytes["total"])
+        phase_ms=phase_ms, alg_bytes=nbytes["total"], schedule="single-pass" if single else "two-pass")
 
 
 def cpu_baseline(res, seconds):
@@ -346,7 +360,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"snapkv-{wl.name}", "batch": wl.B, "heads": wl.H, "head_dim": wl.D,
                    "prompt_len": wl.L, "window": wl.window, "budget": wl.budget,
-                   "pool_kernel": wl.pool_kernel},
+                   "pool_kernel": wl.pool_kernel, "schedule": res["schedule"]},
         "hbm_gbps_path": res["path_gbps"],
         "hbm_frac_path": res["path_gbps"] * 1e9 / PEAK_HBM,
         "algorithmic_bytes_per_step": res["alg_bytes"],

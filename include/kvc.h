@@ -112,12 +112,46 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Score schedules of kvc_snapkv_compress. Both compute every score in fp32
+ * from the same bf16 / fp32 inputs and select by the same rule; they differ in
+ * how often K is read and in how each window row's softmax normaliser is
+ * formed (so votes may differ in the last bits).
+ *   TWO_PASS     row statistics (max, sum) in one pass over K, votes in a
+ *                second: K is read twice. Bitwise reproducible.
+ *   SINGLE_PASS  bf16 only: one device-wide cooperative pass keeps each key
+ *                tile's scores in registers until its head's normaliser is
+ *                complete, so K is read once. Each row's normaliser is summed
+ *                exactly in fixed point, so the result does not depend on the
+ *                order of the contributions (bitwise reproducible as well).
+ *                It needs cooperative launch and a head of at most four
+ *                device-wide rounds of 128-key units (on MI355X, up to about
+ *                256K keys per head for one head); otherwise the call uses
+ *                TWO_PASS.
+ *   AUTO         the default: TWO_PASS, the faster of the two on MI355X at
+ *                the sizes measured so far. */
+typedef enum {
+  KVC_SNAPKV_AUTO = 0,
+  KVC_SNAPKV_TWO_PASS = 1,
+  KVC_SNAPKV_SINGLE_PASS = 2
+} kvc_snapkv_schedule;
+
+/* Select the schedule for later kvc_snapkv_compress calls on the calling
+ * thread. Returns the previous setting, or -1 (and changes nothing) for an
+ * unknown value. */
+int kvc_snapkv_set_schedule(int schedule);
+
+/* The schedule (TWO_PASS or SINGLE_PASS) the last successful
+ * kvc_snapkv_compress call on the calling thread ran, 0 if none. */
+int kvc_snapkv_last_schedule(void);
+
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its
  * stream at phase boundary i, for i < n_events (at most 8) and events[i] not
  * NULL (each recorded event costs a few microseconds of GPU time): 0 before the
  * first kernel, then after the workspace clear (1), the row-statistics pass
- * (2), the row-statistics merge (3), the vote + pooling + histogram pass (4),
+ * (2; the single score pass under SINGLE_PASS), the row-statistics merge (3;
+ * nothing separate under either schedule), the vote + pooling + histogram pass
+ * (4; pooling + histogram under SINGLE_PASS),
  * classification (5), the final selection (6) and the gather (7). The events are created and owned
  * by the caller; pass NULL or 0 to stop recording. */
 void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events);

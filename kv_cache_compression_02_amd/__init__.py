@@ -14,6 +14,7 @@ Entry points (same names as the C ABI, without the ``kvc_`` prefix):
   H2OCache.step       H2O decode step (kvc_h2o_step)
   SinkCache.append    StreamingLLM sink + recent ring (kvc_sink_recent)
 """
+import contextlib
 import ctypes
 import os
 from collections import namedtuple
@@ -23,16 +24,18 @@ import torch
 __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
     "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS",
+    "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
 ]
 
 KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
 KVC_F32, KVC_BF16 = 0, 1
+SNAPKV_AUTO, SNAPKV_TWO_PASS, SNAPKV_SINGLE_PASS = 0, 1, 2
 _STATUS_NAMES = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED_SYMBOLS = (
     "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
-    "kvc_h2o_prefill_workspace_bytes",
+    "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +95,10 @@ def library():
                                   vp, sz, vp]
     L.kvc_snapkv_set_phase_events.restype = None
     L.kvc_snapkv_set_phase_events.argtypes = [vp, i32]
+    L.kvc_snapkv_set_schedule.restype = i32
+    L.kvc_snapkv_set_schedule.argtypes = [i32]
+    L.kvc_snapkv_last_schedule.restype = i32
+    L.kvc_snapkv_last_schedule.argtypes = []
     L.kvc_sink_recent.restype = i32
     L.kvc_sink_recent.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
     _lib = L
@@ -137,6 +144,24 @@ def snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, dtype):
 
 
 SnapKVResult = namedtuple("SnapKVResult", "k v idx pooled vote")
+
+
+@contextlib.contextmanager
+def snapkv_schedule(schedule):
+    """Run the enclosed snapkv_compress calls (this thread) under ``schedule``
+    (SNAPKV_AUTO, SNAPKV_TWO_PASS or SNAPKV_SINGLE_PASS; kvc_snapkv_set_schedule)."""
+    prev = library().kvc_snapkv_set_schedule(int(schedule))
+    if prev < 0:
+        raise ValueError(f"unknown SnapKV schedule {schedule!r}")
+    try:
+        yield
+    finally:
+        library().kvc_snapkv_set_schedule(prev)
+
+
+def snapkv_last_schedule():
+    """Schedule the last successful snapkv_compress call on this thread ran (0 if none)."""
+    return int(library().kvc_snapkv_last_schedule())
 
 
 def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,

@@ -31,6 +31,9 @@
 // arithmetic.
 #include <math.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "common.hpp"
 
 namespace kvc {
@@ -385,6 +388,508 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
 }
 
+// ------------------------------------ single-pass scores (cooperative, bf16)
+//
+// One read of K. A persistent grid of G workgroups (two per compute unit, all
+// resident: cooperative launch) walks units of kCoopUnit consecutive keys of
+// one head: workgroup g takes units u = r*G + g in rounds r = 0, 1, .... In
+// round r it
+//   * writes the votes of the unit of round r - kCoopLag, whose scores waited
+//     in register bank (r - kCoopLag) % kCoopBanks; they need the head's
+//     log-normaliser c_i = log2(sum_j 2^(s_ij)) of every window row i;
+//   * scores the unit of round r from K staged in LDS by direct-to-LDS loads
+//     issued during round r - 1, into bank r % kCoopBanks, and adds the
+//     unit's per-row l * 2^(m - R_i) (m the unit's row max, l its sum of
+//     2^(s - m)) to the head's row accumulators.
+// R_i is a reference score of row i (its largest score against the window's
+// own keys, computed beforehand), so every accumulated term is bounded below
+// by the window key's own term of about 1. The accumulators are fixed-point
+// integers (kCoopDigits 32-bit digits, lowest weight 2^kCoopDigitBase
+// relative to 2^R_i) summed with integer atomics, so the total is the same
+// in every order. Completion is counted per head: the workgroup whose count
+// increment finishes a head converts its digits into c_i and publishes them,
+// tagged ready. Each cross-workgroup step waits only on something issued a
+// round earlier (a contribution is complete before the count is raised, the
+// count's return picks the finisher, the digits' loads land before the
+// conversion, readers prefetch c a round ahead): at HBM-saturating load such
+// round trips take microseconds, and none of them stalls the K stream.
+// A unit whose row max exceeds R_i by more than kCoopOvfGap (a logit spread
+// beyond the fixed-point range) flags its head, whose c_i is then merged
+// exactly from the per-unit (m, l) partials in unit order.
+constexpr int kCoopThreads = 256;            // 4 waves, one 32-key tile each per unit
+constexpr int kCoopUnit = kWaves * kTile;    // 128 keys
+constexpr int kCoopBanks = 8;
+constexpr int kCoopLag = kCoopBanks - 1;     // rounds between a unit's scores and its votes
+constexpr int kCoopDigits = 11;
+constexpr int kCoopDigitBase = -160;
+constexpr int kCoopRowWords = 16;            // 64-bit words per row accumulator: one 128-byte line
+constexpr int kCoopHeadWords = 32 * kCoopRowWords;
+constexpr int kCoopCtrWords = 32;            // per head: [0] unit count, [16] overflow flag
+constexpr float kCoopOvfGap = 150.f;
+constexpr unsigned kCoopSpin = 1u << 22;
+
+__device__ __forceinline__ void st_agent_u2(uint2* p, uint2 v) {
+  const unsigned long long u = (static_cast<unsigned long long>(v.y) << 32) | v.x;
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint2 ld_agent_u2(const uint2* p) {
+  const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2(static_cast<unsigned>(u), static_cast<unsigned>(u >> 32));
+}
+
+__device__ __forceinline__ unsigned long long ld_agent_u64(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS row layout shared by K tiles and Q: a row is D*2 bytes of kP 16-byte
+// pieces; piece p of row R sits in slot p ^ (R & (kP-1)), so the 32 rows a
+// wave reads for one MFMA k-step hit distinct banks.
+template <int D>
+struct CoopLayout {
+  static constexpr int kRowB = D * 2;
+  static constexpr int kP = kRowB / 16;               // pieces per row (16 or 8)
+  static constexpr int kTileB = kTile * kRowB;        // bytes per 32-row tile
+  static constexpr int kInstPerTile = kTileB / 1024;  // direct loads per tile (64 lanes x 16 B)
+  static constexpr int kRowsPerInst = 1024 / kRowB;
+  static constexpr int kKBytes = kWaves * kTileB;
+  static constexpr int kQBytes = kTileB;              // 32 window rows
+};
+
+// Direct-to-LDS loads of one unit's K tiles (and of the 32 Q rows when
+// with_q), spread over waves 0..2. Rows beyond the data are clamped to valid
+// rows; their scores are masked or never written.
+template <int D>
+__device__ __forceinline__ void coop_issue_loads(const uint16_t* kb, int64_t kst, int key0, int L,
+                                                 const uint16_t* qb, int64_t qst, int w, bool with_q,
+                                                 unsigned char* kbuf, unsigned char* qbuf, int wave, int lane) {
+  using Ly = CoopLayout<D>;
+  const int total = (kWaves + (with_q ? 1 : 0)) * Ly::kInstPerTile;
+  for (int i = wave; i < total; i += 3) {
+    const int tile = i / Ly::kInstPerTile, sub = i - tile * Ly::kInstPerTile;
+    const int row = sub * Ly::kRowsPerInst + lane / Ly::kP;  // row within the tile
+    const int slot = lane % Ly::kP;
+    const int piece = slot ^ (row & (Ly::kP - 1));
+    const uint16_t* src;
+    unsigned char* dst;
+    if (tile < kWaves) {
+      const int key = min(key0 + tile * kTile + row, L - 1);
+      src = kb + static_cast<int64_t>(key) * kst + piece * 8;
+      dst = kbuf + tile * Ly::kTileB + sub * 1024;
+    } else {
+      src = qb + static_cast<int64_t>(min(row, w - 1)) * qst + piece * 8;
+      dst = qbuf + sub * 1024;
+    }
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+  }
+}
+
+// MFMA fragment of row R (lane & 31) from a swizzled LDS tile: k-step s of
+// half h uses piece h*(kP/2) + s.
+template <int D>
+__device__ __forceinline__ bf16x8_t lds_frag(const unsigned char* tile, int R, int half, int s) {
+  using Ly = CoopLayout<D>;
+  const int piece = half * (Ly::kP / 2) + s;
+  const int slot = piece ^ (R & (Ly::kP - 1));
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(tile + R * Ly::kRowB + slot * 16));
+}
+
+// Workgroup barrier for LDS exchanges only: waits for this wave's LDS
+// operations, not for its vector-memory ones, so direct-to-LDS loads of the
+// next round (and pending global stores) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Reference score of every window row (largest score against the window's
+// own keys it sees), and the per-head state of the single pass cleared: row
+// accumulators, count and overflow flag, published normalisers, histogram
+// and selection counters. One workgroup per head.
+template <int D>
+__global__ __launch_bounds__(kThreads) void snap_coop_prep(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
+    float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
+    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr) {
+  __shared__ float red[32][33];
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  for (int i = threadIdx.x; i < kCoopHeadWords; i += kThreads) acc[static_cast<int64_t>(bh) * kCoopHeadWords + i] = 0;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
+  if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
+  if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
+  if (threadIdx.x < 4) ctr[bh * 4 + threadIdx.x] = 0;
+  const int t0 = L - w;
+  const int i = threadIdx.x >> 3;  // window row
+  const uint16_t* qr = q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + min(i, w - 1)) * qst;
+  for (int jj = (threadIdx.x & 7); jj < 32; jj += 8) {
+    float sv = -INFINITY;
+    if (i < w && jj <= i) {
+      const uint16_t* kr = k + b * ksb + h * ksh + static_cast<int64_t>(t0 + jj) * kst;
+      float d = 0.f;
+      for (int e = 0; e < D; ++e)
+        d = fmaf(__uint_as_float(static_cast<unsigned>(qr[e]) << 16), __uint_as_float(static_cast<unsigned>(kr[e]) << 16), d);
+      sv = d * scale_log2;
+    }
+    red[i][jj] = sv;
+  }
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float m = -INFINITY;
+    for (int jj = 0; jj < 32; ++jj) m = fmaxf(m, red[threadIdx.x][jj]);
+    ref[bh * 32 + threadIdx.x] = threadIdx.x < w ? m : 0.f;
+  }
+}
+
+// Everything one workgroup of the single pass needs across rounds.
+struct CoopCtx {
+  const uint16_t* q;
+  int64_t qsb, qsh, qst;
+  int qrow0;
+  const uint16_t* k;
+  int64_t ksb, ksh, kst;
+  int H, L, w, t0, nunit, G, g, rounds;
+  float scale_log2;
+  const float* ref;
+  unsigned long long* acc;
+  unsigned* cnt;
+  uint2* stat;
+  float2* part;
+  unsigned* status;
+  float* vote;
+  unsigned char* kbuf;
+  unsigned char* qbuf;
+  float2 (*wred)[32];
+  float* s_c;
+  unsigned long long (*s_fin)[kCoopDigits + 1];
+  int wave, lane, col, half;
+};
+
+// Wave 3's bookkeeping carried from round to round.
+struct CoopPipe {
+  int ack_head;                  // head of the unit contributed last round (its count is due)
+  int cnt_head;                  // head whose count was raised last round
+  unsigned cnt_ret;              // that count's value before the increment
+  int fin_head;                  // head being finished: its digits were loaded last round
+  unsigned long long fin[6];     // lanes 0..31: digits 0..5 of row lane; 32..63: digits 6..10, overflow flag
+  float fin_ref;                 // that head's reference score of row lane & 31
+  uint2 pre;                     // normaliser prefetched for the next round's votes
+  float ref;                     // reference score of row lane & 31 for this round's unit
+  int q_head;                    // head whose Q rows sit in LDS
+};
+
+__device__ __forceinline__ int coop_head(const CoopCtx& c, int r) { return (r * c.G + c.g) / c.nunit; }
+
+template <int D>
+__device__ __forceinline__ void coop_issue(const CoopCtx& c, CoopPipe& p, int r) {
+  const int u = r * c.G + c.g;
+  const int bh = u / c.nunit, key0 = (u - bh * c.nunit) * kCoopUnit;
+  const bool with_q = bh != p.q_head;
+  p.q_head = bh;
+  if (c.wave >= 3) return;
+  const int b = bh / c.H, h = bh - b * c.H;
+  coop_issue_loads<D>(c.k + b * c.ksb + h * c.ksh, c.kst, key0, c.L,
+                      c.q + b * c.qsb + h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst, c.qst, c.w, with_q,
+                      c.kbuf, c.qbuf, c.wave, c.lane);
+}
+
+// The head's normaliser from its digits (lanes 0..31 hold row lane's digits
+// 0..5, lanes 32..63 its digits 6..10), staged through LDS: exact carry
+// propagation, the total's leading 24 bits as m * 2^E with m in [1, 2), then
+// c = R + E + log2(m). The result is meaningful in lanes 0..31.
+__device__ __forceinline__ float coop_digits_to_c(const unsigned long long (&fin)[6],
+                                                 unsigned long long (*s_fin)[kCoopDigits + 1], int lane, float R) {
+  const int row = lane & 31, d0 = lane < 32 ? 0 : 6;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) s_fin[row][d0 + i] = fin[i];  // lanes 32..63 put the flag in the spare word
+  float cv = R;
+  if (lane < 32) {
+    unsigned long long carry = 0;
+    int top = -1;
+#pragma unroll 1
+    for (int i = 0; i < kCoopDigits; ++i) {
+      const unsigned long long v = s_fin[row][i] + carry;
+      s_fin[row][i] = v & 0xffffffffull;
+      carry = v >> 32;
+      if (v & 0xffffffffull) top = i;
+    }
+    if (top >= 0) {
+      unsigned long long v = (s_fin[row][top] << 32) | (top > 0 ? s_fin[row][top - 1] : 0ull);
+      const int lz = __clzll(static_cast<long long>(v));
+      v <<= lz;  // total ~ v * 2^(kCoopDigitBase + 32 (top - 1) - lz), leading bit at 63
+      const int E = kCoopDigitBase + 32 * (top - 1) - lz + 63;
+      const float mf = __uint_as_float(0x3f800000u | static_cast<unsigned>((v >> 40) & 0x7fffffu));
+      cv = R + (static_cast<float>(E) + log2f(mf));
+    }
+  }
+  return cv;
+}
+
+// Exact normaliser of a flagged head: merge of its per-unit (m, l) partials
+// in unit order (lanes 0..31, one row each).
+__device__ __forceinline__ float coop_exact_c(const CoopCtx& c, int bh, int row) {
+  float m = kNegBig, l = 0.f;
+  const float2* pb = c.part + static_cast<int64_t>(bh) * c.nunit * 32;
+  for (int u0 = 0; u0 < c.nunit; u0 += 4) {
+    uint2 pp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pp[i] = u0 + i < c.nunit ? ld_agent_u2(reinterpret_cast<const uint2*>(&pb[(u0 + i) * 32 + row]))
+                               : make_uint2(__float_as_uint(kNegBig), 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse2_merge(m, l, __uint_as_float(pp[i].x), __uint_as_float(pp[i].y));
+  }
+  return m + log2f(l);
+}
+
+// End-of-round bookkeeping of wave 3 (after the unit's row statistics are in
+// (m, l) of lanes 0..31 when `contributed`), entered after the round's
+// closing wait: whatever it issues is used only after the next round's.
+__device__ __forceinline__ void coop_bookkeeping(const CoopCtx& c, CoopPipe& p, bool contributed, int unit, float m,
+                                                 float l) {
+  const int row = c.lane & 31;
+  // (a) finish the head whose digits were loaded last round
+  if (p.fin_head >= 0) {
+    const bool ovf = __shfl(static_cast<unsigned>(p.fin[5]), 32) != 0u;
+    float cv;
+    if (!ovf) {
+      cv = coop_digits_to_c(p.fin, c.s_fin, c.lane, p.fin_ref);
+    } else {
+      cv = c.lane < 32 && row < c.w ? coop_exact_c(c, p.fin_head, row) : 0.f;
+    }
+    if (c.lane < 32 && row < c.w) st_agent_u2(&c.stat[p.fin_head * 32 + row], make_uint2(__float_as_uint(cv), 1u));
+    p.fin_head = -1;
+  }
+  // (b) the count raised last round: its last unit makes this workgroup the finisher
+  if (p.cnt_head >= 0) {
+    if (__shfl(p.cnt_ret, 0) == static_cast<unsigned>(c.nunit - 1)) {
+      const unsigned long long* a = c.acc + static_cast<int64_t>(p.cnt_head) * kCoopHeadWords + row * kCoopRowWords;
+      const int d0 = c.lane < 32 ? 0 : 6;
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        if (d0 + i < kCoopDigits)
+          p.fin[i] = ld_agent_u64(a + d0 + i);
+        else
+          p.fin[i] = __hip_atomic_load(&c.cnt[p.cnt_head * kCoopCtrWords + 16], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      }
+      p.fin_ref = c.ref[p.cnt_head * 32 + row];
+      p.fin_head = p.cnt_head;
+    }
+    p.cnt_head = -1;
+  }
+  // (c) last round's contributions are complete: count their unit
+  if (p.ack_head >= 0) {
+    unsigned ret = 0;
+    if (c.lane == 0) ret = atomicAdd(&c.cnt[p.ack_head * kCoopCtrWords], 1u);
+    p.cnt_ret = ret;
+    p.cnt_head = p.ack_head;
+    p.ack_head = -1;
+  }
+  // (d) this round's contribution (its reference scores were loaded at the round's start)
+  const float R = p.ref;
+  if (contributed) {
+    const int u = unit;
+    const int bh = u / c.nunit;
+    if (c.lane < 32) {
+      st_agent_u2(reinterpret_cast<uint2*>(&c.part[static_cast<int64_t>(u) * 32 + row]),
+                  make_uint2(__float_as_uint(m), __float_as_uint(l)));
+      if (row < c.w) {
+        const float gap = m - R;
+        if (gap > kCoopOvfGap) {
+          atomicOr(&c.cnt[bh * kCoopCtrWords + 16], 1u);
+        } else if (gap > static_cast<float>(kCoopDigitBase - 40)) {  // smaller terms fall below digit 0
+          // l * 2^gap = y * 2^n with y = l * 2^(gap - n) in [l, 2l), l >= 1 (the unit's max term);
+          // y = mant * 2^(ey - 23) exactly, so the term is mant at bit ey - 23 + n - kCoopDigitBase
+          const float n = floorf(gap);
+          const float y = l * fast_exp2(gap - n);
+          const unsigned bits = __float_as_uint(y);
+          unsigned long long mant = (bits & 0x7fffffu) | 0x800000u;
+          int pos = static_cast<int>((bits >> 23) & 0xffu) - 127 - 23 + static_cast<int>(n) - kCoopDigitBase;
+          if (pos < 0) {
+            mant = -pos >= 64 ? 0ull : mant >> -pos;
+            pos = 0;
+          }
+          if (mant) {
+            const unsigned long long v = mant << (pos & 31);  // < 2^56: two digits
+            unsigned long long* a =
+                c.acc + static_cast<int64_t>(bh) * kCoopHeadWords + row * kCoopRowWords + (pos >> 5);
+            atomicAdd(a, v & 0xffffffffull);
+            if (v >> 32) atomicAdd(a + 1, v >> 32);
+          }
+        }
+      }
+    }
+    p.ack_head = bh;
+  }
+}
+
+template <int D, int BANK>
+__device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
+                                           f32x16_t (&sc)[kCoopBanks], int r) {
+  using Ly = CoopLayout<D>;
+  constexpr int KS = D / 16;
+  const int rb = r - kCoopLag;
+  const bool do_b = rb >= 0 && rb < c.rounds, do_a = r < c.rounds;
+  // ---- round start: the previous round's closing wait covered the staged K
+  // and the prefetched normalisers and reference scores
+  if (c.wave == 3) {
+    if (do_b) {
+      const int hb = coop_head(c, rb);
+      const int row = c.lane & 31;
+      uint2 pre = p.pre;
+      if (__ballot(row < c.w && pre.y != 1u) != 0ull) {  // not yet published: wait (bounded)
+        unsigned polls = 0;
+        bool late;
+        do {
+          __builtin_amdgcn_s_sleep(2);
+          pre = ld_agent_u2(&c.stat[hb * 32 + row]);
+          __builtin_amdgcn_s_waitcnt(0);  // every exit from here has its load back
+          late = __ballot(row < c.w && pre.y != 1u) != 0ull;
+        } while (late && ++polls < kCoopSpin);
+        if (late && c.lane == 0) __hip_atomic_store(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      if (c.lane < 32) c.s_c[c.lane] = __uint_as_float(pre.x);
+    }
+    const int last = max(c.rounds - 1, 0);
+    p.pre = ld_agent_u2(&c.stat[coop_head(c, min(max(rb + 1, 0), last)) * 32 + (c.lane & 31)]);
+    p.ref = c.ref[coop_head(c, min(r, last)) * 32 + (c.lane & 31)];
+  }
+  lds_barrier();
+  // ---- votes of the unit of round rb (bank (BANK + 1) % kCoopBanks)
+  if (do_b) {
+    const int u = rb * c.G + c.g;
+    const int bh = u / c.nunit, c0 = (u - bh * c.nunit) * kCoopUnit;
+    const f32x16_t& s = sc[(BANK + 1) % kCoopBanks];
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = acc_row(i, c.half);
+      v += row < c.w ? fast_exp2(s[i] - c.s_c[row]) : 0.f;
+    }
+    v += __shfl_xor(v, 32);
+    const int j = c0 + c.wave * kTile + c.col;
+    if (c.half == 0 && j < c.t0) c.vote[static_cast<int64_t>(bh) * c.t0 + j] = v;
+  }
+  // ---- scores of the unit of round r into bank BANK
+  float m = kNegBig, l = 0.f;
+  int unit = 0;
+  if (do_a) {
+    unit = r * c.G + c.g;
+    const int bh = unit / c.nunit, c0 = (unit - bh * c.nunit) * kCoopUnit;
+    const unsigned char* tile = c.kbuf + c.wave * Ly::kTileB;
+    f32x16_t acc = {}, bt = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8_t qf = lds_frag<D>(c.qbuf, c.col, c.half, s);
+      const bf16x8_t kf = lds_frag<D>(tile, c.col, c.half, s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf, acc, 0, 0, 0);
+      bt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, bt, 0, 0, 0);
+      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments held in flight
+    }
+    const int jt = c0 + c.wave * kTile;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[BANK][i] = acc[i] * c.scale_log2;
+      const int j = jt + acc_row(i, c.half);
+      bt[i] = (j < c.L && j <= c.t0 + c.col) ? bt[i] * c.scale_log2 : kNegBig;
+      m = fmaxf(m, bt[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) l += fast_exp2(bt[i] - m);
+    lds_barrier();  // staged K and Q consumed
+    if (r + 1 < c.rounds) coop_issue<D>(c, p, r + 1);
+    lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
+    if (c.half == 0) c.wred[c.wave][c.col] = make_float2(m, l);
+    lds_barrier();
+    if (c.wave == 3) {
+      float2 a = c.wred[0][c.lane & 31];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) lse2_merge(a.x, a.y, c.wred[i][c.lane & 31].x, c.wred[i][c.lane & 31].y);
+      m = a.x;
+      l = a.y;
+    }
+  }
+  // closing wait, all waves: the next round's K tiles (waves 0..2); this
+  // round's prefetches and last round's contributions, count and digit loads
+  // (wave 3)
+  __builtin_amdgcn_s_waitcnt(0);
+  if (c.wave == 3) coop_bookkeeping(c, p, do_a, unit, m, l);
+}
+
+template <int D>
+__global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int nunit,
+    int total_units, float scale_log2, const float* __restrict__ ref, unsigned long long* __restrict__ acc,
+    unsigned* __restrict__ cnt, uint2* __restrict__ stat, float2* __restrict__ part,
+    unsigned* __restrict__ status, float* __restrict__ vote) {
+  using Ly = CoopLayout<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[Ly::kKBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char qbuf[Ly::kQBytes];
+  __shared__ float2 wred[kWaves][32];
+  __shared__ float s_c[32];
+  __shared__ unsigned long long s_fin[32][kCoopDigits + 1];
+
+  CoopCtx c;
+  c.q = q; c.qsb = qsb; c.qsh = qsh; c.qst = qst; c.qrow0 = qrow0;
+  c.k = k; c.ksb = ksb; c.ksh = ksh; c.kst = kst;
+  c.H = H; c.L = L; c.w = w; c.t0 = L - w; c.nunit = nunit;
+  c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x);
+  c.rounds = (total_units - c.g + c.G - 1) / c.G;
+  c.scale_log2 = scale_log2;
+  c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.part = part; c.status = status; c.vote = vote;
+  c.kbuf = kbuf; c.qbuf = qbuf; c.wred = wred; c.s_c = s_c; c.s_fin = s_fin;
+  c.lane = lane_id(); c.wave = threadIdx.x / kWave; c.col = c.lane & 31; c.half = c.lane >> 5;
+
+  CoopPipe p;
+  p.ack_head = p.cnt_head = p.fin_head = -1;
+  p.cnt_ret = 0;
+  p.pre = make_uint2(0u, 0u);
+  p.fin_ref = 0.f;
+  p.ref = 0.f;
+  p.q_head = -1;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) p.fin[i] = 0;
+  f32x16_t sc[kCoopBanks];
+  if (c.rounds > 0) coop_issue<D>(c, p, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  // every unit's votes (round rounds - 1 + kCoopLag) and its head's
+  // bookkeeping (three rounds after its last unit) fall inside the loop
+  static_assert(kCoopBanks == 8, "the round loop below is unrolled over the register banks");
+  for (int r0 = 0; r0 < c.rounds + kCoopLag; r0 += kCoopBanks) {
+    coop_round<D, 0>(c, p, sc, r0);
+    coop_round<D, 1>(c, p, sc, r0 + 1);
+    coop_round<D, 2>(c, p, sc, r0 + 2);
+    coop_round<D, 3>(c, p, sc, r0 + 3);
+    coop_round<D, 4>(c, p, sc, r0 + 4);
+    coop_round<D, 5>(c, p, sc, r0 + 5);
+    coop_round<D, 6>(c, p, sc, r0 + 6);
+    coop_round<D, 7>(c, p, sc, r0 + 7);
+  }
+}
+
+// Max-pool of raw votes (neighbours beyond the prefix ignored) and the
+// per-head 12-bit histogram of the pooled scores; used after the single pass.
+__global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restrict__ vote,
+                                                           float* __restrict__ pooled,
+                                                           unsigned* __restrict__ hist, int N, int r) {
+  constexpr int kChunk = 4096;
+  __shared__ float sv[kChunk + 2 * kMaxPoolRadius];
+  __shared__ unsigned sh[kHistBins];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
+  const int c0 = chunk * kChunk, c1 = min(N, c0 + kChunk);
+  const int e0 = max(0, c0 - r), e1 = min(N, c1 + r);
+  const float* vb = vote + static_cast<int64_t>(bh) * N;
+  for (int j = e0 + static_cast<int>(threadIdx.x); j < e1; j += kThreads) sv[j - e0] = vb[j];
+  __syncthreads();
+  pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * N, sh);
+  __syncthreads();
+  flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
+}
+
 // ------------------------------------------------------------ classify
 
 // The bin b* holding the k-th largest value: count(bins > b*) < k <= count(bins >= b*).
@@ -644,9 +1149,11 @@ __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__
 
 struct SnapLayout {
   int64_t BH;
-  int N, kk, nchunk, words;
+  int N, kk, nchunk, words, nunit;
   size_t ctr, hist;
-  size_t part, pooled, sel, cand, bitmap, total;
+  size_t part, pooled, sel, cand, bitmap;
+  size_t cref, cacc, ccnt, cstat, cpart, cstatus;  // single pass (bf16)
+  size_t total;
 };
 
 bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, SnapLayout* o) {
@@ -672,6 +1179,16 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
   o->sel = take(static_cast<size_t>(BH) * o->kk * 4);
   o->cand = take(static_cast<size_t>(BH) * o->N * 8);
   o->bitmap = take(static_cast<size_t>(BH) * o->words * 4);
+  o->nunit = (L + kCoopUnit - 1) / kCoopUnit;
+  o->cref = o->cacc = o->ccnt = o->cstat = o->cpart = o->cstatus = 0;
+  if (dt == KVC_BF16) {
+    o->cref = take(static_cast<size_t>(BH) * 32 * 4);
+    o->cacc = take(static_cast<size_t>(BH) * kCoopHeadWords * 8);
+    o->ccnt = take(static_cast<size_t>(BH) * kCoopCtrWords * 4);
+    o->cstat = take(static_cast<size_t>(BH) * 32 * 8);
+    o->cpart = take(static_cast<size_t>(BH) * o->nunit * 32 * 8);
+    o->cstatus = take(4);
+  }
   o->total = off;
   return true;
 }
@@ -744,10 +1261,112 @@ void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int 
   mark_phase(4, stream);
 }
 
+thread_local int g_schedule = KVC_SNAPKV_AUTO;
+thread_local int g_last_schedule = 0;
+
+// Per device: cooperative launch support, compute units and resident
+// single-pass workgroups per compute unit (index 0: D = 64, 1: D = 128).
+struct CoopCaps {
+  bool queried = false, coop = false;
+  int cus = 0, per_cu[2] = {0, 0};
+};
+
+const CoopCaps& coop_caps() {
+  static std::mutex mu;
+  static CoopCaps caps[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    static const CoopCaps none;
+    return none;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  CoopCaps& c = caps[dev];
+  if (!c.queried) {
+    c.queried = true;
+    int coop = 0, cus = 0, n64 = 0, n128 = 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n64, snap_coop_bf16<64>, kCoopThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n128, snap_coop_bf16<128>, kCoopThreads, 0) == hipSuccess) {
+      c.coop = coop != 0;
+      c.cus = cus;
+      c.per_cu[0] = n64;
+      c.per_cu[1] = n128;
+    }
+    (void)hipGetLastError();
+  }
+  return c;
+}
+
+// Grid of the single pass for these sizes, 0 when it cannot run. The votes of
+// a round-r unit wait (in round r + kCoopLag) for its head's normaliser,
+// which the finishing workgroup publishes three rounds after the head's last
+// unit; with a head spanning at most kCoopLag - 3 consecutive rounds every
+// such wait depends only on heads that started in earlier rounds, so all of
+// them end.
+int coop_grid(const SnapLayout& lay, int D) {
+  const CoopCaps& c = coop_caps();
+  if (!c.coop || c.cus <= 0) return 0;
+  const int per_cu = c.per_cu[D == 128 ? 1 : 0];
+  if (per_cu <= 0) return 0;
+  const int64_t total = lay.BH * lay.nunit;
+  const int G = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(per_cu) * c.cus, total));
+  if (lay.nunit > (kCoopLag - 3) * G) return 0;
+  for (int64_t bh = 0; bh < lay.BH; ++bh) {
+    const int64_t u0 = bh * lay.nunit, u1 = u0 + lay.nunit - 1;
+    if (u1 / G - u0 / G > kCoopLag - 4) return 0;
+  }
+  return G;
+}
+
+// Single pass: the per-head preparation (reference scores, cleared state),
+// the cooperative score pass (raw votes to `vote`), then pooling + histogram.
+// Phase marks 1, 2, 3 and 4.
+template <int D>
+kvc_status launch_single_pass(const SnapLayout& lay, int G, const uint16_t* q, kvc_strides qs, int qrow0,
+                              const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, float scale_log2,
+                              char* ws, float* vote, float* pooled, hipStream_t stream) {
+  float* ref = reinterpret_cast<float*>(ws + lay.cref);
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(ws + lay.cacc);
+  unsigned* cnt = reinterpret_cast<unsigned*>(ws + lay.ccnt);
+  uint2* stat = reinterpret_cast<uint2*>(ws + lay.cstat);
+  float2* part = reinterpret_cast<float2*>(ws + lay.cpart);
+  unsigned* status = reinterpret_cast<unsigned*>(ws + lay.cstatus);
+  unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
+  unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
+  snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
+      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist, ctr);
+  mark_phase(1, stream);
+  int nunit = lay.nunit, total_units = static_cast<int>(lay.BH * lay.nunit);
+  int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
+  const float* cref = ref;
+  void* args[] = {&q,   &qsb,         &qsh,        &qst,  &qrow0, &k,   &ksb,  &ksh,    &kst,   &H,   &L, &w,
+                  &nunit, &total_units, &scale_log2, &cref, &acc,   &cnt, &stat, &part, &status, &vote};
+  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_coop_bf16<D>), dim3(G),
+                                                  dim3(kCoopThreads), args, 0, stream);
+  if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
+  mark_phase(2, stream);
+  mark_phase(3, stream);
+  const dim3 gp((lay.N + 4095) / 4096, static_cast<unsigned>(lay.BH));
+  snap_pool_hist<<<gp, kThreads, 0, stream>>>(vote, pooled, hist, lay.N, r);
+  mark_phase(4, stream);
+  return KVC_OK;
+}
+
 }  // namespace
 }  // namespace kvc
 
 using namespace kvc;
+
+extern "C" int kvc_snapkv_set_schedule(int schedule) {
+  if (schedule != KVC_SNAPKV_AUTO && schedule != KVC_SNAPKV_TWO_PASS && schedule != KVC_SNAPKV_SINGLE_PASS)
+    return -1;
+  const int prev = g_schedule;
+  g_schedule = schedule;
+  return prev;
+}
+
+extern "C" int kvc_snapkv_last_schedule(void) { return g_last_schedule; }
 
 extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
                                              int pool_kernel, kvc_dtype dt) {
@@ -803,14 +1422,32 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
   const int qrow0 = q_len - window;
 
+  // AUTO takes the two-pass schedule: on MI355X it is the faster one for now
+  const int G = (dt == KVC_BF16 && g_schedule == KVC_SNAPKV_SINGLE_PASS) ? coop_grid(lay, D) : 0;
+  int schedule = KVC_SNAPKV_TWO_PASS;
   mark_phase(0, stream);
-  mark_phase(1, stream);  // counters and histograms are cleared by the statistics pass
-  if (dt == KVC_BF16)
-    launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0, static_cast<const uint16_t*>(k),
-                                  kvs, H, L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
-  else
-    launch_score_passes<float>(lay, static_cast<const float*>(q), qs, qrow0, static_cast<const float*>(k), kvs, H,
-                               L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
+  if (G > 0) {
+    // raw votes go to the caller's buffer or to the candidate area, which is
+    // free until classification
+    float* vraw = vote ? vote : reinterpret_cast<float*>(ws + lay.cand);
+    const uint16_t* qb = static_cast<const uint16_t*>(q);
+    const uint16_t* kb = static_cast<const uint16_t*>(k);
+    kvc_status st = D == 128 ? launch_single_pass<128>(lay, G, qb, qs, qrow0, kb, kvs, H, L, window, pool_kernel / 2,
+                                                       scale_log2, ws, vraw, pooled, stream)
+                             : launch_single_pass<64>(lay, G, qb, qs, qrow0, kb, kvs, H, L, window, pool_kernel / 2,
+                                                      scale_log2, ws, vraw, pooled, stream);
+    if (st != KVC_OK) return st;
+    schedule = KVC_SNAPKV_SINGLE_PASS;
+  } else {
+    mark_phase(1, stream);  // counters and histograms are cleared by the statistics pass
+    if (dt == KVC_BF16)
+      launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0,
+                                    static_cast<const uint16_t*>(k), kvs, H, L, D, window, pool_kernel / 2,
+                                    scale_log2, ws, vote, pooled, stream);
+    else
+      launch_score_passes<float>(lay, static_cast<const float*>(q), qs, qrow0, static_cast<const float*>(k), kvs, H,
+                                 L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
+  }
   kvc_status st = check_launch("snapkv score passes");
   if (st != KVC_OK) return st;
 
@@ -835,7 +1472,9 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
                                            vec_per_row, idx_out, static_cast<char*>(k_out),
                                            static_cast<char*>(v_out));
   mark_phase(7, stream);
-  return check_launch("snapkv gather");
+  st = check_launch("snapkv gather");
+  if (st == KVC_OK) g_last_schedule = schedule;
+  return st;
 }
 
 extern "C" void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events) {

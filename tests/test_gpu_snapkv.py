@@ -10,14 +10,27 @@ from tests import parity as par
 
 pytestmark = pytest.mark.gpu
 
+SCHEDULES = {"two_pass": kvc.SNAPKV_TWO_PASS, "single_pass": kvc.SNAPKV_SINGLE_PASS}
 
-def _run(q, k, v, wl_window, budget, pool, dtype, **kw):
+
+@pytest.fixture(params=list(SCHEDULES))
+def schedule(request):
+    """Both score schedules; SINGLE_PASS falls back to TWO_PASS where it cannot run (fp32, long heads)."""
+    return SCHEDULES[request.param]
+
+
+def _run(q, k, v, wl_window, budget, pool, dtype, schedule=kvc.SNAPKV_AUTO, want_vote=True, **kw):
     if "workspace" not in kw:
         B, H, L, D = k.shape
         n = kvc.snapkv_workspace_bytes(B, H, L, D, wl_window, budget, pool, k.dtype)
         kw["workspace"] = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")  # garbage on entry
-    res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=True, want_vote=True, **kw)
+    with kvc.snapkv_schedule(schedule):
+        res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=True, want_vote=want_vote, **kw)
     torch.cuda.synchronize()
+    ran = kvc.snapkv_last_schedule()
+    print(f"[snapkv] schedule asked {schedule} ran {ran}", flush=True)
+    if dtype == "fp32" or schedule == kvc.SNAPKV_TWO_PASS:
+        assert ran == kvc.SNAPKV_TWO_PASS
     return res
 
 
@@ -28,13 +41,14 @@ def _compare(qn, kn, vn, res, window, budget, pool, dtype, heads=None):
     idx = res.idx.cpu().numpy()
     k_out = par.to_host_bits(res.k)
     v_out = par.to_host_bits(res.v)
-    vote = res.vote.cpu().numpy()
+    vote = res.vote.cpu().numpy() if res.vote is not None else None
     pooled = res.pooled.cpu().numpy()
     pairs = heads or [(b, h) for b in range(B) for h in range(H)]
     kinds = []
     for b, h in pairs:
         r = ref.compress_head(qn[b, h, qn.shape[2] - window:], kn[b, h], vn[b, h], budget, pool, dtype)
-        par.assert_close_votes(vote[b, h], r["vote"], f"vote[{b},{h}]")
+        if vote is not None:
+            par.assert_close_votes(vote[b, h], r["vote"], f"vote[{b},{h}]")
         par.assert_close_votes(pooled[b, h], r["pooled"], f"pooled[{b},{h}]")
         kinds.append(par.check_topk(r["pooled"], r["idx"], idx[b, h]))
         par.check_gather(k_out[b, h], v_out[b, h], kn[b, h], vn[b, h], idx[b, h], t0)
@@ -44,37 +58,46 @@ def _compare(qn, kn, vn, res, window, budget, pool, dtype, heads=None):
     return kinds
 
 
-def _workload(wl, heads=None):
+def _workload(wl, heads=None, schedule=kvc.SNAPKV_AUTO, want_vote=True):
     print(f"[snapkv] workload {wl.name} B{wl.B} H{wl.H} D{wl.D} L{wl.L} w{wl.window} "
-          f"C{wl.budget} p{wl.pool_kernel} {wl.dtype}", flush=True)
+          f"C{wl.budget} p{wl.pool_kernel} {wl.dtype} schedule {schedule}", flush=True)
     qn, kn, vn = syn.snapkv_batch(wl)
     q, k, v = (par.to_device(x, wl.dtype) for x in (qn, kn, vn))
-    res = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, wl.dtype)
+    res = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, wl.dtype, schedule, want_vote=want_vote)
     kinds = _compare(qn, kn, vn, res, wl.window, wl.budget, wl.pool_kernel, wl.dtype, heads)
     print(f"[snapkv] {wl.name}: {kinds.count('exact')} exact, {kinds.count('near-tie')} near-tie heads",
           flush=True)
     return kinds
 
 
-def test_tiny_fp32_full():
-    _workload(syn.SNAPKV_WORKLOADS["tiny-fp32"])
+def test_tiny_fp32_full(schedule):
+    _workload(syn.SNAPKV_WORKLOADS["tiny-fp32"], schedule=schedule)
 
 
-def test_16k_shape_ragged_small():
+def test_16k_shape_ragged_small(schedule):
     # several MFMA chunks, pooling chunks and a ragged tail (L - w = 2968)
-    _workload(syn.SNAPKV_WORKLOADS["16k-bf16"].with_(L=3000, H=4))
+    _workload(syn.SNAPKV_WORKLOADS["16k-bf16"].with_(L=3000, H=4), schedule=schedule)
 
 
-def test_16k_full_all_heads():
-    _workload(syn.SNAPKV_WORKLOADS["16k-bf16"])
+def test_16k_full_all_heads(schedule):
+    _workload(syn.SNAPKV_WORKLOADS["16k-bf16"], schedule=schedule)
+    if schedule == kvc.SNAPKV_SINGLE_PASS:
+        assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
 
 
-def test_131k_full_sampled_heads():
-    _workload(syn.SNAPKV_WORKLOADS["131k-bf16"], heads=[(0, 0), (0, 13), (0, 31)])
+def test_131k_full_sampled_heads(schedule):
+    _workload(syn.SNAPKV_WORKLOADS["131k-bf16"], heads=[(0, 0), (0, 13), (0, 31)], schedule=schedule)
+    if schedule == kvc.SNAPKV_SINGLE_PASS:
+        assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
 
 
-def test_380k_full_sampled_heads():
-    _workload(syn.SNAPKV_WORKLOADS["380k-bf16"], heads=[(0, 5), (0, 30)])
+def test_131k_votes_not_requested(schedule):
+    """No vote output: raw votes live in the workspace only."""
+    _workload(syn.SNAPKV_WORKLOADS["131k-bf16"], heads=[(0, 7)], want_vote=False, schedule=schedule)
+
+
+def test_380k_full_sampled_heads(schedule):
+    _workload(syn.SNAPKV_WORKLOADS["380k-bf16"], heads=[(0, 5), (0, 30)], schedule=schedule)
 
 
 EDGE = [
@@ -91,28 +114,35 @@ EDGE = [
 
 
 @pytest.mark.parametrize("dtype,D,w,L,budget,pool", EDGE)
-def test_edge_shapes(dtype, D, w, L, budget, pool):
+def test_edge_shapes(dtype, D, w, L, budget, pool, schedule):
     wl = syn.SnapKVWorkload(name=f"edge-{dtype}-{D}-{w}-{L}", B=1, H=3, D=D, L=L, window=w, budget=budget,
                             pool_kernel=pool, dtype=dtype, n_spans=2, span_len=3, span_boost=2.0,
                             seed=777 + L)
-    _workload(wl)
+    _workload(wl, schedule=schedule)
 
 
-def test_zero_queries_exact_ties():
+def test_single_pass_many_heads_unaligned():
+    """Heads whose units straddle device-wide rounds (B*H*units not a multiple of the grid)."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=3, H=7, L=70001, budget=1500)
+    _workload(wl, heads=[(0, 0), (1, 3), (2, 6)], schedule=kvc.SNAPKV_SINGLE_PASS)
+    assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
+
+
+def test_zero_queries_exact_ties(schedule):
     """Q = 0 makes every vote equal: the tie rule alone decides, so the kept set is 0..k-1."""
     B, H, L, D, w, C = 1, 2, 2000, 128, 32, 300
     rng = np.random.default_rng(0)
     kn = syn.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32))
     qn = np.zeros((B, H, w, D), np.uint16)
     q, k = par.to_device(qn, "bf16"), par.to_device(kn, "bf16")
-    res = _run(q, k, k, w, C, 7, "bf16")
+    res = _run(q, k, k, w, C, 7, "bf16", schedule)
     idx = res.idx.cpu().numpy()
     for h in range(H):
         assert idx[0, h].tolist() == list(range(C - w))
     _compare(qn, kn, kn, res, w, C, 7, "bf16")
 
 
-def test_planted_spike_neighbourhood():
+def test_planted_spike_neighbourhood(schedule):
     B, H, L, D, w, p = 1, 1, 3000, 128, 32, 7
     rng = np.random.default_rng(1)
     q32 = rng.standard_normal((B, H, w, D), dtype=np.float32)
@@ -122,11 +152,11 @@ def test_planted_spike_neighbourhood():
     k32[0, 0, j] += 30.0 * u / np.linalg.norm(u)
     qn, kn = syn.f32_to_bf16_bits(q32), syn.f32_to_bf16_bits(k32)
     res = _run(par.to_device(qn, "bf16"), par.to_device(kn, "bf16"), par.to_device(kn, "bf16"), w, w + p, p,
-               "bf16")
+               "bf16", schedule)
     assert res.idx[0, 0].cpu().tolist() == list(range(j - 3, j + 4))
 
 
-def test_strided_inputs():
+def test_strided_inputs(schedule):
     """q_len > window and K/V row strides wider than D (views into padded buffers)."""
     B, H, L, D, w, C, p = 2, 3, 2500, 128, 32, 256, 7
     rng = np.random.default_rng(2)
@@ -136,25 +166,25 @@ def test_strided_inputs():
     qd, kd, vd = (par.to_device(x, "bf16") for x in (qbig, kbig, vbig))
     k, v = kd[..., :D], vd[..., :D]
     assert k.stride(2) == D + 64
-    res = _run(qd, k, v, w, C, p, "bf16")
+    res = _run(qd, k, v, w, C, p, "bf16", schedule)
     _compare(qbig, np.ascontiguousarray(kbig[..., :D]), np.ascontiguousarray(vbig[..., :D]), res, w, C, p,
              "bf16")
 
 
-def test_deterministic_and_workspace_reuse():
+def test_deterministic_and_workspace_reuse(schedule):
     wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(L=6000, H=4)
     qn, kn, vn = syn.snapkv_batch(wl)
     q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
     nbytes = kvc.snapkv_workspace_bytes(wl.B, wl.H, wl.L, wl.D, wl.window, wl.budget, wl.pool_kernel,
                                         torch.bfloat16)
     ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")  # garbage on entry
-    a = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", workspace=ws)
+    a = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", schedule, workspace=ws)
     # a different input through the same workspace, then the first again
     wl2 = wl.with_(seed=wl.seed + 1)
     qn2, kn2, vn2 = syn.snapkv_batch(wl2)
     q2, k2, v2 = (par.to_device(x, "bf16") for x in (qn2, kn2, vn2))
-    b = _run(q2, k2, v2, wl.window, wl.budget, wl.pool_kernel, "bf16", workspace=ws)
-    c = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", workspace=ws)
+    b = _run(q2, k2, v2, wl.window, wl.budget, wl.pool_kernel, "bf16", schedule, workspace=ws)
+    c = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", schedule, workspace=ws)
     assert torch.equal(a.idx, c.idx) and torch.equal(a.vote, c.vote) and torch.equal(a.k, c.k)
     _compare(qn2, kn2, vn2, b, wl.window, wl.budget, wl.pool_kernel, "bf16")
 
@@ -174,3 +204,24 @@ def test_error_statuses():
     with pytest.raises(kvc.KvcError) as e:
         kvc.snapkv_compress(k, k, k, 32, 100, 4)  # even pool kernel
     assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_schedules_agree():
+    """Both schedules on one input: same kept set up to near-ties, votes within rounding."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(L=9000, H=4)
+    qn, kn, vn = syn.snapkv_batch(wl)
+    q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
+    a = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", kvc.SNAPKV_TWO_PASS)
+    b = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", kvc.SNAPKV_SINGLE_PASS)
+    assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
+    va, vb = a.vote.cpu().numpy(), b.vote.cpu().numpy()
+    for h in range(wl.H):
+        par.assert_close_votes(vb[0, h], va[0, h].astype(np.float64), f"vote[0,{h}] single vs two-pass")
+    same = (a.idx == b.idx).float().mean().item()
+    assert same > 0.99, same
+
+
+def test_schedule_setting_rejects_unknown():
+    with pytest.raises(ValueError):
+        with kvc.snapkv_schedule(7):
+            pass
