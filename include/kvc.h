@@ -127,8 +127,9 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  *                device-wide rounds of 128-key units (on MI355X, up to about
  *                256K keys per head for one head); otherwise the call uses
  *                TWO_PASS.
- *   AUTO         the default: TWO_PASS, the faster of the two on MI355X at
- *                the sizes measured so far. */
+ *   AUTO         the default: SINGLE_PASS where it can run (the faster of
+ *                the two on MI355X at the sizes measured so far), else
+ *                TWO_PASS; also TWO_PASS if the cooperative launch fails. */
 typedef enum {
   KVC_SNAPKV_AUTO = 0,
   KVC_SNAPKV_TWO_PASS = 1,

@@ -398,17 +398,19 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
 //     in register bank (r - kCoopLag) % kCoopBanks; they need the head's
 //     log-normaliser c_i = log2(sum_j 2^(s_ij)) of every window row i;
 //   * scores the unit of round r from K staged in LDS by direct-to-LDS loads
-//     issued during round r - 1, into bank r % kCoopBanks, and adds the
-//     unit's per-row l * 2^(m - R_i) (m the unit's row max, l its sum of
-//     2^(s - m)) to the head's row accumulators.
+//     issued during round r - 1, into bank r % kCoopBanks, and folds the
+//     unit's per-row (m, l) (m the unit's row max, l its sum of 2^(s - m))
+//     into a running pair for the head; after its last unit of the head the
+//     workgroup adds l * 2^(m - R_i) to the head's row accumulators.
 // R_i is a reference score of row i (its largest score against the window's
 // own keys, computed beforehand), so every accumulated term is bounded below
-// by the window key's own term of about 1. The accumulators are fixed-point
-// integers (kCoopDigits 32-bit digits, lowest weight 2^kCoopDigitBase
-// relative to 2^R_i) summed with integer atomics, so the total is the same
-// in every order. Completion is counted per head: the workgroup whose count
-// increment finishes a head converts its digits into c_i and publishes them,
-// tagged ready. Each cross-workgroup step waits only on something issued a
+// by the window key's own term of about 1. A row accumulator is a fixed-point
+// integer: kCoopWords 64-bit words, word k summing terms of weight
+// 2^(16 k + kCoopDigitBase) relative to 2^R_i; each term (a 24-bit mantissa
+// shifted by less than 16 bits) is one integer atomic add, so the total is
+// the same in every order. Completion is counted per head (one count per
+// contributing workgroup): the workgroup whose count increment finishes a
+// head converts its words into c_i and publishes them, tagged ready. Each cross-workgroup step waits only on something issued a
 // round earlier (a contribution is complete before the count is raised, the
 // count's return picks the finisher, the digits' loads land before the
 // conversion, readers prefetch c a round ahead): at HBM-saturating load such
@@ -420,10 +422,12 @@ constexpr int kCoopThreads = 256;            // 4 waves, one 32-key tile each pe
 constexpr int kCoopUnit = kWaves * kTile;    // 128 keys
 constexpr int kCoopBanks = 8;
 constexpr int kCoopLag = kCoopBanks - 1;     // rounds between a unit's scores and its votes
-constexpr int kCoopDigits = 11;
+constexpr int kCoopWords = 20;               // accumulator words per row (a term lands in word <= 18)
 constexpr int kCoopDigitBase = -160;
-constexpr int kCoopRowWords = 16;            // 64-bit words per row accumulator: one 128-byte line
+constexpr int kCoopRowWords = 544;           // row stride in 64-bit words: 4 KB + 256 B, so that the
+                                             // rows' atomics spread over memory channels
 constexpr int kCoopHeadWords = 32 * kCoopRowWords;
+constexpr int kCoopFinWords = 24;            // words per row the finisher stages (room for the carries)
 constexpr int kCoopCtrWords = 32;            // per head: [0] unit count, [16] overflow flag
 constexpr float kCoopOvfGap = 150.f;
 constexpr unsigned kCoopSpin = 1u << 22;
@@ -459,31 +463,54 @@ struct CoopLayout {
   static constexpr int kQBytes = kTileB;              // 32 window rows
 };
 
-// Direct-to-LDS loads of one unit's K tiles (and of the 32 Q rows when
-// with_q), spread over waves 0..2. Rows beyond the data are clamped to valid
-// rows; their scores are masked or never written.
+// Direct-to-LDS loads of one unit's K tiles, spread over waves 0..2. Rows
+// beyond the data are clamped to valid rows; their scores are masked or never
+// written.
 template <int D>
-__device__ __forceinline__ void coop_issue_loads(const uint16_t* kb, int64_t kst, int key0, int L,
-                                                 const uint16_t* qb, int64_t qst, int w, bool with_q,
-                                                 unsigned char* kbuf, unsigned char* qbuf, int wave, int lane) {
+__device__ __forceinline__ void coop_issue_k_loads(const uint16_t* kb, int64_t kst, int key0, int L,
+                                                   unsigned char* kbuf, int wave, int lane) {
   using Ly = CoopLayout<D>;
-  const int total = (kWaves + (with_q ? 1 : 0)) * Ly::kInstPerTile;
-  for (int i = wave; i < total; i += 3) {
+  for (int i = wave; i < kWaves * Ly::kInstPerTile; i += 3) {
     const int tile = i / Ly::kInstPerTile, sub = i - tile * Ly::kInstPerTile;
     const int row = sub * Ly::kRowsPerInst + lane / Ly::kP;  // row within the tile
     const int slot = lane % Ly::kP;
     const int piece = slot ^ (row & (Ly::kP - 1));
-    const uint16_t* src;
-    unsigned char* dst;
-    if (tile < kWaves) {
-      const int key = min(key0 + tile * kTile + row, L - 1);
-      src = kb + static_cast<int64_t>(key) * kst + piece * 8;
-      dst = kbuf + tile * Ly::kTileB + sub * 1024;
-    } else {
-      src = qb + static_cast<int64_t>(min(row, w - 1)) * qst + piece * 8;
-      dst = qbuf + sub * 1024;
-    }
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+    const int key = min(key0 + tile * kTile + row, L - 1);
+    __builtin_amdgcn_global_load_lds(kb + static_cast<int64_t>(key) * kst + piece * 8,
+                                     (lds_void*)(kbuf + tile * Ly::kTileB + sub * 1024), 16, 0, 0);
+  }
+}
+
+// The same loads for a unit whose 128 rows all exist: instruction i covers
+// unit rows i*kRowsPerInst + lane/kP, so its address is a uniform row base
+// plus a per-lane 32-bit offset (lane/kP) * row_bytes + 16 * piece, where
+// piece = (lane % kP) ^ (lane / kP) ^ ((i * kRowsPerInst) & (kP - 1)) (the
+// two xor terms occupy disjoint bits).
+template <int D>
+__device__ __forceinline__ void coop_issue_k_full(const char* rows, int64_t row_bytes, unsigned char* kbuf, int wave,
+                                                  int lane) {
+  using Ly = CoopLayout<D>;
+  const unsigned lrow = static_cast<unsigned>(lane / Ly::kP) * static_cast<unsigned>(row_bytes);
+  const unsigned x16 = static_cast<unsigned>((lane % Ly::kP) ^ (lane / Ly::kP)) << 4;
+  for (int i = wave; i < kWaves * Ly::kInstPerTile; i += 3) {
+    const unsigned b16 = static_cast<unsigned>((i * Ly::kRowsPerInst) & (Ly::kP - 1)) << 4;
+    const char* base = rows + static_cast<int64_t>(i * Ly::kRowsPerInst) * row_bytes;
+    __builtin_amdgcn_global_load_lds(base + (lrow + (x16 ^ b16)), (lds_void*)(kbuf + i * 1024), 16, 0, 0);
+  }
+}
+
+// Direct-to-LDS loads of the 32 window query rows (rows past the window
+// repeat its last row), spread over waves 0..2.
+template <int D>
+__device__ __forceinline__ void coop_issue_q_loads(const uint16_t* qb, int64_t qst, int w, unsigned char* qbuf,
+                                                   int wave, int lane) {
+  using Ly = CoopLayout<D>;
+  for (int sub = wave; sub < Ly::kInstPerTile; sub += 3) {
+    const int row = sub * Ly::kRowsPerInst + lane / Ly::kP;
+    const int slot = lane % Ly::kP;
+    const int piece = slot ^ (row & (Ly::kP - 1));
+    __builtin_amdgcn_global_load_lds(qb + static_cast<int64_t>(min(row, w - 1)) * qst + piece * 8,
+                                     (lds_void*)(qbuf + sub * 1024), 16, 0, 0);
   }
 }
 
@@ -514,7 +541,8 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr) {
   __shared__ float red[32][33];
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
-  for (int i = threadIdx.x; i < kCoopHeadWords; i += kThreads) acc[static_cast<int64_t>(bh) * kCoopHeadWords + i] = 0;
+  for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
+    acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
   if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
   if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
@@ -557,11 +585,13 @@ struct CoopCtx {
   float2* part;
   unsigned* status;
   float* vote;
-  unsigned char* kbuf;
+  unsigned char* kbuf0;  // K tiles of even rounds
+  unsigned char* kbuf1;  // K tiles of odd rounds
   unsigned char* qbuf;
   float2 (*wred)[32];
   float* s_c;
-  unsigned long long (*s_fin)[kCoopDigits + 1];
+  unsigned long long (*s_fin)[kCoopFinWords];
+  int cnt_target;        // contributions per head: min(units per head, G)
   int wave, lane, col, half;
 };
 
@@ -570,9 +600,11 @@ struct CoopPipe {
   int ack_head;                  // head of the unit contributed last round (its count is due)
   int cnt_head;                  // head whose count was raised last round
   unsigned cnt_ret;              // that count's value before the increment
-  int fin_head;                  // head being finished: its digits were loaded last round
-  unsigned long long fin[6];     // lanes 0..31: digits 0..5 of row lane; 32..63: digits 6..10, overflow flag
+  int fin_head;                  // head being finished: its words were loaded into LDS last round
+  unsigned fin_ovf;              // that head's overflow flag
   float fin_ref;                 // that head's reference score of row lane & 31
+  int run_head;                  // head of the running (m, l) pair, -1 if none
+  float run_m, run_l;            // running row max and sum of this workgroup's units of run_head
   uint2 pre;                     // normaliser prefetched for the next round's votes
   float ref;                     // reference score of row lane & 31 for this round's unit
   int q_head;                    // head whose Q rows sit in LDS
@@ -580,49 +612,64 @@ struct CoopPipe {
 
 __device__ __forceinline__ int coop_head(const CoopCtx& c, int r) { return (r * c.G + c.g) / c.nunit; }
 
+// lane & 31, opaque to the optimiser: addresses derived from it are formed
+// where they are used (a scalar base plus a 32-bit lane offset) instead of
+// being kept live as 64-bit per-lane pointers across the whole round loop.
+__device__ __forceinline__ int coop_row(const CoopCtx& c) {
+  int row = c.lane & 31;
+  asm volatile("" : "+v"(row));
+  return row;
+}
+
+// K tiles of round r's unit into `kbuf` (waves 0..2).
 template <int D>
-__device__ __forceinline__ void coop_issue(const CoopCtx& c, CoopPipe& p, int r) {
+__device__ __forceinline__ void coop_issue_k(const CoopCtx& c, int r, unsigned char* kbuf) {
+  if (c.wave >= 3) return;
   const int u = r * c.G + c.g;
   const int bh = u / c.nunit, key0 = (u - bh * c.nunit) * kCoopUnit;
-  const bool with_q = bh != p.q_head;
+  const int b = bh / c.H, h = bh - b * c.H;
+  const uint16_t* kb = c.k + b * c.ksb + h * c.ksh;
+  if (key0 + kCoopUnit <= c.L)
+    coop_issue_k_full<D>(reinterpret_cast<const char*>(kb + static_cast<int64_t>(key0) * c.kst), c.kst * 2, kbuf,
+                         c.wave, c.lane);
+  else
+    coop_issue_k_loads<D>(kb, c.kst, key0, c.L, kbuf, c.wave, c.lane);
+}
+
+// Q rows of round r's head, unless they are the ones already staged.
+template <int D>
+__device__ __forceinline__ void coop_issue_q(const CoopCtx& c, CoopPipe& p, int r) {
+  const int bh = coop_head(c, r);
+  if (bh == p.q_head) return;
   p.q_head = bh;
   if (c.wave >= 3) return;
   const int b = bh / c.H, h = bh - b * c.H;
-  coop_issue_loads<D>(c.k + b * c.ksb + h * c.ksh, c.kst, key0, c.L,
-                      c.q + b * c.qsb + h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst, c.qst, c.w, with_q,
-                      c.kbuf, c.qbuf, c.wave, c.lane);
+  coop_issue_q_loads<D>(c.q + b * c.qsb + h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst, c.qst, c.w, c.qbuf,
+                        c.wave, c.lane);
 }
 
-// The head's normaliser from its digits (lanes 0..31 hold row lane's digits
-// 0..5, lanes 32..63 its digits 6..10), staged through LDS: exact carry
-// propagation, the total's leading 24 bits as m * 2^E with m in [1, 2), then
-// c = R + E + log2(m). The result is meaningful in lanes 0..31.
-__device__ __forceinline__ float coop_digits_to_c(const unsigned long long (&fin)[6],
-                                                 unsigned long long (*s_fin)[kCoopDigits + 1], int lane, float R) {
-  const int row = lane & 31, d0 = lane < 32 ? 0 : 6;
-#pragma unroll
-  for (int i = 0; i < 6; ++i) s_fin[row][d0 + i] = fin[i];  // lanes 32..63 put the flag in the spare word
-  float cv = R;
-  if (lane < 32) {
-    unsigned long long carry = 0;
-    int top = -1;
+// The head's normaliser from its accumulator words (staged in s_fin[row]):
+// exact carry propagation into 16-bit digits, the total's leading 24 bits as
+// mf * 2^E with mf in [1, 2), then c = R + E + log2(mf). Lanes 0..31.
+__device__ __forceinline__ float coop_words_to_c(unsigned long long (*s_fin)[kCoopFinWords], int row, float R) {
+  unsigned long long carry = 0;
+  int top = -1;
 #pragma unroll 1
-    for (int i = 0; i < kCoopDigits; ++i) {
-      const unsigned long long v = s_fin[row][i] + carry;
-      s_fin[row][i] = v & 0xffffffffull;
-      carry = v >> 32;
-      if (v & 0xffffffffull) top = i;
-    }
-    if (top >= 0) {
-      unsigned long long v = (s_fin[row][top] << 32) | (top > 0 ? s_fin[row][top - 1] : 0ull);
-      const int lz = __clzll(static_cast<long long>(v));
-      v <<= lz;  // total ~ v * 2^(kCoopDigitBase + 32 (top - 1) - lz), leading bit at 63
-      const int E = kCoopDigitBase + 32 * (top - 1) - lz + 63;
-      const float mf = __uint_as_float(0x3f800000u | static_cast<unsigned>((v >> 40) & 0x7fffffu));
-      cv = R + (static_cast<float>(E) + log2f(mf));
-    }
+  for (int k = 0; k < kCoopFinWords; ++k) {
+    const unsigned long long v = s_fin[row][k] + carry;
+    s_fin[row][k] = v & 0xffffull;
+    carry = v >> 16;
+    if (v & 0xffffull) top = k;
   }
-  return cv;
+  if (top < 0) return R;  // no mass at all (cannot happen for a window row)
+  unsigned long long wv = 0;
+#pragma unroll 1
+  for (int k = top; k > top - 4; --k) wv = (wv << 16) | (k >= 0 ? s_fin[row][k] : 0ull);
+  const int lz = __clzll(static_cast<long long>(wv));
+  wv <<= lz;  // total ~ wv * 2^(16 (top - 3) + kCoopDigitBase - lz), leading bit at 63
+  const int E = 16 * (top - 3) + kCoopDigitBase - lz + 63;
+  const float mf = __uint_as_float(0x3f800000u | static_cast<unsigned>((wv >> 40) & 0x7fffffu));
+  return R + (static_cast<float>(E) + __builtin_amdgcn_logf(mf));
 }
 
 // Exact normaliser of a flagged head: merge of its per-unit (m, l) partials
@@ -639,46 +686,73 @@ __device__ __forceinline__ float coop_exact_c(const CoopCtx& c, int bh, int row)
 #pragma unroll
     for (int i = 0; i < 4; ++i) lse2_merge(m, l, __uint_as_float(pp[i].x), __uint_as_float(pp[i].y));
   }
-  return m + log2f(l);
+  return m + __builtin_amdgcn_logf(l);  // v_log_f32: log2 to about an ulp, no constants to keep live
+}
+
+// Adds a row's l * 2^(m - R) to its accumulator (lanes 0..31, rows < w):
+// l * 2^gap = y * 2^n with y = l * 2^(gap - n) in [l, 2l) and l >= 1 (the
+// max term), y = mant * 2^(ey - 23) exactly, so the term is the 24-bit mant
+// at bit pos = ey - 23 + n - kCoopDigitBase, i.e. mant << (pos % 16) in word
+// pos / 16. Terms below word 0 are dropped (they are at least 2^-100 times
+// the window key's own term); a gap above kCoopOvfGap flags the head.
+__device__ __forceinline__ void coop_contribute(const CoopCtx& c, int bh, int row, float m, float l, float R) {
+  const float gap = m - R;
+  if (gap > kCoopOvfGap) {
+    atomicOr(&c.cnt[bh * kCoopCtrWords + 16], 1u);
+  } else if (gap > static_cast<float>(kCoopDigitBase + 60)) {
+    const float n = floorf(gap);
+    const float y = l * fast_exp2(gap - n);
+    const unsigned bits = __float_as_uint(y);
+    unsigned long long mant = (bits & 0x7fffffu) | 0x800000u;
+    int pos = static_cast<int>((bits >> 23) & 0xffu) - 127 - 23 + static_cast<int>(n) - kCoopDigitBase;
+    if (pos < 0) {
+      mant >>= -pos;  // -pos < 40 here
+      pos = 0;
+    }
+    const unsigned off = static_cast<unsigned>(row * kCoopRowWords + (pos >> 4)) * 8u;
+    atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(c.acc + static_cast<int64_t>(bh) *
+                                                                                         kCoopHeadWords) + off),
+              mant << (pos & 15));
+  }
 }
 
 // End-of-round bookkeeping of wave 3 (after the unit's row statistics are in
 // (m, l) of lanes 0..31 when `contributed`), entered after the round's
 // closing wait: whatever it issues is used only after the next round's.
 __device__ __forceinline__ void coop_bookkeeping(const CoopCtx& c, CoopPipe& p, bool contributed, int unit, float m,
-                                                 float l) {
-  const int row = c.lane & 31;
-  // (a) finish the head whose digits were loaded last round
+                                                 float l, int r) {
+  const int row = coop_row(c);
+  // (a) finish the head whose words were staged last round
   if (p.fin_head >= 0) {
-    const bool ovf = __shfl(static_cast<unsigned>(p.fin[5]), 32) != 0u;
-    float cv;
-    if (!ovf) {
-      cv = coop_digits_to_c(p.fin, c.s_fin, c.lane, p.fin_ref);
+    float cv = 0.f;
+    if (__builtin_amdgcn_readfirstlane(p.fin_ovf) == 0u) {
+      if (c.lane < 32) cv = coop_words_to_c(c.s_fin, row, p.fin_ref);
     } else {
-      cv = c.lane < 32 && row < c.w ? coop_exact_c(c, p.fin_head, row) : 0.f;
+      if (c.lane < 32 && row < c.w) cv = coop_exact_c(c, p.fin_head, row);
     }
     if (c.lane < 32 && row < c.w) st_agent_u2(&c.stat[p.fin_head * 32 + row], make_uint2(__float_as_uint(cv), 1u));
     p.fin_head = -1;
   }
-  // (b) the count raised last round: its last unit makes this workgroup the finisher
+  // (b) the count raised last round: the last contribution makes this
+  // workgroup the finisher; stage the head's words in LDS
   if (p.cnt_head >= 0) {
-    if (__shfl(p.cnt_ret, 0) == static_cast<unsigned>(c.nunit - 1)) {
-      const unsigned long long* a = c.acc + static_cast<int64_t>(p.cnt_head) * kCoopHeadWords + row * kCoopRowWords;
-      const int d0 = c.lane < 32 ? 0 : 6;
+    if (__builtin_amdgcn_readfirstlane(p.cnt_ret) == static_cast<unsigned>(c.cnt_target - 1)) {
+      const unsigned long long* a = c.acc + static_cast<int64_t>(p.cnt_head) * kCoopHeadWords;
+      constexpr int kPieces = 32 * kCoopFinWords / 2;  // 16-byte pieces
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        if (d0 + i < kCoopDigits)
-          p.fin[i] = ld_agent_u64(a + d0 + i);
-        else
-          p.fin[i] = __hip_atomic_load(&c.cnt[p.cnt_head * kCoopCtrWords + 16], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < kPieces / 64; ++i) {
+        const int piece = i * 64 + c.lane, prow = piece / (kCoopFinWords / 2), pj = piece % (kCoopFinWords / 2);
+        __builtin_amdgcn_global_load_lds(a + prow * kCoopRowWords + pj * 2,
+                                         (lds_void*)(&c.s_fin[0][0] + i * 128), 16, 0, 16 /* sc1 */);
       }
+      p.fin_ovf = __hip_atomic_load(&c.cnt[p.cnt_head * kCoopCtrWords + 16], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
       p.fin_ref = c.ref[p.cnt_head * 32 + row];
       p.fin_head = p.cnt_head;
     }
     p.cnt_head = -1;
   }
-  // (c) last round's contributions are complete: count their unit
+  // (c) last round's contribution is complete: count it
   if (p.ack_head >= 0) {
     unsigned ret = 0;
     if (c.lane == 0) ret = atomicAdd(&c.cnt[p.ack_head * kCoopCtrWords], 1u);
@@ -686,41 +760,25 @@ __device__ __forceinline__ void coop_bookkeeping(const CoopCtx& c, CoopPipe& p, 
     p.cnt_head = p.ack_head;
     p.ack_head = -1;
   }
-  // (d) this round's contribution (its reference scores were loaded at the round's start)
-  const float R = p.ref;
+  // (d) this round's unit: its partial, the running pair, and the
+  // contribution after this workgroup's last unit of the head
   if (contributed) {
-    const int u = unit;
-    const int bh = u / c.nunit;
-    if (c.lane < 32) {
-      st_agent_u2(reinterpret_cast<uint2*>(&c.part[static_cast<int64_t>(u) * 32 + row]),
+    const int bh = unit / c.nunit;
+    if (c.lane < 32)
+      st_agent_u2(reinterpret_cast<uint2*>(&c.part[static_cast<int64_t>(unit) * 32 + row]),
                   make_uint2(__float_as_uint(m), __float_as_uint(l)));
-      if (row < c.w) {
-        const float gap = m - R;
-        if (gap > kCoopOvfGap) {
-          atomicOr(&c.cnt[bh * kCoopCtrWords + 16], 1u);
-        } else if (gap > static_cast<float>(kCoopDigitBase - 40)) {  // smaller terms fall below digit 0
-          // l * 2^gap = y * 2^n with y = l * 2^(gap - n) in [l, 2l), l >= 1 (the unit's max term);
-          // y = mant * 2^(ey - 23) exactly, so the term is mant at bit ey - 23 + n - kCoopDigitBase
-          const float n = floorf(gap);
-          const float y = l * fast_exp2(gap - n);
-          const unsigned bits = __float_as_uint(y);
-          unsigned long long mant = (bits & 0x7fffffu) | 0x800000u;
-          int pos = static_cast<int>((bits >> 23) & 0xffu) - 127 - 23 + static_cast<int>(n) - kCoopDigitBase;
-          if (pos < 0) {
-            mant = -pos >= 64 ? 0ull : mant >> -pos;
-            pos = 0;
-          }
-          if (mant) {
-            const unsigned long long v = mant << (pos & 31);  // < 2^56: two digits
-            unsigned long long* a =
-                c.acc + static_cast<int64_t>(bh) * kCoopHeadWords + row * kCoopRowWords + (pos >> 5);
-            atomicAdd(a, v & 0xffffffffull);
-            if (v >> 32) atomicAdd(a + 1, v >> 32);
-          }
-        }
-      }
+    if (p.run_head == bh) {
+      lse2_merge(p.run_m, p.run_l, m, l);
+    } else {
+      p.run_m = m;
+      p.run_l = l;
+      p.run_head = bh;
     }
-    p.ack_head = bh;
+    if (!(r + 1 < c.rounds && coop_head(c, r + 1) == bh)) {
+      if (c.lane < 32 && row < c.w) coop_contribute(c, bh, row, p.run_m, p.run_l, p.ref);
+      p.ack_head = bh;
+      p.run_head = -1;
+    }
   }
 }
 
@@ -756,17 +814,23 @@ __device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
     p.pre = ld_agent_u2(&c.stat[coop_head(c, min(max(rb + 1, 0), last)) * 32 + (c.lane & 31)]);
     p.ref = c.ref[coop_head(c, min(r, last)) * 32 + (c.lane & 31)];
   }
-  lds_barrier();
+  lds_barrier();  // everyone is past round r - 1: its K buffer is free again
+  if (r + 1 < c.rounds) coop_issue_k<D>(c, r + 1, (BANK & 1) ? c.kbuf0 : c.kbuf1);
   // ---- votes of the unit of round rb (bank (BANK + 1) % kCoopBanks)
   if (do_b) {
     const int u = rb * c.G + c.g;
     const int bh = u / c.nunit, c0 = (u - bh * c.nunit) * kCoopUnit;
     const f32x16_t& s = sc[(BANK + 1) % kCoopBanks];
     float v = 0.f;
+    if (c.w == kMaxWindow) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = acc_row(i, c.half);
-      v += row < c.w ? fast_exp2(s[i] - c.s_c[row]) : 0.f;
+      for (int i = 0; i < 16; ++i) v += fast_exp2(s[i] - c.s_c[acc_row(i, c.half)]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = acc_row(i, c.half);
+        v += row < c.w ? fast_exp2(s[i] - c.s_c[row]) : 0.f;
+      }
     }
     v += __shfl_xor(v, 32);
     const int j = c0 + c.wave * kTile + c.col;
@@ -778,7 +842,7 @@ __device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
   if (do_a) {
     unit = r * c.G + c.g;
     const int bh = unit / c.nunit, c0 = (unit - bh * c.nunit) * kCoopUnit;
-    const unsigned char* tile = c.kbuf + c.wave * Ly::kTileB;
+    const unsigned char* tile = ((BANK & 1) ? c.kbuf1 : c.kbuf0) + c.wave * Ly::kTileB;
     f32x16_t acc = {}, bt = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -790,16 +854,25 @@ __device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
     }
     const int jt = c0 + c.wave * kTile;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[BANK][i] = acc[i] * c.scale_log2;
-      const int j = jt + acc_row(i, c.half);
-      bt[i] = (j < c.L && j <= c.t0 + c.col) ? bt[i] * c.scale_log2 : kNegBig;
-      m = fmaxf(m, bt[i]);
+    for (int i = 0; i < 16; ++i) sc[BANK][i] = acc[i] * c.scale_log2;
+    if (c0 + kCoopUnit <= c.t0) {  // the whole unit is prefix: every query sees every key
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        bt[i] *= c.scale_log2;
+        m = fmaxf(m, bt[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = jt + acc_row(i, c.half);
+        bt[i] = (j < c.L && j <= c.t0 + c.col) ? bt[i] * c.scale_log2 : kNegBig;
+        m = fmaxf(m, bt[i]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) l += fast_exp2(bt[i] - m);
-    lds_barrier();  // staged K and Q consumed
-    if (r + 1 < c.rounds) coop_issue<D>(c, p, r + 1);
+    lds_barrier();  // staged Q consumed
+    if (r + 1 < c.rounds) coop_issue_q<D>(c, p, r + 1);
     lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
     if (c.half == 0) c.wred[c.wave][c.col] = make_float2(m, l);
     lds_barrier();
@@ -815,7 +888,7 @@ __device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
   // round's prefetches and last round's contributions, count and digit loads
   // (wave 3)
   __builtin_amdgcn_s_waitcnt(0);
-  if (c.wave == 3) coop_bookkeeping(c, p, do_a, unit, m, l);
+  if (c.wave == 3) coop_bookkeeping(c, p, do_a, unit, m, l, r);
 }
 
 template <int D>
@@ -826,11 +899,12 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
     unsigned* __restrict__ cnt, uint2* __restrict__ stat, float2* __restrict__ part,
     unsigned* __restrict__ status, float* __restrict__ vote) {
   using Ly = CoopLayout<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char kbuf[Ly::kKBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf0[Ly::kKBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf1[Ly::kKBytes];
   __shared__ __attribute__((aligned(16))) unsigned char qbuf[Ly::kQBytes];
   __shared__ float2 wred[kWaves][32];
   __shared__ float s_c[32];
-  __shared__ unsigned long long s_fin[32][kCoopDigits + 1];
+  __shared__ unsigned long long s_fin[32][kCoopFinWords];
 
   CoopCtx c;
   c.q = q; c.qsb = qsb; c.qsh = qsh; c.qst = qst; c.qrow0 = qrow0;
@@ -838,22 +912,29 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
   c.H = H; c.L = L; c.w = w; c.t0 = L - w; c.nunit = nunit;
   c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x);
   c.rounds = (total_units - c.g + c.G - 1) / c.G;
+  c.cnt_target = min(nunit, c.G);
   c.scale_log2 = scale_log2;
   c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.part = part; c.status = status; c.vote = vote;
-  c.kbuf = kbuf; c.qbuf = qbuf; c.wred = wred; c.s_c = s_c; c.s_fin = s_fin;
-  c.lane = lane_id(); c.wave = threadIdx.x / kWave; c.col = c.lane & 31; c.half = c.lane >> 5;
-
+  c.kbuf0 = kbuf0; c.kbuf1 = kbuf1; c.qbuf = qbuf; c.wred = wred; c.s_c = s_c; c.s_fin = s_fin;
+  c.lane = lane_id(); c.col = c.lane & 31; c.half = c.lane >> 5;
+  c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // uniform: keeps wave-indexed
+                                                                                     // addresses in scalar registers
   CoopPipe p;
   p.ack_head = p.cnt_head = p.fin_head = -1;
   p.cnt_ret = 0;
+  p.fin_ovf = 0;
+  p.run_head = -1;
+  p.run_m = kNegBig;
+  p.run_l = 0.f;
   p.pre = make_uint2(0u, 0u);
   p.fin_ref = 0.f;
   p.ref = 0.f;
   p.q_head = -1;
-#pragma unroll
-  for (int i = 0; i < 6; ++i) p.fin[i] = 0;
   f32x16_t sc[kCoopBanks];
-  if (c.rounds > 0) coop_issue<D>(c, p, 0);
+  if (c.rounds > 0) {
+    coop_issue_k<D>(c, 0, c.kbuf0);
+    coop_issue_q<D>(c, p, 0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   // every unit's votes (round rounds - 1 + kCoopLag) and its head's
   // bookkeeping (three rounds after its last unit) fall inside the loop
@@ -1422,8 +1503,10 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
   const int qrow0 = q_len - window;
 
-  // AUTO takes the two-pass schedule: on MI355X it is the faster one for now
-  const int G = (dt == KVC_BF16 && g_schedule == KVC_SNAPKV_SINGLE_PASS) ? coop_grid(lay, D) : 0;
+  // AUTO takes the single pass where it can run (it reads K once and measures
+  // faster on MI355X) and falls back to two passes if the device refuses the
+  // cooperative launch
+  const int G = (dt == KVC_BF16 && g_schedule != KVC_SNAPKV_TWO_PASS) ? coop_grid(lay, D) : 0;
   int schedule = KVC_SNAPKV_TWO_PASS;
   mark_phase(0, stream);
   if (G > 0) {
@@ -1436,9 +1519,16 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
                                                        scale_log2, ws, vraw, pooled, stream)
                              : launch_single_pass<64>(lay, G, qb, qs, qrow0, kb, kvs, H, L, window, pool_kernel / 2,
                                                       scale_log2, ws, vraw, pooled, stream);
-    if (st != KVC_OK) return st;
-    schedule = KVC_SNAPKV_SINGLE_PASS;
-  } else {
+    if (st == KVC_OK) {
+      schedule = KVC_SNAPKV_SINGLE_PASS;
+    } else if (g_schedule == KVC_SNAPKV_SINGLE_PASS) {
+      return st;
+    } else {
+      clear_error();
+      (void)hipGetLastError();
+    }
+  }
+  if (schedule == KVC_SNAPKV_TWO_PASS) {
     mark_phase(1, stream);  // counters and histograms are cleared by the statistics pass
     if (dt == KVC_BF16)
       launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0,
@@ -1481,3 +1571,4 @@ extern "C" void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events) {
   g_phase_events = n_events > 0 ? events : nullptr;
   g_phase_count = n_events > 0 ? n_events : 0;
 }
+
