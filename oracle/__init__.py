@@ -11,6 +11,6 @@ this oracle, pinned only by self-consistency and the invariants in the tests):
 the 1/sqrt(D) score scale, the tie rules, the pooling edges and the H2O
 prompt-score initialisation.
 """
-from . import snapkv, h2o, sink
+from . import snapkv, h2o, sink, attention
 
-__all__ = ["snapkv", "h2o", "sink"]
+__all__ = ["snapkv", "h2o", "sink", "attention"]
