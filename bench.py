@@ -191,6 +191,8 @@ def bench_snapkv(args, ev):
     torch.cuda.synchronize()
     set_events(None)
     lib.kvc_snapkv_set_schedule(0)
+    dec_att = time_decode(kvc, ev, q[:, :, -1].contiguous(), out.k, out.v, wl.budget, 200,
+                          f"SnapKV-compressed {wl.name} layer B{B} H{H} {wl.budget} rows")
     phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / args.steps for j, p in enumerate(phases)}
     step_ms = elapsed / args.steps * 1e3
     nbytes = snapkv_bytes(wl)
@@ -209,7 +211,8 @@ def bench_snapkv(args, ev):
                   "frac": achieved / PEAK_HBM, "traffic": traffic, "kernel": kernel_name,
                   "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": kern_ms[dominant],
                   "score_pass_ms": kern_ms},
-        phase_ms=phase_ms, alg_bytes=nbytes["total"], schedule="single-pass" if single else "two-pass")
+        phase_ms=phase_ms, alg_bytes=nbytes["total"], schedule="single-pass" if single else "two-pass",
+        decode_attention=dec_att)
 
 
 def cpu_baseline(res, seconds):
@@ -240,6 +243,35 @@ def cpu_baseline(res, seconds):
             "kind": "oracle", "affinity_cores": cores,
             "sample": f"{done} whole-head compressions cycling over the {len(heads)} heads of the {wl.name} "
                       f"layer (fp64 numpy, BLAS threads as reported), {t:.1f}s; scaled to one layer"}
+
+
+def time_decode(kvc, ev, q, k, v, n, reps, label):
+    """kvc_decode_attention over the first n rows of k/v: average time of `reps` back-to-back
+    calls bracketed by two events on the library's stream, and its HBM roofline (K and V rows
+    read once, q read, the fp32 output written)."""
+    import torch
+
+    B, H, _, D = k.shape
+    es = k.element_size()
+    ws = torch.empty(max(kvc.decode_attention_workspace_bytes(B, H, n, D), 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        kvc.decode_attention(q, k, v, n, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    e = ev.create(2)
+    ev.record(e[0], stream)
+    for _ in range(reps):
+        kvc.decode_attention(q, k, v, n, workspace=ws, out=out)
+    ev.record(e[1], stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(e[0], e[1]) / reps
+    nbytes = B * H * (2 * n * D * es + D * es + D * 4)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"decode attention, {label}: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s")
+    return {"cache": label, "ms_per_call": ms, "calls": reps, "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": gbps * 1e9 / PEAK_HBM, "kernel": "decode_partial + decode_merge"}}
 
 
 def bench_h2o(args, ev):
@@ -297,6 +329,12 @@ def bench_h2o(args, ev):
     step_bytes = [B * H * (N * (D * es + 12) + 5 * D * es) for N in ns]
     kern_s = sum(h2o_ms) * 1e-3
     achieved = sum(step_bytes) / kern_s
+    # decode attention (the generation step over the policies' caches) with the last step's queries
+    q_last = dec[steps - 1, 0]
+    dec_att = [time_decode(kvc, ev, q_last, sink.k, sink.v, min(sink.length, wl.n_sink + wl.sink_recent), 20,
+                           f"sink + recent ring B{B} H{H} {wl.n_sink}+{wl.sink_recent} slots"),
+               time_decode(kvc, ev, q_last, cache.k, cache.v, cache.n, 20,
+                           f"H2O cache B{B} H{H} {cache.n} slots")]
     return {
         "workload": f"{wl.name}: B{B} H{H} D{D}, prompt {Lp} (GPU prompt-score prefill, untimed) then "
                     f"{steps} decode steps, "
@@ -311,6 +349,7 @@ def bench_h2o(args, ev):
                      "kernel": "h2o_step_kernel", "algorithmic_bytes_per_launch": sum(step_bytes) / steps,
                      "avg_launch_ms": kern_s / steps * 1e3},
         "prefill_ms": prefill_ms,
+        "decode_attention": dec_att,
         "inputs": "prompt from the seeded host generator; decode q/k/v drawn on the GPU with a seeded "
                   "torch generator (N(0,1), bf16)",
     }
@@ -366,6 +405,7 @@ def main():
         "algorithmic_bytes_per_step": res["alg_bytes"],
         "roofline": res["roofline"],
         "phase_ms": res["phase_ms"],
+        "decode_attention_compressed": res["decode_attention"],
     }
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)

@@ -238,6 +238,41 @@ kvc_status kvc_sink_recent(void* ring_k, void* ring_v, int32_t* slot_pos,
                            int n_sink, int n_recent, int B, int H, int D,
                            kvc_dtype dt, int32_t* kept_idx_out, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* Decode attention over a compacted or windowed cache.                       */
+/* ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace kvc_decode_attention needs (0 if the sizes are
+ * invalid; a small non-zero size when no workspace is used). */
+size_t kvc_decode_attention_workspace_bytes(int B, int H, int n, int D);
+
+/* One query per head attends over the first n cached rows of that head:
+ *   out[b,h,:] = sum_j softmax_j(q[b,h,:].k[b,h,j,:] / sqrt(D)) v[b,h,j,:],
+ * j = 0 .. n-1. This is the generation step after compression: over the
+ * compressed cache only (SnapKV page, processing flow step 4), or over the
+ * sink and recent tokens only (StreamingLLM page, inference flow). The rows
+ * may be in any order (no positional re-encoding inside the cache), so the
+ * outputs of kvc_snapkv_compress (n = budget), a kvc_sink_recent ring
+ * (n = min(len, n_sink + n_recent)) or an H2O cache (n = its n) are all
+ * valid inputs.
+ *
+ * q       [B, H, D] with element strides qs.b, qs.h (qs.t unused).
+ * k, v    [B, H, >= n, D], both with strides kvs (D contiguous).
+ * out     [B, H, D] float32, contiguous; every element is written.
+ * workspace  device buffer of kvc_decode_attention_workspace_bytes(...)
+ *         bytes, used when the rows are split over several workgroups per
+ *         head (n > 256, or n > 128 when B*H*ceil(n/256) < 512) and their
+ *         partial results merged; may be NULL otherwise. Contents on entry
+ *         do not matter.
+ * Requires n >= 1, D in {64, 128}, 16-byte aligned pointers and strides.
+ * Scores and the softmax are fp32 (2^x on the hardware unit); bf16 inputs are
+ * widened exactly. */
+kvc_status kvc_decode_attention(const void* q, kvc_strides qs, const void* k,
+                                const void* v, kvc_strides kvs, int B, int H,
+                                int n, int D, kvc_dtype dt, float* out,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
     "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS",
     "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
+    "decode_attention_workspace_bytes", "decode_attention",
 ]
 
 KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
+    "kvc_decode_attention_workspace_bytes", "kvc_decode_attention",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +97,10 @@ def library():
                                   vp, sz, vp]
     L.kvc_snapkv_set_phase_events.restype = None
     L.kvc_snapkv_set_phase_events.argtypes = [vp, i32]
+    L.kvc_decode_attention_workspace_bytes.restype = sz
+    L.kvc_decode_attention_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.kvc_decode_attention.restype = i32
+    L.kvc_decode_attention.argtypes = [vp, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, vp, vp, sz, vp]
     L.kvc_snapkv_set_schedule.restype = i32
     L.kvc_snapkv_set_schedule.argtypes = [i32]
     L.kvc_snapkv_last_schedule.restype = i32
@@ -201,6 +207,38 @@ def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, 
         window, budget, pool_kernel, dt, _ptr(k_out), _ptr(v_out), _ptr(idx), _ptr(pooled),
         _ptr(vote), _ptr(workspace), workspace.numel(), _stream()))
     return SnapKVResult(k_out, v_out, idx, pooled, vote)
+
+
+def decode_attention_workspace_bytes(B, H, n, D):
+    return int(library().kvc_decode_attention_workspace_bytes(B, H, n, D))
+
+
+def decode_attention(q, k, v, n=None, *, workspace=None, out=None):
+    """Attention of one query per head over the first ``n`` cached rows (kvc_decode_attention).
+
+    q: [B, H, D]; k, v: [B, H, N, D] with the same strides (D contiguous), bf16 or fp32 on
+    the GPU; ``n`` defaults to N. Returns float32 [B, H, D] (``out`` if given, contiguous).
+    """
+    _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, H, D] and k, v [B, H, N, D]")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, D = k.shape
+    if tuple(q.shape) != (B, H, D):
+        raise ValueError("q must be [B, H, D] matching k")
+    n = N if n is None else int(n)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    if workspace is None:
+        nbytes = decode_attention_workspace_bytes(B, H, n, D)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=k.device)
+    _check(library().kvc_decode_attention(
+        _ptr(q), Strides(q.stride(0), q.stride(1), 0), _ptr(k), _ptr(v), _strides4(k), B, H, n, D,
+        _dtype_code(k), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
 
 
 class H2OCache:

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvc.so")
-SOURCES = ["api.hip", "snapkv.hip", "h2o.hip", "sink.hip"]
+SOURCES = ["api.hip", "snapkv.hip", "h2o.hip", "sink.hip", "decode.hip"]
 ARCH = "gfx950"
 
 

@@ -102,6 +102,30 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned* scratc
   return res;
 }
 
+template <typename T>
+struct Vec16;  // a 16-byte piece of a row as float lanes
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int kN = 8;
+  __device__ static void load(const void* p, float (&x)[8]) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int kN = 4;
+  __device__ static void load(const void* p, float (&x)[4]) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = u[i];
+  }
+};
+
 // (m, l) pairs of a base-2 softmax: m is a running maximum, l = sum 2^(s - m).
 __device__ __forceinline__ void lse2_merge(float& m, float& l, float m2, float l2) {
   const float mm = fmaxf(m, m2);

@@ -100,3 +100,42 @@ def test_sink_argument_checks():
         args = list(good)
         args[i] = bad
         assert lib.kvc_sink_recent(*args) != kvc.KVC_OK
+
+
+def test_decode_attention_workspace_query():
+    lib = kvc.library()
+    assert lib.kvc_decode_attention_workspace_bytes(64, 32, 1024, 128) == 2048 * 4 * 130 * 4  # chunks of 256 rows
+    assert lib.kvc_decode_attention_workspace_bytes(1, 32, 2048, 128) == 32 * 16 * 130 * 4   # few heads: 128 rows
+    assert lib.kvc_decode_attention_workspace_bytes(1, 32, 50, 128) > 0                      # one chunk: no partials
+    assert lib.kvc_decode_attention_workspace_bytes(1, 32, 0, 128) == 0
+    assert lib.kvc_decode_attention_workspace_bytes(1, 32, 100, 96) == 0
+
+
+DEC_OK = dict(q=16, k=32, v=48, out=64, ws=80, B=1, H=2, n=1000, D=128, dt=kvc.KVC_BF16,
+              qs=kvc.Strides(256, 128, 0), kvs=kvc.Strides(2 * 1024 * 128, 1024 * 128, 128), wsb=1 << 20)
+
+
+def _decode(**over):
+    a = dict(DEC_OK, **over)
+    lib = kvc.library()
+    vp = ctypes.c_void_p
+    st = lib.kvc_decode_attention(vp(a["q"]), a["qs"], vp(a["k"]), vp(a["v"]), a["kvs"], a["B"], a["H"], a["n"],
+                                  a["D"], a["dt"], vp(a["out"]), vp(a["ws"]), a["wsb"], None)
+    return st, lib.kvc_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), kvc.KVC_ERR_INVALID_ARG),
+    (dict(out=0), kvc.KVC_ERR_INVALID_ARG),
+    (dict(n=0), kvc.KVC_ERR_INVALID_ARG),
+    (dict(D=96), kvc.KVC_ERR_UNSUPPORTED),
+    (dict(dt=5), kvc.KVC_ERR_INVALID_ARG),
+    (dict(k=40), kvc.KVC_ERR_INVALID_ARG),                       # misaligned
+    (dict(kvs=kvc.Strides(0, 0, 100)), kvc.KVC_ERR_INVALID_ARG),  # 200-byte rows
+    (dict(kvs=kvc.Strides(0, 0, 64)), kvc.KVC_ERR_INVALID_ARG),   # rows shorter than D
+    (dict(ws=0), kvc.KVC_ERR_WORKSPACE),                          # several chunks need partials
+    (dict(wsb=16), kvc.KVC_ERR_WORKSPACE),
+])
+def test_decode_attention_argument_checks(over, status):
+    st, msg = _decode(**over)
+    assert st == status and msg
