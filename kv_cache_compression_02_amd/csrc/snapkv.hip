@@ -539,7 +539,6 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
     float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
     uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr) {
-  __shared__ float red[32][33];
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
@@ -547,26 +546,49 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
   if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
   if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
   if (threadIdx.x < 4) ctr[bh * 4 + threadIdx.x] = 0;
+  // thread (i, part): window row i, dims part*D/8 .. part*D/8 + D/8 - 1 (two or one
+  // 16-byte pieces); the row's 8 threads are adjacent lanes and sum their parts by shuffles
+  constexpr int kDims = D / 8, kPieces = kDims / 8;
   const int t0 = L - w;
-  const int i = threadIdx.x >> 3;  // window row
-  const uint16_t* qr = q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + min(i, w - 1)) * qst;
-  for (int jj = (threadIdx.x & 7); jj < 32; jj += 8) {
-    float sv = -INFINITY;
-    if (i < w && jj <= i) {
-      const uint16_t* kr = k + b * ksb + h * ksh + static_cast<int64_t>(t0 + jj) * kst;
-      float d = 0.f;
-      for (int e = 0; e < D; ++e)
-        d = fmaf(__uint_as_float(static_cast<unsigned>(qr[e]) << 16), __uint_as_float(static_cast<unsigned>(kr[e]) << 16), d);
-      sv = d * scale_log2;
+  const int i = threadIdx.x >> 3, part = threadIdx.x & 7;
+  const uint16_t* qr = q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + min(i, w - 1)) * qst + part * kDims;
+  const uint16_t* kw = k + b * ksb + h * ksh + static_cast<int64_t>(t0) * kst + part * kDims;
+  float qv[kDims];
+#pragma unroll
+  for (int pc = 0; pc < kPieces; ++pc) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qr + pc * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[pc * 8 + 2 * e] = __uint_as_float(u[e] << 16);
+      qv[pc * 8 + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
     }
-    red[i][jj] = sv;
   }
-  __syncthreads();
-  if (threadIdx.x < 32) {
-    float m = -INFINITY;
-    for (int jj = 0; jj < 32; ++jj) m = fmaxf(m, red[threadIdx.x][jj]);
-    ref[bh * 32 + threadIdx.x] = threadIdx.x < w ? m : 0.f;
+  float m = -INFINITY;
+  for (int j0 = 0; j0 < w; j0 += 8) {  // uniform trip count: every lane takes part in the shuffles
+    u32x4_t kv[8][kPieces];              // eight window keys' pieces in flight together
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      const uint16_t* kr = kw + static_cast<int64_t>(min(j0 + jb, w - 1)) * kst;
+#pragma unroll
+      for (int pc = 0; pc < kPieces; ++pc) kv[jb][pc] = *reinterpret_cast<const u32x4_t*>(kr + pc * 8);
+    }
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      float d = 0.f;
+#pragma unroll
+      for (int pc = 0; pc < kPieces; ++pc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d = fmaf(qv[pc * 8 + 2 * e], __uint_as_float(kv[jb][pc][e] << 16), d);
+          d = fmaf(qv[pc * 8 + 2 * e + 1], __uint_as_float(kv[jb][pc][e] & 0xFFFF0000u), d);
+        }
+      d += __shfl_xor(d, 1);
+      d += __shfl_xor(d, 2);
+      d += __shfl_xor(d, 4);
+      if (j0 + jb <= i && j0 + jb < w) m = fmaxf(m, d * scale_log2);
+    }
   }
+  if (part == 0) ref[bh * 32 + i] = i < w ? m : 0.f;
 }
 
 // Everything one workgroup of the single pass needs across rounds.
