@@ -160,9 +160,10 @@ def bench_snapkv(args, ev):
         call()
     torch.cuda.synchronize()
     single = kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
+    score_kernel = kvc.snapkv_last_score_kernel()
     phases = PHASES_SINGLE if single else PHASES
     passes = ("score", "pool") if single else ("stats", "votes")
-    log(f"schedule: {'single pass' if single else 'two passes'}")
+    log(f"schedule: {'single pass' if single else 'two passes'} ({score_kernel})")
     # Timed region: events only around the score passes (boundaries 1, 2 and 4;
     # every recorded event costs the GPU a few microseconds).
     timed = []
@@ -200,7 +201,7 @@ def bench_snapkv(args, ev):
     dom_bytes = nbytes[dominant]
     achieved = dom_bytes / (kern_ms[dominant] * 1e-3)
     suffix = "bf16" if wl.dtype == "bf16" else "f32"
-    kernel_name = "snap_coop_bf16" if single else f"snap_{dominant}_{suffix}"
+    kernel_name = score_kernel if single else f"snap_{dominant}_{suffix}"
     traffic = load_traffic(kernel_name, ["snapkv.hip", "common.hpp"])
     log(f"step {step_ms:.3f} ms; phases (ms): " + ", ".join(f"{p} {phase_ms[p]:.4f}" for p in phases))
     return dict(

@@ -123,10 +123,14 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  *                complete, so K is read once. Each row's normaliser is summed
  *                exactly in fixed point, so the result does not depend on the
  *                order of the contributions (bitwise reproducible as well).
- *                It needs cooperative launch and a head of at most four
- *                device-wide rounds of 128-key units (on MI355X, up to about
- *                256K keys per head for one head); otherwise the call uses
- *                TWO_PASS.
+ *                Two kernels implement it. snap_wave_bf16, whose waves work
+ *                independently on 32-key tiles, runs where every workgroup
+ *                has tiles in every head and a head spans at most six of its
+ *                rounds (on MI355X: about 64K to 320K keys per head).
+ *                snap_coop_bf16, whose workgroups step through 128-key units
+ *                together, covers shorter heads (a head of at most four
+ *                device-wide rounds of units). Where neither can run, the call
+ *                uses TWO_PASS.
  *   AUTO         the default: SINGLE_PASS where it can run (the faster of
  *                the two on MI355X at the sizes measured so far), else
  *                TWO_PASS; also TWO_PASS if the cooperative launch fails. */
@@ -144,6 +148,11 @@ int kvc_snapkv_set_schedule(int schedule);
 /* The schedule (TWO_PASS or SINGLE_PASS) the last successful
  * kvc_snapkv_compress call on the calling thread ran, 0 if none. */
 int kvc_snapkv_last_schedule(void);
+
+/* Name of the kernel (or kernels, joined by '+') that computed the scores in
+ * the last successful kvc_snapkv_compress call on the calling thread: a
+ * static string, "" if none. For reports and tests; it does not change. */
+const char* kvc_snapkv_last_score_kernel(void);
 
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its

@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
+    "kvc_snapkv_last_score_kernel",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention",
 )
 
@@ -105,6 +106,8 @@ def library():
     L.kvc_snapkv_set_schedule.argtypes = [i32]
     L.kvc_snapkv_last_schedule.restype = i32
     L.kvc_snapkv_last_schedule.argtypes = []
+    L.kvc_snapkv_last_score_kernel.restype = ctypes.c_char_p
+    L.kvc_snapkv_last_score_kernel.argtypes = []
     L.kvc_sink_recent.restype = i32
     L.kvc_sink_recent.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
     _lib = L
@@ -168,6 +171,11 @@ def snapkv_schedule(schedule):
 def snapkv_last_schedule():
     """Schedule the last successful snapkv_compress call on this thread ran (0 if none)."""
     return int(library().kvc_snapkv_last_schedule())
+
+
+def snapkv_last_score_kernel():
+    """Kernel name(s) that computed the scores in the last successful snapkv_compress call."""
+    return library().kvc_snapkv_last_score_kernel().decode()
 
 
 def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,

@@ -538,8 +538,11 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
     float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
-    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr) {
+    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr, u32x4_t* __restrict__ wg_part,
+    int part_pieces) {
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  for (int i = threadIdx.x; i < part_pieces; i += kThreads)  // 16-byte pieces of this head's partials
+    wg_part[static_cast<int64_t>(bh) * part_pieces + i] = u32x4_t{0u, 0u, 0u, 0u};
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
@@ -643,6 +646,14 @@ __device__ __forceinline__ int coop_row(const CoopCtx& c) {
   return row;
 }
 
+// x, opaque to the optimiser: values derived from it inside a rarely taken
+// branch are computed there, instead of being hoisted out of the round loop
+// and kept live (or spilled) for the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // K tiles of round r's unit into `kbuf` (waves 0..2).
 template <int D>
 __device__ __forceinline__ void coop_issue_k(const CoopCtx& c, int r, unsigned char* kbuf) {
@@ -717,10 +728,25 @@ __device__ __forceinline__ float coop_exact_c(const CoopCtx& c, int bh, int row)
 // at bit pos = ey - 23 + n - kCoopDigitBase, i.e. mant << (pos % 16) in word
 // pos / 16. Terms below word 0 are dropped (they are at least 2^-100 times
 // the window key's own term); a gap above kCoopOvfGap flags the head.
-__device__ __forceinline__ void coop_contribute(const CoopCtx& c, int bh, int row, float m, float l, float R) {
+// With kCounted (the independent-wave kernel) every contribution also adds 1
+// to bits 48..63 of the word it lands in (a value part stays below 2^48: at
+// most 2^9 terms below 2^39 each); a dropped term adds only that count to
+// word 0 and an overflowing one to word kWvOvfWord, so that a row's words
+// alone show how many contributions have landed (and whether one overflowed).
+constexpr int kWvOvfWord = 20;
+constexpr unsigned long long kWvCountOne = 1ull << 48;
+
+template <bool kCounted = false>
+__device__ __forceinline__ void fixed_point_add(unsigned long long* acc_head, unsigned* ovf_flag, int row, float m,
+                                                float l, float R) {
   const float gap = m - R;
+  unsigned long long* arow = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_head) +
+                                                                   static_cast<unsigned>(row * kCoopRowWords) * 8u);
   if (gap > kCoopOvfGap) {
-    atomicOr(&c.cnt[bh * kCoopCtrWords + 16], 1u);
+    if (kCounted)
+      atomicAdd(arow + kWvOvfWord, kWvCountOne);
+    else
+      atomicOr(ovf_flag, 1u);
   } else if (gap > static_cast<float>(kCoopDigitBase + 60)) {
     const float n = floorf(gap);
     const float y = l * fast_exp2(gap - n);
@@ -732,10 +758,15 @@ __device__ __forceinline__ void coop_contribute(const CoopCtx& c, int bh, int ro
       pos = 0;
     }
     const unsigned off = static_cast<unsigned>(row * kCoopRowWords + (pos >> 4)) * 8u;
-    atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(c.acc + static_cast<int64_t>(bh) *
-                                                                                         kCoopHeadWords) + off),
-              mant << (pos & 15));
+    atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_head) + off),
+              (mant << (pos & 15)) + (kCounted ? kWvCountOne : 0ull));
+  } else if (kCounted) {
+    atomicAdd(arow, kWvCountOne);
   }
+}
+
+__device__ __forceinline__ void coop_contribute(const CoopCtx& c, int bh, int row, float m, float l, float R) {
+  fixed_point_add(c.acc + static_cast<int64_t>(bh) * kCoopHeadWords, &c.cnt[bh * kCoopCtrWords + 16], row, m, l, R);
 }
 
 // End-of-round bookkeeping of wave 3 (after the unit's row statistics are in
@@ -970,6 +1001,592 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
     coop_round<D, 5>(c, p, sc, r0 + 5);
     coop_round<D, 6>(c, p, sc, r0 + 6);
     coop_round<D, 7>(c, p, sc, r0 + 7);
+  }
+}
+
+// --------------------------- single-pass scores, independent waves (bf16)
+//
+// The computation of snap_coop_bf16 without the workgroup's lockstep. Every
+// wave is a worker of its own: worker v = g * kWvWaves + wave takes the
+// 32-key tiles u = r * W + v in rounds r = 0, 1, ... (W = G * kWvWaves
+// workers; tiles numbered head by head, a head's tile count padded to a
+// multiple of kWvWaves, so that the tiles of one workgroup in one round share
+// a head). A wave keeps its next tile in flight while it works on the
+// current one: K by direct-to-LDS loads into a private two-slot ring, Q by
+// plain loads into the registers that the current tile's MFMAs have just
+// read. Round r's scores wait in register bank r % kWvBanks; just before
+// round r's scores replace them, the bank's previous contents (the tile of
+// round r - kWvBanks) are turned into votes.
+// The per-row (max, sum) pairs of a wave's tiles of one head are merged in
+// LDS by whichever wave of the workgroup finishes the head last (an LDS
+// counter elects it; there is no barrier), and that wave adds the merged pair
+// to the head's fixed-point row accumulators exactly as snap_coop_bf16 does.
+// The workgroup whose count increment completes the head converts the
+// accumulators into the normalisers c_i and publishes them. A wave's only
+// full wait is the one for its next tile at the start of a round, which also
+// covers everything else it issued in the previous round (Q, contributions,
+// the count, staged words, prefetched normalisers), so each cross-worker step
+// takes one round and none of them holds up the K stream.
+//
+// Registers: the eight banks (128), Q (32) and the two MFMA accumulators
+// fill most of the 256 a wave has at two waves per SIMD, so every per-lane
+// value a round needs is derived inside the round from one opaque lane index
+// instead of being kept live across the loop (a spilled value's reload would
+// have to wait behind the next tile's loads).
+constexpr int kWvWaves = 8;
+constexpr int kWvThreads = kWvWaves * kWave;
+constexpr int kWvBanks = 8;
+constexpr int kWvRowWords = 24;  // accumulator words per row a finisher stages (values in words 0..19)
+constexpr int kWvFinBufs = 4;    // finisher staging buffers, by head mod 4
+constexpr int kWvMaxSpan = 5;    // a head spans at most this many rounds after its first
+constexpr unsigned kWvSpin = 1u << 18;  // polls before a wait gives up (far beyond any legitimate wait)
+
+template <int D>
+struct WvLayout {
+  static constexpr int kRowB = D * 2;
+  static constexpr int kP = kRowB / 16;               // 16-byte pieces per row
+  static constexpr int kTileB = kTile * kRowB;        // bytes per 32-row tile
+  static constexpr int kInst = kTileB / 1024;         // direct loads per tile (64 lanes x 16 B)
+  static constexpr int kRowsPerInst = 1024 / kRowB;
+};
+
+// A finisher's copy of one head's accumulator words (row-major, kWvRowWords
+// per row) and reference scores.
+struct WvFin {
+  unsigned long long words[32 * kWvRowWords];
+  float ref[32];
+};
+
+struct WvShared {
+  float2 mslot[2][kWvWaves][32];  // the waves' row pairs of head h, in slot h & 1
+  float s_c[kWvWaves][32];        // each wave's normalisers for its votes
+  WvFin fin[kWvFinBufs];
+  int fin_owner[kWvFinBufs];      // head staged in a finisher buffer, -1 if free
+  int mcnt[2];                    // waves that have stored their pair in a slot
+  int mtag[2];                    // the head a slot is open for
+};
+
+struct WvPos {
+  int head, b, h, t;  // tile t of head `head` = batch b, head h
+};
+
+struct WvCtx {
+  const uint16_t* q;
+  int64_t qsb, qsh, qst;
+  int qrow0;
+  const uint16_t* k;
+  int64_t ksb, ksh, kst;
+  int H, L, w, t0, nt, BH, G, g, W, rounds, wave;
+  float scale_log2;
+  const float* ref;
+  unsigned long long* acc;
+  unsigned* cnt;
+  uint2* stat;
+  float2* part;
+  unsigned* status;
+  float* vote;
+  WvShared* sh;
+};
+
+// A wave's state carried from round to round.
+struct WvPipe {
+  int cnt_head;      // head whose count this wave raised last round
+  unsigned cnt_ret;  // that count's value before the increment
+  int fin_head;      // head whose words this wave staged last round
+  float run_m, run_l;  // running row max (raw q.k) and sum of 2^(s - max) of this wave's tiles of the current head
+  uint2 pre[2];      // normalisers for the votes of the rounds of each parity
+  float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
+  int vhead, vtile;  // the tile whose votes are next (round r - kWvBanks in round r)
+  int merge_head;    // head this wave merges for its workgroup once all its waves have stored their pairs
+  float merge_R;     // that head's reference score of row lane & 31
+  bool gave_up;      // a bounded wait has run out: no further waits (the results are invalid)
+};
+
+// The next round's tile: W tiles on (W <= tiles per head, so at most one head boundary).
+__device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
+  p.t += c.W;
+  if (p.t >= c.nt) {
+    p.t -= c.nt;
+    ++p.head;
+    if (++p.h == c.H) {
+      p.h = 0;
+      ++p.b;
+    }
+  }
+  return p;
+}
+
+// Direct-to-LDS loads of one 32-row K tile into `slot` (XOR-swizzled rows:
+// 16-byte piece p of row R at slot p ^ (R & (kP-1))).
+template <int D>
+__device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsigned char* slot, int lane) {
+  using Ly = WvLayout<D>;
+  const uint16_t* kb = c.k + p.b * c.ksb + p.h * c.ksh;
+  const int key0 = p.t * kTile;
+  if (key0 + kTile <= c.L) {
+    // instruction i covers rows i*kRowsPerInst + lane/kP: a uniform row base plus
+    // the per-lane 32-bit offset (lane/kP) * row_bytes + 16 * piece
+    const char* rows = reinterpret_cast<const char*>(kb + static_cast<int64_t>(key0) * c.kst);
+    const int64_t rb = c.kst * 2;
+    const unsigned lrow = static_cast<unsigned>(lane / Ly::kP) * static_cast<unsigned>(rb);
+    const unsigned x16 = static_cast<unsigned>((lane % Ly::kP) ^ (lane / Ly::kP)) << 4;
+#pragma unroll
+    for (int i = 0; i < Ly::kInst; ++i) {
+      const unsigned b16 = static_cast<unsigned>((i * Ly::kRowsPerInst) & (Ly::kP - 1)) << 4;
+      __builtin_amdgcn_global_load_lds(rows + static_cast<int64_t>(i * Ly::kRowsPerInst) * rb + (lrow + (x16 ^ b16)),
+                                       (lds_void*)(slot + i * 1024), 16, 0, 0);
+    }
+  } else {  // the head's last, ragged tile or a padding tile: rows clamped to the data
+#pragma unroll
+    for (int i = 0; i < Ly::kInst; ++i) {
+      const int row = i * Ly::kRowsPerInst + lane / Ly::kP;
+      const int piece = (lane % Ly::kP) ^ (row & (Ly::kP - 1));
+      const int key = min(key0 + row, c.L - 1);
+      __builtin_amdgcn_global_load_lds(kb + static_cast<int64_t>(key) * c.kst + piece * 8,
+                                       (lds_void*)(slot + i * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// The lane's Q fragments (window row lane & 31, rows past the window repeat
+// its last row; half lane >> 5 of the contraction) for the tile at p.
+template <int D>
+__device__ __forceinline__ void wv_load_q(const WvCtx& c, const WvPos& p, bf16x8_t (&qf)[D / 16], int lane) {
+  const char* base = reinterpret_cast<const char*>(c.q + p.b * c.qsb + p.h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst);
+  const unsigned off = static_cast<unsigned>(min(lane & 31, c.w - 1)) * static_cast<unsigned>(c.qst * 2) +
+                       static_cast<unsigned>((lane >> 5) * D);
+  load_half_row<D>(reinterpret_cast<const uint16_t*>(base + off), qf);
+}
+
+// Head h's normaliser of row lane & 31 from its staged words (lanes of half
+// 0 take words 0..11, half 1 words 12..23). Bits 48..63 of a word count the
+// contributions that landed in it; the value parts (words 0..19) are below
+// 2^48, exact in a double, and so is each scaled term; both halves add the
+// two partial sums in the same order, so the value is the same in every lane
+// and every run. `count` is the row's number of contributions and `ovf`
+// whether one of them overflowed the fixed-point range.
+__device__ __forceinline__ float wv_words_to_c(const WvFin& f, int lane, unsigned& count, bool& ovf) {
+  constexpr int kHalf = kWvRowWords / 2;
+  const int row = lane & 31, half = lane >> 5;
+  const uint2* wr = reinterpret_cast<const uint2*>(f.words) + row * kWvRowWords + half * kHalf;
+  const int e0 = 16 * half * kHalf + kCoopDigitBase;
+  double t = 0.0;
+  unsigned n = 0;
+  bool o = false;
+#pragma unroll
+  for (int k = 0; k < kHalf; ++k) {
+    const uint2 x = wr[k];
+    n += x.y >> 16;
+    const int word = half * kHalf + k;
+    if (word == kWvOvfWord) o = (x.y >> 16) != 0u;
+    if (word < kWvOvfWord) {
+      const double d = __builtin_amdgcn_ldexp(static_cast<double>(x.y & 0xffffu), 32) + static_cast<double>(x.x);
+      t += __builtin_amdgcn_ldexp(d, e0 + 16 * k);
+    }
+  }
+  t += __shfl_xor(t, 32);
+  count = n + __shfl_xor(n, 32);
+  ovf = o;
+  float cv = f.ref[row];
+  if (t > 0.0)  // t = mant * 2^E, mant in [0.5, 1)
+    cv += static_cast<float>(__builtin_amdgcn_frexp_exp(t)) +
+          __builtin_amdgcn_logf(static_cast<float>(__builtin_amdgcn_frexp_mant(t)));
+  return cv;
+}
+
+// Exact normaliser of a flagged head: merge of the workgroups' partials in
+// workgroup order (half 0 takes the first half of the grid, half 1 the rest).
+__device__ __forceinline__ float wv_exact_c(const WvCtx& c, int bh, int lane) {
+  float m = kNegBig, l = 0.f;
+  const float2* pb = c.part + static_cast<int64_t>(bh) * c.G * 32 + (lane & 31);
+  const int half = lane >> 5;
+  const bool live = (lane & 31) < c.w;
+  const int g0 = half ? c.G / 2 : 0, g1 = half ? c.G : c.G / 2;
+  for (int gg = g0; gg < g1; gg += 4) {
+    uint2 pp[4];
+    // a partial's l is never 0 once stored (it counts the row's largest
+    // term), and the buffer is cleared beforehand: wait (bounded) until the
+    // workgroups' stores have landed
+    unsigned polls = 0;
+    bool missing;
+    do {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pp[i] = gg + i < g1 ? ld_agent_u2(reinterpret_cast<const uint2*>(&pb[(gg + i) * 32]))
+                            : make_uint2(__float_as_uint(kNegBig), 1u);
+      __builtin_amdgcn_s_waitcnt(0);
+      missing = __ballot(live && (pp[0].y == 0u || pp[1].y == 0u || pp[2].y == 0u || pp[3].y == 0u)) != 0ull;
+    } while (missing && ++polls < kWvSpin);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse2_merge(m, l, __uint_as_float(pp[i].x), __uint_as_float(pp[i].y));
+  }
+  lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
+  return m + __builtin_amdgcn_logf(l);
+}
+
+// s_waitcnt vmcnt(0), as the builtin (so that the compiler's own wait
+// placement knows every vector-memory operation issued so far is complete:
+// later uses of last round's loads need no wait that would also hold for
+// this round's tile) and as a compiler barrier (the tile's LDS reads stay
+// after it).
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS copy of head h's accumulator words and reference scores into
+// finisher buffer h % kWvFinBufs (which must be free or already h's).
+__device__ __forceinline__ void wv_stage(const WvCtx& c, int h, int lane) {
+  const int b = h & (kWvFinBufs - 1);
+  WvFin& f = c.sh->fin[b];
+  asm volatile("" ::: "memory");
+  if (c.sh->fin_owner[b] != h) {
+    // another head of this workgroup still holds the buffer (only if its
+    // finisher had to retry for rounds); bounded wait
+    for (unsigned polls = 0; c.sh->fin_owner[b] >= 0 && polls < kWvSpin; ++polls) {
+      __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");
+    }
+    if (lane == 0) c.sh->fin_owner[b] = h;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  const unsigned long long* a = c.acc + static_cast<int64_t>(h) * kCoopHeadWords;
+  constexpr int kHalf = kWvRowWords / 2;  // 16-byte pieces per row
+#pragma unroll
+  for (int i = 0; i < 32 * kHalf / 64; ++i) {
+    const int piece = i * 64 + lane, prow = piece / kHalf, pj = piece - prow * kHalf;
+    __builtin_amdgcn_global_load_lds(a + prow * kCoopRowWords + pj * 2, (lds_void*)(f.words + i * 128), 16, 0,
+                                     16 /* sc1 */);
+  }
+  if (lane < 8) __builtin_amdgcn_global_load_lds(c.ref + h * 32 + lane * 4, (lds_void*)f.ref, 16, 0, 0);
+}
+
+// The finisher's step for its staged head (the words landed at this round's
+// start): if every window row has all G contributions, convert and publish
+// the normalisers (from the exact merge of the workgroups' partials if one
+// contribution overflowed); otherwise stage the words again for next round.
+__device__ __forceinline__ void wv_finish(const WvCtx& c, WvPipe& p, int lane) {
+  const int h = p.fin_head, ln = opaque(lane), row = ln & 31;
+  const WvFin& f = c.sh->fin[h & (kWvFinBufs - 1)];
+  unsigned count;
+  bool ovf;
+  float cv = wv_words_to_c(f, ln, count, ovf);
+  if (__ballot(row < c.w && count != static_cast<unsigned>(c.G)) != 0ull) {
+    wv_stage(c, h, ln);  // a contribution is still in flight
+    return;
+  }
+  if (__ballot(ovf) != 0ull) cv = wv_exact_c(c, h, ln);
+  if (ln < 32 && row < c.w) st_agent_u2(&c.stat[h * 32 + row], make_uint2(__float_as_uint(cv), 1u));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer read before it is released
+  if (ln == 0) c.sh->fin_owner[h & (kWvFinBufs - 1)] = -1;
+  p.fin_head = -1;
+}
+
+// The next round's prefetches: the normalisers for its votes (head
+// pre_head) and the reference score of its tile (head ref_head).
+template <int PAR>
+__device__ __forceinline__ void wv_prefetch(const WvCtx& c, WvPipe& p, int pre_head, int ref_head, int lane) {
+  const int row = lane & 31;
+  p.pre[PAR ^ 1] = ld_agent_u2(&c.stat[pre_head * 32 + row]);
+  p.rref[PAR ^ 1] = c.ref[ref_head * 32 + row];
+}
+
+__device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane);
+
+// Votes of the tile (head hv, tile tv) whose raw dot products q.k are in s, with the
+// normalisers `pre` prefetched a round ago (waited for, bounded, if the head
+// is not yet published).
+__device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, const f32x16_t& s, int hv, int tv,
+                                         int lane) {
+  const int row = lane & 31, half = lane >> 5;
+  if (!p.gave_up && __ballot(row < c.w && pre.y != 1u) != 0ull) {
+    unsigned polls = 0;
+    bool late;
+    do {
+      __builtin_amdgcn_s_sleep(2);
+      pre = ld_agent_u2(&c.stat[hv * 32 + row]);
+      wait_vm_all();  // every exit from here has its load back
+      wv_service(c, p, lane);  // what this wave owes others may be what it waits for
+      late = __ballot(row < c.w && pre.y != 1u) != 0ull;
+    } while (late && ++polls < kWvSpin);
+    if (late) {  // a protocol failure: record it and never wait again
+      p.gave_up = true;
+      if (lane == 0) __hip_atomic_store(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  float* cs = c.sh->s_c[c.wave];
+  if (half == 0) cs[row] = __uint_as_float(pre.x);
+  float v = 0.f;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {  // registers 4a..4a+3 hold rows 8a + 4 half + 0..3
+    const f32x4_t cc = *reinterpret_cast<const f32x4_t*>(cs + 8 * a + 4 * half);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * a + e;
+      v += (c.w == kMaxWindow || acc_row(i, half) < c.w) ? fast_exp2(fmaf(s[i], c.scale_log2, -cc[e])) : 0.f;
+    }
+  }
+  v += __shfl_xor(v, 32);
+  const int j = tv * kTile + row;
+  if (half == 0 && j < c.t0) c.vote[static_cast<int64_t>(hv) * c.t0 + j] = v;
+}
+
+// LDS add (by the lanes of the calling branch), issued as inline assembly:
+// as a compiler atomic it would make the compiler wait for the direct loads
+// in flight into the tile ring as well.
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
+  asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
+// The merge of head h for this workgroup, by its designated wave, once all
+// kWvWaves waves have stored their row pairs in slot h & 1: the pairs merged
+// in wave order, the slot reopened for head h + 2, the merged pairs added to
+// the head's accumulators and stored as the workgroup's partial, and the
+// head's count raised. The workgroup whose increment is the last stages and
+// converts the words (which carry their own contribution counts, so the
+// increment need not wait for the contributions to land). Skipped while the
+// previous count's return has not been looked at.
+__device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane) {
+  if (p.cnt_head >= 0) return;
+  WvShared* sh = c.sh;
+  const int h = p.merge_head, sl = h & 1, ln = opaque(lane), col = ln & 31;
+  asm volatile("" ::: "memory");
+  if (__builtin_amdgcn_readfirstlane(sh->mcnt[sl]) != kWvWaves) return;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float2 a = sh->mslot[sl][0][col];
+#pragma unroll
+  for (int wv = 1; wv < kWvWaves; ++wv) {
+    const float2 b = sh->mslot[sl][wv][col];
+    lse2_merge(a.x, a.y, b.x, b.y);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // pairs read before the slot reopens
+  if (ln == 0) {
+    sh->mcnt[sl] = 0;
+    sh->mtag[sl] = h + 2;
+  }
+  asm volatile("" ::: "memory");
+  if (ln < 32 && col < c.w) {
+    st_agent_u2(reinterpret_cast<uint2*>(&c.part[(static_cast<int64_t>(h) * c.G + c.g) * 32 + col]),
+                make_uint2(__float_as_uint(a.x), __float_as_uint(a.y)));
+    fixed_point_add<true>(c.acc + static_cast<int64_t>(h) * kCoopHeadWords, nullptr, col, a.x, a.y, p.merge_R);
+  }
+  // (an address the compiler cannot prove uniform: its atomic optimizer would
+  // otherwise broadcast the return at once, waiting for the next tile too)
+  unsigned ret = 0;
+  if (ln == 0) ret = atomicAdd(&c.cnt[h * kCoopCtrWords] + opaque(0), 1u);
+  p.cnt_ret = ret;
+  p.cnt_head = h;
+  p.merge_head = -1;
+}
+
+// Work this wave owes other waves, done after a full wait (every memory
+// operation it issued before is complete): publish a staged head, stage the
+// words of a head whose count this wave's increment completed, merge its
+// workgroup's pairs of a head it is designated for. Every bounded wait of the
+// kernel calls it, so that no wave waits for something it owes itself.
+__device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane) {
+  if (p.fin_head >= 0) wv_finish(c, p, lane);
+  if (p.cnt_head >= 0) {
+    if (__builtin_amdgcn_readfirstlane(p.cnt_ret) == static_cast<unsigned>(c.G - 1)) {
+      // a head still being retried by this wave is finished first (rare)
+      for (unsigned t = 0; p.fin_head >= 0 && t < kWvSpin; ++t) {
+        wait_vm_all();
+        wv_finish(c, p, lane);
+      }
+      wv_stage(c, p.cnt_head, opaque(lane));
+      p.fin_head = p.cnt_head;
+    }
+    p.cnt_head = -1;
+  }
+  if (p.merge_head >= 0) wv_try_merge(c, p, lane);
+}
+
+// This wave has scored its last tile of head h: its row pairs go to slot
+// h & 1 of the workgroup (once the slot is open for h), and the designated
+// wave (h + g) % kWvWaves, which spreads the merges evenly, merges them when
+// all waves have stored theirs (now if it is the last, else at a later
+// service).
+__device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, float R, int lane) {
+  float m = p.run_m * c.scale_log2, l = p.run_l;  // the running max is kept in raw q.k units
+  lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));  // lanes col and col+32 hold the same row
+  p.run_m = kNegBig;
+  p.run_l = 0.f;
+  WvShared* sh = c.sh;
+  const int sl = h & 1, ln = opaque(lane), col = ln & 31;
+  // plain LDS reads behind compiler barriers: an atomic load here would make
+  // the compiler wait for the direct loads in flight into the tile ring
+  asm volatile("" ::: "memory");
+  if (!p.gave_up && sh->mtag[sl] != h) {
+    // the slot still holds head h - 2 (its merge is pending)
+    unsigned polls = 0;
+    bool late;
+    do {
+      __builtin_amdgcn_s_sleep(1);
+      wait_vm_all();
+      wv_service(c, p, ln);
+      asm volatile("" ::: "memory");
+      late = sh->mtag[sl] != h;
+    } while (late && ++polls < kWvSpin);
+    if (late) {
+      p.gave_up = true;
+      if (ln == 0) __hip_atomic_store(c.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (ln < 32) sh->mslot[sl][c.wave][col] = make_float2(m, l);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the pair is in LDS before the count says so
+  if (ln == 0) lds_add(&sh->mcnt[sl], 1);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (c.wave == ((h + c.g) & (kWvWaves - 1))) {
+    p.merge_head = h;
+    p.merge_R = R;
+    wv_try_merge(c, p, ln);
+  }
+}
+
+template <int D, int BANK>
+__device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, f32x16_t (&sc)[kWvBanks],
+                                         bf16x8_t (&qf)[D / 16], unsigned char* ring0, unsigned char* ring1,
+                                         int r) {
+  using Ly = WvLayout<D>;
+  constexpr int KS = D / 16;
+  constexpr int PAR = BANK & 1;  // ring slot and prefetch parity of round r (kWvBanks is even)
+  const bool do_a = r < c.rounds;
+  const bool do_b = r >= kWvBanks && r - kWvBanks < c.rounds;
+  // this round's tile, Q and reference score, and everything issued last round
+  wait_vm_all();
+  const int lane = opaque(lane_id());
+  wv_service(c, p, lane);  // before the K loads: its reads of staged words then wait for nothing
+  const WvPos nxt = wv_next(c, pos);
+  const bool more = r + 1 < c.rounds;
+  if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
+  // the tile whose votes come next round: tile r - 7 (tile 0 before round 8)
+  WvPos vn{p.vhead, 0, 0, p.vtile};
+  if (r >= kWvBanks) vn = wv_next(c, vn);
+  wv_prefetch<PAR>(c, p, min(vn.head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
+  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
+  if (r >= kWvBanks) {
+    p.vhead = vn.head;
+    p.vtile = vn.t;
+  }
+  if (do_a) {
+    const int col = lane & 31, half = lane >> 5;
+    // fragment k-step s of row col: piece half*kP/2 + s at slot piece ^ (col & (kP-1)),
+    // i.e. address A ^ (s << 4) (the tile's rows start at multiples of 256 bytes)
+    const unsigned char* tile = PAR ? ring1 : ring0;
+    const unsigned A = static_cast<unsigned>(col * Ly::kRowB) +
+                       (static_cast<unsigned>((half * (Ly::kP / 2)) ^ (col & (Ly::kP - 1))) << 4);
+    f32x16_t acc = {}, bt = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8_t kf =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(tile + (A ^ static_cast<unsigned>(s << 4))));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf, acc, 0, 0, 0);
+      bt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], bt, 0, 0, 0);
+      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight
+    }
+    // Q of the next tile's head into the registers just read (a head's tiles share Q)
+    if (more && nxt.head != pos.head) wv_load_q<D>(c, nxt, qf, lane);
+    sc[BANK] = acc;  // raw q.k; the votes apply the scale in their exponent
+    // the row statistics in raw units: max over the tile's keys the row sees,
+    // then sum 2^(scale * (s - max)) with the scale folded into one fma
+    const int key0 = pos.t * kTile;
+    float m = kNegBig;
+    if (key0 + kTile <= c.t0) {  // every query sees every key of the tile
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, bt[i]);
+    } else {
+      const int ln = opaque(lane), cl = ln & 31, hf = ln >> 5;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = key0 + acc_row(i, hf);
+        bt[i] = (j < c.L && j <= c.t0 + cl) ? bt[i] : kNegBig;
+        m = fmaxf(m, bt[i]);
+      }
+    }
+    const float mn = fmaxf(p.run_m, m), mns = -mn * c.scale_log2;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) l += fast_exp2(fmaf(bt[i], c.scale_log2, mns));
+    p.run_l = p.run_l * fast_exp2(fmaf(p.run_m, c.scale_log2, mns)) + l;
+    p.run_m = mn;
+    if (!more || nxt.head != pos.head) wv_head_end(c, p, pos.head, p.rref[PAR], lane);
+  }
+  pos = nxt;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int nt,
+    int total_tiles, int BH, float scale_log2, const float* __restrict__ ref, unsigned long long* __restrict__ acc,
+    unsigned* __restrict__ cnt, uint2* __restrict__ stat, float2* __restrict__ part, unsigned* __restrict__ status,
+    float* __restrict__ vote) {
+  using Ly = WvLayout<D>;
+  // the two tile slots of every wave's ring, as two arrays: the reads of one
+  // slot are then known not to alias the direct loads in flight into the other
+  __shared__ __attribute__((aligned(1024))) unsigned char ring_even[kWvWaves * Ly::kTileB];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring_odd[kWvWaves * Ly::kTileB];
+  __shared__ __attribute__((aligned(16))) WvShared sh;
+
+  WvCtx c;
+  c.q = q; c.qsb = qsb; c.qsh = qsh; c.qst = qst; c.qrow0 = qrow0;
+  c.k = k; c.ksb = ksb; c.ksh = ksh; c.kst = kst;
+  c.H = H; c.L = L; c.w = w; c.t0 = L - w; c.nt = nt; c.BH = BH;
+  c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x); c.W = c.G * kWvWaves;
+  c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
+  c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  c.scale_log2 = scale_log2;
+  c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.part = part; c.status = status; c.vote = vote;
+  c.sh = &sh;
+  unsigned char* ring0 = ring_even + c.wave * Ly::kTileB;
+  unsigned char* ring1 = ring_odd + c.wave * Ly::kTileB;
+  if (threadIdx.x == 0) {
+    sh.mcnt[0] = sh.mcnt[1] = 0;
+    sh.mtag[0] = 0;  // every workgroup has tiles in every head, starting with head 0
+    sh.mtag[1] = 1;
+  }
+  if (threadIdx.x < kWvFinBufs) sh.fin_owner[threadIdx.x] = -1;
+  WvPipe p;
+  p.cnt_head = p.fin_head = p.merge_head = -1;
+  p.merge_R = 0.f;
+  p.cnt_ret = 0;
+  p.run_m = kNegBig;
+  p.run_l = 0.f;
+  p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
+  p.rref[0] = p.rref[1] = 0.f;
+  p.gave_up = false;
+  WvPos pos{0, 0, 0, c.g * kWvWaves + c.wave};  // round 0: tile v of head 0 (v < W <= tiles per head)
+  p.vhead = 0;
+  p.vtile = pos.t;
+  bf16x8_t qf[D / 16];
+  if (c.rounds > 0) {
+    const int lane = lane_id();
+    wv_issue_k<D>(c, pos, ring0, lane);
+    wv_load_q<D>(c, pos, qf, lane);
+    p.rref[0] = ref[lane & 31];
+  }
+  __syncthreads();  // the slot counters are set
+  f32x16_t sc[kWvBanks];
+  static_assert(kWvBanks == 8, "the round loop below is unrolled over the register banks");
+  // the last tile's votes fall in round rounds - 1 + kWvBanks, and the last
+  // head's publication three rounds after its last tile
+  for (int r0 = 0; r0 < c.rounds + kWvBanks; r0 += kWvBanks) {
+    wv_round<D, 0>(c, p, pos, sc, qf, ring0, ring1, r0);
+    wv_round<D, 1>(c, p, pos, sc, qf, ring0, ring1, r0 + 1);
+    wv_round<D, 2>(c, p, pos, sc, qf, ring0, ring1, r0 + 2);
+    wv_round<D, 3>(c, p, pos, sc, qf, ring0, ring1, r0 + 3);
+    wv_round<D, 4>(c, p, pos, sc, qf, ring0, ring1, r0 + 4);
+    wv_round<D, 5>(c, p, pos, sc, qf, ring0, ring1, r0 + 5);
+    wv_round<D, 6>(c, p, pos, sc, qf, ring0, ring1, r0 + 6);
+    wv_round<D, 7>(c, p, pos, sc, qf, ring0, ring1, r0 + 7);
+  }
+  // work still owed after the last round: a pending merge, election or
+  // publication (bounded)
+  for (unsigned t = 0; (p.fin_head >= 0 || p.cnt_head >= 0 || p.merge_head >= 0) && t < kWvSpin; ++t) {
+    wait_vm_all();
+    __builtin_amdgcn_s_sleep(2);
+    wv_service(c, p, lane_id());
   }
 }
 
@@ -1371,7 +1988,7 @@ thread_local int g_last_schedule = 0;
 // single-pass workgroups per compute unit (index 0: D = 64, 1: D = 128).
 struct CoopCaps {
   bool queried = false, coop = false;
-  int cus = 0, per_cu[2] = {0, 0};
+  int cus = 0, per_cu[2] = {0, 0}, wv_per_cu[2] = {0, 0};
 };
 
 const CoopCaps& coop_caps() {
@@ -1386,15 +2003,19 @@ const CoopCaps& coop_caps() {
   CoopCaps& c = caps[dev];
   if (!c.queried) {
     c.queried = true;
-    int coop = 0, cus = 0, n64 = 0, n128 = 0;
+    int coop = 0, cus = 0, n64 = 0, n128 = 0, w64 = 0, w128 = 0;
     if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&n64, snap_coop_bf16<64>, kCoopThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n128, snap_coop_bf16<128>, kCoopThreads, 0) == hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n128, snap_coop_bf16<128>, kCoopThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w64, snap_wave_bf16<64>, kWvThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w128, snap_wave_bf16<128>, kWvThreads, 0) == hipSuccess) {
       c.coop = coop != 0;
       c.cus = cus;
       c.per_cu[0] = n64;
       c.per_cu[1] = n128;
+      c.wv_per_cu[0] = w64;
+      c.wv_per_cu[1] = w128;
     }
     (void)hipGetLastError();
   }
@@ -1422,11 +2043,40 @@ int coop_grid(const SnapLayout& lay, int D) {
   return G;
 }
 
+// Tiles per head of the independent-wave single pass: 32-key tiles, padded to
+// a multiple of kWvWaves.
+int64_t wave_tiles(int L) { return ((L + kTile - 1) / kTile + kWvWaves - 1) / kWvWaves * kWvWaves; }
+
+// Grid of the independent-wave single pass, 0 when it cannot run. Every
+// workgroup must have tiles in every head (a head's padded tile count is at
+// least the worker count W), the per-workgroup partials must fit the partial
+// buffer (G <= units per head), and a head may span at most kWvMaxSpan rounds
+// beyond its first: a vote waits (in round r) for the normaliser of a tile
+// of round r - kWvBanks, which its finisher publishes three rounds after the
+// head's last tile, so every such wait then depends only on heads that
+// started earlier and all of them end.
+int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
+  const CoopCaps& c = coop_caps();
+  if (!c.coop || c.cus <= 0) return 0;
+  const int per_cu = c.wv_per_cu[D == 128 ? 1 : 0];
+  if (per_cu <= 0) return 0;
+  const int64_t G = static_cast<int64_t>(per_cu) * c.cus, W = G * kWvWaves, nt = wave_tiles(L);
+  if (nt < W || G > lay.nunit || lay.BH * nt > INT32_MAX) return 0;
+  if (kst * 2 * 8 >= (int64_t(1) << 32) || qst * 2 * 32 >= (int64_t(1) << 32)) return 0;  // 32-bit lane offsets
+  for (int64_t bh = 0; bh < lay.BH; ++bh) {
+    const int64_t r0 = bh * nt / W, r1 = ((bh + 1) * nt - 1) / W;
+    if (r1 - r0 > kWvMaxSpan) return 0;
+  }
+  return static_cast<int>(G);
+}
+
+thread_local const char* g_last_kernel = "";
+
 // Single pass: the per-head preparation (reference scores, cleared state),
 // the cooperative score pass (raw votes to `vote`), then pooling + histogram.
 // Phase marks 1, 2, 3 and 4.
 template <int D>
-kvc_status launch_single_pass(const SnapLayout& lay, int G, const uint16_t* q, kvc_strides qs, int qrow0,
+kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint16_t* q, kvc_strides qs, int qrow0,
                               const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, float scale_log2,
                               char* ws, float* vote, float* pooled, hipStream_t stream) {
   float* ref = reinterpret_cast<float*>(ws + lay.cref);
@@ -1437,16 +2087,32 @@ kvc_status launch_single_pass(const SnapLayout& lay, int G, const uint16_t* q, k
   unsigned* status = reinterpret_cast<unsigned*>(ws + lay.cstatus);
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
   unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
+  // the wave kernel's per-workgroup partials (G x 32 float2 per head) start cleared
+  const int part_pieces = Gw > 0 ? Gw * 32 / 2 : 0;
   snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
-      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist, ctr);
+      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist, ctr,
+      reinterpret_cast<u32x4_t*>(part), part_pieces);
   mark_phase(1, stream);
-  int nunit = lay.nunit, total_units = static_cast<int>(lay.BH * lay.nunit);
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
-  void* args[] = {&q,   &qsb,         &qsh,        &qst,  &qrow0, &k,   &ksb,  &ksh,    &kst,   &H,   &L, &w,
-                  &nunit, &total_units, &scale_log2, &cref, &acc,   &cnt, &stat, &part, &status, &vote};
-  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_coop_bf16<D>), dim3(G),
-                                                  dim3(kCoopThreads), args, 0, stream);
+  hipError_t e = hipErrorInvalidValue;
+  if (Gw > 0) {
+    int nt = static_cast<int>(wave_tiles(L)), total = static_cast<int>(lay.BH * nt), BH = static_cast<int>(lay.BH);
+    void* args[] = {&q,  &qsb,   &qsh, &qst, &qrow0,      &k,    &ksb, &ksh, &kst,  &H,    &L,      &w,
+                    &nt, &total, &BH,  &scale_log2, &cref, &acc, &cnt, &stat, &part, &status, &vote};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_wave_bf16<D>), dim3(Gw), dim3(kWvThreads),
+                                   args, 0, stream);
+    if (e == hipSuccess) g_last_kernel = "snap_wave_bf16";
+    else (void)hipGetLastError();
+  }
+  if (e != hipSuccess && Gc > 0) {
+    int nunit = lay.nunit, total_units = static_cast<int>(lay.BH * lay.nunit);
+    void* args[] = {&q,     &qsb,         &qsh,        &qst,  &qrow0, &k,   &ksb,  &ksh,  &kst,    &H,   &L, &w,
+                    &nunit, &total_units, &scale_log2, &cref, &acc,   &cnt, &stat, &part, &status, &vote};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_coop_bf16<D>), dim3(Gc), dim3(kCoopThreads),
+                                   args, 0, stream);
+    if (e == hipSuccess) g_last_kernel = "snap_coop_bf16";
+  }
   if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
   mark_phase(2, stream);
   mark_phase(3, stream);
@@ -1470,6 +2136,8 @@ extern "C" int kvc_snapkv_set_schedule(int schedule) {
 }
 
 extern "C" int kvc_snapkv_last_schedule(void) { return g_last_schedule; }
+
+extern "C" const char* kvc_snapkv_last_score_kernel(void) { return g_last_kernel; }
 
 extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
                                              int pool_kernel, kvc_dtype dt) {
@@ -1528,19 +2196,21 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   // AUTO takes the single pass where it can run (it reads K once and measures
   // faster on MI355X) and falls back to two passes if the device refuses the
   // cooperative launch
-  const int G = (dt == KVC_BF16 && g_schedule != KVC_SNAPKV_TWO_PASS) ? coop_grid(lay, D) : 0;
+  const bool try_single = dt == KVC_BF16 && g_schedule != KVC_SNAPKV_TWO_PASS;
+  const int Gw = try_single ? wave_grid(lay, D, L, kvs.t, qs.t) : 0;
+  const int Gc = try_single ? coop_grid(lay, D) : 0;
   int schedule = KVC_SNAPKV_TWO_PASS;
   mark_phase(0, stream);
-  if (G > 0) {
+  if (Gw > 0 || Gc > 0) {
     // raw votes go to the caller's buffer or to the candidate area, which is
     // free until classification
     float* vraw = vote ? vote : reinterpret_cast<float*>(ws + lay.cand);
     const uint16_t* qb = static_cast<const uint16_t*>(q);
     const uint16_t* kb = static_cast<const uint16_t*>(k);
-    kvc_status st = D == 128 ? launch_single_pass<128>(lay, G, qb, qs, qrow0, kb, kvs, H, L, window, pool_kernel / 2,
-                                                       scale_log2, ws, vraw, pooled, stream)
-                             : launch_single_pass<64>(lay, G, qb, qs, qrow0, kb, kvs, H, L, window, pool_kernel / 2,
-                                                      scale_log2, ws, vraw, pooled, stream);
+    kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window,
+                                                       pool_kernel / 2, scale_log2, ws, vraw, pooled, stream)
+                             : launch_single_pass<64>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window,
+                                                      pool_kernel / 2, scale_log2, ws, vraw, pooled, stream);
     if (st == KVC_OK) {
       schedule = KVC_SNAPKV_SINGLE_PASS;
     } else if (g_schedule == KVC_SNAPKV_SINGLE_PASS) {
@@ -1552,6 +2222,7 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   }
   if (schedule == KVC_SNAPKV_TWO_PASS) {
     mark_phase(1, stream);  // counters and histograms are cleared by the statistics pass
+    g_last_kernel = dt == KVC_BF16 ? "snap_stats_bf16+snap_votes_bf16" : "snap_stats_f32+snap_votes_f32";
     if (dt == KVC_BF16)
       launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0,
                                     static_cast<const uint16_t*>(k), kvs, H, L, D, window, pool_kernel / 2,

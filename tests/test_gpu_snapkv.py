@@ -28,7 +28,7 @@ def _run(q, k, v, wl_window, budget, pool, dtype, schedule=kvc.SNAPKV_AUTO, want
         res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=True, want_vote=want_vote, **kw)
     torch.cuda.synchronize()
     ran = kvc.snapkv_last_schedule()
-    print(f"[snapkv] schedule asked {schedule} ran {ran}", flush=True)
+    print(f"[snapkv] schedule asked {schedule} ran {ran} ({kvc.snapkv_last_score_kernel()})", flush=True)
     if dtype == "fp32" or schedule == kvc.SNAPKV_TWO_PASS:
         assert ran == kvc.SNAPKV_TWO_PASS
     return res
@@ -219,6 +219,41 @@ def test_schedules_agree():
         par.assert_close_votes(vb[0, h], va[0, h].astype(np.float64), f"vote[0,{h}] single vs two-pass")
     same = (a.idx == b.idx).float().mean().item()
     assert same > 0.99, same
+
+
+@pytest.mark.parametrize("L,kernel", [(9000, "snap_coop_bf16"), (70000, "snap_wave_bf16")])
+def test_single_pass_logit_overflow(L, kernel):
+    """A key scoring 2^180 above window row 0's reference flags the head: its normalisers
+    come from the exact merge of per-unit / per-workgroup partials instead of the
+    fixed-point accumulators, and the votes still match the oracle."""
+    B, H, D, w, C, p = 1, 2, 128, 32, 400, 7
+    rng = np.random.default_rng(5)
+    q32 = rng.standard_normal((B, H, w, D), dtype=np.float32)
+    k32 = rng.standard_normal((B, H, L, D), dtype=np.float32)
+    j = 5000
+    for h in range(H):
+        u = q32[0, h, 0]
+        k32[0, h, j] = 130.0 * u / np.linalg.norm(u)  # row 0: score ~ 1.44 * 130 in log2 units
+    qn, kn = syn.f32_to_bf16_bits(q32), syn.f32_to_bf16_bits(k32)
+    vn = syn.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32))
+    q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
+    print(f"[snapkv] overflow case L{L}", flush=True)
+    res = _run(q, k, v, w, C, p, "bf16", kvc.SNAPKV_SINGLE_PASS)
+    assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
+    assert kvc.snapkv_last_score_kernel() == kernel
+    _compare(qn, kn, vn, res, w, C, p, "bf16")
+
+
+def test_single_pass_kernel_choice():
+    """Long prompts take the independent-wave kernel, short ones the lockstep one."""
+    for L, kernel in ((3000, "snap_coop_bf16"), (131072, "snap_wave_bf16")):
+        B, H, D = 1, 2, 128
+        q = torch.zeros((B, H, 32, D), dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device="cuda")
+        _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_SINGLE_PASS)
+        assert kvc.snapkv_last_score_kernel() == kernel, (L, kvc.snapkv_last_score_kernel())
+    _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_TWO_PASS)
+    assert kvc.snapkv_last_score_kernel() == "snap_stats_bf16+snap_votes_bf16"
 
 
 def test_schedule_setting_rejects_unknown():
