@@ -530,7 +530,7 @@ __device__ __forceinline__ bf16x8_t lds_frag(const unsigned char* tile, int R, i
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Reference score of every window row (largest score against the window's
-// own keys it sees), and the per-head state of the single pass cleared: row
+// own keys it sees; rows past the window repeat the last row's), and the per-head state of the single pass cleared: row
 // accumulators, count and overflow flag, published normalisers, histogram
 // and selection counters. One workgroup per head.
 template <int D>
@@ -538,11 +538,8 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
     float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
-    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr, u32x4_t* __restrict__ wg_part,
-    int part_pieces) {
+    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr) {
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
-  for (int i = threadIdx.x; i < part_pieces; i += kThreads)  // 16-byte pieces of this head's partials
-    wg_part[static_cast<int64_t>(bh) * part_pieces + i] = u32x4_t{0u, 0u, 0u, 0u};
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
@@ -591,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
       if (j0 + jb <= i && j0 + jb < w) m = fmaxf(m, d * scale_log2);
     }
   }
-  if (part == 0) ref[bh * 32 + i] = i < w ? m : 0.f;
+  if (part == 0) ref[bh * 32 + i] = m;  // rows past the window repeat row w - 1 (same query, same keys)
 }
 
 // Everything one workgroup of the single pass needs across rounds.
@@ -728,25 +725,11 @@ __device__ __forceinline__ float coop_exact_c(const CoopCtx& c, int bh, int row)
 // at bit pos = ey - 23 + n - kCoopDigitBase, i.e. mant << (pos % 16) in word
 // pos / 16. Terms below word 0 are dropped (they are at least 2^-100 times
 // the window key's own term); a gap above kCoopOvfGap flags the head.
-// With kCounted (the independent-wave kernel) every contribution also adds 1
-// to bits 48..63 of the word it lands in (a value part stays below 2^48: at
-// most 2^9 terms below 2^39 each); a dropped term adds only that count to
-// word 0 and an overflowing one to word kWvOvfWord, so that a row's words
-// alone show how many contributions have landed (and whether one overflowed).
-constexpr int kWvOvfWord = 20;
-constexpr unsigned long long kWvCountOne = 1ull << 48;
-
-template <bool kCounted = false>
 __device__ __forceinline__ void fixed_point_add(unsigned long long* acc_head, unsigned* ovf_flag, int row, float m,
                                                 float l, float R) {
   const float gap = m - R;
-  unsigned long long* arow = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_head) +
-                                                                   static_cast<unsigned>(row * kCoopRowWords) * 8u);
   if (gap > kCoopOvfGap) {
-    if (kCounted)
-      atomicAdd(arow + kWvOvfWord, kWvCountOne);
-    else
-      atomicOr(ovf_flag, 1u);
+    atomicOr(ovf_flag, 1u);
   } else if (gap > static_cast<float>(kCoopDigitBase + 60)) {
     const float n = floorf(gap);
     const float y = l * fast_exp2(gap - n);
@@ -758,10 +741,7 @@ __device__ __forceinline__ void fixed_point_add(unsigned long long* acc_head, un
       pos = 0;
     }
     const unsigned off = static_cast<unsigned>(row * kCoopRowWords + (pos >> 4)) * 8u;
-    atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_head) + off),
-              (mant << (pos & 15)) + (kCounted ? kWvCountOne : 0ull));
-  } else if (kCounted) {
-    atomicAdd(arow, kWvCountOne);
+    atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_head) + off), mant << (pos & 15));
   }
 }
 
@@ -1006,33 +986,47 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
 
 // --------------------------- single-pass scores, independent waves (bf16)
 //
-// The computation of snap_coop_bf16 without the workgroup's lockstep. Every
-// wave is a worker of its own: worker v = g * kWvWaves + wave takes the
+// The single-pass computation with the workgroup's lockstep removed and the
+// softmax reorganised around a fixed per-row offset. R_i (the reference score
+// of window row i, computed beforehand) is one of row i's own scores, so with
+// e_ij = 2^(s_ij - R_i) and L_i = sum_j e_ij >= 1 the normaliser is
+// c_i = R_i + log2 L_i and the vote of key j is
+//     vote_j = sum_i 2^(s_ij - c_i) = sum_i e_ij * w_i,   w_i = 1 / L_i <= 1,
+// exactly (in real arithmetic). Scores are therefore exponentiated once; the
+// row sums need no running maximum, and the votes no exponential.
+//
+// Every wave is a worker of its own: worker v = g * kWvWaves + wave takes the
 // 32-key tiles u = r * W + v in rounds r = 0, 1, ... (W = G * kWvWaves
 // workers; tiles numbered head by head, a head's tile count padded to a
 // multiple of kWvWaves, so that the tiles of one workgroup in one round share
 // a head). A wave keeps its next tile in flight while it works on the
-// current one: K by direct-to-LDS loads into a private two-slot ring, Q by
-// plain loads into the registers that the current tile's MFMAs have just
-// read. Round r's scores wait in register bank r % kWvBanks; just before
-// round r's scores replace them, the bank's previous contents (the tile of
-// round r - kWvBanks) are turned into votes.
-// The per-row (max, sum) pairs of a wave's tiles of one head are merged in
-// LDS by whichever wave of the workgroup finishes the head last (an LDS
-// counter elects it; there is no barrier), and that wave adds the merged pair
-// to the head's fixed-point row accumulators exactly as snap_coop_bf16 does.
-// The workgroup whose count increment completes the head converts the
-// accumulators into the normalisers c_i and publishes them. A wave's only
-// full wait is the one for its next tile at the start of a round, which also
-// covers everything else it issued in the previous round (Q, contributions,
-// the count, staged words, prefetched normalisers), so each cross-worker step
-// takes one round and none of them holds up the K stream.
+// current one: K by direct-to-LDS loads into a private two-slot ring, Q (when
+// the head changes) by plain loads into the registers the MFMAs have just
+// read. One MFMA orientation serves both uses: lane = key, registers = rows.
+// Round r's e_ij wait in register bank r % kWvBanks and each lane adds them
+// into per-row partial sums; just before round r's values replace them, the
+// bank's previous contents (the tile of round r - kWvBanks) become votes.
+// At the end of a head a wave reduces its partial sums across lanes, stores
+// them in an LDS slot of its workgroup, and the workgroup's designated wave
+// for that head ((h + g) % kWvWaves, spreading the work evenly) adds the
+// waves' sums in wave order and contributes them to the head's fixed-point
+// row accumulators (order-independent integer adds that also count the
+// contributions). The workgroup whose count increment completes the head
+// stages the accumulators into LDS, converts them into w_i once every
+// contribution has landed, and publishes them. A wave's only full wait is
+// the one for its next tile at the start of a round; everything else it
+// issued in the previous round is complete there too, so each cross-worker
+// step takes a round and none of them holds up the K stream.
 //
-// Registers: the eight banks (128), Q (32) and the two MFMA accumulators
-// fill most of the 256 a wave has at two waves per SIMD, so every per-lane
-// value a round needs is derived inside the round from one opaque lane index
-// instead of being kept live across the loop (a spilled value's reload would
-// have to wait behind the next tile's loads).
+// e_ij is finite unless a score exceeds its row's reference by 2^127; such a
+// head is flagged and its votes are recomputed afterwards by
+// snap_fixup_bf16 (the usual path's votes of that head are discarded).
+//
+// Registers: the eight banks (128), Q (32), the MFMA accumulator and the row
+// sums fill most of the 256 a wave has at two waves per SIMD, so every
+// per-lane value a round needs is derived inside the round from one opaque
+// lane index instead of being kept live across the loop (a spilled value's
+// reload would have to wait behind the next tile's loads).
 constexpr int kWvWaves = 8;
 constexpr int kWvThreads = kWvWaves * kWave;
 constexpr int kWvBanks = 8;
@@ -1040,6 +1034,8 @@ constexpr int kWvRowWords = 24;  // accumulator words per row a finisher stages 
 constexpr int kWvFinBufs = 4;    // finisher staging buffers, by head mod 4
 constexpr int kWvMaxSpan = 5;    // a head spans at most this many rounds after its first
 constexpr unsigned kWvSpin = 1u << 18;  // polls before a wait gives up (far beyond any legitimate wait)
+constexpr int kWvOvfWord = 20;   // a non-finite row sum adds its count here (the head is then flagged)
+constexpr unsigned long long kWvCountOne = 1ull << 48;
 
 template <int D>
 struct WvLayout {
@@ -1050,20 +1046,18 @@ struct WvLayout {
   static constexpr int kRowsPerInst = 1024 / kRowB;
 };
 
-// A finisher's copy of one head's accumulator words (row-major, kWvRowWords
-// per row) and reference scores.
+// A finisher's copy of one head's accumulator words (row-major, kWvRowWords per row).
 struct WvFin {
   unsigned long long words[32 * kWvRowWords];
-  float ref[32];
 };
 
 struct WvShared {
-  float2 mslot[2][kWvWaves][32];  // the waves' row pairs of head h, in slot h & 1
-  float s_c[kWvWaves][32];        // each wave's normalisers for its votes
-  WvFin fin[kWvFinBufs];
-  int fin_owner[kWvFinBufs];      // head staged in a finisher buffer, -1 if free
-  int mcnt[2];                    // waves that have stored their pair in a slot
-  int mtag[2];                    // the head a slot is open for
+  float lslot[2][kWvWaves][32];  // the waves' row sums of head h, in slot h & 1
+  float s_w[kWvWaves][32];       // each wave's vote weights w_i for its votes
+  float s_r[kWvWaves][32];       // each wave's reference scores R_i for its tile
+  int fin_owner[kWvFinBufs];     // head staged in a finisher buffer, -1 if free
+  int mcnt[2];                   // waves that have stored their sums in a slot
+  int mtag[2];                   // the head a slot is open for
 };
 
 struct WvPos {
@@ -1082,23 +1076,21 @@ struct WvCtx {
   unsigned long long* acc;
   unsigned* cnt;
   uint2* stat;
-  float2* part;
   unsigned* status;
   float* vote;
   WvShared* sh;
+  WvFin* fin;  // the finisher buffers: an array of their own, so that LDS accesses to the
+               // workgroup's other shared state are known not to alias their direct loads
 };
 
 // A wave's state carried from round to round.
 struct WvPipe {
-  int cnt_head;      // head whose count this wave raised last round
+  int cnt_head;      // head whose count this wave raised (its return is looked at after a full wait)
   unsigned cnt_ret;  // that count's value before the increment
-  int fin_head;      // head whose words this wave staged last round
-  float run_m, run_l;  // running row max (raw q.k) and sum of 2^(s - max) of this wave's tiles of the current head
-  uint2 pre[2];      // normalisers for the votes of the rounds of each parity
+  int merge_head;    // head this wave merges for its workgroup once all its waves have stored their sums
+  uint2 pre[2];      // vote weights prefetched for the votes of the rounds of each parity
   float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
   int vhead, vtile;  // the tile whose votes are next (round r - kWvBanks in round r)
-  int merge_head;    // head this wave merges for its workgroup once all its waves have stored their pairs
-  float merge_R;     // that head's reference score of row lane & 31
   bool gave_up;      // a bounded wait has run out: no further waits (the results are invalid)
 };
 
@@ -1158,14 +1150,53 @@ __device__ __forceinline__ void wv_load_q(const WvCtx& c, const WvPos& p, bf16x8
   load_half_row<D>(reinterpret_cast<const uint16_t*>(base + off), qf);
 }
 
-// Head h's normaliser of row lane & 31 from its staged words (lanes of half
-// 0 take words 0..11, half 1 words 12..23). Bits 48..63 of a word count the
-// contributions that landed in it; the value parts (words 0..19) are below
-// 2^48, exact in a double, and so is each scaled term; both halves add the
-// two partial sums in the same order, so the value is the same in every lane
-// and every run. `count` is the row's number of contributions and `ovf`
-// whether one of them overflowed the fixed-point range.
-__device__ __forceinline__ float wv_words_to_c(const WvFin& f, int lane, unsigned& count, bool& ovf) {
+// s_waitcnt vmcnt(0), as the builtin (so that the compiler's own wait
+// placement knows every vector-memory operation issued so far is complete:
+// later uses of last round's loads need no wait that would also hold for
+// this round's tile) and as a compiler barrier (the tile's LDS reads stay
+// after it).
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
+  asm volatile("" ::: "memory");
+}
+
+// LDS add (by the lanes of the calling branch), issued as inline assembly:
+// as a compiler atomic it would make the compiler wait for the direct loads
+// in flight into the tile ring as well.
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
+  asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
+// Adds a workgroup's row sum L (of e_ij = 2^(s_ij - R_i)) to row `row` of a
+// head's fixed-point accumulator: L = mant * 2^(ey - 23), so the 24-bit
+// mantissa goes to bit pos = ey - 23 - kCoopDigitBase, i.e. mant << (pos % 16)
+// in word pos / 16 (pos <= 264 for a finite fp32), together with a count of 1
+// in bits 48..63 (a word's value part stays below 2^48: at most 2^9 terms
+// below 2^39 each). Sums below 2^-100 (at least 2^-100 times the row's total)
+// add only the count, a non-finite one adds its count to word kWvOvfWord.
+__device__ __forceinline__ void wv_add_sum(unsigned long long* acc_head, int row, float L) {
+  unsigned long long* arow = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_head) +
+                                                                   static_cast<unsigned>(row * kCoopRowWords) * 8u);
+  if (!(L <= 3.0e38f)) {
+    atomicAdd(arow + kWvOvfWord, kWvCountOne);
+  } else if (L < 7.9e-31f) {  // 2^-100
+    atomicAdd(arow, kWvCountOne);
+  } else {
+    const unsigned bits = __float_as_uint(L);
+    const unsigned long long mant = (bits & 0x7fffffu) | 0x800000u;
+    const int pos = static_cast<int>(bits >> 23) - 127 - 23 - kCoopDigitBase;
+    atomicAdd(arow + (pos >> 4), (mant << (pos & 15)) + kWvCountOne);
+  }
+}
+
+// Head h's vote weight of row lane & 31 from its staged words (lanes of half
+// 0 take words 0..11, half 1 words 12..23): L = sum of the value parts (each
+// word's is below 2^48, exact in a double, and so is each scaled term; both
+// halves add the two partial sums in the same order, so the value is the same
+// in every lane and every run), w = 1 / L. `count` is the row's number of
+// contributions and `ovf` whether one of them was not finite.
+__device__ __forceinline__ float wv_words_to_w(const WvFin& f, int lane, unsigned& count, bool& ovf) {
   constexpr int kHalf = kWvRowWords / 2;
   const int row = lane & 31, half = lane >> 5;
   const uint2* wr = reinterpret_cast<const uint2*>(f.words) + row * kWvRowWords + half * kHalf;
@@ -1173,8 +1204,8 @@ __device__ __forceinline__ float wv_words_to_c(const WvFin& f, int lane, unsigne
   double t = 0.0;
   unsigned n = 0;
   bool o = false;
-#pragma unroll
-  for (int k = 0; k < kHalf; ++k) {
+#pragma unroll 1
+  for (int k = 0; k < kHalf; ++k) {  // rare path: a rolled loop keeps its registers few
     const uint2 x = wr[k];
     n += x.y >> 16;
     const int word = half * kHalf + k;
@@ -1187,58 +1218,14 @@ __device__ __forceinline__ float wv_words_to_c(const WvFin& f, int lane, unsigne
   t += __shfl_xor(t, 32);
   count = n + __shfl_xor(n, 32);
   ovf = o;
-  float cv = f.ref[row];
-  if (t > 0.0)  // t = mant * 2^E, mant in [0.5, 1)
-    cv += static_cast<float>(__builtin_amdgcn_frexp_exp(t)) +
-          __builtin_amdgcn_logf(static_cast<float>(__builtin_amdgcn_frexp_mant(t)));
-  return cv;
+  return t > 0.0 ? static_cast<float>(1.0 / t) : 0.f;
 }
 
-// Exact normaliser of a flagged head: merge of the workgroups' partials in
-// workgroup order (half 0 takes the first half of the grid, half 1 the rest).
-__device__ __forceinline__ float wv_exact_c(const WvCtx& c, int bh, int lane) {
-  float m = kNegBig, l = 0.f;
-  const float2* pb = c.part + static_cast<int64_t>(bh) * c.G * 32 + (lane & 31);
-  const int half = lane >> 5;
-  const bool live = (lane & 31) < c.w;
-  const int g0 = half ? c.G / 2 : 0, g1 = half ? c.G : c.G / 2;
-  for (int gg = g0; gg < g1; gg += 4) {
-    uint2 pp[4];
-    // a partial's l is never 0 once stored (it counts the row's largest
-    // term), and the buffer is cleared beforehand: wait (bounded) until the
-    // workgroups' stores have landed
-    unsigned polls = 0;
-    bool missing;
-    do {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pp[i] = gg + i < g1 ? ld_agent_u2(reinterpret_cast<const uint2*>(&pb[(gg + i) * 32]))
-                            : make_uint2(__float_as_uint(kNegBig), 1u);
-      __builtin_amdgcn_s_waitcnt(0);
-      missing = __ballot(live && (pp[0].y == 0u || pp[1].y == 0u || pp[2].y == 0u || pp[3].y == 0u)) != 0ull;
-    } while (missing && ++polls < kWvSpin);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lse2_merge(m, l, __uint_as_float(pp[i].x), __uint_as_float(pp[i].y));
-  }
-  lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
-  return m + __builtin_amdgcn_logf(l);
-}
-
-// s_waitcnt vmcnt(0), as the builtin (so that the compiler's own wait
-// placement knows every vector-memory operation issued so far is complete:
-// later uses of last round's loads need no wait that would also hold for
-// this round's tile) and as a compiler barrier (the tile's LDS reads stay
-// after it).
-__device__ __forceinline__ void wait_vm_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
-  asm volatile("" ::: "memory");
-}
-
-// Direct-to-LDS copy of head h's accumulator words and reference scores into
-// finisher buffer h % kWvFinBufs (which must be free or already h's).
+// Direct-to-LDS copy of head h's accumulator words into finisher buffer
+// h % kWvFinBufs (which must be free or already h's).
 __device__ __forceinline__ void wv_stage(const WvCtx& c, int h, int lane) {
   const int b = h & (kWvFinBufs - 1);
-  WvFin& f = c.sh->fin[b];
+  WvFin& f = c.fin[b];
   asm volatile("" ::: "memory");
   if (c.sh->fin_owner[b] != h) {
     // another head of this workgroup still holds the buffer (only if its
@@ -1258,44 +1245,98 @@ __device__ __forceinline__ void wv_stage(const WvCtx& c, int h, int lane) {
     __builtin_amdgcn_global_load_lds(a + prow * kCoopRowWords + pj * 2, (lds_void*)(f.words + i * 128), 16, 0,
                                      16 /* sc1 */);
   }
-  if (lane < 8) __builtin_amdgcn_global_load_lds(c.ref + h * 32 + lane * 4, (lds_void*)f.ref, 16, 0, 0);
 }
 
-// The finisher's step for its staged head (the words landed at this round's
-// start): if every window row has all G contributions, convert and publish
-// the normalisers (from the exact merge of the workgroups' partials if one
-// contribution overflowed); otherwise stage the words again for next round.
-__device__ __forceinline__ void wv_finish(const WvCtx& c, WvPipe& p, int lane) {
-  const int h = p.fin_head, ln = opaque(lane), row = ln & 31;
-  const WvFin& f = c.sh->fin[h & (kWvFinBufs - 1)];
-  unsigned count;
-  bool ovf;
-  float cv = wv_words_to_c(f, ln, count, ovf);
-  if (__ballot(row < c.w && count != static_cast<unsigned>(c.G)) != 0ull) {
-    wv_stage(c, h, ln);  // a contribution is still in flight
-    return;
+// The finisher's work for head h: stage the words, wait for them, and once
+// every window row has all G contributions (else stage again: one may still
+// be in flight; bounded) publish the vote weights (0 for a flagged head,
+// whose votes are recomputed). Staging and use within one call, with a full
+// wait between them, leave no direct load into LDS in flight behind it.
+__device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int lane) {
+  const int ln = opaque(lane), row = ln & 31;
+  const WvFin& f = c.fin[h & (kWvFinBufs - 1)];
+  for (unsigned t = 0; t < kWvSpin; ++t) {
+    wv_stage(c, h, ln);
+    wait_vm_all();
+    unsigned count;
+    bool ovf;
+    float wv = wv_words_to_w(f, ln, count, ovf);
+    if (__ballot(row < c.w && count != static_cast<unsigned>(c.G)) == 0ull) {
+      if (__ballot(ovf) != 0ull) wv = 0.f;
+      if (ln < 32 && row < c.w) st_agent_u2(&c.stat[h * 32 + row], make_uint2(__float_as_uint(wv), 1u));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer read before it is released
+      if (ln == 0) c.sh->fin_owner[h & (kWvFinBufs - 1)] = -1;
+      asm volatile("" ::: "memory");
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);  // a contribution is still in flight
   }
-  if (__ballot(ovf) != 0ull) cv = wv_exact_c(c, h, ln);
-  if (ln < 32 && row < c.w) st_agent_u2(&c.stat[h * 32 + row], make_uint2(__float_as_uint(cv), 1u));
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer read before it is released
-  if (ln == 0) c.sh->fin_owner[h & (kWvFinBufs - 1)] = -1;
-  p.fin_head = -1;
+  p.gave_up = true;
+  if (ln == 0) __hip_atomic_store(c.status, 3u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The next round's prefetches: the normalisers for its votes (head
+// The merge of head h for this workgroup, by its designated wave, once all
+// kWvWaves waves have stored their row sums in slot h & 1: the sums added in
+// wave order, the slot reopened for head h + 2, the result added to the
+// head's accumulators, and the head's count raised. The workgroup whose
+// increment is the last stages and converts the words (which carry their own
+// contribution counts, so the increment need not wait for the contributions
+// to land). Skipped while the previous count's return has not been looked at.
+__device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane) {
+  if (p.cnt_head >= 0) return;
+  WvShared* sh = c.sh;
+  const int h = p.merge_head, sl = h & 1, ln = opaque(lane), col = ln & 31;
+  asm volatile("" ::: "memory");
+  if (__builtin_amdgcn_readfirstlane(sh->mcnt[sl]) != kWvWaves) return;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float L = sh->lslot[sl][0][col];
+#pragma unroll
+  for (int wv = 1; wv < kWvWaves; ++wv) L += sh->lslot[sl][wv][col];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sums read before the slot reopens
+  if (ln == 0) {
+    sh->mcnt[sl] = 0;
+    sh->mtag[sl] = h + 2;
+  }
+  asm volatile("" ::: "memory");
+  if (ln < 32 && col < c.w) wv_add_sum(c.acc + static_cast<int64_t>(h) * kCoopHeadWords, col, L);
+  // (an address the compiler cannot prove uniform: its atomic optimizer would
+  // otherwise broadcast the return at once, waiting for the next tile too)
+  unsigned ret = 0;
+  if (ln == 0) ret = atomicAdd(&c.cnt[h * kCoopCtrWords] + opaque(0), 1u);
+  p.cnt_ret = ret;
+  p.cnt_head = h;
+  p.merge_head = -1;
+}
+
+// Work this wave owes other waves, done after a full wait (every memory
+// operation it issued before is complete): publish the head whose count this
+// wave's increment completed, merge its workgroup's sums of a head it is
+// designated for. Every bounded wait of the kernel calls it, so that no wave
+// waits for something it owes itself.
+__device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane) {
+  if (p.cnt_head >= 0) {
+    if (__builtin_amdgcn_readfirstlane(p.cnt_ret) == static_cast<unsigned>(c.G - 1))
+      wv_publish(c, p, p.cnt_head, lane);
+    p.cnt_head = -1;
+  }
+  if (p.merge_head >= 0) wv_try_merge(c, p, lane);
+}
+
+// The next round's prefetches: the vote weights for its votes (head
 // pre_head) and the reference score of its tile (head ref_head).
+// (Addresses here and in the votes are a uniform base plus an unsigned 32-bit
+// lane offset, which the scalar-base addressing form takes directly.)
 template <int PAR>
 __device__ __forceinline__ void wv_prefetch(const WvCtx& c, WvPipe& p, int pre_head, int ref_head, int lane) {
-  const int row = lane & 31;
-  p.pre[PAR ^ 1] = ld_agent_u2(&c.stat[pre_head * 32 + row]);
-  p.rref[PAR ^ 1] = c.ref[ref_head * 32 + row];
+  const unsigned row = static_cast<unsigned>(lane & 31);
+  p.pre[PAR ^ 1] = ld_agent_u2(reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(c.stat + pre_head * 32) +
+                                                              row * 8u));
+  p.rref[PAR ^ 1] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(c.ref + ref_head * 32) + row * 4u);
 }
 
-__device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane);
-
-// Votes of the tile (head hv, tile tv) whose raw dot products q.k are in s, with the
-// normalisers `pre` prefetched a round ago (waited for, bounded, if the head
-// is not yet published).
+// Votes of the tile (head hv, tile tv) whose e_ij are in s, with the weights
+// `pre` prefetched a round ago (waited for, bounded, if the head is not yet
+// published). Rows past the window have weight 0 (never published).
 __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, const f32x16_t& s, int hv, int tv,
                                          int lane) {
   const int row = lane & 31, half = lane >> 5;
@@ -1314,106 +1355,58 @@ __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, c
       if (lane == 0) __hip_atomic_store(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  float* cs = c.sh->s_c[c.wave];
-  if (half == 0) cs[row] = __uint_as_float(pre.x);
+  float* ws = c.sh->s_w[c.wave];
+  if (half == 0) ws[row] = __uint_as_float(pre.x);
   float v = 0.f;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {  // registers 4a..4a+3 hold rows 8a + 4 half + 0..3
-    const f32x4_t cc = *reinterpret_cast<const f32x4_t*>(cs + 8 * a + 4 * half);
+    const f32x4_t ww = *reinterpret_cast<const f32x4_t*>(ws + 8 * a + 4 * half);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * a + e;
-      v += (c.w == kMaxWindow || acc_row(i, half) < c.w) ? fast_exp2(fmaf(s[i], c.scale_log2, -cc[e])) : 0.f;
-    }
+    for (int e = 0; e < 4; ++e) v = fmaf(s[4 * a + e], ww[e], v);
   }
   v += __shfl_xor(v, 32);
   const int j = tv * kTile + row;
-  if (half == 0 && j < c.t0) c.vote[static_cast<int64_t>(hv) * c.t0 + j] = v;
+  float* vrow = c.vote + static_cast<int64_t>(hv) * c.t0 + tv * kTile;  // uniform
+  if (half == 0 && j < c.t0) *reinterpret_cast<float*>(reinterpret_cast<char*>(vrow) + static_cast<unsigned>(row) * 4u) = v;
 }
 
-// LDS add (by the lanes of the calling branch), issued as inline assembly:
-// as a compiler atomic it would make the compiler wait for the direct loads
-// in flight into the tile ring as well.
-__device__ __forceinline__ void lds_add(int* p, int v) {
-  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
-  asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(v) : "memory");
+// This wave has scored its last tile of head h: its per-lane row sums are
+// reduced across the lanes of each half (a transposing butterfly: after the
+// steps over lane bits 0..3 a lane keeps register bitrev4(lane & 15); a last
+// step adds the partner across bit 4), the results go to slot h & 1 of the
+// workgroup (once the slot is open for h), and the designated wave
+// (h + g) % kWvWaves merges them when all waves have stored theirs (now if it
+// is the last, else at a later service). A non-finite sum flags the head.
+// (a & m) | (b & ~m) for a mask m that is all ones or all zeros per lane: the
+// lane-dependent choice between two registers, written so that the compiler
+// cannot turn it into an indexed read of the register array (which it lowers
+// as a chain of compares and selects over all sixteen elements).
+__device__ __forceinline__ float lane_pick(float a, float b, unsigned m) {
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
 }
 
-// The merge of head h for this workgroup, by its designated wave, once all
-// kWvWaves waves have stored their row pairs in slot h & 1: the pairs merged
-// in wave order, the slot reopened for head h + 2, the merged pairs added to
-// the head's accumulators and stored as the workgroup's partial, and the
-// head's count raised. The workgroup whose increment is the last stages and
-// converts the words (which carry their own contribution counts, so the
-// increment need not wait for the contributions to land). Skipped while the
-// previous count's return has not been looked at.
-__device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane) {
-  if (p.cnt_head >= 0) return;
-  WvShared* sh = c.sh;
-  const int h = p.merge_head, sl = h & 1, ln = opaque(lane), col = ln & 31;
-  asm volatile("" ::: "memory");
-  if (__builtin_amdgcn_readfirstlane(sh->mcnt[sl]) != kWvWaves) return;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  float2 a = sh->mslot[sl][0][col];
+__device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f32x16_t& ls, int lane) {
+  const int ln = opaque(lane);
+  // step over lane bit k: a lane with the bit set keeps the upper half of its
+  // registers and sends the lower half (masks opaque, all ones where the bit is set)
+  const unsigned m1 = opaque(-(ln & 1)), m2 = opaque(-((ln >> 1) & 1)), m4 = opaque(-((ln >> 2) & 1)),
+                 m8 = opaque(-((ln >> 3) & 1));
+  float x8[8], x4[4], x2[2], x1;
 #pragma unroll
-  for (int wv = 1; wv < kWvWaves; ++wv) {
-    const float2 b = sh->mslot[sl][wv][col];
-    lse2_merge(a.x, a.y, b.x, b.y);
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // pairs read before the slot reopens
-  if (ln == 0) {
-    sh->mcnt[sl] = 0;
-    sh->mtag[sl] = h + 2;
-  }
-  asm volatile("" ::: "memory");
-  if (ln < 32 && col < c.w) {
-    st_agent_u2(reinterpret_cast<uint2*>(&c.part[(static_cast<int64_t>(h) * c.G + c.g) * 32 + col]),
-                make_uint2(__float_as_uint(a.x), __float_as_uint(a.y)));
-    fixed_point_add<true>(c.acc + static_cast<int64_t>(h) * kCoopHeadWords, nullptr, col, a.x, a.y, p.merge_R);
-  }
-  // (an address the compiler cannot prove uniform: its atomic optimizer would
-  // otherwise broadcast the return at once, waiting for the next tile too)
-  unsigned ret = 0;
-  if (ln == 0) ret = atomicAdd(&c.cnt[h * kCoopCtrWords] + opaque(0), 1u);
-  p.cnt_ret = ret;
-  p.cnt_head = h;
-  p.merge_head = -1;
-}
-
-// Work this wave owes other waves, done after a full wait (every memory
-// operation it issued before is complete): publish a staged head, stage the
-// words of a head whose count this wave's increment completed, merge its
-// workgroup's pairs of a head it is designated for. Every bounded wait of the
-// kernel calls it, so that no wave waits for something it owes itself.
-__device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane) {
-  if (p.fin_head >= 0) wv_finish(c, p, lane);
-  if (p.cnt_head >= 0) {
-    if (__builtin_amdgcn_readfirstlane(p.cnt_ret) == static_cast<unsigned>(c.G - 1)) {
-      // a head still being retried by this wave is finished first (rare)
-      for (unsigned t = 0; p.fin_head >= 0 && t < kWvSpin; ++t) {
-        wait_vm_all();
-        wv_finish(c, p, lane);
-      }
-      wv_stage(c, p.cnt_head, opaque(lane));
-      p.fin_head = p.cnt_head;
-    }
-    p.cnt_head = -1;
-  }
-  if (p.merge_head >= 0) wv_try_merge(c, p, lane);
-}
-
-// This wave has scored its last tile of head h: its row pairs go to slot
-// h & 1 of the workgroup (once the slot is open for h), and the designated
-// wave (h + g) % kWvWaves, which spreads the merges evenly, merges them when
-// all waves have stored theirs (now if it is the last, else at a later
-// service).
-__device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, float R, int lane) {
-  float m = p.run_m * c.scale_log2, l = p.run_l;  // the running max is kept in raw q.k units
-  lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));  // lanes col and col+32 hold the same row
-  p.run_m = kNegBig;
-  p.run_l = 0.f;
+  for (int i = 0; i < 8; ++i) x8[i] = lane_pick(ls[i + 8], ls[i], m1) + __shfl_xor(lane_pick(ls[i], ls[i + 8], m1), 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x4[i] = lane_pick(x8[i + 4], x8[i], m2) + __shfl_xor(lane_pick(x8[i], x8[i + 4], m2), 2);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) x2[i] = lane_pick(x4[i + 2], x4[i], m4) + __shfl_xor(lane_pick(x4[i], x4[i + 2], m4), 4);
+  x1 = lane_pick(x2[1], x2[0], m8) + __shfl_xor(lane_pick(x2[0], x2[1], m8), 8);
+  x1 += __shfl_xor(x1, 16);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ls[i] = 0.f;
+  const int r = ((ln & 1) << 3) | ((ln & 2) << 1) | ((ln & 4) >> 1) | ((ln & 8) >> 3);
+  const int row = acc_row(r, ln >> 5);
+  if (__ballot(!(x1 <= 3.0e38f)) != 0ull && ln == 0) atomicOr(&c.cnt[h * kCoopCtrWords + 16], 1u);
   WvShared* sh = c.sh;
-  const int sl = h & 1, ln = opaque(lane), col = ln & 31;
+  const int sl = h & 1;
   // plain LDS reads behind compiler barriers: an atomic load here would make
   // the compiler wait for the direct loads in flight into the tile ring
   asm volatile("" ::: "memory");
@@ -1433,21 +1426,20 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, fl
       if (ln == 0) __hip_atomic_store(c.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (ln < 32) sh->mslot[sl][c.wave][col] = make_float2(m, l);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the pair is in LDS before the count says so
+  if ((ln & 16) == 0) sh->lslot[sl][c.wave][row] = x1;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the sums are in LDS before the count says so
   if (ln == 0) lds_add(&sh->mcnt[sl], 1);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (c.wave == ((h + c.g) & (kWvWaves - 1))) {
     p.merge_head = h;
-    p.merge_R = R;
     wv_try_merge(c, p, ln);
   }
 }
 
 template <int D, int BANK>
 __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, f32x16_t (&sc)[kWvBanks],
-                                         bf16x8_t (&qf)[D / 16], unsigned char* ring0, unsigned char* ring1,
-                                         int r) {
+                                         f32x16_t& ls, bf16x8_t (&qf)[D / 16], unsigned char* ring0,
+                                         unsigned char* ring1, int r) {
   using Ly = WvLayout<D>;
   constexpr int KS = D / 16;
   constexpr int PAR = BANK & 1;  // ring slot and prefetch parity of round r (kWvBanks is even)
@@ -1456,7 +1448,6 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   // this round's tile, Q and reference score, and everything issued last round
   wait_vm_all();
   const int lane = opaque(lane_id());
-  wv_service(c, p, lane);  // before the K loads: its reads of staged words then wait for nothing
   const WvPos nxt = wv_next(c, pos);
   const bool more = r + 1 < c.rounds;
   if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
@@ -1464,11 +1455,9 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   WvPos vn{p.vhead, 0, 0, p.vtile};
   if (r >= kWvBanks) vn = wv_next(c, vn);
   wv_prefetch<PAR>(c, p, min(vn.head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
-  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
-  if (r >= kWvBanks) {
-    p.vhead = vn.head;
-    p.vtile = vn.t;
-  }
+  // this tile's MFMAs first, then the next head's Q loads (which then have the
+  // votes and the row sums to land behind), then the votes of round r - 8
+  f32x16_t acc = {};
   if (do_a) {
     const int col = lane & 31, half = lane >> 5;
     // fragment k-step s of row col: piece half*kP/2 + s at slot piece ^ (col & (kP-1)),
@@ -1476,43 +1465,53 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     const unsigned char* tile = PAR ? ring1 : ring0;
     const unsigned A = static_cast<unsigned>(col * Ly::kRowB) +
                        (static_cast<unsigned>((half * (Ly::kP / 2)) ^ (col & (Ly::kP - 1))) << 4);
-    f32x16_t acc = {}, bt = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8_t kf =
           __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(tile + (A ^ static_cast<unsigned>(s << 4))));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf, acc, 0, 0, 0);
-      bt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], bt, 0, 0, 0);
       if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight
     }
     // Q of the next tile's head into the registers just read (a head's tiles share Q)
     if (more && nxt.head != pos.head) wv_load_q<D>(c, nxt, qf, lane);
-    sc[BANK] = acc;  // raw q.k; the votes apply the scale in their exponent
-    // the row statistics in raw units: max over the tile's keys the row sees,
-    // then sum 2^(scale * (s - max)) with the scale folded into one fma
+  }
+  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
+  if (r >= kWvBanks) {
+    p.vhead = vn.head;
+    p.vtile = vn.t;
+  }
+  if (do_a) {
+    const int col = lane & 31, half = lane >> 5;
+    float* rs = c.sh->s_r[c.wave];
+    if (half == 0) rs[col] = p.rref[PAR];  // R_i of this tile's head, read back per register below
+    // e_ij = 2^(s_ij - R_i) for key j = key0 + col and the lane's 16 rows i
     const int key0 = pos.t * kTile;
-    float m = kNegBig;
-    if (key0 + kTile <= c.t0) {  // every query sees every key of the tile
+    const bool full = key0 + kTile <= c.t0;  // every row sees every key of the tile
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, bt[i]);
-    } else {
-      const int ln = opaque(lane), cl = ln & 31, hf = ln >> 5;
+    for (int a = 0; a < 4; ++a) {
+      const f32x4_t rr = *reinterpret_cast<const f32x4_t*>(rs + 8 * a + 4 * half);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = key0 + acc_row(i, hf);
-        bt[i] = (j < c.L && j <= c.t0 + cl) ? bt[i] : kNegBig;
-        m = fmaxf(m, bt[i]);
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * a + e;
+        float x = fast_exp2(fmaf(acc[i], c.scale_log2, -rr[e]));
+        if (!full) {
+          const int j = key0 + col;
+          x = (j < c.L && j <= c.t0 + acc_row(i, half)) ? x : 0.f;
+        }
+        sc[BANK][i] = x;
+        ls[i] += x;
       }
     }
-    const float mn = fmaxf(p.run_m, m), mns = -mn * c.scale_log2;
-    float l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) l += fast_exp2(fmaf(bt[i], c.scale_log2, mns));
-    p.run_l = p.run_l * fast_exp2(fmaf(p.run_m, c.scale_log2, mns)) + l;
-    p.run_m = mn;
-    if (!more || nxt.head != pos.head) wv_head_end(c, p, pos.head, p.rref[PAR], lane);
+    if (!more || nxt.head != pos.head) wv_head_end(c, p, pos.head, ls, lane);
   }
   pos = nxt;
+  // owed work after a full wait (the next round starts with that wait anyway:
+  // it only comes earlier): a count raised this round is looked at, so the
+  // head a merge completes is published within the round
+  if (p.cnt_head >= 0 || p.merge_head >= 0) {
+    wait_vm_all();
+    wv_service(c, p, lane);
+  }
 }
 
 template <int D>
@@ -1520,24 +1519,25 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int nt,
     int total_tiles, int BH, float scale_log2, const float* __restrict__ ref, unsigned long long* __restrict__ acc,
-    unsigned* __restrict__ cnt, uint2* __restrict__ stat, float2* __restrict__ part, unsigned* __restrict__ status,
-    float* __restrict__ vote) {
+    unsigned* __restrict__ cnt, uint2* __restrict__ stat, unsigned* __restrict__ status, float* __restrict__ vote) {
   using Ly = WvLayout<D>;
   // the two tile slots of every wave's ring, as two arrays: the reads of one
   // slot are then known not to alias the direct loads in flight into the other
   __shared__ __attribute__((aligned(1024))) unsigned char ring_even[kWvWaves * Ly::kTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char ring_odd[kWvWaves * Ly::kTileB];
   __shared__ __attribute__((aligned(16))) WvShared sh;
+  __shared__ __attribute__((aligned(16))) WvFin fin[kWvFinBufs];
 
   WvCtx c;
   c.q = q; c.qsb = qsb; c.qsh = qsh; c.qst = qst; c.qrow0 = qrow0;
   c.k = k; c.ksb = ksb; c.ksh = ksh; c.kst = kst;
   c.H = H; c.L = L; c.w = w; c.t0 = L - w; c.nt = nt; c.BH = BH;
+  c.fin = fin;
   c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x); c.W = c.G * kWvWaves;
   c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
   c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   c.scale_log2 = scale_log2;
-  c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.part = part; c.status = status; c.vote = vote;
+  c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.status = status; c.vote = vote;
   c.sh = &sh;
   unsigned char* ring0 = ring_even + c.wave * Ly::kTileB;
   unsigned char* ring1 = ring_odd + c.wave * Ly::kTileB;
@@ -1548,11 +1548,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   }
   if (threadIdx.x < kWvFinBufs) sh.fin_owner[threadIdx.x] = -1;
   WvPipe p;
-  p.cnt_head = p.fin_head = p.merge_head = -1;
-  p.merge_R = 0.f;
+  p.cnt_head = p.merge_head = -1;
   p.cnt_ret = 0;
-  p.run_m = kNegBig;
-  p.run_l = 0.f;
   p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
   p.rref[0] = p.rref[1] = 0.f;
   p.gave_up = false;
@@ -1568,25 +1565,98 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   }
   __syncthreads();  // the slot counters are set
   f32x16_t sc[kWvBanks];
+  f32x16_t ls = {};
   static_assert(kWvBanks == 8, "the round loop below is unrolled over the register banks");
   // the last tile's votes fall in round rounds - 1 + kWvBanks, and the last
-  // head's publication three rounds after its last tile
+  // head's publication a few rounds after its last tile
   for (int r0 = 0; r0 < c.rounds + kWvBanks; r0 += kWvBanks) {
-    wv_round<D, 0>(c, p, pos, sc, qf, ring0, ring1, r0);
-    wv_round<D, 1>(c, p, pos, sc, qf, ring0, ring1, r0 + 1);
-    wv_round<D, 2>(c, p, pos, sc, qf, ring0, ring1, r0 + 2);
-    wv_round<D, 3>(c, p, pos, sc, qf, ring0, ring1, r0 + 3);
-    wv_round<D, 4>(c, p, pos, sc, qf, ring0, ring1, r0 + 4);
-    wv_round<D, 5>(c, p, pos, sc, qf, ring0, ring1, r0 + 5);
-    wv_round<D, 6>(c, p, pos, sc, qf, ring0, ring1, r0 + 6);
-    wv_round<D, 7>(c, p, pos, sc, qf, ring0, ring1, r0 + 7);
+    wv_round<D, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0);
+    wv_round<D, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 1);
+    wv_round<D, 2>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 2);
+    wv_round<D, 3>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 3);
+    wv_round<D, 4>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 4);
+    wv_round<D, 5>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 5);
+    wv_round<D, 6>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 6);
+    wv_round<D, 7>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 7);
   }
-  // work still owed after the last round: a pending merge, election or
-  // publication (bounded)
-  for (unsigned t = 0; (p.fin_head >= 0 || p.cnt_head >= 0 || p.merge_head >= 0) && t < kWvSpin; ++t) {
+  // work still owed after the last round: a pending merge or election (bounded)
+  for (unsigned t = 0; (p.cnt_head >= 0 || p.merge_head >= 0) && t < kWvSpin; ++t) {
     wait_vm_all();
     __builtin_amdgcn_s_sleep(2);
     wv_service(c, p, lane_id());
+  }
+}
+
+// Exact votes of the heads the single pass flagged (a score more than 2^127
+// above its row's reference): one workgroup per head, two plain passes over
+// the head's keys in fp32 (row maxima and sums of 2^(s - m), then the votes
+// with c_i = m_i + log2 l_i); a head that is not flagged returns at once.
+template <int D>
+__global__ __launch_bounds__(kThreads) void snap_fixup_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
+    const unsigned* __restrict__ cnt, float* __restrict__ vote) {
+  const int bh = blockIdx.x;
+  if (cnt[bh * kCoopCtrWords + 16] == 0u) return;
+  __shared__ float qs[kMaxWindow][D];
+  __shared__ float red_m[kThreads / kWave][kMaxWindow], red_l[kThreads / kWave][kMaxWindow];
+  __shared__ float cst[kMaxWindow];
+  const int b = bh / H, h = bh - b * H, t0 = L - w, wave = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
+    const int rr = i / D, d = i - rr * D;
+    qs[rr][d] = rr < w ? bf16_to_f32(q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rr) * qst + d]) : 0.f;
+  }
+  __syncthreads();
+  const uint16_t* kb = k + b * ksb + h * ksh;
+  float m[kMaxWindow], l[kMaxWindow];
+#pragma unroll
+  for (int i = 0; i < kMaxWindow; ++i) {
+    m[i] = kNegBig;
+    l[i] = 0.f;
+  }
+  for (int j = threadIdx.x; j < L; j += kThreads) {
+    float s[kMaxWindow];
+#pragma unroll
+    for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
+    for (int d = 0; d < D; ++d) {
+      const float kv = bf16_to_f32(kb[static_cast<int64_t>(j) * kst + d]);
+#pragma unroll
+      for (int i = 0; i < kMaxWindow; ++i) s[i] = fmaf(qs[i][d], kv, s[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxWindow; ++i)
+      if (i < w && j <= t0 + i) lse2_merge(m[i], l[i], s[i] * scale_log2, 1.f);
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxWindow; ++i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lse2_merge(m[i], l[i], __shfl_xor(m[i], o), __shfl_xor(l[i], o));
+    if (lane_id() == 0) {
+      red_m[wave][i] = m[i];
+      red_l[wave][i] = l[i];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kMaxWindow) {
+    float mm = red_m[0][threadIdx.x], ll = red_l[0][threadIdx.x];
+    for (int wv = 1; wv < kThreads / kWave; ++wv) lse2_merge(mm, ll, red_m[wv][threadIdx.x], red_l[wv][threadIdx.x]);
+    cst[threadIdx.x] = mm + __builtin_amdgcn_logf(ll);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < t0; j += kThreads) {
+    float s[kMaxWindow];
+#pragma unroll
+    for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
+    for (int d = 0; d < D; ++d) {
+      const float kv = bf16_to_f32(kb[static_cast<int64_t>(j) * kst + d]);
+#pragma unroll
+      for (int i = 0; i < kMaxWindow; ++i) s[i] = fmaf(qs[i][d], kv, s[i]);
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxWindow; ++i)
+      if (i < w) v += fast_exp2(s[i] * scale_log2 - cst[i]);
+    vote[static_cast<int64_t>(bh) * t0 + j] = v;
   }
 }
 
@@ -2049,8 +2119,7 @@ int64_t wave_tiles(int L) { return ((L + kTile - 1) / kTile + kWvWaves - 1) / kW
 
 // Grid of the independent-wave single pass, 0 when it cannot run. Every
 // workgroup must have tiles in every head (a head's padded tile count is at
-// least the worker count W), the per-workgroup partials must fit the partial
-// buffer (G <= units per head), and a head may span at most kWvMaxSpan rounds
+// least the worker count W), and a head may span at most kWvMaxSpan rounds
 // beyond its first: a vote waits (in round r) for the normaliser of a tile
 // of round r - kWvBanks, which its finisher publishes three rounds after the
 // head's last tile, so every such wait then depends only on heads that
@@ -2061,7 +2130,7 @@ int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
   const int per_cu = c.wv_per_cu[D == 128 ? 1 : 0];
   if (per_cu <= 0) return 0;
   const int64_t G = static_cast<int64_t>(per_cu) * c.cus, W = G * kWvWaves, nt = wave_tiles(L);
-  if (nt < W || G > lay.nunit || lay.BH * nt > INT32_MAX) return 0;
+  if (nt < W || lay.BH * nt > INT32_MAX) return 0;
   if (kst * 2 * 8 >= (int64_t(1) << 32) || qst * 2 * 32 >= (int64_t(1) << 32)) return 0;  // 32-bit lane offsets
   for (int64_t bh = 0; bh < lay.BH; ++bh) {
     const int64_t r0 = bh * nt / W, r1 = ((bh + 1) * nt - 1) / W;
@@ -2087,23 +2156,26 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   unsigned* status = reinterpret_cast<unsigned*>(ws + lay.cstatus);
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
   unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
-  // the wave kernel's per-workgroup partials (G x 32 float2 per head) start cleared
-  const int part_pieces = Gw > 0 ? Gw * 32 / 2 : 0;
   snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
-      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist, ctr,
-      reinterpret_cast<u32x4_t*>(part), part_pieces);
+      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist, ctr);
   mark_phase(1, stream);
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
   hipError_t e = hipErrorInvalidValue;
   if (Gw > 0) {
     int nt = static_cast<int>(wave_tiles(L)), total = static_cast<int>(lay.BH * nt), BH = static_cast<int>(lay.BH);
-    void* args[] = {&q,  &qsb,   &qsh, &qst, &qrow0,      &k,    &ksb, &ksh, &kst,  &H,    &L,      &w,
-                    &nt, &total, &BH,  &scale_log2, &cref, &acc, &cnt, &stat, &part, &status, &vote};
+    void* args[] = {&q,  &qsb,   &qsh, &qst, &qrow0,      &k,    &ksb, &ksh, &kst,  &H,      &L,  &w,
+                    &nt, &total, &BH,  &scale_log2, &cref, &acc, &cnt, &stat, &status, &vote};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_wave_bf16<D>), dim3(Gw), dim3(kWvThreads),
                                    args, 0, stream);
-    if (e == hipSuccess) g_last_kernel = "snap_wave_bf16";
-    else (void)hipGetLastError();
+    if (e == hipSuccess) {
+      g_last_kernel = "snap_wave_bf16";
+      // votes of any head flagged for a score beyond the offset's range, exactly
+      snap_fixup_bf16<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
+          q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, scale_log2, cnt, vote);
+    } else {
+      (void)hipGetLastError();
+    }
   }
   if (e != hipSuccess && Gc > 0) {
     int nunit = lay.nunit, total_units = static_cast<int>(lay.BH * lay.nunit);
