@@ -1061,7 +1061,9 @@ struct WvShared {
 };
 
 struct WvPos {
-  int head, b, h, t;  // tile t of head `head` = batch b, head h
+  int head, h, t;      // tile t of head `head` (h = head % H)
+  const char* kt;      // K row 32 t of that head
+  const char* qb;      // the head's first window query row
 };
 
 struct WvCtx {
@@ -1071,6 +1073,7 @@ struct WvCtx {
   const uint16_t* k;
   int64_t ksb, ksh, kst;
   int H, L, w, t0, nt, BH, G, g, W, rounds, wave;
+  int64_t dk_tile, dk_head, dk_batch, dq_head, dq_batch;  // byte steps of WvPos::kt and WvPos::qb
   float scale_log2;
   const float* ref;
   unsigned long long* acc;
@@ -1094,18 +1097,32 @@ struct WvPipe {
   bool gave_up;      // a bounded wait has run out: no further waits (the results are invalid)
 };
 
-// The next round's tile: W tiles on (W <= tiles per head, so at most one head boundary).
+// The next round's tile: W tiles on (W <= tiles per head, so at most one
+// head boundary); the K and Q pointers move by precomputed byte steps.
 __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
   p.t += c.W;
+  p.kt += c.dk_tile;
   if (p.t >= c.nt) {
     p.t -= c.nt;
     ++p.head;
+    p.kt += c.dk_head;
+    p.qb += c.dq_head;
     if (++p.h == c.H) {
       p.h = 0;
-      ++p.b;
+      p.kt += c.dk_batch;
+      p.qb += c.dq_batch;
     }
   }
   return p;
+}
+
+// The tile after t for the vote tracker (head and tile only).
+__device__ __forceinline__ void wv_next_ht(const WvCtx& c, int& head, int& t) {
+  t += c.W;
+  if (t >= c.nt) {
+    t -= c.nt;
+    ++head;
+  }
 }
 
 // Direct-to-LDS loads of one 32-row K tile into `slot` (XOR-swizzled rows:
@@ -1113,12 +1130,11 @@ __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
 template <int D>
 __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsigned char* slot, int lane) {
   using Ly = WvLayout<D>;
-  const uint16_t* kb = c.k + p.b * c.ksb + p.h * c.ksh;
   const int key0 = p.t * kTile;
-  if (key0 + kTile <= c.L) {
+  if (__builtin_expect(key0 + kTile <= c.L, 1)) {
     // instruction i covers rows i*kRowsPerInst + lane/kP: a uniform row base plus
     // the per-lane 32-bit offset (lane/kP) * row_bytes + 16 * piece
-    const char* rows = reinterpret_cast<const char*>(kb + static_cast<int64_t>(key0) * c.kst);
+    const char* rows = p.kt;
     const int64_t rb = c.kst * 2;
     const unsigned lrow = static_cast<unsigned>(lane / Ly::kP) * static_cast<unsigned>(rb);
     const unsigned x16 = static_cast<unsigned>((lane % Ly::kP) ^ (lane / Ly::kP)) << 4;
@@ -1129,6 +1145,7 @@ __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsig
                                        (lds_void*)(slot + i * 1024), 16, 0, 0);
     }
   } else {  // the head's last, ragged tile or a padding tile: rows clamped to the data
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.kt) - static_cast<int64_t>(key0) * c.kst;
 #pragma unroll
     for (int i = 0; i < Ly::kInst; ++i) {
       const int row = i * Ly::kRowsPerInst + lane / Ly::kP;
@@ -1144,7 +1161,7 @@ __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsig
 // its last row; half lane >> 5 of the contraction) for the tile at p.
 template <int D>
 __device__ __forceinline__ void wv_load_q(const WvCtx& c, const WvPos& p, bf16x8_t (&qf)[D / 16], int lane) {
-  const char* base = reinterpret_cast<const char*>(c.q + p.b * c.qsb + p.h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst);
+  const char* base = p.qb;
   const unsigned off = static_cast<unsigned>(min(lane & 31, c.w - 1)) * static_cast<unsigned>(c.qst * 2) +
                        static_cast<unsigned>((lane >> 5) * D);
   load_half_row<D>(reinterpret_cast<const uint16_t*>(base + off), qf);
@@ -1340,7 +1357,7 @@ __device__ __forceinline__ void wv_prefetch(const WvCtx& c, WvPipe& p, int pre_h
 __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, const f32x16_t& s, int hv, int tv,
                                          int lane) {
   const int row = lane & 31, half = lane >> 5;
-  if (!p.gave_up && __ballot(row < c.w && pre.y != 1u) != 0ull) {
+  if (__builtin_expect(!p.gave_up && __ballot(row < c.w && pre.y != 1u) != 0ull, 0)) {
     unsigned polls = 0;
     bool late;
     do {
@@ -1404,13 +1421,13 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f3
   for (int i = 0; i < 16; ++i) ls[i] = 0.f;
   const int r = ((ln & 1) << 3) | ((ln & 2) << 1) | ((ln & 4) >> 1) | ((ln & 8) >> 3);
   const int row = acc_row(r, ln >> 5);
-  if (__ballot(!(x1 <= 3.0e38f)) != 0ull && ln == 0) atomicOr(&c.cnt[h * kCoopCtrWords + 16], 1u);
+  if (__builtin_expect(__ballot(!(x1 <= 3.0e38f)) != 0ull, 0) && ln == 0) atomicOr(&c.cnt[h * kCoopCtrWords + 16], 1u);
   WvShared* sh = c.sh;
   const int sl = h & 1;
   // plain LDS reads behind compiler barriers: an atomic load here would make
   // the compiler wait for the direct loads in flight into the tile ring
   asm volatile("" ::: "memory");
-  if (!p.gave_up && sh->mtag[sl] != h) {
+  if (__builtin_expect(!p.gave_up && sh->mtag[sl] != h, 0)) {
     // the slot still holds head h - 2 (its merge is pending)
     unsigned polls = 0;
     bool late;
@@ -1452,9 +1469,9 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   const bool more = r + 1 < c.rounds;
   if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
   // the tile whose votes come next round: tile r - 7 (tile 0 before round 8)
-  WvPos vn{p.vhead, 0, 0, p.vtile};
-  if (r >= kWvBanks) vn = wv_next(c, vn);
-  wv_prefetch<PAR>(c, p, min(vn.head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
+  int vn_head = p.vhead, vn_t = p.vtile;
+  if (r >= kWvBanks) wv_next_ht(c, vn_head, vn_t);
+  wv_prefetch<PAR>(c, p, min(vn_head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
   // this tile's MFMAs first, then the next head's Q loads (which then have the
   // votes and the row sums to land behind), then the votes of round r - 8
   f32x16_t acc = {};
@@ -1477,8 +1494,8 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   }
   if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
   if (r >= kWvBanks) {
-    p.vhead = vn.head;
-    p.vtile = vn.t;
+    p.vhead = vn_head;
+    p.vtile = vn_t;
   }
   if (do_a) {
     const int col = lane & 31, half = lane >> 5;
@@ -1494,7 +1511,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * a + e;
         float x = fast_exp2(fmaf(acc[i], c.scale_log2, -rr[e]));
-        if (!full) {
+        if (__builtin_expect(!full, 0)) {
           const int j = key0 + col;
           x = (j < c.L && j <= c.t0 + acc_row(i, half)) ? x : 0.f;
         }
@@ -1508,7 +1525,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   // owed work after a full wait (the next round starts with that wait anyway:
   // it only comes earlier): a count raised this round is looked at, so the
   // head a merge completes is published within the round
-  if (p.cnt_head >= 0 || p.merge_head >= 0) {
+  if (__builtin_expect(p.cnt_head >= 0 || p.merge_head >= 0, 0)) {
     wait_vm_all();
     wv_service(c, p, lane);
   }
@@ -1536,6 +1553,11 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x); c.W = c.G * kWvWaves;
   c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
   c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  c.dk_tile = static_cast<int64_t>(c.W) * kTile * kst * 2;
+  c.dk_head = ksh * 2 - static_cast<int64_t>(nt) * kTile * kst * 2;
+  c.dk_batch = (ksb - H * ksh) * 2;
+  c.dq_head = qsh * 2;
+  c.dq_batch = (qsb - H * qsh) * 2;
   c.scale_log2 = scale_log2;
   c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.status = status; c.vote = vote;
   c.sh = &sh;
@@ -1553,7 +1575,10 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
   p.rref[0] = p.rref[1] = 0.f;
   p.gave_up = false;
-  WvPos pos{0, 0, 0, c.g * kWvWaves + c.wave};  // round 0: tile v of head 0 (v < W <= tiles per head)
+  // round 0: tile v of head 0 (v < W <= tiles per head)
+  WvPos pos{0, 0, c.g * kWvWaves + c.wave, nullptr, nullptr};
+  pos.kt = reinterpret_cast<const char*>(k + static_cast<int64_t>(pos.t) * kTile * kst);
+  pos.qb = reinterpret_cast<const char*>(q + static_cast<int64_t>(qrow0) * qst);
   p.vhead = 0;
   p.vtile = pos.t;
   bf16x8_t qf[D / 16];
