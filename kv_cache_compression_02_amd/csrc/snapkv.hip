@@ -49,7 +49,8 @@ constexpr int kMaxWindow = 32;
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 19;       // pooled >= 0: bits 30..19 = exponent + 4 mantissa bits
-constexpr int kClassChunk = 16384;   // pooled scores per workgroup in classify
+constexpr int kClassChunk = 4096;    // pooled scores per workgroup in classify
+constexpr int kCtrWords = 8;         // per head: {selected, candidates, b*, picks left, pooled chunks done, -, -, -}
 constexpr int kMaxPoolRadius = 32;
 constexpr int kFinThreads = 1024;
 constexpr int kCandLds = 4096;       // candidates staged in LDS by finalize
@@ -84,7 +85,7 @@ __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 
 // pass; the vote pass that fills them starts after it has finished).
 __device__ __forceinline__ void clear_head(unsigned* hist, unsigned* ctr, int bh) {
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
-  if (threadIdx.x < 4) ctr[bh * 4 + threadIdx.x] = 0;
+  if (threadIdx.x < kCtrWords) ctr[bh * kCtrWords + threadIdx.x] = 0;
 }
 
 // Merge the per-chunk partials (m, l) of the 32 window rows of head bh into
@@ -136,6 +137,38 @@ __device__ void pool_and_count(const float* sv, int e0, int e1, int c0, int c1, 
 __device__ void flush_hist(const unsigned* sh, unsigned* hist_row) {
   for (int i = threadIdx.x; i < kHistBins; i += kThreads)
     if (sh[i]) atomicAdd(&hist_row[i], sh[i]);
+}
+
+__device__ void find_kth_bin(const unsigned* sh, unsigned kk, unsigned* scratch, unsigned* bin, unsigned* above);
+
+// After this workgroup's histogram adds: the last of the head's nchunk
+// workgroups to get here finds the bin b* holding the kk-th largest pooled
+// score and stores b* and the picks left among its members (ctr_row[2], [3]).
+// `sh` (kHistBins words of LDS) is reused for the head's histogram.
+__device__ void hist_threshold_if_last(const unsigned* hist_row, unsigned* ctr_row, int nchunk, unsigned kk,
+                                       unsigned* sh) {
+  __shared__ unsigned s_last, s_bin, s_above;
+  __shared__ unsigned scratch[kWaves + 1];
+  // this workgroup's adds (device-scope atomics, performed where every
+  // workgroup sees them) have completed before its count: a wait for them,
+  // not a release fence (which would also write back the cache's pooled scores)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&ctr_row[4], 1u) == static_cast<unsigned>(nchunk - 1);
+  __syncthreads();
+  if (!s_last) return;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+    sh[i] = __hip_atomic_load(&hist_row[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    s_bin = 0;
+    s_above = 0;
+  }
+  __syncthreads();
+  find_kth_bin(sh, kk, scratch, &s_bin, &s_above);
+  if (threadIdx.x == 0) {
+    ctr_row[2] = s_bin;
+    ctr_row[3] = kk - s_above;
+  }
 }
 
 // ------------------------------------------------ pass 1: row statistics
@@ -273,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
     float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
-    float* __restrict__ pooled, unsigned* __restrict__ hist) {
+    float* __restrict__ pooled, unsigned* __restrict__ hist, unsigned* __restrict__ ctr, int kk) {
   constexpr int KS = D / 16;
   __shared__ float sv[kChunkMfma + 2 * kMaxPoolRadius];
   __shared__ unsigned sh[kHistBins];
@@ -338,6 +371,8 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
+  hist_threshold_if_last(hist + static_cast<int64_t>(bh) * kHistBins, ctr + bh * kCtrWords, gridDim.x,
+                         static_cast<unsigned>(kk), sh);
 }
 
 // fp32, VALU: a key per thread, the window rows and their statistics in LDS.
@@ -346,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
     float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
-    float* __restrict__ pooled, unsigned* __restrict__ hist) {
+    float* __restrict__ pooled, unsigned* __restrict__ hist, unsigned* __restrict__ ctr, int kk) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float2 st[kMaxWindow];
   __shared__ float sv[kChunkF32 + 2 * kMaxPoolRadius];
@@ -386,6 +421,8 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
+  hist_threshold_if_last(hist + static_cast<int64_t>(bh) * kHistBins, ctr + bh * kCtrWords, gridDim.x,
+                         static_cast<unsigned>(kk), sh);
 }
 
 // ------------------------------------ single-pass scores (cooperative, bf16)
@@ -545,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
   if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
   if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
-  if (threadIdx.x < 4) ctr[bh * 4 + threadIdx.x] = 0;
+  if (threadIdx.x < kCtrWords) ctr[bh * kCtrWords + threadIdx.x] = 0;
   // thread (i, part): window row i, dims part*D/8 .. part*D/8 + D/8 - 1 (two or one
   // 16-byte pieces); the row's 8 threads are adjacent lanes and sum their parts by shuffles
   constexpr int kDims = D / 8, kPieces = kDims / 8;
@@ -1689,7 +1726,8 @@ __global__ __launch_bounds__(kThreads) void snap_fixup_bf16(
 // per-head 12-bit histogram of the pooled scores; used after the single pass.
 __global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restrict__ vote,
                                                            float* __restrict__ pooled,
-                                                           unsigned* __restrict__ hist, int N, int r) {
+                                                           unsigned* __restrict__ hist, int N, int r,
+                                                           unsigned* __restrict__ ctr, int kk) {
   constexpr int kChunk = 4096;
   __shared__ float sv[kChunk + 2 * kMaxPoolRadius];
   __shared__ unsigned sh[kHistBins];
@@ -1703,6 +1741,8 @@ __global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restri
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * N, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
+  hist_threshold_if_last(hist + static_cast<int64_t>(bh) * kHistBins, ctr + bh * kCtrWords, gridDim.x,
+                         static_cast<unsigned>(kk), sh);
 }
 
 // ------------------------------------------------------------ classify
@@ -1734,30 +1774,21 @@ __device__ void find_kth_bin(const unsigned* sh, unsigned kk, unsigned* scratch,
   __syncthreads();
 }
 
-// ctr[bh] = {selected count, candidate count, b*, picks left for the candidates}
-// Each thread classifies kClassChunk / kThreads positions strided by the block
-// size (coalesced loads; the order inside the lists does not matter, the
+// Positions above the threshold bin b* (found by the last pooling workgroup of
+// the head) go to the head's selected list, the bin's members to its candidate
+// list. Each thread classifies kClassChunk / kThreads positions strided by the
+// block size (coalesced loads; the order inside the lists does not matter, the
 // final selection orders positions through a bitmap). Block-wide prefix sums
 // give every thread its output slots, so a workgroup makes one atomic per
 // list (per-wave atomics on one address serialise).
-__global__ __launch_bounds__(kThreads) void snap_classify(const float* __restrict__ pooled,
-                                                          const unsigned* __restrict__ hist, int N,
-                                                          int kk, unsigned* __restrict__ ctr,
-                                                          int* __restrict__ sel,
+__global__ __launch_bounds__(kThreads) void snap_classify(const float* __restrict__ pooled, int N, int kk,
+                                                          unsigned* __restrict__ ctr, int* __restrict__ sel,
                                                           uint2* __restrict__ cand) {
-  constexpr int kPer = kClassChunk / kThreads;  // 16
-  __shared__ unsigned sh[kHistBins];
+  constexpr int kPer = kClassChunk / kThreads;
   __shared__ unsigned scratch[kWaves + 1];
-  __shared__ unsigned s_bin, s_above, s_base_sel, s_base_cand;
+  __shared__ unsigned s_base_sel, s_base_cand;
   const int chunk = blockIdx.x, bh = blockIdx.y;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = hist[static_cast<int64_t>(bh) * kHistBins + i];
-  __syncthreads();
-  find_kth_bin(sh, static_cast<unsigned>(kk), scratch, &s_bin, &s_above);
-  const unsigned bstar = s_bin;
-  if (chunk == 0 && threadIdx.x == 0) {
-    ctr[bh * 4 + 2] = bstar;
-    ctr[bh * 4 + 3] = static_cast<unsigned>(kk) - s_above;
-  }
+  const unsigned bstar = ctr[bh * kCtrWords + 2];
   const float* pb = pooled + static_cast<int64_t>(bh) * N;
   const int j0 = chunk * kClassChunk + static_cast<int>(threadIdx.x);
   unsigned u[kPer];
@@ -1774,8 +1805,8 @@ __global__ __launch_bounds__(kThreads) void snap_classify(const float* __restric
   unsigned os = block_excl_scan<kThreads>(ns, scratch, &ts);
   unsigned oc = block_excl_scan<kThreads>(nc, scratch, &tc);
   if (threadIdx.x == 0) {
-    s_base_sel = ts ? atomicAdd(&ctr[bh * 4 + 0], ts) : 0u;
-    s_base_cand = tc ? atomicAdd(&ctr[bh * 4 + 1], tc) : 0u;
+    s_base_sel = ts ? atomicAdd(&ctr[bh * kCtrWords + 0], ts) : 0u;
+    s_base_cand = tc ? atomicAdd(&ctr[bh * kCtrWords + 1], tc) : 0u;
   }
   __syncthreads();
   int* sb = sel + static_cast<int64_t>(bh) * kk;
@@ -1820,9 +1851,9 @@ __global__ __launch_bounds__(kFinThreads) void snap_finalize(const unsigned* __r
   __shared__ unsigned s_digit, s_above;
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const unsigned n_sel = min(ctr[bh * 4 + 0], static_cast<unsigned>(kk));
-  const unsigned n_cand = min(ctr[bh * 4 + 1], static_cast<unsigned>(N));
-  unsigned rem = ctr[bh * 4 + 3];
+  const unsigned n_sel = min(ctr[bh * kCtrWords + 0], static_cast<unsigned>(kk));
+  const unsigned n_cand = min(ctr[bh * kCtrWords + 1], static_cast<unsigned>(N));
+  unsigned rem = ctr[bh * kCtrWords + 3];
   const int words = (N + 31) >> 5;
   unsigned* bm = words <= kBitmapLds ? bm_lds : bitmap_g + static_cast<int64_t>(bh) * words;
   for (int i = tid; i < words; i += kFinThreads) bm[i] = 0;
@@ -1987,7 +2018,7 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
     off = align_up(off + bytes, 256);
     return at;
   };
-  o->ctr = take(static_cast<size_t>(BH) * 16);
+  o->ctr = take(static_cast<size_t>(BH) * kCtrWords * 4);
   o->hist = take(static_cast<size_t>(BH) * kHistBins * 4);
   o->part = take(static_cast<size_t>(BH) * o->nchunk * 32 * 8);
   o->pooled = take(static_cast<size_t>(BH) * o->N * 4);
@@ -2043,7 +2074,8 @@ void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
   const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
   snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
                                                 scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
-                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
+                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist),
+                                                reinterpret_cast<unsigned*>(ws + lay.ctr), lay.kk);
 }
 
 template <int D>
@@ -2053,7 +2085,8 @@ void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
   const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
   snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
                                                scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
-                                               vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
+                                               vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist),
+                                               reinterpret_cast<unsigned*>(ws + lay.ctr), lay.kk);
 }
 
 // Pass 1 (row statistics; it also clears the histograms and counters), then
@@ -2214,7 +2247,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   mark_phase(2, stream);
   mark_phase(3, stream);
   const dim3 gp((lay.N + 4095) / 4096, static_cast<unsigned>(lay.BH));
-  snap_pool_hist<<<gp, kThreads, 0, stream>>>(vote, pooled, hist, lay.N, r);
+  snap_pool_hist<<<gp, kThreads, 0, stream>>>(vote, pooled, hist, lay.N, r, ctr, lay.kk);
   mark_phase(4, stream);
   return KVC_OK;
 }
@@ -2332,7 +2365,7 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   if (st != KVC_OK) return st;
 
   const dim3 gp((lay.N + kClassChunk - 1) / kClassChunk, static_cast<unsigned>(lay.BH));
-  snap_classify<<<gp, kThreads, 0, stream>>>(pooled, hist, lay.N, lay.kk, ctr,
+  snap_classify<<<gp, kThreads, 0, stream>>>(pooled, lay.N, lay.kk, ctr,
                                              reinterpret_cast<int*>(ws + lay.sel),
                                              reinterpret_cast<uint2*>(ws + lay.cand));
   mark_phase(5, stream);
