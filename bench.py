@@ -26,10 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
-PHASES = ["zero", "stats", "merge", "votes", "classify", "finalize", "gather"]
-# the same boundaries under the single-pass schedule: counter reset, the score
-# pass, (nothing), pooling + histogram, then the shared selection phases
-PHASES_SINGLE = ["reset", "score", "none", "pool", "classify", "finalize", "gather"]
+PHASES = ["zero", "stats", "merge", "votes", "select", "gather"]
+# the same boundaries under the single-pass schedule: the preparation kernel,
+# the score pass, (nothing), pooling + histogram, then the shared phases
+PHASES_SINGLE = ["prep", "score", "none", "pool", "select", "gather"]
 SCHEDULES = {"auto": 0, "two-pass": 1, "single-pass": 2}
 
 

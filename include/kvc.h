@@ -156,14 +156,15 @@ const char* kvc_snapkv_last_score_kernel(void);
 
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its
- * stream at phase boundary i, for i < n_events (at most 8) and events[i] not
+ * stream at phase boundary i, for i < n_events (at most 7) and events[i] not
  * NULL (each recorded event costs a few microseconds of GPU time): 0 before the
- * first kernel, then after the workspace clear (1), the row-statistics pass
- * (2; the single score pass under SINGLE_PASS), the row-statistics merge (3;
- * nothing separate under either schedule), the vote + pooling + histogram pass
- * (4; pooling + histogram under SINGLE_PASS),
- * classification (5), the final selection (6) and the gather (7). The events are created and owned
- * by the caller; pass NULL or 0 to stop recording. */
+ * first kernel, then after the workspace clear (1; the single pass's
+ * preparation kernel under SINGLE_PASS), the row-statistics pass (2; the
+ * single score pass under SINGLE_PASS), the row-statistics merge (3; nothing
+ * separate under either schedule), the vote + pooling + histogram pass (4;
+ * pooling + histogram under SINGLE_PASS), the per-head selection (5) and the
+ * gather (6). The events are created and owned by the caller; pass NULL or 0
+ * to stop recording. */
 void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events);
 
 /* ------------------------------------------------------------------------- */

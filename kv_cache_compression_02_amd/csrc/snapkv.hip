@@ -49,12 +49,8 @@ constexpr int kMaxWindow = 32;
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 19;       // pooled >= 0: bits 30..19 = exponent + 4 mantissa bits
-constexpr int kClassChunk = 4096;    // pooled scores per workgroup in classify
-constexpr int kCtrWords = 8;         // per head: {selected, candidates, b*, picks left, pooled chunks done, -, -, -}
 constexpr int kMaxPoolRadius = 32;
-constexpr int kFinThreads = 1024;
-constexpr int kCandLds = 4096;       // candidates staged in LDS by finalize
-constexpr int kBitmapLds = 16384;    // bitmap words kept in LDS (N <= 524288)
+constexpr int kSelCtrWords = 2;     // per head: candidates listed, selection workgroups finished
 constexpr float kNegBig = -1.0e30f;  // "no score" sentinel: 2^(kNegBig - m) == 0
 
 // ------------------------------------------------------------------ loaders
@@ -82,10 +78,10 @@ __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 
 // ------------------------------------------------------- row-stat merging
 
 // Clear one head's histogram and selection counters (run by the statistics
-// pass; the vote pass that fills them starts after it has finished).
-__device__ __forceinline__ void clear_head(unsigned* hist, unsigned* ctr, int bh) {
+// pass; the kernels that fill them start after it has finished).
+__device__ __forceinline__ void clear_head(unsigned* hist, unsigned* sel_ctr, int bh) {
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
-  if (threadIdx.x < kCtrWords) ctr[bh * kCtrWords + threadIdx.x] = 0;
+  if (threadIdx.x < kSelCtrWords) sel_ctr[bh * kSelCtrWords + threadIdx.x] = 0;
 }
 
 // Merge the per-chunk partials (m, l) of the 32 window rows of head bh into
@@ -139,38 +135,6 @@ __device__ void flush_hist(const unsigned* sh, unsigned* hist_row) {
     if (sh[i]) atomicAdd(&hist_row[i], sh[i]);
 }
 
-__device__ void find_kth_bin(const unsigned* sh, unsigned kk, unsigned* scratch, unsigned* bin, unsigned* above);
-
-// After this workgroup's histogram adds: the last of the head's nchunk
-// workgroups to get here finds the bin b* holding the kk-th largest pooled
-// score and stores b* and the picks left among its members (ctr_row[2], [3]).
-// `sh` (kHistBins words of LDS) is reused for the head's histogram.
-__device__ void hist_threshold_if_last(const unsigned* hist_row, unsigned* ctr_row, int nchunk, unsigned kk,
-                                       unsigned* sh) {
-  __shared__ unsigned s_last, s_bin, s_above;
-  __shared__ unsigned scratch[kWaves + 1];
-  // this workgroup's adds (device-scope atomics, performed where every
-  // workgroup sees them) have completed before its count: a wait for them,
-  // not a release fence (which would also write back the cache's pooled scores)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&ctr_row[4], 1u) == static_cast<unsigned>(nchunk - 1);
-  __syncthreads();
-  if (!s_last) return;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads)
-    sh[i] = __hip_atomic_load(&hist_row[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0) {
-    s_bin = 0;
-    s_above = 0;
-  }
-  __syncthreads();
-  find_kth_bin(sh, kk, scratch, &s_bin, &s_above);
-  if (threadIdx.x == 0) {
-    ctr_row[2] = s_bin;
-    ctr_row[3] = kk - s_above;
-  }
-}
-
 // ------------------------------------------------ pass 1: row statistics
 
 // bf16, MFMA 32x32x16. Output orientation S^T: M = keys of the tile, N = the 32
@@ -181,10 +145,10 @@ __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
     int nchunk, float scale_log2, float2* __restrict__ part, unsigned* __restrict__ hist,
-    unsigned* __restrict__ ctr) {
+    unsigned* __restrict__ sel_ctr) {
   constexpr int KS = D / 16;
   const int chunk = blockIdx.x, bh = blockIdx.y;
-  if (chunk == 0) clear_head(hist, ctr, bh);
+  if (chunk == 0) clear_head(hist, sel_ctr, bh);
   const int b = bh / H, h = bh - b * H;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int col = lane & 31, half = lane >> 5;
@@ -251,11 +215,11 @@ __global__ __launch_bounds__(kThreads) void snap_stats_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w,
     int nchunk, float scale_log2, float2* __restrict__ part, unsigned* __restrict__ hist,
-    unsigned* __restrict__ ctr) {
+    unsigned* __restrict__ sel_ctr) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float ss[kMaxWindow][kThreads + 1];
   const int chunk = blockIdx.x, bh = blockIdx.y;
-  if (chunk == 0) clear_head(hist, ctr, bh);
+  if (chunk == 0) clear_head(hist, sel_ctr, bh);
   const int b = bh / H, h = bh - b * H;
   const int t0 = L - w;
   for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
@@ -306,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
     float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
-    float* __restrict__ pooled, unsigned* __restrict__ hist, unsigned* __restrict__ ctr, int kk) {
+    float* __restrict__ pooled, unsigned* __restrict__ hist) {
   constexpr int KS = D / 16;
   __shared__ float sv[kChunkMfma + 2 * kMaxPoolRadius];
   __shared__ unsigned sh[kHistBins];
@@ -371,8 +335,6 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
-  hist_threshold_if_last(hist + static_cast<int64_t>(bh) * kHistBins, ctr + bh * kCtrWords, gridDim.x,
-                         static_cast<unsigned>(kk), sh);
 }
 
 // fp32, VALU: a key per thread, the window rows and their statistics in LDS.
@@ -381,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
     float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
-    float* __restrict__ pooled, unsigned* __restrict__ hist, unsigned* __restrict__ ctr, int kk) {
+    float* __restrict__ pooled, unsigned* __restrict__ hist) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float2 st[kMaxWindow];
   __shared__ float sv[kChunkF32 + 2 * kMaxPoolRadius];
@@ -421,8 +383,6 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
-  hist_threshold_if_last(hist + static_cast<int64_t>(bh) * kHistBins, ctr + bh * kCtrWords, gridDim.x,
-                         static_cast<unsigned>(kk), sh);
 }
 
 // ------------------------------------ single-pass scores (cooperative, bf16)
@@ -575,14 +535,14 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
     float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
-    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ ctr) {
+    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ sel_ctr) {
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
   if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
   if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
-  if (threadIdx.x < kCtrWords) ctr[bh * kCtrWords + threadIdx.x] = 0;
+  if (threadIdx.x < kSelCtrWords) sel_ctr[bh * kSelCtrWords + threadIdx.x] = 0;
   // thread (i, part): window row i, dims part*D/8 .. part*D/8 + D/8 - 1 (two or one
   // 16-byte pieces); the row's 8 threads are adjacent lanes and sum their parts by shuffles
   constexpr int kDims = D / 8, kPieces = kDims / 8;
@@ -1723,17 +1683,91 @@ __global__ __launch_bounds__(kThreads) void snap_fixup_bf16(
 }
 
 // Max-pool of raw votes (neighbours beyond the prefix ignored) and the
-// per-head 12-bit histogram of the pooled scores; used after the single pass.
-__global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restrict__ vote,
-                                                           float* __restrict__ pooled,
-                                                           unsigned* __restrict__ hist, int N, int r,
-                                                           unsigned* __restrict__ ctr, int kk) {
-  constexpr int kChunk = 4096;
-  __shared__ float sv[kChunk + 2 * kMaxPoolRadius];
+// per-head 12-bit histogram of the pooled scores, after the single pass. A
+// thread pools kPoolPer consecutive positions from a register window of their
+// votes with a halo of R on each side (rounded up to whole 16-byte pieces);
+// neighbouring pooled scores often share a histogram bin, so each run of equal
+// bins is one LDS add.
+constexpr int kPoolPer = 16;
+constexpr int kPoolChunk = kThreads * kPoolPer;
+constexpr int kPoolRegRadius = 7;  // larger radii pool from LDS (snap_pool_lds)
+
+template <int R, bool VEC>
+__global__ __launch_bounds__(kThreads) void snap_pool(const float* __restrict__ vote, float* __restrict__ pooled,
+                                                      unsigned* __restrict__ hist, int N) {
+  constexpr int kHalo = (R + 3) / 4 * 4;
+  constexpr int kX = kPoolPer + 2 * kHalo;
+  __shared__ unsigned sh[kHistBins];
+  const int bh = blockIdx.y;
+  const int j0 = (static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x)) * kPoolPer;
+  const float* vb = vote + static_cast<int64_t>(bh) * N;
+  float x[kX];
+  if (VEC && j0 >= kHalo && j0 + kPoolPer + kHalo <= N) {
+#pragma unroll
+    for (int p = 0; p < kX / 4; ++p) {
+      const f32x4_t f = *reinterpret_cast<const f32x4_t*>(vb + j0 - kHalo + 4 * p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * p + e] = f[e];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kX; ++i) {
+      const int j = j0 - kHalo + i;
+      x[i] = j >= 0 && j < N ? vb[j] : -__builtin_huge_valf();
+    }
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
+  float o[kPoolPer];
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) {
+    float m = x[i + kHalo - R];
+#pragma unroll
+    for (int d = 1; d <= 2 * R; ++d) m = fmaxf(m, x[i + kHalo - R + d]);
+    o[i] = m;
+  }
+  float* pr = pooled + static_cast<int64_t>(bh) * N + j0;
+  if (VEC && j0 + kPoolPer <= N) {
+#pragma unroll
+    for (int p = 0; p < kPoolPer / 4; ++p) {
+      f32x4_t f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = o[4 * p + e];
+      *reinterpret_cast<f32x4_t*>(pr + 4 * p) = f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPoolPer; ++i)
+      if (j0 + i < N) pr[i] = o[i];
+  }
+  __syncthreads();  // histogram cleared
+  unsigned run_bin = 0, run = 0;
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) {
+    const unsigned bin = (__float_as_uint(o[i]) >> kHistShift) & (kHistBins - 1);
+    if (j0 + i < N) {
+      if (run && bin != run_bin) {
+        atomicAdd(&sh[run_bin], run);
+        run = 0;
+      }
+      run_bin = bin;
+      ++run;
+    }
+  }
+  if (run) atomicAdd(&sh[run_bin], run);
+  __syncthreads();
+  flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
+}
+
+// The same for pooling radii beyond kPoolRegRadius: the chunk's votes and halo
+// staged in LDS, one output position per thread and step.
+__global__ __launch_bounds__(kThreads) void snap_pool_lds(const float* __restrict__ vote,
+                                                          float* __restrict__ pooled,
+                                                          unsigned* __restrict__ hist, int N, int r) {
+  __shared__ float sv[kPoolChunk + 2 * kMaxPoolRadius];
   __shared__ unsigned sh[kHistBins];
   const int chunk = blockIdx.x, bh = blockIdx.y;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
-  const int c0 = chunk * kChunk, c1 = min(N, c0 + kChunk);
+  const int c0 = chunk * kPoolChunk, c1 = min(N, c0 + kPoolChunk);
   const int e0 = max(0, c0 - r), e1 = min(N, c1 + r);
   const float* vb = vote + static_cast<int64_t>(bh) * N;
   for (int j = e0 + static_cast<int>(threadIdx.x); j < e1; j += kThreads) sv[j - e0] = vb[j];
@@ -1741,205 +1775,335 @@ __global__ __launch_bounds__(kThreads) void snap_pool_hist(const float* __restri
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * N, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
-  hist_threshold_if_last(hist + static_cast<int64_t>(bh) * kHistBins, ctr + bh * kCtrWords, gridDim.x,
-                         static_cast<unsigned>(kk), sh);
 }
 
-// ------------------------------------------------------------ classify
+// ------------------------------------------------------------ selection
+//
+// The kk kept prefix positions of a head are those with the largest pooled
+// scores, ties going to the lower position, written in ascending order. A
+// position's key is its score's bits (scores are non-negative, so their bits
+// order like their values) above its inverted position. Each head's prefix is
+// split into kSelChunk-position ranges, one workgroup each:
+//  1. every workgroup finds, from the head's 12-bit histogram, the bin b*
+//     holding the kk-th largest key and the number `rem` of picks left among
+//     that bin's members;
+//  2. it classifies its range: positions in bins above b* become bits of the
+//     head's bitmap (whole words, each stored once), members of b* go to the
+//     head's candidate list (one slot reservation per workgroup); both are
+//     stored at device scope and complete before the workgroup counts itself
+//     finished;
+//  3. the head's last workgroup to finish loads the bitmap and the
+//     candidates, finds the rem-th largest candidate key (12-bit radix passes
+//     below the bits b* fixes while more than a wave's worth of candidates
+//     share the prefix, then a direct rank within one wave), adds the bits of
+//     the candidates at or above it and compacts the bitmap into ascending
+//     positions.
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelPer = 4;                            // 16-byte score pieces per thread
+constexpr int kSelChunk = kSelThreads * kSelPer * 4;  // positions per workgroup
+constexpr int kCandLds = 4096;                        // candidates a workgroup holds in LDS
+constexpr int kBitmapLds = 16384;                     // bitmap words kept in LDS (N <= 524288)
+constexpr int kKeyFixed = 51;                         // key bits 63..51: the sign (clear) and the bin
 
-// The bin b* holding the k-th largest value: count(bins > b*) < k <= count(bins >= b*).
-// Every thread of the block calls it; results land in *bin / *above.
-__device__ void find_kth_bin(const unsigned* sh, unsigned kk, unsigned* scratch, unsigned* bin,
-                             unsigned* above) {
-  constexpr int kPer = kHistBins / kThreads;
-  const int t = threadIdx.x;
-  unsigned c = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) c += sh[t * kPer + i];
-  unsigned total;
-  const unsigned pre = block_excl_scan<kThreads>(c, scratch, &total);
-  const unsigned higher = total - pre - c;  // members of bins owned by higher threads
-  if (higher < kk && higher + c >= kk) {
-    unsigned run = higher;
-    for (int i = kPer - 1; i >= 0; --i) {
-      const unsigned hb = sh[t * kPer + i];
-      if (run + hb >= kk) {
-        *bin = t * kPer + i;
-        *above = run;
-        break;
-      }
-      run += hb;
-    }
-  }
-  __syncthreads();
-}
-
-// Positions above the threshold bin b* (found by the last pooling workgroup of
-// the head) go to the head's selected list, the bin's members to its candidate
-// list. Each thread classifies kClassChunk / kThreads positions strided by the
-// block size (coalesced loads; the order inside the lists does not matter, the
-// final selection orders positions through a bitmap). Block-wide prefix sums
-// give every thread its output slots, so a workgroup makes one atomic per
-// list (per-wave atomics on one address serialise).
-__global__ __launch_bounds__(kThreads) void snap_classify(const float* __restrict__ pooled, int N, int kk,
-                                                          unsigned* __restrict__ ctr, int* __restrict__ sel,
-                                                          uint2* __restrict__ cand) {
-  constexpr int kPer = kClassChunk / kThreads;
-  __shared__ unsigned scratch[kWaves + 1];
-  __shared__ unsigned s_base_sel, s_base_cand;
-  const int chunk = blockIdx.x, bh = blockIdx.y;
-  const unsigned bstar = ctr[bh * kCtrWords + 2];
-  const float* pb = pooled + static_cast<int64_t>(bh) * N;
-  const int j0 = chunk * kClassChunk + static_cast<int>(threadIdx.x);
-  unsigned u[kPer];
-  unsigned ns = 0, nc = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int j = j0 + e * kThreads;
-    u[e] = j < N ? __float_as_uint(pb[j]) : 0u;
-    const unsigned bin = (u[e] >> kHistShift) & (kHistBins - 1);
-    ns += (j < N && bin > bstar);
-    nc += (j < N && bin == bstar);
-  }
-  unsigned ts, tc;
-  unsigned os = block_excl_scan<kThreads>(ns, scratch, &ts);
-  unsigned oc = block_excl_scan<kThreads>(nc, scratch, &tc);
-  if (threadIdx.x == 0) {
-    s_base_sel = ts ? atomicAdd(&ctr[bh * kCtrWords + 0], ts) : 0u;
-    s_base_cand = tc ? atomicAdd(&ctr[bh * kCtrWords + 1], tc) : 0u;
-  }
-  __syncthreads();
-  int* sb = sel + static_cast<int64_t>(bh) * kk;
-  uint2* cb = cand + static_cast<int64_t>(bh) * N;
-  os += s_base_sel;
-  oc += s_base_cand;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int j = j0 + e * kThreads;
-    if (j >= N) break;
-    const unsigned bin = (u[e] >> kHistShift) & (kHistBins - 1);
-    if (bin > bstar) {
-      if (os < static_cast<unsigned>(kk)) sb[os] = j;
-      ++os;
-    } else if (bin == bstar) {
-      if (oc < static_cast<unsigned>(N)) cb[oc] = make_uint2(u[e], static_cast<unsigned>(j));
-      ++oc;
-    }
-  }
-}
-
-// ------------------------------------------------------------ finalize
-
-// Candidate order key: larger score first, then lower position first.
-__device__ __forceinline__ unsigned long long cand_key(uint2 c) {
-  return (static_cast<unsigned long long>(c.x) << 32) | static_cast<unsigned long long>(~c.y);
+__device__ __forceinline__ unsigned long long sel_key(unsigned u, unsigned j) {
+  return (static_cast<unsigned long long>(u & 0x7FFFFFFFu) << 32) | static_cast<unsigned long long>(~j);
 }
 
 __device__ __forceinline__ unsigned load_word(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kFinThreads) void snap_finalize(const unsigned* __restrict__ ctr,
-                                                             const int* __restrict__ sel,
-                                                             const uint2* __restrict__ cand, int N,
-                                                             int kk, unsigned* __restrict__ bitmap_g,
-                                                             int* __restrict__ idx_out) {
-  __shared__ uint2 cl[kCandLds];
-  __shared__ unsigned bm_lds[kBitmapLds];
-  __shared__ unsigned dh[256];
-  __shared__ unsigned scratch[kFinThreads / kWave + 1];
-  __shared__ unsigned s_digit, s_above;
-  const int bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const unsigned n_sel = min(ctr[bh * kCtrWords + 0], static_cast<unsigned>(kk));
-  const unsigned n_cand = min(ctr[bh * kCtrWords + 1], static_cast<unsigned>(N));
-  unsigned rem = ctr[bh * kCtrWords + 3];
-  const int words = (N + 31) >> 5;
-  unsigned* bm = words <= kBitmapLds ? bm_lds : bitmap_g + static_cast<int64_t>(bh) * words;
-  for (int i = tid; i < words; i += kFinThreads) bm[i] = 0;
+__device__ __forceinline__ void store_word(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-  const uint2* cg = cand + static_cast<int64_t>(bh) * N;
-  const bool in_lds = n_cand <= static_cast<unsigned>(kCandLds);
-  if (in_lds)
-    for (unsigned i = tid; i < n_cand; i += kFinThreads) cl[i] = cg[i];
-  __shared__ unsigned long long s_thresh;
-  if (tid == 0) s_thresh = ~0ull;  // stays "keep no candidate" if the counts were inconsistent
+// LDS fetch-and-add by each active lane, as written (no wave-level rewrite).
+__device__ __forceinline__ unsigned lds_add_rtn(unsigned* p, unsigned v) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned*)p));
+  unsigned r;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a), "v"(v) : "memory");
+  return r;
+}
+
+// Inclusive prefix sum over the wave: shifts within each 16-lane row, then the
+// row totals carried into the rows above.
+__device__ __forceinline__ unsigned wave_scan_dpp(unsigned x) {
+  int v = static_cast<int>(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+  return static_cast<unsigned>(v);
+}
+
+// Exclusive prefix sum over the block with one barrier; *total gets the block
+// sum. `wsum` (kSelWaves words) may be written again only after a barrier.
+__device__ __forceinline__ unsigned sel_block_scan(unsigned x, unsigned* wsum, unsigned* total) {
+  const int w = static_cast<int>(threadIdx.x) / kWave;
+  const unsigned incl = wave_scan_dpp(x);
+  if (lane_id() == kWave - 1) wsum[w] = incl;
   __syncthreads();
-  const uint2* src = in_lds ? cl : cg;
-
-  // the rem-th largest candidate key: by direct ranking when every candidate
-  // fits one per thread (the usual case), else by radix select, 8 bits at a
-  // time from the top
-  unsigned long long prefix = 0, pmask = 0;
-  const bool direct = in_lds && n_cand <= static_cast<unsigned>(kFinThreads);
-  if (direct) {
-    if (static_cast<unsigned>(tid) < n_cand) {
-      const unsigned long long mine = cand_key(cl[tid]);
-      unsigned greater = 0;
-      for (unsigned i = 0; i < n_cand; ++i) greater += cand_key(cl[i]) > mine;
-      if (greater + 1 == rem) s_thresh = mine;  // keys are distinct: exactly one thread
-    }
-    __syncthreads();
-    prefix = s_thresh;
-  }
-  for (int shift = 56; shift >= 0 && !direct; shift -= 8) {
-    if (tid < 256) dh[tid] = 0;
-    __syncthreads();
-    for (unsigned i = tid; i < n_cand; i += kFinThreads) {
-      const unsigned long long key = cand_key(src[i]);
-      if ((key & pmask) == prefix) atomicAdd(&dh[(key >> shift) & 255], 1u);
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      // lane owns digits [4*lane, 4*lane+4); suffix counts from the top digit
-      unsigned c4[4], c = 0;
+  unsigned before = 0, all = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c4[i] = dh[4 * tid + i];
-        c += c4[i];
+  for (int i = 0; i < kSelWaves; ++i) {
+    const unsigned v = wsum[i];
+    all += v;
+    before += i < w ? v : 0u;
+  }
+  *total = all;
+  return before + incl - x;
+}
+
+// The bin b holding the kk-th largest member of the LDS histogram h:
+// count(bins > b) < kk <= count(bins >= b). Every thread calls it; *bin and
+// *above are written before its closing barrier (left as they were if h holds
+// fewer than kk members).
+__device__ void sel_find_bin(const unsigned* h, unsigned kk, unsigned* wsum, unsigned* bin, unsigned* above) {
+  constexpr int kPer = kHistBins / kSelThreads;
+  const int t = threadIdx.x;
+  unsigned c[kPer], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    c[i] = h[t * kPer + i];
+    sum += c[i];
+  }
+  unsigned total;
+  const unsigned pre = sel_block_scan(sum, wsum, &total);
+  const unsigned higher = total - pre - sum;  // members of bins owned by higher threads
+  if (higher < kk && higher + sum >= kk) {
+    unsigned run = higher;
+#pragma unroll
+    for (int i = kPer - 1; i >= 0; --i) {
+      if (run + c[i] >= kk) {
+        *bin = t * kPer + i;
+        *above = run;
+        break;
       }
-      const unsigned incl = wave_incl_scan(c);
-      const unsigned total = __shfl(incl, kWave - 1);
-      const unsigned higher = total - incl;  // digits owned by higher lanes
-      if (higher < rem && higher + c >= rem) {
-        unsigned run = higher;
-        for (int i = 3; i >= 0; --i) {
-          if (run + c4[i] >= rem) {
-            s_digit = 4 * tid + i;
-            s_above = run;
-            break;
-          }
-          run += c4[i];
+      run += c[i];
+    }
+  }
+  __syncthreads();
+}
+
+struct SelShared {
+  unsigned bm[kBitmapLds];
+  uint2 cand[kCandLds];
+  unsigned sh[kHistBins];
+  unsigned long long mem[kWave];
+  unsigned wsum[kSelWaves];
+  unsigned long long thr;
+  unsigned bin, above, nloc, base, last, nmem;
+};
+
+// A candidate found by this workgroup: held in LDS while there is room, else
+// listed in the head's workspace list at once.
+__device__ __forceinline__ void sel_add_cand(SelShared& s, unsigned* ctr_head, uint2* cand_g, int N, unsigned u,
+                                             unsigned j, unsigned slot) {
+  const uint2 c = make_uint2(u, j);
+  if (slot < static_cast<unsigned>(kCandLds)) {
+    s.cand[slot] = c;
+  } else {
+    const unsigned g = atomicAdd(&ctr_head[0], 1u);
+    if (g < static_cast<unsigned>(N)) st_agent_u2(&cand_g[g], c);
+  }
+}
+
+// OR over the 8 lanes of each aligned lane octet.
+__device__ __forceinline__ unsigned octet_or(unsigned m) {
+  m |= static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  m |= static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  m |= static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x141, 0xF, 0xF, false));  // half-row mirror
+  return m;
+}
+
+// One 16-byte piece f of scores (positions 4f .. 4f+3) per lane. The wave's
+// pieces are consecutive and start at a multiple of 64, so the lanes of an
+// octet hold the 32 positions of bitmap word f >> 3, which one of them stores.
+__device__ __forceinline__ void sel_piece(SelShared& s, unsigned* bm_g, unsigned* ctr_head, uint2* cand_g, int N,
+                                          f32x4_t x, int f, bool valid, unsigned bstar) {
+  const int lane = lane_id();
+  unsigned m = 0, nc = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned bin = (__float_as_uint(x[e]) >> kHistShift) & (kHistBins - 1);
+    m |= static_cast<unsigned>(valid && bin > bstar) << e;
+    nc += valid && bin == bstar;
+  }
+  m = octet_or(m << (4 * (lane & 7)));
+  if (valid && (lane & 7) == 0) store_word(&bm_g[f >> 3], m);
+  if (nc != 0u) {
+    unsigned slot = lds_add_rtn(&s.nloc, nc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned u = __float_as_uint(x[e]);
+      if (valid && ((u >> kHistShift) & (kHistBins - 1)) == bstar) {
+        sel_add_cand(s, ctr_head, cand_g, N, u, static_cast<unsigned>(4 * f + e), slot);
+        ++slot;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ pooled, int vec,
+                                                           const unsigned* __restrict__ hist, int N, int kk,
+                                                           unsigned* __restrict__ ctr, uint2* __restrict__ cand_ws,
+                                                           unsigned* __restrict__ bitmap_ws,
+                                                           int* __restrict__ idx_out) {
+  __shared__ SelShared s;
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const float* pb = pooled + static_cast<int64_t>(bh) * N;
+  const int words = (N + 31) >> 5;
+  unsigned* bm_g = bitmap_ws + static_cast<int64_t>(bh) * words;
+  uint2* cand_g = cand_ws + static_cast<int64_t>(bh) * N;
+  unsigned* ctr_head = ctr + bh * kSelCtrWords;
+  const unsigned* hb = hist + static_cast<int64_t>(bh) * kHistBins;
+  const int c0 = blk * kSelChunk, c1 = min(N, c0 + kSelChunk);
+
+  // 1. the range's scores on their way (off the 16-byte path the loads read,
+  // and ignore, the histogram row), then the threshold bin
+  constexpr int kHistPer = kHistBins / kSelThreads;
+  unsigned hv[kHistPer];
+#pragma unroll
+  for (int r = 0; r < kHistPer; ++r) hv[r] = hb[tid + r * kSelThreads];
+  const int nf = vec ? N >> 2 : 1;
+  const int fb = vec ? c0 >> 2 : 0;
+  const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(vec ? static_cast<const void*>(pb) : static_cast<const void*>(hb));
+  f32x4_t xb[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) xb[k] = pv[min(fb + tid + k * kSelThreads, nf - 1)];
+#pragma unroll
+  for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = hv[r];
+  if (tid == 0) {
+    s.bin = 0;
+    s.above = 0;
+    s.nloc = 0;
+  }
+  __syncthreads();
+  sel_find_bin(s.sh, static_cast<unsigned>(kk), s.wsum, &s.bin, &s.above);
+  const unsigned bstar = s.bin;
+  unsigned rem = static_cast<unsigned>(kk) - s.above;
+
+  // 2. classification of [c0, c1)
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kSelPer; ++k) {
+      const int f = fb + tid + k * kSelThreads;
+      sel_piece(s, bm_g, ctr_head, cand_g, N, xb[k], f, f < nf, bstar);
+    }
+  } else {
+    for (int w = (c0 >> 5) + tid; w < ((c1 + 31) >> 5); w += kSelThreads) {
+      unsigned bits = 0;
+      for (int b = 0; b < 32; ++b) {
+        const int j = w * 32 + b;
+        if (j >= c1) break;
+        const unsigned u = __float_as_uint(pb[j]);
+        const unsigned bin = (u >> kHistShift) & (kHistBins - 1);
+        bits |= static_cast<unsigned>(bin > bstar) << b;
+        if (bin == bstar) sel_add_cand(s, ctr_head, cand_g, N, u, static_cast<unsigned>(j), lds_add_rtn(&s.nloc, 1u));
+      }
+      store_word(&bm_g[w], bits);
+    }
+  }
+  __syncthreads();
+  const unsigned nl = min(s.nloc, static_cast<unsigned>(kCandLds));
+  if (tid == 0) s.base = nl ? atomicAdd(&ctr_head[0], nl) : 0u;
+  __syncthreads();
+  for (unsigned i = tid; i < nl; i += kSelThreads)
+    if (s.base + i < static_cast<unsigned>(N)) st_agent_u2(&cand_g[s.base + i], s.cand[i]);
+  // this thread's device-scope stores are complete before the workgroup counts
+  // itself finished
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s.last = atomicAdd(&ctr_head[1], 1u) == gridDim.x - 1u;
+  __syncthreads();
+  if (!s.last) return;
+
+  // 3. the head's last workgroup: candidates and bitmap, ranking, compaction
+  const unsigned n_cand = min(load_word(&ctr_head[0]), static_cast<unsigned>(N));
+  const bool in_lds = n_cand <= static_cast<unsigned>(kCandLds);
+  const bool lds_bm = words <= kBitmapLds;
+  if (in_lds)
+    for (unsigned i = tid; i < n_cand; i += kSelThreads) s.cand[i] = ld_agent_u2(&cand_g[i]);
+  if (lds_bm)
+    for (int i = tid; i < words; i += kSelThreads) s.bm[i] = load_word(&bm_g[i]);
+  unsigned long long prefix = static_cast<unsigned long long>(bstar) << kKeyFixed;
+  unsigned long long pmask = ~0ull << kKeyFixed;
+  unsigned long long thr = prefix;  // candidate keys >= thr are kept
+  unsigned members = n_cand;        // candidates whose key matches prefix under pmask
+  __syncthreads();
+  for (int lo = kKeyFixed; members != rem && lo > 0;) {
+    if (members <= static_cast<unsigned>(kWave)) {
+      // direct rank of the few members left, by one wave
+      if (tid == 0) {
+        s.nmem = 0;
+        s.thr = prefix;
+      }
+      __syncthreads();
+      for (unsigned i = tid; i < n_cand; i += kSelThreads) {
+        const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
+        const unsigned long long key = sel_key(c.x, c.y);
+        if ((key & pmask) == prefix) {
+          const unsigned slot = lds_add_rtn(&s.nmem, 1u);
+          if (slot < static_cast<unsigned>(kWave)) s.mem[slot] = key;
         }
       }
+      __syncthreads();
+      const unsigned nm = min(s.nmem, static_cast<unsigned>(kWave));
+      if (static_cast<unsigned>(tid) < nm) {
+        const unsigned long long mine = s.mem[tid];
+        unsigned greater = 0;
+        for (unsigned i = 0; i < nm; ++i) greater += s.mem[i] > mine;
+        if (greater + 1u == rem) s.thr = mine;  // keys are distinct: one lane at most
+      }
+      __syncthreads();
+      thr = s.thr;
+      break;
+    }
+    const int nb = lo >= 12 ? 12 : lo;
+    lo -= nb;
+    const unsigned dmask = (1u << nb) - 1u;
+#pragma unroll
+    for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = 0;
+    if (tid == 0) {
+      s.bin = 0;
+      s.above = 0;
     }
     __syncthreads();
-    rem -= s_above;
-    prefix |= static_cast<unsigned long long>(s_digit) << shift;
-    pmask |= 0xFFull << shift;
+    for (unsigned i = tid; i < n_cand; i += kSelThreads) {
+      const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
+      const unsigned long long key = sel_key(c.x, c.y);
+      if ((key & pmask) == prefix) atomicAdd(&s.sh[static_cast<unsigned>(key >> lo) & dmask], 1u);
+    }
     __syncthreads();
+    sel_find_bin(s.sh, rem, s.wsum, &s.bin, &s.above);
+    const unsigned d = s.bin;
+    rem -= s.above;
+    members = s.sh[d];
+    prefix |= static_cast<unsigned long long>(d) << lo;
+    pmask |= static_cast<unsigned long long>(dmask) << lo;
+    thr = prefix;
+    __syncthreads();  // every thread has read the digit before the next pass clears it
   }
-  // prefix is now the exact key of the last candidate to keep
-  for (unsigned i = tid; i < n_sel; i += kFinThreads) {
-    const int j = sel[static_cast<int64_t>(bh) * kk + i];
-    if (j >= 0 && j < N) atomicOr(&bm[j >> 5], 1u << (j & 31));
+  unsigned* bm = lds_bm ? s.bm : bm_g;
+  for (unsigned i = tid; i < n_cand; i += kSelThreads) {
+    const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
+    if (sel_key(c.x, c.y) >= thr && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
   }
-  for (unsigned i = tid; i < n_cand; i += kFinThreads) {
-    const uint2 c = src[i];
-    if (cand_key(c) >= prefix && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
-  }
-  __syncthreads();  // the bitmap lives in LDS or in this XCD's L2: workgroup scope suffices
+  __syncthreads();
 
   // ordered compaction of the bitmap into ascending positions
-  const int wpt = (words + kFinThreads - 1) / kFinThreads;
+  const int wpt = (words + kSelThreads - 1) / kSelThreads;
   const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
   unsigned cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(load_word(&bm[i]));
+  for (int i = w0; i < w1; ++i) cnt += __popc(lds_bm ? s.bm[i] : load_word(&bm_g[i]));
   unsigned total;
-  unsigned off = block_excl_scan<kFinThreads>(cnt, scratch, &total);
+  unsigned off = sel_block_scan(cnt, s.wsum, &total);
   int* out = idx_out + static_cast<int64_t>(bh) * kk;
   for (int i = w0; i < w1; ++i) {
-    unsigned wv = load_word(&bm[i]);
+    unsigned wv = lds_bm ? s.bm[i] : load_word(&bm_g[i]);
     while (wv) {
       const int bit = __ffs(wv) - 1;
       if (off < static_cast<unsigned>(kk)) out[off] = i * 32 + bit;
@@ -1996,8 +2160,8 @@ __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__
 struct SnapLayout {
   int64_t BH;
   int N, kk, nchunk, words, nunit;
-  size_t ctr, hist;
-  size_t part, pooled, sel, cand, bitmap;
+  size_t hist, sel_ctr;
+  size_t part, pooled, cand, bitmap;
   size_t cref, cacc, ccnt, cstat, cpart, cstatus;  // single pass (bf16)
   size_t total;
 };
@@ -2018,11 +2182,10 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
     off = align_up(off + bytes, 256);
     return at;
   };
-  o->ctr = take(static_cast<size_t>(BH) * kCtrWords * 4);
   o->hist = take(static_cast<size_t>(BH) * kHistBins * 4);
+  o->sel_ctr = take(static_cast<size_t>(BH) * kSelCtrWords * 4);
   o->part = take(static_cast<size_t>(BH) * o->nchunk * 32 * 8);
   o->pooled = take(static_cast<size_t>(BH) * o->N * 4);
-  o->sel = take(static_cast<size_t>(BH) * o->kk * 4);
   o->cand = take(static_cast<size_t>(BH) * o->N * 8);
   o->bitmap = take(static_cast<size_t>(BH) * o->words * 4);
   o->nunit = (L + kCoopUnit - 1) / kCoopUnit;
@@ -2054,7 +2217,7 @@ void launch_stats(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
   snap_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
                                                 lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
                                                 reinterpret_cast<unsigned*>(ws + lay.hist),
-                                                reinterpret_cast<unsigned*>(ws + lay.ctr));
+                                                reinterpret_cast<unsigned*>(ws + lay.sel_ctr));
 }
 
 template <int D>
@@ -2064,7 +2227,7 @@ void launch_stats(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
   snap_stats_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w,
                                                lay.nchunk, scale_log2, reinterpret_cast<float2*>(ws + lay.part),
                                                reinterpret_cast<unsigned*>(ws + lay.hist),
-                                               reinterpret_cast<unsigned*>(ws + lay.ctr));
+                                               reinterpret_cast<unsigned*>(ws + lay.sel_ctr));
 }
 
 template <int D>
@@ -2074,8 +2237,7 @@ void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
   const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
   snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
                                                 scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
-                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist),
-                                                reinterpret_cast<unsigned*>(ws + lay.ctr), lay.kk);
+                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
 template <int D>
@@ -2085,8 +2247,7 @@ void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
   const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
   snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
                                                scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
-                                               vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist),
-                                               reinterpret_cast<unsigned*>(ws + lay.ctr), lay.kk);
+                                               vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
 // Pass 1 (row statistics; it also clears the histograms and counters), then
@@ -2202,6 +2363,34 @@ thread_local const char* g_last_kernel = "";
 // Single pass: the per-head preparation (reference scores, cleared state),
 // the cooperative score pass (raw votes to `vote`), then pooling + histogram.
 // Phase marks 1, 2, 3 and 4.
+template <int R>
+void launch_pool_r(const float* vote, float* pooled, unsigned* hist, int BH, int N, hipStream_t stream) {
+  const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
+  if (N % 4 == 0 && aligned16(vote) && aligned16(pooled))
+    snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N);
+  else
+    snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N);
+}
+
+// Max-pool of the raw votes with the histogram of the results.
+void launch_pool(const float* vote, float* pooled, unsigned* hist, int BH, int N, int r, hipStream_t stream) {
+  static_assert(kPoolRegRadius == 7, "the cases below cover radii 0 .. kPoolRegRadius");
+  switch (r) {
+    case 0: return launch_pool_r<0>(vote, pooled, hist, BH, N, stream);
+    case 1: return launch_pool_r<1>(vote, pooled, hist, BH, N, stream);
+    case 2: return launch_pool_r<2>(vote, pooled, hist, BH, N, stream);
+    case 3: return launch_pool_r<3>(vote, pooled, hist, BH, N, stream);
+    case 4: return launch_pool_r<4>(vote, pooled, hist, BH, N, stream);
+    case 5: return launch_pool_r<5>(vote, pooled, hist, BH, N, stream);
+    case 6: return launch_pool_r<6>(vote, pooled, hist, BH, N, stream);
+    case 7: return launch_pool_r<7>(vote, pooled, hist, BH, N, stream);
+    default: {
+      const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
+      snap_pool_lds<<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, r);
+    }
+  }
+}
+
 template <int D>
 kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint16_t* q, kvc_strides qs, int qrow0,
                               const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, float scale_log2,
@@ -2213,9 +2402,9 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   float2* part = reinterpret_cast<float2*>(ws + lay.cpart);
   unsigned* status = reinterpret_cast<unsigned*>(ws + lay.cstatus);
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
-  unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
   snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
-      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist, ctr);
+      q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist,
+      reinterpret_cast<unsigned*>(ws + lay.sel_ctr));
   mark_phase(1, stream);
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
@@ -2246,8 +2435,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
   mark_phase(2, stream);
   mark_phase(3, stream);
-  const dim3 gp((lay.N + 4095) / 4096, static_cast<unsigned>(lay.BH));
-  snap_pool_hist<<<gp, kThreads, 0, stream>>>(vote, pooled, hist, lay.N, r, ctr, lay.kk);
+  launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, stream);
   mark_phase(4, stream);
   return KVC_OK;
 }
@@ -2320,7 +2508,6 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   float* vote = vote_out;  // votes are written only when asked for
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
   float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(ws + lay.pooled);
-  unsigned* ctr = reinterpret_cast<unsigned*>(ws + lay.ctr);
   const int qrow0 = q_len - window;
 
   // AUTO takes the single pass where it can run (it reads K once and measures
@@ -2364,15 +2551,13 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   kvc_status st = check_launch("snapkv score passes");
   if (st != KVC_OK) return st;
 
-  const dim3 gp((lay.N + kClassChunk - 1) / kClassChunk, static_cast<unsigned>(lay.BH));
-  snap_classify<<<gp, kThreads, 0, stream>>>(pooled, lay.N, lay.kk, ctr,
-                                             reinterpret_cast<int*>(ws + lay.sel),
-                                             reinterpret_cast<uint2*>(ws + lay.cand));
+  const int vec = lay.N % 4 == 0 && aligned16(pooled);
+  const dim3 gs((lay.N + kSelChunk - 1) / kSelChunk, static_cast<unsigned>(lay.BH));
+  snap_select<<<gs, kSelThreads, 0, stream>>>(pooled, vec, hist, lay.N, lay.kk,
+                                              reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
+                                              reinterpret_cast<uint2*>(ws + lay.cand),
+                                              reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
   mark_phase(5, stream);
-  snap_finalize<<<static_cast<unsigned>(lay.BH), kFinThreads, 0, stream>>>(
-      ctr, reinterpret_cast<const int*>(ws + lay.sel), reinterpret_cast<const uint2*>(ws + lay.cand), lay.N,
-      lay.kk, reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
-  mark_phase(6, stream);
   st = check_launch("snapkv selection");
   if (st != KVC_OK) return st;
 
@@ -2384,7 +2569,7 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
                                            kvs.b * es, kvs.h * es, kvs.t * es, H, L, window, budget, lay.kk,
                                            vec_per_row, idx_out, static_cast<char*>(k_out),
                                            static_cast<char*>(v_out));
-  mark_phase(7, stream);
+  mark_phase(6, stream);
   st = check_launch("snapkv gather");
   if (st == KVC_OK) g_last_schedule = schedule;
   return st;
