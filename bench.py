@@ -28,8 +28,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 PHASES = ["zero", "stats", "merge", "votes", "select", "gather"]
 # the same boundaries under the single-pass schedule: the preparation kernel,
-# the score pass, (nothing), pooling + histogram, then the shared phases
-PHASES_SINGLE = ["prep", "score", "none", "pool", "select", "gather"]
+# the score kernel, its overflow fixup, pooling + histogram, then the shared phases
+PHASES_SINGLE = ["prep", "score", "fixup", "pool", "select", "gather"]
 SCHEDULES = {"auto": 0, "two-pass": 1, "single-pass": 2}
 
 
@@ -164,26 +164,28 @@ def bench_snapkv(args, ev):
     phases = PHASES_SINGLE if single else PHASES
     passes = ("score", "pool") if single else ("stats", "votes")
     log(f"schedule: {'single pass' if single else 'two passes'} ({score_kernel})")
-    # Timed region: events only around the score passes (boundaries 1, 2 and 4;
-    # every recorded event costs the GPU a few microseconds).
-    timed = []
-    for _ in range(args.steps):
-        arr = (ctypes.c_void_p * n_ev)()
-        e = ev.create(3)
-        arr[1], arr[2], arr[4] = e[0], e[1], e[2]
-        timed.append(e)
+    # Timed region: K steps back to back with no events in the stream (a
+    # recorded event between two kernels costs the GPU several microseconds).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        arr = (ctypes.c_void_p * n_ev)()
-        arr[1], arr[2], arr[4] = timed[i][0], timed[i][1], timed[i][2]
-        set_events(arr)
         call()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # The same K steps again with events around the score passes only
+    # (boundaries 1 to 4): 1 -> 2 is the statistics pass or the single score
+    # kernel, 3 -> 4 the vote pass or the pooling kernel.
+    timed = [ev.create(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * n_ev)()
+        arr[1], arr[2], arr[3], arr[4] = timed[i]
+        set_events(arr)
+        call()
+    torch.cuda.synchronize()
     set_events(None)
     kern_ms = {passes[0]: sum(ev.ms(e[0], e[1]) for e in timed) / args.steps,
-               passes[1]: sum(ev.ms(e[1], e[2]) for e in timed) / args.steps}
+               passes[1]: sum(ev.ms(e[2], e[3]) for e in timed) / args.steps}
     # Untimed instrumented pass: every phase boundary, for the breakdown only.
     events = [ev.create(n_ev) for _ in range(args.steps)]
     for i in range(args.steps):

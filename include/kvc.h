@@ -160,8 +160,9 @@ const char* kvc_snapkv_last_score_kernel(void);
  * NULL (each recorded event costs a few microseconds of GPU time): 0 before the
  * first kernel, then after the workspace clear (1; the single pass's
  * preparation kernel under SINGLE_PASS), the row-statistics pass (2; the
- * single score pass under SINGLE_PASS), the row-statistics merge (3; nothing
- * separate under either schedule), the vote + pooling + histogram pass (4;
+ * single score kernel under SINGLE_PASS), the row-statistics merge (3; nothing
+ * separate under TWO_PASS, the score-overflow fixup kernel under SINGLE_PASS,
+ * if any), the vote + pooling + histogram pass (4;
  * pooling + histogram under SINGLE_PASS), the per-head selection (5) and the
  * gather (6). The events are created and owned by the caller; pass NULL or 0
  * to stop recording. */

@@ -543,49 +543,29 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
   if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
   if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
   if (threadIdx.x < kSelCtrWords) sel_ctr[bh * kSelCtrWords + threadIdx.x] = 0;
-  // thread (i, part): window row i, dims part*D/8 .. part*D/8 + D/8 - 1 (two or one
-  // 16-byte pieces); the row's 8 threads are adjacent lanes and sum their parts by shuffles
-  constexpr int kDims = D / 8, kPieces = kDims / 8;
-  const int t0 = L - w;
-  const int i = threadIdx.x >> 3, part = threadIdx.x & 7;
-  const uint16_t* qr = q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + min(i, w - 1)) * qst + part * kDims;
-  const uint16_t* kw = k + b * ksb + h * ksh + static_cast<int64_t>(t0) * kst + part * kDims;
-  float qv[kDims];
+  // the window's 32 x 32 score block on one wave's MFMA: the window keys as
+  // rows (M), the window queries as columns (N), so each lane holds 16 keys'
+  // scores for query (lane & 31) and the row max takes one exchange between
+  // the wave's halves; rows and keys past the window repeat row w - 1
+  if (threadIdx.x < kWave) {
+    constexpr int KS = D / 16;
+    const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+    const int rw = min(col, w - 1);
+    bf16x8_t qf[KS], kf[KS];
+    load_half_row<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rw) * qst + half * (D / 2), qf);
+    load_half_row<D>(k + b * ksb + h * ksh + static_cast<int64_t>(L - w + rw) * kst + half * (D / 2), kf);
+    f32x16_t sc = {};
 #pragma unroll
-  for (int pc = 0; pc < kPieces; ++pc) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qr + pc * 8);
+    for (int st = 0; st < KS; ++st) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sc, 0, 0, 0);
+    float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[pc * 8 + 2 * e] = __uint_as_float(u[e] << 16);
-      qv[pc * 8 + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    for (int i = 0; i < 16; ++i) {
+      const int j = acc_row(i, half);
+      if (j <= col && j < w) m = fmaxf(m, sc[i] * scale_log2);
     }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (half == 0) ref[bh * 32 + col] = m;
   }
-  float m = -INFINITY;
-  for (int j0 = 0; j0 < w; j0 += 8) {  // uniform trip count: every lane takes part in the shuffles
-    u32x4_t kv[8][kPieces];              // eight window keys' pieces in flight together
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb) {
-      const uint16_t* kr = kw + static_cast<int64_t>(min(j0 + jb, w - 1)) * kst;
-#pragma unroll
-      for (int pc = 0; pc < kPieces; ++pc) kv[jb][pc] = *reinterpret_cast<const u32x4_t*>(kr + pc * 8);
-    }
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb) {
-      float d = 0.f;
-#pragma unroll
-      for (int pc = 0; pc < kPieces; ++pc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d = fmaf(qv[pc * 8 + 2 * e], __uint_as_float(kv[jb][pc][e] << 16), d);
-          d = fmaf(qv[pc * 8 + 2 * e + 1], __uint_as_float(kv[jb][pc][e] & 0xFFFF0000u), d);
-        }
-      d += __shfl_xor(d, 1);
-      d += __shfl_xor(d, 2);
-      d += __shfl_xor(d, 4);
-      if (j0 + jb <= i && j0 + jb < w) m = fmaxf(m, d * scale_log2);
-    }
-  }
-  if (part == 0) ref[bh * 32 + i] = m;  // rows past the window repeat row w - 1 (same query, same keys)
 }
 
 // Everything one workgroup of the single pass needs across rounds.
@@ -2094,21 +2074,56 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
   }
   __syncthreads();
 
-  // ordered compaction of the bitmap into ascending positions
+  // ordered compaction of the bitmap into ascending positions: prefix counts
+  // of each thread's run of words, then (bitmap in LDS) every output slot t
+  // finds its word by binary search over the words' prefix counts and its bit
+  // by halving popcounts, so that all lanes do the same work; else each
+  // thread writes its own words' positions
+  int* out = idx_out + static_cast<int64_t>(bh) * kk;
   const int wpt = (words + kSelThreads - 1) / kSelThreads;
   const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
   unsigned cnt = 0;
   for (int i = w0; i < w1; ++i) cnt += __popc(lds_bm ? s.bm[i] : load_word(&bm_g[i]));
   unsigned total;
-  unsigned off = sel_block_scan(cnt, s.wsum, &total);
-  int* out = idx_out + static_cast<int64_t>(bh) * kk;
-  for (int i = w0; i < w1; ++i) {
-    unsigned wv = lds_bm ? s.bm[i] : load_word(&bm_g[i]);
-    while (wv) {
-      const int bit = __ffs(wv) - 1;
-      if (off < static_cast<unsigned>(kk)) out[off] = i * 32 + bit;
-      ++off;
-      wv &= wv - 1;
+  unsigned run = sel_block_scan(cnt, s.wsum, &total);
+  if (lds_bm && words <= 2 * kCandLds) {
+    unsigned* pre = reinterpret_cast<unsigned*>(s.cand);  // the candidates are no longer needed
+    for (int i = w0; i < w1; ++i) {
+      pre[i] = run;
+      run += __popc(s.bm[i]);
+    }
+    __syncthreads();
+    const unsigned n_out = min(total, static_cast<unsigned>(kk));
+    for (unsigned t = tid; t < n_out; t += kSelThreads) {
+      int lo = 0, hi = words;  // pre[lo] <= t < pre[hi], pre[words] standing for the total
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= t)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      unsigned x = s.bm[lo], r = t - pre[lo];
+      int pos = 0;
+#pragma unroll
+      for (int sh = 16; sh; sh >>= 1) {
+        const unsigned c = __popc(x & ((1u << sh) - 1u));
+        if (r >= c) {
+          r -= c;
+          x >>= sh;
+          pos += sh;
+        }
+      }
+      out[t] = lo * 32 + pos;
+    }
+  } else {
+    for (int i = w0; i < w1; ++i) {
+      unsigned x = lds_bm ? s.bm[i] : load_word(&bm_g[i]);
+      while (x) {
+        if (run < static_cast<unsigned>(kk)) out[run] = i * 32 + __ffs(x) - 1;
+        ++run;
+        x &= x - 1;
+      }
     }
   }
 }
@@ -2417,6 +2432,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
                                    args, 0, stream);
     if (e == hipSuccess) {
       g_last_kernel = "snap_wave_bf16";
+      mark_phase(2, stream);
       // votes of any head flagged for a score beyond the offset's range, exactly
       snap_fixup_bf16<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
           q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, scale_log2, cnt, vote);
@@ -2430,10 +2446,12 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
                     &nunit, &total_units, &scale_log2, &cref, &acc,   &cnt, &stat, &part, &status, &vote};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_coop_bf16<D>), dim3(Gc), dim3(kCoopThreads),
                                    args, 0, stream);
-    if (e == hipSuccess) g_last_kernel = "snap_coop_bf16";
+    if (e == hipSuccess) {
+      g_last_kernel = "snap_coop_bf16";
+      mark_phase(2, stream);
+    }
   }
   if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
-  mark_phase(2, stream);
   mark_phase(3, stream);
   launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, stream);
   mark_phase(4, stream);
