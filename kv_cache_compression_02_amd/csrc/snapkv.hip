@@ -1675,6 +1675,7 @@ constexpr int kPoolRegRadius = 7;  // larger radii pool from LDS (snap_pool_lds)
 template <int R, bool VEC>
 __global__ __launch_bounds__(kThreads) void snap_pool(const float* __restrict__ vote, float* __restrict__ pooled,
                                                       unsigned* __restrict__ hist, int N) {
+  // pooled may be NULL: then only the histogram is produced
   constexpr int kHalo = (R + 3) / 4 * 4;
   constexpr int kX = kPoolPer + 2 * kHalo;
   __shared__ unsigned sh[kHistBins];
@@ -1705,19 +1706,21 @@ __global__ __launch_bounds__(kThreads) void snap_pool(const float* __restrict__ 
     for (int d = 1; d <= 2 * R; ++d) m = fmaxf(m, x[i + kHalo - R + d]);
     o[i] = m;
   }
-  float* pr = pooled + static_cast<int64_t>(bh) * N + j0;
-  if (VEC && j0 + kPoolPer <= N) {
+  if (pooled) {  // the pooled scores are stored only when something reads them
+    float* pr = pooled + static_cast<int64_t>(bh) * N + j0;
+    if (VEC && j0 + kPoolPer <= N) {
 #pragma unroll
-    for (int p = 0; p < kPoolPer / 4; ++p) {
-      f32x4_t f;
+      for (int p = 0; p < kPoolPer / 4; ++p) {
+        f32x4_t f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = o[4 * p + e];
-      *reinterpret_cast<f32x4_t*>(pr + 4 * p) = f;
+        for (int e = 0; e < 4; ++e) f[e] = o[4 * p + e];
+        *reinterpret_cast<f32x4_t*>(pr + 4 * p) = f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPoolPer; ++i)
+        if (j0 + i < N) pr[i] = o[i];
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kPoolPer; ++i)
-      if (j0 + i < N) pr[i] = o[i];
   }
   __syncthreads();  // histogram cleared
   unsigned run_bin = 0, run = 0;
@@ -1785,6 +1788,7 @@ constexpr int kSelChunk = kSelThreads * kSelPer * 4;  // positions per workgroup
 constexpr int kCandLds = 4096;                        // candidates a workgroup holds in LDS
 constexpr int kBitmapLds = 16384;                     // bitmap words kept in LDS (N <= 524288)
 constexpr int kKeyFixed = 51;                         // key bits 63..51: the sign (clear) and the bin
+constexpr int kSelMaxRad = 4;                         // pooling radius the selection applies to raw votes
 
 __device__ __forceinline__ unsigned long long sel_key(unsigned u, unsigned j) {
   return (static_cast<unsigned long long>(u & 0x7FFFFFFFu) << 32) | static_cast<unsigned long long>(~j);
@@ -1927,14 +1931,62 @@ __device__ __forceinline__ void sel_piece(SelShared& s, unsigned* bm_g, unsigned
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ pooled, int vec,
+// The max-pool (radius rad <= kSelMaxRad, neighbours past the prefix ignored)
+// of piece f of a row of raw votes, from the lane's piece `cur`, its wave
+// neighbours' pieces (DPP wave shifts) and, for the wave's first and last lane,
+// the piece beyond the wave (`edge`: piece f - 1 for lane 0, f + 1 for lane 63).
+__device__ __forceinline__ f32x4_t sel_pool_piece(f32x4_t cur, f32x4_t edge, int f, int nf, int rad) {
+  if (rad == 0) return cur;
+  const float ninf = -__builtin_huge_valf();
+  float x[12];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // wave_shr:1 gives lane l the value of lane l - 1 (lane 0 keeps `old`); wave_shl:1 of lane l + 1
+    x[e] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(edge[e]), __float_as_int(cur[e]), 0x138, 0xF,
+                                                      0xF, false));
+    x[4 + e] = cur[e];
+    x[8 + e] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(edge[e]), __float_as_int(cur[e]), 0x130, 0xF,
+                                                          0xF, false));
+  }
+  if (f == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = ninf;
+  }
+  if (f + 1 >= nf) {  // past the row (the lanes there hold clamped copies)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[8 + e] = ninf;
+  }
+  f32x4_t out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float m = x[4 + e];
+#pragma unroll
+    for (int d = 1; d <= kSelMaxRad; ++d)
+      if (d <= rad) m = fmaxf(m, fmaxf(x[4 + e - d], x[4 + e + d]));
+    out[e] = m;
+  }
+  return out;
+}
+
+// The max-pool (radius rad) of position j of a row of N raw votes, one by one.
+__device__ __forceinline__ float sel_pool_at(const float* pb, int j, int N, int rad) {
+  float m = pb[j];
+  for (int d = 1; d <= rad; ++d) {
+    if (j - d >= 0) m = fmaxf(m, pb[j - d]);
+    if (j + d < N) m = fmaxf(m, pb[j + d]);
+  }
+  return m;
+}
+
+// src: per head N pooled scores (rad = 0) or raw votes (pooled here with radius rad)
+__global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ src, int vec, int rad,
                                                            const unsigned* __restrict__ hist, int N, int kk,
                                                            unsigned* __restrict__ ctr, uint2* __restrict__ cand_ws,
                                                            unsigned* __restrict__ bitmap_ws,
                                                            int* __restrict__ idx_out) {
   __shared__ SelShared s;
   const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const float* pb = pooled + static_cast<int64_t>(bh) * N;
+  const float* pb = src + static_cast<int64_t>(bh) * N;
   const int words = (N + 31) >> 5;
   unsigned* bm_g = bitmap_ws + static_cast<int64_t>(bh) * words;
   uint2* cand_g = cand_ws + static_cast<int64_t>(bh) * N;
@@ -1951,9 +2003,14 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
   const int nf = vec ? N >> 2 : 1;
   const int fb = vec ? c0 >> 2 : 0;
   const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(vec ? static_cast<const void*>(pb) : static_cast<const void*>(hb));
-  f32x4_t xb[kSelPer];
+  f32x4_t xb[kSelPer], xe[kSelPer];
 #pragma unroll
-  for (int k = 0; k < kSelPer; ++k) xb[k] = pv[min(fb + tid + k * kSelThreads, nf - 1)];
+  for (int k = 0; k < kSelPer; ++k) {
+    const int f = fb + tid + k * kSelThreads;
+    xb[k] = pv[min(f, nf - 1)];
+    // the piece just beyond the wave, for lanes 0 and 63 (a clamped copy for the others)
+    xe[k] = pv[min(max((lane_id() == 0 ? f - 1 : f + 1), 0), nf - 1)];
+  }
 #pragma unroll
   for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = hv[r];
   if (tid == 0) {
@@ -1971,7 +2028,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
 #pragma unroll
     for (int k = 0; k < kSelPer; ++k) {
       const int f = fb + tid + k * kSelThreads;
-      sel_piece(s, bm_g, ctr_head, cand_g, N, xb[k], f, f < nf, bstar);
+      sel_piece(s, bm_g, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
     }
   } else {
     for (int w = (c0 >> 5) + tid; w < ((c1 + 31) >> 5); w += kSelThreads) {
@@ -1979,7 +2036,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
       for (int b = 0; b < 32; ++b) {
         const int j = w * 32 + b;
         if (j >= c1) break;
-        const unsigned u = __float_as_uint(pb[j]);
+        const unsigned u = __float_as_uint(sel_pool_at(pb, j, N, rad));
         const unsigned bin = (u >> kHistShift) & (kHistBins - 1);
         bits |= static_cast<unsigned>(bin > bstar) << b;
         if (bin == bstar) sel_add_cand(s, ctr_head, cand_g, N, u, static_cast<unsigned>(j), lds_add_rtn(&s.nloc, 1u));
@@ -2381,13 +2438,14 @@ thread_local const char* g_last_kernel = "";
 template <int R>
 void launch_pool_r(const float* vote, float* pooled, unsigned* hist, int BH, int N, hipStream_t stream) {
   const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
-  if (N % 4 == 0 && aligned16(vote) && aligned16(pooled))
+  if (N % 4 == 0 && aligned16(vote) && (!pooled || aligned16(pooled)))
     snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N);
   else
     snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N);
 }
 
-// Max-pool of the raw votes with the histogram of the results.
+// Max-pool of the raw votes with the histogram of the results (pooled scores
+// stored if `pooled` is not NULL; radii beyond kPoolRegRadius always store them).
 void launch_pool(const float* vote, float* pooled, unsigned* hist, int BH, int N, int r, hipStream_t stream) {
   static_assert(kPoolRegRadius == 7, "the cases below cover radii 0 .. kPoolRegRadius");
   switch (r) {
@@ -2536,18 +2594,32 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   const int Gc = try_single ? coop_grid(lay, D) : 0;
   int schedule = KVC_SNAPKV_TWO_PASS;
   mark_phase(0, stream);
+  // what the selection reads: the pooled scores, or (single pass, small
+  // pooling radius) the raw votes, which it then pools itself
+  const float* sel_src = pooled;
+  int sel_rad = 0;
   if (Gw > 0 || Gc > 0) {
-    // raw votes go to the caller's buffer or to the candidate area, which is
-    // free until classification
-    float* vraw = vote ? vote : reinterpret_cast<float*>(ws + lay.cand);
+    // Raw votes go to the caller's buffer, else to the pooled-score area when
+    // the selection pools them (nothing else is stored there then), else to
+    // the candidate area, which is free until the selection starts (the
+    // pooling kernel has read them by then). The pooling kernel stores pooled
+    // scores only if the caller asked for them or the selection reads them.
+    const int r = pool_kernel / 2;
+    const bool sel_pools = r <= kSelMaxRad;
+    float* vraw = vote ? vote : reinterpret_cast<float*>(ws + (sel_pools ? lay.pooled : lay.cand));
+    float* pooled_dst = pooled_out ? pooled_out : sel_pools ? nullptr : pooled;
     const uint16_t* qb = static_cast<const uint16_t*>(q);
     const uint16_t* kb = static_cast<const uint16_t*>(k);
-    kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window,
-                                                       pool_kernel / 2, scale_log2, ws, vraw, pooled, stream)
-                             : launch_single_pass<64>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window,
-                                                      pool_kernel / 2, scale_log2, ws, vraw, pooled, stream);
+    kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r,
+                                                       scale_log2, ws, vraw, pooled_dst, stream)
+                             : launch_single_pass<64>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r,
+                                                      scale_log2, ws, vraw, pooled_dst, stream);
     if (st == KVC_OK) {
       schedule = KVC_SNAPKV_SINGLE_PASS;
+      if (sel_pools) {
+        sel_src = vraw;
+        sel_rad = r;
+      }
     } else if (g_schedule == KVC_SNAPKV_SINGLE_PASS) {
       return st;
     } else {
@@ -2569,9 +2641,9 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   kvc_status st = check_launch("snapkv score passes");
   if (st != KVC_OK) return st;
 
-  const int vec = lay.N % 4 == 0 && aligned16(pooled);
+  const int vec = lay.N % 4 == 0 && aligned16(sel_src);
   const dim3 gs((lay.N + kSelChunk - 1) / kSelChunk, static_cast<unsigned>(lay.BH));
-  snap_select<<<gs, kSelThreads, 0, stream>>>(pooled, vec, hist, lay.N, lay.kk,
+  snap_select<<<gs, kSelThreads, 0, stream>>>(sel_src, vec, sel_rad, hist, lay.N, lay.kk,
                                               reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
                                               reinterpret_cast<uint2*>(ws + lay.cand),
                                               reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);

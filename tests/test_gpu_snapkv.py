@@ -19,13 +19,14 @@ def schedule(request):
     return SCHEDULES[request.param]
 
 
-def _run(q, k, v, wl_window, budget, pool, dtype, schedule=kvc.SNAPKV_AUTO, want_vote=True, **kw):
+def _run(q, k, v, wl_window, budget, pool, dtype, schedule=kvc.SNAPKV_AUTO, want_vote=True, want_pooled=True, **kw):
     if "workspace" not in kw:
         B, H, L, D = k.shape
         n = kvc.snapkv_workspace_bytes(B, H, L, D, wl_window, budget, pool, k.dtype)
         kw["workspace"] = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")  # garbage on entry
     with kvc.snapkv_schedule(schedule):
-        res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=True, want_vote=want_vote, **kw)
+        res = kvc.snapkv_compress(q, k, v, wl_window, budget, pool, want_pooled=want_pooled, want_vote=want_vote,
+                                  **kw)
     torch.cuda.synchronize()
     ran = kvc.snapkv_last_schedule()
     print(f"[snapkv] schedule asked {schedule} ran {ran} ({kvc.snapkv_last_score_kernel()})", flush=True)
@@ -42,14 +43,15 @@ def _compare(qn, kn, vn, res, window, budget, pool, dtype, heads=None):
     k_out = par.to_host_bits(res.k)
     v_out = par.to_host_bits(res.v)
     vote = res.vote.cpu().numpy() if res.vote is not None else None
-    pooled = res.pooled.cpu().numpy()
+    pooled = res.pooled.cpu().numpy() if res.pooled is not None else None
     pairs = heads or [(b, h) for b in range(B) for h in range(H)]
     kinds = []
     for b, h in pairs:
         r = ref.compress_head(qn[b, h, qn.shape[2] - window:], kn[b, h], vn[b, h], budget, pool, dtype)
         if vote is not None:
             par.assert_close_votes(vote[b, h], r["vote"], f"vote[{b},{h}]")
-        par.assert_close_votes(pooled[b, h], r["pooled"], f"pooled[{b},{h}]")
+        if pooled is not None:
+            par.assert_close_votes(pooled[b, h], r["pooled"], f"pooled[{b},{h}]")
         kinds.append(par.check_topk(r["pooled"], r["idx"], idx[b, h]))
         par.check_gather(k_out[b, h], v_out[b, h], kn[b, h], vn[b, h], idx[b, h], t0)
         if kinds[-1] == "exact":
@@ -119,6 +121,23 @@ def test_edge_shapes(dtype, D, w, L, budget, pool, schedule):
                             pool_kernel=pool, dtype=dtype, n_spans=2, span_len=3, span_boost=2.0,
                             seed=777 + L)
     _workload(wl, schedule=schedule)
+
+
+@pytest.mark.parametrize("L,w,pool", [(6000, 32, 7), (6000, 32, 9), (6000, 32, 11), (5002, 17, 5), (3000, 8, 1)])
+def test_no_optional_outputs(L, w, pool, schedule):
+    """Only the kept indices and rows asked for (no votes, no pooled scores): the
+    path where the selection pools the raw votes itself (radius <= 4), reads
+    pooled scores the pooling kernel stored only for it (larger radii), or
+    takes scalar loads (prefix length not a multiple of 4)."""
+    wl = syn.SnapKVWorkload(name=f"noout-{L}-{w}-{pool}", B=1, H=5, D=128, L=L, window=w, budget=400,
+                            pool_kernel=pool, dtype="bf16", n_spans=6, span_len=5, span_boost=1.5, seed=4242 + pool)
+    qn, kn, vn = syn.snapkv_batch(wl)
+    q, k, v = par.to_device(qn, "bf16"), par.to_device(kn, "bf16"), par.to_device(vn, "bf16")
+    print(f"[snapkv] no optional outputs L{L} w{w} p{pool} schedule {schedule}", flush=True)
+    res = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", schedule, want_vote=False, want_pooled=False)
+    assert res.vote is None and res.pooled is None
+    kinds = _compare(qn, kn, vn, res, wl.window, wl.budget, wl.pool_kernel, "bf16")
+    print(f"[snapkv] {wl.name}: {kinds.count('exact')} exact, {kinds.count('near-tie')} near-tie heads", flush=True)
 
 
 def test_single_pass_many_heads_unaligned():
