@@ -118,19 +118,24 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  * formed (so votes may differ in the last bits).
  *   TWO_PASS     row statistics (max, sum) in one pass over K, votes in a
  *                second: K is read twice. Bitwise reproducible.
- *   SINGLE_PASS  bf16 only: one device-wide cooperative pass keeps each key
- *                tile's scores in registers until its head's normaliser is
- *                complete, so K is read once. Each row's normaliser is summed
- *                exactly in fixed point, so the result does not depend on the
- *                order of the contributions (bitwise reproducible as well).
- *                Two kernels implement it. snap_wave_bf16, whose waves work
- *                independently on 32-key tiles, runs where every workgroup
- *                has tiles in every head and a head spans at most six of its
- *                rounds (on MI355X: about 64K to 320K keys per head).
- *                snap_coop_bf16, whose workgroups step through 128-key units
- *                together, covers shorter heads (a head of at most four
- *                device-wide rounds of units). Where neither can run, the call
- *                uses TWO_PASS.
+ *   SINGLE_PASS  bf16 only: one device-wide pass keeps each key tile's
+ *                scores in registers until its head's normaliser is complete,
+ *                so K is read once. Each row's normaliser is summed exactly in
+ *                fixed point, so the result does not depend on the order of
+ *                the contributions (bitwise reproducible as well). Two kernels
+ *                implement it, and both need all their workgroups resident at
+ *                once. snap_wave_bf16, whose waves work independently on
+ *                32-key tiles, runs where every workgroup has tiles in every
+ *                head and a head spans at most six of its rounds (on MI355X:
+ *                about 64K to 320K keys per head); it is launched like any
+ *                kernel and checks residency at its start: if its workgroups
+ *                cannot all start within about a millisecond (other work
+ *                holding the compute units), it flags every head and a plain
+ *                exact kernel computes the votes instead (the same results,
+ *                far slower). snap_coop_bf16, whose workgroups step through
+ *                128-key units together, covers shorter heads (a head of at
+ *                most four device-wide rounds of units) with a cooperative
+ *                launch. Where neither can run, the call uses TWO_PASS.
  *   AUTO         the default: SINGLE_PASS where it can run (the faster of
  *                the two on MI355X at the sizes measured so far), else
  *                TWO_PASS; also TWO_PASS if the cooperative launch fails. */
@@ -153,6 +158,14 @@ int kvc_snapkv_last_schedule(void);
  * the last successful kvc_snapkv_compress call on the calling thread: a
  * static string, "" if none. For reports and tests; it does not change. */
 const char* kvc_snapkv_last_score_kernel(void);
+
+/* Testing (not part of the method): while `on` is non-zero, the calling
+ * thread's single-pass calls run the independent-wave score kernel with a
+ * residency check that cannot pass (it waits for one workgroup more than the
+ * grid holds, 16 polls), so the kernel takes its fallback: it flags every head
+ * and the exact fixup kernel computes all votes, as when the kernel's
+ * workgroups cannot all be resident at once. Returns the previous setting. */
+int kvc_snapkv_force_residency_fallback(int on);
 
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its

@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
-    "kvc_snapkv_last_score_kernel",
+    "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention",
 )
 

@@ -535,8 +535,9 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
     float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
-    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ sel_ctr) {
+    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ sel_ctr, unsigned* __restrict__ gate) {
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  if (bh == 0 && threadIdx.x < 2) gate[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
@@ -1005,6 +1006,7 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
 // lane index instead of being kept live across the loop (a spilled value's
 // reload would have to wait behind the next tile's loads).
 constexpr int kWvWaves = 8;
+constexpr unsigned kWvGateSpin = 1u << 14;  // residency-check polls (~1 ms) before the exact fallback
 constexpr int kWvThreads = kWvWaves * kWave;
 constexpr int kWvBanks = 8;
 constexpr int kWvRowWords = 24;  // accumulator words per row a finisher stages (values in words 0..19)
@@ -1513,7 +1515,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int nt,
     int total_tiles, int BH, float scale_log2, const float* __restrict__ ref, unsigned long long* __restrict__ acc,
-    unsigned* __restrict__ cnt, uint2* __restrict__ stat, unsigned* __restrict__ status, float* __restrict__ vote) {
+    unsigned* __restrict__ cnt, uint2* __restrict__ stat, unsigned* __restrict__ status, float* __restrict__ vote,
+    unsigned* __restrict__ gate, unsigned gate_target, unsigned gate_spin) {
   using Ly = WvLayout<D>;
   // the two tile slots of every wave's ring, as two arrays: the reads of one
   // slot are then known not to alias the direct loads in flight into the other
@@ -1540,6 +1543,32 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.sh = &sh;
   unsigned char* ring0 = ring_even + c.wave * Ly::kTileB;
   unsigned char* ring1 = ring_odd + c.wave * Ly::kTileB;
+  // Residency check, in place of a launch that guarantees it: the waits below
+  // need every workgroup resident at once. Each workgroup counts itself in on
+  // gate[0]; the one whose count reaches gate_target opens the pass (gate[1]:
+  // 0 -> 1). A workgroup still waiting after gate_spin polls closes it
+  // instead (0 -> 2): some workgroups could not start while the others held
+  // the compute units. One compare-and-swap decides, so every workgroup,
+  // late ones included, takes the same branch; when the pass is closed every
+  // head is flagged and snap_fixup_bf16 computes all votes.
+  __shared__ unsigned s_gate;
+  if (threadIdx.x == 0) {
+    if (atomicAdd(&gate[0], 1u) + 1u == gate_target) atomicCAS(&gate[1], 0u, 1u);
+    unsigned st = __hip_atomic_load(&gate[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (unsigned polls = 0; st == 0u && polls < gate_spin; ++polls) {
+      __builtin_amdgcn_s_sleep(2);
+      st = __hip_atomic_load(&gate[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (st == 0u) {
+      const unsigned prev = atomicCAS(&gate[1], 0u, 2u);
+      st = prev == 0u ? 2u : prev;
+    }
+    if (st != 1u)
+      for (int h = 0; h < BH; ++h) atomicOr(&cnt[h * kCoopCtrWords + 16], 1u);
+    s_gate = st;
+  }
+  __syncthreads();
+  if (s_gate != 1u) return;
   if (threadIdx.x == 0) {
     sh.mcnt[0] = sh.mcnt[1] = 0;
     sh.mtag[0] = 0;  // every workgroup has tiles in every head, starting with head 0
@@ -1590,7 +1619,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
 }
 
 // Exact votes of the heads the single pass flagged (a score more than 2^127
-// above its row's reference): one workgroup per head, two plain passes over
+// above its row's reference, or every head when its workgroups could not all
+// be resident): one workgroup per head, two plain passes over
 // the head's keys in fp32 (row maxima and sums of 2^(s - m), then the votes
 // with c_i = m_i + log2 l_i); a head that is not flagged returns at once.
 template <int D>
@@ -2268,7 +2298,7 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
     o->ccnt = take(static_cast<size_t>(BH) * kCoopCtrWords * 4);
     o->cstat = take(static_cast<size_t>(BH) * 32 * 8);
     o->cpart = take(static_cast<size_t>(BH) * o->nunit * 32 * 8);
-    o->cstatus = take(4);
+    o->cstatus = take(16);  // [0] status, [1] [2] the single pass's residency gate
   }
   o->total = off;
   return true;
@@ -2408,7 +2438,8 @@ int coop_grid(const SnapLayout& lay, int D) {
 // a multiple of kWvWaves.
 int64_t wave_tiles(int L) { return ((L + kTile - 1) / kTile + kWvWaves - 1) / kWvWaves * kWvWaves; }
 
-// Grid of the independent-wave single pass, 0 when it cannot run. Every
+// Grid of the independent-wave single pass (one workgroup per resident slot,
+// which the kernel checks at its start), 0 when it cannot run. Every
 // workgroup must have tiles in every head (a head's padded tile count is at
 // least the worker count W), and a head may span at most kWvMaxSpan rounds
 // beyond its first: a vote waits (in round r) for the normaliser of a tile
@@ -2417,7 +2448,7 @@ int64_t wave_tiles(int L) { return ((L + kTile - 1) / kTile + kWvWaves - 1) / kW
 // started earlier and all of them end.
 int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
   const CoopCaps& c = coop_caps();
-  if (!c.coop || c.cus <= 0) return 0;
+  if (c.cus <= 0) return 0;
   const int per_cu = c.wv_per_cu[D == 128 ? 1 : 0];
   if (per_cu <= 0) return 0;
   const int64_t G = static_cast<int64_t>(per_cu) * c.cus, W = G * kWvWaves, nt = wave_tiles(L);
@@ -2431,10 +2462,8 @@ int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
 }
 
 thread_local const char* g_last_kernel = "";
+thread_local bool g_force_residency_fail = false;
 
-// Single pass: the per-head preparation (reference scores, cleared state),
-// the cooperative score pass (raw votes to `vote`), then pooling + histogram.
-// Phase marks 1, 2, 3 and 4.
 template <int R>
 void launch_pool_r(const float* vote, float* pooled, unsigned* hist, int BH, int N, hipStream_t stream) {
   const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
@@ -2464,6 +2493,10 @@ void launch_pool(const float* vote, float* pooled, unsigned* hist, int BH, int N
   }
 }
 
+// Single pass: the per-head preparation (reference scores, cleared state),
+// the score pass (raw votes to `vote`; the independent-wave kernel, else the
+// cooperative one), the exact fixup of flagged heads, then pooling +
+// histogram (pooled scores to `pooled` unless it is NULL). Phase marks 1 to 4.
 template <int D>
 kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint16_t* q, kvc_strides qs, int qrow0,
                               const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, float scale_log2,
@@ -2475,19 +2508,24 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   float2* part = reinterpret_cast<float2*>(ws + lay.cpart);
   unsigned* status = reinterpret_cast<unsigned*>(ws + lay.cstatus);
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
+  unsigned* gate = status + 1;
   snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
       q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist,
-      reinterpret_cast<unsigned*>(ws + lay.sel_ctr));
+      reinterpret_cast<unsigned*>(ws + lay.sel_ctr), gate);
   mark_phase(1, stream);
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
   hipError_t e = hipErrorInvalidValue;
   if (Gw > 0) {
-    int nt = static_cast<int>(wave_tiles(L)), total = static_cast<int>(lay.BH * nt), BH = static_cast<int>(lay.BH);
-    void* args[] = {&q,  &qsb,   &qsh, &qst, &qrow0,      &k,    &ksb, &ksh, &kst,  &H,      &L,  &w,
-                    &nt, &total, &BH,  &scale_log2, &cref, &acc, &cnt, &stat, &status, &vote};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(snap_wave_bf16<D>), dim3(Gw), dim3(kWvThreads),
-                                   args, 0, stream);
+    // an ordinary launch: the kernel checks residency itself (a cooperative
+    // launch would guarantee it, at ~10 us of extra queue work on each side)
+    const int nt = static_cast<int>(wave_tiles(L)), total = static_cast<int>(lay.BH * nt);
+    const unsigned target = static_cast<unsigned>(Gw) + (g_force_residency_fail ? 1u : 0u);
+    const unsigned spin = g_force_residency_fail ? 16u : kWvGateSpin;
+    snap_wave_bf16<D><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
+        q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref, acc,
+        cnt, stat, status, vote, gate, target, spin);
+    e = hipGetLastError();
     if (e == hipSuccess) {
       g_last_kernel = "snap_wave_bf16";
       mark_phase(2, stream);
@@ -2532,6 +2570,12 @@ extern "C" int kvc_snapkv_set_schedule(int schedule) {
 extern "C" int kvc_snapkv_last_schedule(void) { return g_last_schedule; }
 
 extern "C" const char* kvc_snapkv_last_score_kernel(void) { return g_last_kernel; }
+
+extern "C" int kvc_snapkv_force_residency_fallback(int on) {
+  const int prev = g_force_residency_fail ? 1 : 0;
+  g_force_residency_fail = on != 0;
+  return prev;
+}
 
 extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
                                              int pool_kernel, kvc_dtype dt) {

@@ -140,6 +140,21 @@ def test_no_optional_outputs(L, w, pool, schedule):
     print(f"[snapkv] {wl.name}: {kinds.count('exact')} exact, {kinds.count('near-tie')} near-tie heads", flush=True)
 
 
+def test_single_pass_residency_fallback():
+    """The score kernel's residency check forced to fail from the host (it waits
+    for one workgroup more than its grid has, briefly): the kernel flags every
+    head, the exact fixup computes all votes, and the results still match the
+    oracle."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=1, H=2, L=70000, budget=1200)
+    lib = kvc.library()
+    prev = lib.kvc_snapkv_force_residency_fallback(1)
+    try:
+        _workload(wl, schedule=kvc.SNAPKV_SINGLE_PASS)
+        assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
+    finally:
+        lib.kvc_snapkv_force_residency_fallback(prev)
+
+
 def test_single_pass_many_heads_unaligned():
     """Heads whose units straddle device-wide rounds (B*H*units not a multiple of the grid)."""
     wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=3, H=7, L=70001, budget=1500)
