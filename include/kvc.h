@@ -136,9 +136,10 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  *                128-key units together, covers shorter heads (a head of at
  *                most four device-wide rounds of units) with a cooperative
  *                launch. Where neither can run, the call uses TWO_PASS.
- *   AUTO         the default: SINGLE_PASS where it can run (the faster of
- *                the two on MI355X at the sizes measured so far), else
- *                TWO_PASS; also TWO_PASS if the cooperative launch fails. */
+ *   AUTO         the default: SINGLE_PASS where snap_wave_bf16 can run
+ *                (there the faster schedule on MI355X), else TWO_PASS (which
+ *                measures faster than snap_coop_bf16 on shorter heads); also
+ *                TWO_PASS if the single-pass launch fails. */
 typedef enum {
   KVC_SNAPKV_AUTO = 0,
   KVC_SNAPKV_TWO_PASS = 1,

@@ -2630,12 +2630,15 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(ws + lay.pooled);
   const int qrow0 = q_len - window;
 
-  // AUTO takes the single pass where it can run (it reads K once and measures
-  // faster on MI355X) and falls back to two passes if the device refuses the
-  // cooperative launch
+  // AUTO takes the single pass where the independent-wave kernel runs (it
+  // reads K once and measures faster there on MI355X), else two passes: the
+  // lockstep single-pass kernel that covers shorter heads measures slower than
+  // two passes (16K-key heads: 0.156 against 0.125 ms per call), so only an
+  // explicit SINGLE_PASS takes it. A failed single-pass launch under AUTO
+  // falls back to two passes.
   const bool try_single = dt == KVC_BF16 && g_schedule != KVC_SNAPKV_TWO_PASS;
   const int Gw = try_single ? wave_grid(lay, D, L, kvs.t, qs.t) : 0;
-  const int Gc = try_single ? coop_grid(lay, D) : 0;
+  const int Gc = try_single && (g_schedule == KVC_SNAPKV_SINGLE_PASS || Gw > 0) ? coop_grid(lay, D) : 0;
   int schedule = KVC_SNAPKV_TWO_PASS;
   mark_phase(0, stream);
   // what the selection reads: the pooled scores, or (single pass, small

@@ -279,7 +279,8 @@ def test_single_pass_logit_overflow(L, kernel):
 
 
 def test_single_pass_kernel_choice():
-    """Long prompts take the independent-wave kernel, short ones the lockstep one."""
+    """Long prompts take the independent-wave kernel, short ones the lockstep one
+    (when the single pass is asked for)."""
     for L, kernel in ((3000, "snap_coop_bf16"), (131072, "snap_wave_bf16")):
         B, H, D = 1, 2, 128
         q = torch.zeros((B, H, 32, D), dtype=torch.bfloat16, device="cuda")
@@ -288,6 +289,12 @@ def test_single_pass_kernel_choice():
         assert kvc.snapkv_last_score_kernel() == kernel, (L, kvc.snapkv_last_score_kernel())
     _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_TWO_PASS)
     assert kvc.snapkv_last_score_kernel() == "snap_stats_bf16+snap_votes_bf16"
+    # AUTO: the independent-wave kernel where it runs, else two passes
+    for L, kernel in ((3000, "snap_stats_bf16+snap_votes_bf16"), (131072, "snap_wave_bf16")):
+        q = torch.zeros((1, 2, 32, 128), dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros((1, 2, L, 128), dtype=torch.bfloat16, device="cuda")
+        _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_AUTO)
+        assert kvc.snapkv_last_score_kernel() == kernel, (L, kvc.snapkv_last_score_kernel())
 
 
 def test_schedule_setting_rejects_unknown():
