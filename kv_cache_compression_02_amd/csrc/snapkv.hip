@@ -1543,32 +1543,6 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.sh = &sh;
   unsigned char* ring0 = ring_even + c.wave * Ly::kTileB;
   unsigned char* ring1 = ring_odd + c.wave * Ly::kTileB;
-  // Residency check, in place of a launch that guarantees it: the waits below
-  // need every workgroup resident at once. Each workgroup counts itself in on
-  // gate[0]; the one whose count reaches gate_target opens the pass (gate[1]:
-  // 0 -> 1). A workgroup still waiting after gate_spin polls closes it
-  // instead (0 -> 2): some workgroups could not start while the others held
-  // the compute units. One compare-and-swap decides, so every workgroup,
-  // late ones included, takes the same branch; when the pass is closed every
-  // head is flagged and snap_fixup_bf16 computes all votes.
-  __shared__ unsigned s_gate;
-  if (threadIdx.x == 0) {
-    if (atomicAdd(&gate[0], 1u) + 1u == gate_target) atomicCAS(&gate[1], 0u, 1u);
-    unsigned st = __hip_atomic_load(&gate[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (unsigned polls = 0; st == 0u && polls < gate_spin; ++polls) {
-      __builtin_amdgcn_s_sleep(2);
-      st = __hip_atomic_load(&gate[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (st == 0u) {
-      const unsigned prev = atomicCAS(&gate[1], 0u, 2u);
-      st = prev == 0u ? 2u : prev;
-    }
-    if (st != 1u)
-      for (int h = 0; h < BH; ++h) atomicOr(&cnt[h * kCoopCtrWords + 16], 1u);
-    s_gate = st;
-  }
-  __syncthreads();
-  if (s_gate != 1u) return;
   if (threadIdx.x == 0) {
     sh.mcnt[0] = sh.mcnt[1] = 0;
     sh.mtag[0] = 0;  // every workgroup has tiles in every head, starting with head 0
@@ -1594,7 +1568,37 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     wv_load_q<D>(c, pos, qf, lane);
     p.rref[0] = ref[lane & 31];
   }
-  __syncthreads();  // the slot counters are set
+  // Residency check, in place of a launch that guarantees it (its wait
+  // overlaps the first tile's loads): the waits below need every workgroup
+  // resident at once. Each workgroup counts itself in on gate[0]; the one
+  // whose count reaches gate_target opens the pass (gate[1]: 0 -> 1). A
+  // workgroup still waiting after gate_spin polls closes it instead (0 -> 2):
+  // some workgroups could not start while the others held the compute units.
+  // One compare-and-swap decides, so every workgroup, late ones included,
+  // takes the same branch; when the pass is closed every head is flagged and
+  // snap_fixup_bf16 computes all votes.
+  __shared__ unsigned s_gate;
+  if (threadIdx.x == 0) {
+    if (atomicAdd(&gate[0], 1u) + 1u == gate_target) atomicCAS(&gate[1], 0u, 1u);
+    unsigned st = __hip_atomic_load(&gate[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (unsigned polls = 0; st == 0u && polls < gate_spin; ++polls) {
+      __builtin_amdgcn_s_sleep(2);
+      st = __hip_atomic_load(&gate[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (st == 0u) {
+      const unsigned prev = atomicCAS(&gate[1], 0u, 2u);
+      st = prev == 0u ? 2u : prev;
+    }
+    if (st != 1u)
+      for (int h = 0; h < BH; ++h) atomicOr(&cnt[h * kCoopCtrWords + 16], 1u);
+    s_gate = st;
+  }
+  __syncthreads();  // also: the slot counters are set
+  if (s_gate != 1u) {
+    wait_vm_all();  // no direct load may still be landing in LDS when the wave ends
+    return;
+  }
+
   f32x16_t sc[kWvBanks];
   f32x16_t ls = {};
   static_assert(kWvBanks == 8, "the round loop below is unrolled over the register banks");
