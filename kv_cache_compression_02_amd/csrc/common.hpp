@@ -47,22 +47,81 @@ __device__ __forceinline__ int popc_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
+// The value x holds in lane (lane ^ K) of the wave, K a power of two below 64.
+// K = 1, 2, 4, 8: DPP moves within each 16-lane row (quad permutations; row
+// shifts by 4 written into alternate 4-lane banks; a row rotation by 8).
+// K = 16, 32: gfx950's lane-swap instructions, which exchange one half of their
+// two operands (odd rows of the first with even rows of the second, or the
+// upper 32 lanes of the first with the lower 32 of the second); with x as both
+// operands, the two results and x hold the partner's value and x twice, so
+// their XOR is the partner's value. A few cycles each, against a round trip
+// through LDS for __shfl_xor (ds_bpermute).
+template <int K>
+__device__ __forceinline__ unsigned lane_xor_u(unsigned x) {
+  static_assert(K == 1 || K == 2 || K == 4 || K == 8 || K == 16 || K == 32, "K: a power of two below 64");
+  const int v = static_cast<int>(x);
+  if constexpr (K == 1) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  } else if constexpr (K == 2) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  } else if constexpr (K == 4) {
+    const int t = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0x5, false);            // row_shl:4, banks 0 and 2
+    return static_cast<unsigned>(__builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false));  // row_shr:4, banks 1 and 3
+  } else if constexpr (K == 8) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else if constexpr (K == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return r[0] ^ r[1] ^ x;
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return r[0] ^ r[1] ^ x;
+  }
+}
+
+template <int K>
+__device__ __forceinline__ float lane_xor(float x) {
+  return __uint_as_float(lane_xor_u<K>(__float_as_uint(x)));
+}
+
+// lane_xor for a stride that is a constant only once the caller's loop is
+// unrolled; any other stride goes through __shfl_xor.
+__device__ __forceinline__ float lane_xor_n(float x, int k) {
+  switch (k) {
+    case 1: return lane_xor<1>(x);
+    case 2: return lane_xor<2>(x);
+    case 4: return lane_xor<4>(x);
+    case 8: return lane_xor<8>(x);
+    case 16: return lane_xor<16>(x);
+    case 32: return lane_xor<32>(x);
+    default: return __shfl_xor(x, k);
+  }
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, lane_xor<32>(x));
+  x = fmaxf(x, lane_xor<16>(x));
+  x = fmaxf(x, lane_xor<8>(x));
+  x = fmaxf(x, lane_xor<4>(x));
+  x = fmaxf(x, lane_xor<2>(x));
+  return fmaxf(x, lane_xor<1>(x));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += lane_xor<32>(x);
+  x += lane_xor<16>(x);
+  x += lane_xor<8>(x);
+  x += lane_xor<4>(x);
+  x += lane_xor<2>(x);
+  return x + lane_xor<1>(x);
 }
 
 __device__ __forceinline__ unsigned wave_sum_u(unsigned x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += lane_xor_u<32>(x);
+  x += lane_xor_u<16>(x);
+  x += lane_xor_u<8>(x);
+  x += lane_xor_u<4>(x);
+  x += lane_xor_u<2>(x);
+  return x + lane_xor_u<1>(x);
 }
 
 // Inclusive prefix sum across the wave (Hillis-Steele over 64 lanes).

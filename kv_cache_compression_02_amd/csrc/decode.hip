@@ -61,14 +61,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(const T* __restric
 #pragma unroll
     for (int e = 0; e < VE; ++e) d = fmaf(qv[e], kv[e], d);
 #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o);  // the row's lanes are adjacent
+    for (int o = LPR / 2; o > 0; o >>= 1) d += lane_xor_n(d, o);  // the row's lanes are adjacent
     sc[st] = row < n ? d * scale_log2 : -INFINITY;
   }
   float m = -INFINITY;
 #pragma unroll
   for (int st = 0; st < S; ++st) m = fmaxf(m, sc[st]);
 #pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  for (int o = LPR; o < kWave; o <<= 1) m = fmaxf(m, lane_xor_n(m, o));
 
   float l = 0.f, ov[VE];
 #pragma unroll
@@ -85,9 +85,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(const T* __restric
   }
 #pragma unroll
   for (int o = LPR; o < kWave; o <<= 1) {
-    l += __shfl_xor(l, o);
+    l += lane_xor_n(l, o);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) ov[e] += __shfl_xor(ov[e], o);
+    for (int e = 0; e < VE; ++e) ov[e] += lane_xor_n(ov[e], o);
   }
   if (lane == 0) {
     s_m[wave] = m;

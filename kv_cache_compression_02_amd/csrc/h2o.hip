@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
       for (int e = 0; e < VE; ++e) dot += qv[e] * kx[e];
     }
 #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    for (int o = LPR / 2; o > 0; o >>= 1) dot += lane_xor_n(dot, o);
     if (j < N && sub == 0) {
       const float s2 = dot * scale_log2;
       s_val[j] = s2;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
 #pragma unroll
     for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) ov[e] += __shfl_xor(ov[e], o);
+      for (int e = 0; e < VE; ++e) ov[e] += lane_xor_n(ov[e], o);
     if (grp == 0)
 #pragma unroll
       for (int e = 0; e < VE; ++e) ored[wave][sub * VE + e] = ov[e];
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void h2o_prefill_stats_bf16(
     l_run = l_run * fast_exp2(m_run - mnew) + add;
     m_run = mnew;
   }
-  lse2_merge(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
+  lse2_merge(m_run, l_run, lane_xor<32>(m_run), lane_xor<32>(l_run));
   if (half == 0) wred[wave][col] = make_float2(m_run, l_run);
   __syncthreads();
   if (threadIdx.x < 32 && qt * kPTile + static_cast<int>(threadIdx.x) < Lp) {
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void h2o_prefill_colsum_bf16(
       }
     }
   }
-  csum += __shfl_xor(csum, 32);
+  csum += lane_xor<32>(csum);
   if (half == 0) wsum[wave][col] = csum;
   __syncthreads();
   if (threadIdx.x < 32 && kt * kPTile + static_cast<int>(threadIdx.x) < Lp) {

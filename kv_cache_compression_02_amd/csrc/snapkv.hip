@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
     }
   }
   // lanes col and col+32 hold the same query
-  lse2_merge(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
+  lse2_merge(m_run, l_run, lane_xor<32>(m_run), lane_xor<32>(l_run));
   __shared__ float2 wred[kWaves][32];
   if (half == 0) wred[wave][col] = make_float2(m_run, l_run);
   __syncthreads();
@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kThreads) void snap_stats_f32(
   for (int c = seg * 32; c < seg * 32 + 32; ++c) m = fmaxf(m, ss[row][c]);
   float l = 0.f;
   for (int c = seg * 32; c < seg * 32 + 32; ++c) l += fast_exp2(ss[row][c] - m);
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) lse2_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+  lse2_merge(m, l, lane_xor<1>(m), lane_xor<1>(l));
+  lse2_merge(m, l, lane_xor<2>(m), lane_xor<2>(l));
+  lse2_merge(m, l, lane_xor<4>(m), lane_xor<4>(l));
   if (seg == 0) part[(static_cast<int64_t>(bh) * nchunk + chunk) * 32 + row] = make_float2(m, l);
 }
 
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     float v = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) v += fast_exp2(acc[i] * scale_log2 - mr[i]) * il[i];
-    v += __shfl_xor(v, 32);
+    v += lane_xor<32>(v);
     const int j = tile + col;
     if (half == 0 && j < e1) {
       sv[j - e0] = v;
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
       const int j = acc_row(i, half);
       if (j <= col && j < w) m = fmaxf(m, sc[i] * scale_log2);
     }
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = fmaxf(m, lane_xor<32>(m));
     if (half == 0) ref[bh * 32 + col] = m;
   }
 }
@@ -843,7 +844,7 @@ __device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
         v += row < c.w ? fast_exp2(s[i] - c.s_c[row]) : 0.f;
       }
     }
-    v += __shfl_xor(v, 32);
+    v += lane_xor<32>(v);
     const int j = c0 + c.wave * kTile + c.col;
     if (c.half == 0 && j < c.t0) c.vote[static_cast<int64_t>(bh) * c.t0 + j] = v;
   }
@@ -884,7 +885,7 @@ __device__ __forceinline__ void coop_round(const CoopCtx& c, CoopPipe& p,
     for (int i = 0; i < 16; ++i) l += fast_exp2(bt[i] - m);
     lds_barrier();  // staged Q consumed
     if (r + 1 < c.rounds) coop_issue_q<D>(c, p, r + 1);
-    lse2_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
+    lse2_merge(m, l, lane_xor<32>(m), lane_xor<32>(l));
     if (c.half == 0) c.wred[c.wave][c.col] = make_float2(m, l);
     lds_barrier();
     if (c.wave == 3) {
@@ -1211,8 +1212,8 @@ __device__ __forceinline__ float wv_words_to_w(const WvFin& f, int lane, unsigne
       t += __builtin_amdgcn_ldexp(d, e0 + 16 * k);
     }
   }
-  t += __shfl_xor(t, 32);
-  count = n + __shfl_xor(n, 32);
+  t += lane_xor<32>(t);
+  count = n + lane_xor_u<32>(n);
   ovf = o;
   return t > 0.0 ? static_cast<float>(1.0 / t) : 0.f;
 }
@@ -1360,7 +1361,7 @@ __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, c
 #pragma unroll
     for (int e = 0; e < 4; ++e) v = fmaf(s[4 * a + e], ww[e], v);
   }
-  v += __shfl_xor(v, 32);
+  v += lane_xor<32>(v);
   const int j = tv * kTile + row;
   float* vrow = c.vote + static_cast<int64_t>(hv) * c.t0 + tv * kTile;  // uniform
   if (half == 0 && j < c.t0) *reinterpret_cast<float*>(reinterpret_cast<char*>(vrow) + static_cast<unsigned>(row) * 4u) = v;
@@ -1389,13 +1390,13 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f3
                  m8 = opaque(-((ln >> 3) & 1));
   float x8[8], x4[4], x2[2], x1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x8[i] = lane_pick(ls[i + 8], ls[i], m1) + __shfl_xor(lane_pick(ls[i], ls[i + 8], m1), 1);
+  for (int i = 0; i < 8; ++i) x8[i] = lane_pick(ls[i + 8], ls[i], m1) + lane_xor<1>(lane_pick(ls[i], ls[i + 8], m1));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) x4[i] = lane_pick(x8[i + 4], x8[i], m2) + __shfl_xor(lane_pick(x8[i], x8[i + 4], m2), 2);
+  for (int i = 0; i < 4; ++i) x4[i] = lane_pick(x8[i + 4], x8[i], m2) + lane_xor<2>(lane_pick(x8[i], x8[i + 4], m2));
 #pragma unroll
-  for (int i = 0; i < 2; ++i) x2[i] = lane_pick(x4[i + 2], x4[i], m4) + __shfl_xor(lane_pick(x4[i], x4[i + 2], m4), 4);
-  x1 = lane_pick(x2[1], x2[0], m8) + __shfl_xor(lane_pick(x2[0], x2[1], m8), 8);
-  x1 += __shfl_xor(x1, 16);
+  for (int i = 0; i < 2; ++i) x2[i] = lane_pick(x4[i + 2], x4[i], m4) + lane_xor<4>(lane_pick(x4[i], x4[i + 2], m4));
+  x1 = lane_pick(x2[1], x2[0], m8) + lane_xor<8>(lane_pick(x2[0], x2[1], m8));
+  x1 += lane_xor<16>(x1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) ls[i] = 0.f;
   const int r = ((ln & 1) << 3) | ((ln & 2) << 1) | ((ln & 4) >> 1) | ((ln & 8) >> 3);
@@ -1665,8 +1666,12 @@ __global__ __launch_bounds__(kThreads) void snap_fixup_bf16(
   }
 #pragma unroll
   for (int i = 0; i < kMaxWindow; ++i) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lse2_merge(m[i], l[i], __shfl_xor(m[i], o), __shfl_xor(l[i], o));
+    lse2_merge(m[i], l[i], lane_xor<32>(m[i]), lane_xor<32>(l[i]));
+    lse2_merge(m[i], l[i], lane_xor<16>(m[i]), lane_xor<16>(l[i]));
+    lse2_merge(m[i], l[i], lane_xor<8>(m[i]), lane_xor<8>(l[i]));
+    lse2_merge(m[i], l[i], lane_xor<4>(m[i]), lane_xor<4>(l[i]));
+    lse2_merge(m[i], l[i], lane_xor<2>(m[i]), lane_xor<2>(l[i]));
+    lse2_merge(m[i], l[i], lane_xor<1>(m[i]), lane_xor<1>(l[i]));
     if (lane_id() == 0) {
       red_m[wave][i] = m[i];
       red_l[wave][i] = l[i];
