@@ -100,7 +100,7 @@ __device__ unsigned long long evict_threshold(const float* s_val, const int* s_p
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void h2o_step_kernel(
+__global__ __launch_bounds__(kThreads, 8) void h2o_step_kernel(
     char* __restrict__ kc, char* __restrict__ vc, int* __restrict__ pos_g, float* __restrict__ acc_g,
     int cap, int n, int new_pos, const char* __restrict__ q, const char* __restrict__ kn,
     const char* __restrict__ vn, int n_heavy, int n_recent, float scale_log2, float* __restrict__ out) {
@@ -137,23 +137,32 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
   float qv[VE];
   Vec16<T>::load(q + static_cast<int64_t>(bh) * RB + sub * 16, qv);
 
-  // Scores of all N slots; the new token's key is read from k_new.
+  // Scores of all N slots; the new token's key is read from k_new. kStepRows
+  // row groups per iteration, their loads all issued before any is used.
+  constexpr int kStepRows = D >= 128 ? 4 : 2;
   float lmax = -INFINITY;
-  for (int j0 = wave * RPW; j0 < N; j0 += kWaves * RPW) {
-    const int j = j0 + grp;
-    float dot = 0.f;
-    if (j < N) {
-      float kx[VE];
-      Vec16<T>::load((j < n ? kb + static_cast<int64_t>(j) * RB : knr) + sub * 16, kx);
+  for (int j0 = wave * RPW; j0 < N; j0 += kWaves * RPW * kStepRows) {
+    float kx[kStepRows][VE];
 #pragma unroll
-      for (int e = 0; e < VE; ++e) dot += qv[e] * kx[e];
+    for (int u = 0; u < kStepRows; ++u) {
+      const int j = j0 + u * kWaves * RPW + grp;
+      if (j < N) Vec16<T>::load((j < n ? kb + static_cast<int64_t>(j) * RB : knr) + sub * 16, kx[u]);
     }
 #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) dot += lane_xor_n(dot, o);
-    if (j < N && sub == 0) {
-      const float s2 = dot * scale_log2;
-      s_val[j] = s2;
-      lmax = fmaxf(lmax, s2);
+    for (int u = 0; u < kStepRows; ++u) {
+      const int j = j0 + u * kWaves * RPW + grp;
+      float dot = 0.f;
+      if (j < N) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) dot += qv[e] * kx[u][e];
+      }
+#pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) dot += lane_xor_n(dot, o);
+      if (j < N && sub == 0) {
+        const float s2 = dot * scale_log2;
+        s_val[j] = s2;
+        lmax = fmaxf(lmax, s2);
+      }
     }
   }
   for (int j = threadIdx.x; j < N; j += kThreads) s_pos[j] = j < n ? pos_g[slot0 + j] : new_pos;
@@ -168,14 +177,21 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(
     float ov[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) ov[e] = 0.f;
-    for (int j0 = wave * RPW; j0 < N; j0 += kWaves * RPW) {
-      const int j = j0 + grp;
-      if (j < N) {
-        const float p = fast_exp2(s_val[j] - m2) * inv;
-        float vx[VE];
-        Vec16<T>::load((j < n ? vb + static_cast<int64_t>(j) * RB : vnr) + sub * 16, vx);
+    for (int j0 = wave * RPW; j0 < N; j0 += kWaves * RPW * kStepRows) {
+      float vx[kStepRows][VE];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) ov[e] += p * vx[e];
+      for (int u = 0; u < kStepRows; ++u) {
+        const int j = j0 + u * kWaves * RPW + grp;
+        if (j < N) Vec16<T>::load((j < n ? vb + static_cast<int64_t>(j) * RB : vnr) + sub * 16, vx[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kStepRows; ++u) {
+        const int j = j0 + u * kWaves * RPW + grp;
+        if (j < N) {
+          const float p = fast_exp2(s_val[j] - m2) * inv;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) ov[e] += p * vx[u][e];
+        }
       }
     }
 #pragma unroll
