@@ -28,8 +28,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 PHASES = ["zero", "stats", "merge", "votes", "select", "gather"]
 # the same boundaries under the single-pass schedule: the preparation kernel,
-# the score kernel, its overflow fixup, pooling + histogram, then the shared phases
-PHASES_SINGLE = ["prep", "score", "fixup", "pool", "select", "gather"]
+# the score kernel, (nothing), pooling + histogram, then the shared phases
+PHASES_SINGLE = ["prep", "score", "none", "pool", "select", "gather"]
 SCHEDULES = {"auto": 0, "two-pass": 1, "single-pass": 2}
 
 

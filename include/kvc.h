@@ -130,9 +130,9 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  *                about 64K to 320K keys per head); it is launched like any
  *                kernel and checks residency at its start: if its workgroups
  *                cannot all start within about a millisecond (other work
- *                holding the compute units), it flags every head and a plain
- *                exact kernel computes the votes instead (the same results,
- *                far slower). snap_coop_bf16, whose workgroups step through
+ *                holding the compute units), it flags every head and the
+ *                pooling kernel computes their votes exactly instead (the
+ *                same results, far slower). snap_coop_bf16, whose workgroups step through
  *                128-key units together, covers shorter heads (a head of at
  *                most four device-wide rounds of units) with a cooperative
  *                launch. Where neither can run, the call uses TWO_PASS.
@@ -164,7 +164,7 @@ const char* kvc_snapkv_last_score_kernel(void);
  * thread's single-pass calls run the independent-wave score kernel with a
  * residency check that cannot pass (it waits for one workgroup more than the
  * grid holds, 16 polls), so the kernel takes its fallback: it flags every head
- * and the exact fixup kernel computes all votes, as when the kernel's
+ * and the pooling kernel computes all votes exactly, as when the kernel's
  * workgroups cannot all be resident at once. Returns the previous setting. */
 int kvc_snapkv_force_residency_fallback(int on);
 
@@ -175,8 +175,7 @@ int kvc_snapkv_force_residency_fallback(int on);
  * first kernel, then after the workspace clear (1; the single pass's
  * preparation kernel under SINGLE_PASS), the row-statistics pass (2; the
  * single score kernel under SINGLE_PASS), the row-statistics merge (3; nothing
- * separate under TWO_PASS, the score-overflow fixup kernel under SINGLE_PASS,
- * if any), the vote + pooling + histogram pass (4;
+ * separate under either schedule), the vote + pooling + histogram pass (4;
  * pooling + histogram under SINGLE_PASS), the per-head selection (5) and the
  * gather (6). The events are created and owned by the caller; pass NULL or 0
  * to stop recording. */

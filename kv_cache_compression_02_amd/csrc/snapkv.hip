@@ -998,8 +998,8 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
 // step takes a round and none of them holds up the K stream.
 //
 // e_ij is finite unless a score exceeds its row's reference by 2^127; such a
-// head is flagged and its votes are recomputed afterwards by
-// snap_fixup_bf16 (the usual path's votes of that head are discarded).
+// head is flagged and the pooling kernel recomputes its votes exactly (the
+// usual path's votes of that head are discarded).
 //
 // Registers: the eight banks (128), Q (32), the MFMA accumulator and the row
 // sums fill most of the 256 a wave has at two waves per SIMD, so every
@@ -1577,7 +1577,7 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   // some workgroups could not start while the others held the compute units.
   // One compare-and-swap decides, so every workgroup, late ones included,
   // takes the same branch; when the pass is closed every head is flagged and
-  // snap_fixup_bf16 computes all votes.
+  // the pooling kernel computes all votes exactly.
   __shared__ unsigned s_gate;
   if (threadIdx.x == 0) {
     if (atomicAdd(&gate[0], 1u) + 1u == gate_target) atomicCAS(&gate[1], 0u, 1u);
@@ -1624,81 +1624,122 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
 }
 
 // Exact votes of the heads the single pass flagged (a score more than 2^127
-// above its row's reference, or every head when its workgroups could not all
-// be resident): one workgroup per head, two plain passes over
-// the head's keys in fp32 (row maxima and sums of 2^(s - m), then the votes
-// with c_i = m_i + log2 l_i); a head that is not flagged returns at once.
-template <int D>
-__global__ __launch_bounds__(kThreads) void snap_fixup_bf16(
-    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
-    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
-    const unsigned* __restrict__ cnt, float* __restrict__ vote) {
-  const int bh = blockIdx.x;
-  if (cnt[bh * kCoopCtrWords + 16] == 0u) return;
-  __shared__ float qs[kMaxWindow][D];
-  __shared__ float red_m[kThreads / kWave][kMaxWindow], red_l[kThreads / kWave][kMaxWindow];
-  __shared__ float cst[kMaxWindow];
-  const int b = bh / H, h = bh - b * H, t0 = L - w, wave = threadIdx.x / kWave;
-  for (int i = threadIdx.x; i < kMaxWindow * D; i += kThreads) {
-    const int rr = i / D, d = i - rr * D;
-    qs[rr][d] = rr < w ? bf16_to_f32(q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rr) * qst + d]) : 0.f;
+// above its row's reference, or every head when the independent-wave kernel's
+// workgroups could not all be resident), recomputed in fp32 by the pooling
+// kernel's workgroups, each for the positions it pools: one plain pass over
+// the head's keys gives every window row's (max, sum of 2^(s - m)), then the
+// vote of a position is sum_i 2^(s_i - c_i) with c_i = m_i + log2 sum_i.
+// Every workgroup of a flagged head repeats the first pass: a fallback for
+// inputs far outside the usual range, not a fast path.
+struct ExactArgs {
+  const uint16_t* q;
+  int64_t qsb, qsh, qst;
+  int qrow0;
+  const uint16_t* k;
+  int64_t ksb, ksh, kst;
+  int H, L, w, D;
+  float scale_log2;
+  const unsigned* flags;  // per head at word 16 of its counters; NULL: no head is flagged
+};
+
+struct ExactShared {
+  float qs[kMaxWindow][128];
+  float red_m[kWaves][kMaxWindow], red_l[kWaves][kMaxWindow];
+  float cst[kMaxWindow];
+};
+
+// A pooling workgroup's LDS: the histogram, or (before it, for a flagged
+// head) the exact recomputation's rows and statistics.
+union PoolShared {
+  unsigned sh[kHistBins];
+  ExactShared es;
+};
+
+__device__ __forceinline__ bool exact_flagged(const ExactArgs& a, int bh) {
+  return a.flags && a.flags[bh * kCoopCtrWords + 16] != 0u;
+}
+
+// Rows 8g .. 8g+7 of the window's fp32 scores against key j (rows past w
+// are zero rows). Eight rows at a time keep the fallback's registers few: the
+// pooling kernels that carry it must keep their occupancy.
+constexpr int kExactRows = 8;
+
+__device__ __forceinline__ void exact_scores(const ExactShared& e, const ExactArgs& a, const uint16_t* kb, int j,
+                                             int g, float (&s)[kExactRows]) {
+#pragma unroll
+  for (int i = 0; i < kExactRows; ++i) s[i] = 0.f;
+  for (int d = 0; d < a.D; ++d) {
+    const float kv = bf16_to_f32(kb[static_cast<int64_t>(j) * a.kst + d]);
+#pragma unroll
+    for (int i = 0; i < kExactRows; ++i) s[i] = fmaf(e.qs[g * kExactRows + i][d], kv, s[i]);
+  }
+}
+
+// The head's window rows into LDS, then c_i from one pass over its keys per
+// group of rows (every thread of the workgroup calls it).
+__device__ void exact_prepare(ExactShared& e, const ExactArgs& a, int bh) {
+  const int b = bh / a.H, h = bh - b * a.H, t0 = a.L - a.w, wave = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kMaxWindow * a.D; i += kThreads) {
+    const int rr = i / a.D, d = i - rr * a.D;
+    e.qs[rr][d] = rr < a.w ? bf16_to_f32(a.q[b * a.qsb + h * a.qsh + static_cast<int64_t>(a.qrow0 + rr) * a.qst + d])
+                           : 0.f;
   }
   __syncthreads();
-  const uint16_t* kb = k + b * ksb + h * ksh;
-  float m[kMaxWindow], l[kMaxWindow];
+  const uint16_t* kb = a.k + b * a.ksb + h * a.ksh;
+#pragma unroll 1
+  for (int g = 0; g < kMaxWindow / kExactRows; ++g) {
+    float m[kExactRows], l[kExactRows];
 #pragma unroll
-  for (int i = 0; i < kMaxWindow; ++i) {
-    m[i] = kNegBig;
-    l[i] = 0.f;
-  }
-  for (int j = threadIdx.x; j < L; j += kThreads) {
-    float s[kMaxWindow];
+    for (int i = 0; i < kExactRows; ++i) {
+      m[i] = kNegBig;
+      l[i] = 0.f;
+    }
+    for (int j = threadIdx.x; j < a.L; j += kThreads) {
+      float s[kExactRows];
+      exact_scores(e, a, kb, j, g, s);
 #pragma unroll
-    for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
-    for (int d = 0; d < D; ++d) {
-      const float kv = bf16_to_f32(kb[static_cast<int64_t>(j) * kst + d]);
-#pragma unroll
-      for (int i = 0; i < kMaxWindow; ++i) s[i] = fmaf(qs[i][d], kv, s[i]);
+      for (int i = 0; i < kExactRows; ++i) {
+        const int row = g * kExactRows + i;
+        if (row < a.w && j <= t0 + row) lse2_merge(m[i], l[i], s[i] * a.scale_log2, 1.f);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < kMaxWindow; ++i)
-      if (i < w && j <= t0 + i) lse2_merge(m[i], l[i], s[i] * scale_log2, 1.f);
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxWindow; ++i) {
-    lse2_merge(m[i], l[i], lane_xor<32>(m[i]), lane_xor<32>(l[i]));
-    lse2_merge(m[i], l[i], lane_xor<16>(m[i]), lane_xor<16>(l[i]));
-    lse2_merge(m[i], l[i], lane_xor<8>(m[i]), lane_xor<8>(l[i]));
-    lse2_merge(m[i], l[i], lane_xor<4>(m[i]), lane_xor<4>(l[i]));
-    lse2_merge(m[i], l[i], lane_xor<2>(m[i]), lane_xor<2>(l[i]));
-    lse2_merge(m[i], l[i], lane_xor<1>(m[i]), lane_xor<1>(l[i]));
-    if (lane_id() == 0) {
-      red_m[wave][i] = m[i];
-      red_l[wave][i] = l[i];
+    for (int i = 0; i < kExactRows; ++i) {
+      lse2_merge(m[i], l[i], lane_xor<32>(m[i]), lane_xor<32>(l[i]));
+      lse2_merge(m[i], l[i], lane_xor<16>(m[i]), lane_xor<16>(l[i]));
+      lse2_merge(m[i], l[i], lane_xor<8>(m[i]), lane_xor<8>(l[i]));
+      lse2_merge(m[i], l[i], lane_xor<4>(m[i]), lane_xor<4>(l[i]));
+      lse2_merge(m[i], l[i], lane_xor<2>(m[i]), lane_xor<2>(l[i]));
+      lse2_merge(m[i], l[i], lane_xor<1>(m[i]), lane_xor<1>(l[i]));
+      if (lane_id() == 0) {
+        e.red_m[wave][g * kExactRows + i] = m[i];
+        e.red_l[wave][g * kExactRows + i] = l[i];
+      }
     }
   }
   __syncthreads();
   if (threadIdx.x < kMaxWindow) {
-    float mm = red_m[0][threadIdx.x], ll = red_l[0][threadIdx.x];
-    for (int wv = 1; wv < kThreads / kWave; ++wv) lse2_merge(mm, ll, red_m[wv][threadIdx.x], red_l[wv][threadIdx.x]);
-    cst[threadIdx.x] = mm + __builtin_amdgcn_logf(ll);
+    float mm = e.red_m[0][threadIdx.x], ll = e.red_l[0][threadIdx.x];
+    for (int wv = 1; wv < kWaves; ++wv) lse2_merge(mm, ll, e.red_m[wv][threadIdx.x], e.red_l[wv][threadIdx.x]);
+    e.cst[threadIdx.x] = mm + __builtin_amdgcn_logf(ll);
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < t0; j += kThreads) {
-    float s[kMaxWindow];
+}
+
+// The exact vote of prefix position j of head bh (after exact_prepare).
+__device__ float exact_vote(const ExactShared& e, const ExactArgs& a, int bh, int j) {
+  const int b = bh / a.H, h = bh - b * a.H;
+  const uint16_t* kb = a.k + b * a.ksb + h * a.ksh;
+  float v = 0.f;
+#pragma unroll 1
+  for (int g = 0; g < kMaxWindow / kExactRows; ++g) {
+    float s[kExactRows];
+    exact_scores(e, a, kb, j, g, s);
 #pragma unroll
-    for (int i = 0; i < kMaxWindow; ++i) s[i] = 0.f;
-    for (int d = 0; d < D; ++d) {
-      const float kv = bf16_to_f32(kb[static_cast<int64_t>(j) * kst + d]);
-#pragma unroll
-      for (int i = 0; i < kMaxWindow; ++i) s[i] = fmaf(qs[i][d], kv, s[i]);
-    }
-    float v = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxWindow; ++i)
-      if (i < w) v += fast_exp2(s[i] * scale_log2 - cst[i]);
-    vote[static_cast<int64_t>(bh) * t0 + j] = v;
+    for (int i = 0; i < kExactRows; ++i)
+      if (g * kExactRows + i < a.w) v += fast_exp2(s[i] * a.scale_log2 - e.cst[g * kExactRows + i]);
   }
+  return v;
 }
 
 // Max-pool of raw votes (neighbours beyond the prefix ignored) and the
@@ -1712,17 +1753,29 @@ constexpr int kPoolChunk = kThreads * kPoolPer;
 constexpr int kPoolRegRadius = 7;  // larger radii pool from LDS (snap_pool_lds)
 
 template <int R, bool VEC>
-__global__ __launch_bounds__(kThreads) void snap_pool(const float* __restrict__ vote, float* __restrict__ pooled,
-                                                      unsigned* __restrict__ hist, int N) {
+__global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, float* __restrict__ pooled,
+                                                      unsigned* __restrict__ hist, int N, const ExactArgs ea) {
   // pooled may be NULL: then only the histogram is produced
   constexpr int kHalo = (R + 3) / 4 * 4;
   constexpr int kX = kPoolPer + 2 * kHalo;
-  __shared__ unsigned sh[kHistBins];
+  __shared__ PoolShared ps;
+  unsigned* sh = ps.sh;
   const int bh = blockIdx.y;
   const int j0 = (static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x)) * kPoolPer;
-  const float* vb = vote + static_cast<int64_t>(bh) * N;
+  float* vb = vote + static_cast<int64_t>(bh) * N;
   float x[kX];
-  if (VEC && j0 >= kHalo && j0 + kPoolPer + kHalo <= N) {
+  if (exact_flagged(ea, bh)) {
+    // exact votes (halo included) for a flagged head; the thread's own
+    // positions go back to the vote buffer, where the selection and the
+    // caller read them
+    exact_prepare(ps.es, ea, bh);
+    for (int i = 0; i < kX; ++i) {
+      const int j = j0 - kHalo + i;
+      x[i] = j >= 0 && j < N ? exact_vote(ps.es, ea, bh, j) : -__builtin_huge_valf();
+      if (i >= kHalo && i < kHalo + kPoolPer && j < N) vb[j] = x[i];
+    }
+    __syncthreads();  // the rows are read before the histogram reuses their LDS
+  } else if (VEC && j0 >= kHalo && j0 + kPoolPer + kHalo <= N) {
 #pragma unroll
     for (int p = 0; p < kX / 4; ++p) {
       const f32x4_t f = *reinterpret_cast<const f32x4_t*>(vb + j0 - kHalo + 4 * p);
@@ -1782,17 +1835,27 @@ __global__ __launch_bounds__(kThreads) void snap_pool(const float* __restrict__ 
 
 // The same for pooling radii beyond kPoolRegRadius: the chunk's votes and halo
 // staged in LDS, one output position per thread and step.
-__global__ __launch_bounds__(kThreads) void snap_pool_lds(const float* __restrict__ vote,
-                                                          float* __restrict__ pooled,
-                                                          unsigned* __restrict__ hist, int N, int r) {
+__global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vote, float* __restrict__ pooled,
+                                                          unsigned* __restrict__ hist, int N, int r,
+                                                          const ExactArgs ea) {
   __shared__ float sv[kPoolChunk + 2 * kMaxPoolRadius];
-  __shared__ unsigned sh[kHistBins];
+  __shared__ PoolShared ps;
+  unsigned* sh = ps.sh;
   const int chunk = blockIdx.x, bh = blockIdx.y;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
   const int c0 = chunk * kPoolChunk, c1 = min(N, c0 + kPoolChunk);
   const int e0 = max(0, c0 - r), e1 = min(N, c1 + r);
-  const float* vb = vote + static_cast<int64_t>(bh) * N;
-  for (int j = e0 + static_cast<int>(threadIdx.x); j < e1; j += kThreads) sv[j - e0] = vb[j];
+  float* vb = vote + static_cast<int64_t>(bh) * N;
+  if (exact_flagged(ea, bh)) {  // exact votes of a flagged head, as in snap_pool
+    exact_prepare(ps.es, ea, bh);
+    for (int j = e0 + static_cast<int>(threadIdx.x); j < e1; j += kThreads) {
+      sv[j - e0] = exact_vote(ps.es, ea, bh, j);
+      if (j >= c0 && j < c1) vb[j] = sv[j - e0];
+    }
+    __syncthreads();  // the rows are read before the histogram reuses their LDS
+  } else {
+    for (int j = e0 + static_cast<int>(threadIdx.x); j < e1; j += kThreads) sv[j - e0] = vb[j];
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
   __syncthreads();
   pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * N, sh);
   __syncthreads();
@@ -2474,38 +2537,41 @@ thread_local const char* g_last_kernel = "";
 thread_local bool g_force_residency_fail = false;
 
 template <int R>
-void launch_pool_r(const float* vote, float* pooled, unsigned* hist, int BH, int N, hipStream_t stream) {
+void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, const ExactArgs& ea,
+                   hipStream_t stream) {
   const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
   if (N % 4 == 0 && aligned16(vote) && (!pooled || aligned16(pooled)))
-    snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N);
+    snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, ea);
   else
-    snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N);
+    snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, ea);
 }
 
 // Max-pool of the raw votes with the histogram of the results (pooled scores
 // stored if `pooled` is not NULL; radii beyond kPoolRegRadius always store them).
-void launch_pool(const float* vote, float* pooled, unsigned* hist, int BH, int N, int r, hipStream_t stream) {
+void launch_pool(float* vote, float* pooled, unsigned* hist, int BH, int N, int r, const ExactArgs& ea,
+                 hipStream_t stream) {
   static_assert(kPoolRegRadius == 7, "the cases below cover radii 0 .. kPoolRegRadius");
   switch (r) {
-    case 0: return launch_pool_r<0>(vote, pooled, hist, BH, N, stream);
-    case 1: return launch_pool_r<1>(vote, pooled, hist, BH, N, stream);
-    case 2: return launch_pool_r<2>(vote, pooled, hist, BH, N, stream);
-    case 3: return launch_pool_r<3>(vote, pooled, hist, BH, N, stream);
-    case 4: return launch_pool_r<4>(vote, pooled, hist, BH, N, stream);
-    case 5: return launch_pool_r<5>(vote, pooled, hist, BH, N, stream);
-    case 6: return launch_pool_r<6>(vote, pooled, hist, BH, N, stream);
-    case 7: return launch_pool_r<7>(vote, pooled, hist, BH, N, stream);
+    case 0: return launch_pool_r<0>(vote, pooled, hist, BH, N, ea, stream);
+    case 1: return launch_pool_r<1>(vote, pooled, hist, BH, N, ea, stream);
+    case 2: return launch_pool_r<2>(vote, pooled, hist, BH, N, ea, stream);
+    case 3: return launch_pool_r<3>(vote, pooled, hist, BH, N, ea, stream);
+    case 4: return launch_pool_r<4>(vote, pooled, hist, BH, N, ea, stream);
+    case 5: return launch_pool_r<5>(vote, pooled, hist, BH, N, ea, stream);
+    case 6: return launch_pool_r<6>(vote, pooled, hist, BH, N, ea, stream);
+    case 7: return launch_pool_r<7>(vote, pooled, hist, BH, N, ea, stream);
     default: {
       const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
-      snap_pool_lds<<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, r);
+      snap_pool_lds<<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, r, ea);
     }
   }
 }
 
 // Single pass: the per-head preparation (reference scores, cleared state),
 // the score pass (raw votes to `vote`; the independent-wave kernel, else the
-// cooperative one), the exact fixup of flagged heads, then pooling +
-// histogram (pooled scores to `pooled` unless it is NULL). Phase marks 1 to 4.
+// cooperative one), then pooling + histogram (pooled scores to `pooled`
+// unless it is NULL; after the independent-wave kernel, exact votes of any
+// flagged head first). Phase marks 1 to 4.
 template <int D>
 kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint16_t* q, kvc_strides qs, int qrow0,
                               const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, float scale_log2,
@@ -2525,6 +2591,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
   hipError_t e = hipErrorInvalidValue;
+  ExactArgs ea{q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, D, scale_log2, nullptr};
   if (Gw > 0) {
     // an ordinary launch: the kernel checks residency itself (a cooperative
     // launch would guarantee it, at ~10 us of extra queue work on each side)
@@ -2538,9 +2605,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
     if (e == hipSuccess) {
       g_last_kernel = "snap_wave_bf16";
       mark_phase(2, stream);
-      // votes of any head flagged for a score beyond the offset's range, exactly
-      snap_fixup_bf16<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
-          q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, scale_log2, cnt, vote);
+      ea.flags = cnt;  // the pooling kernel recomputes the votes of flagged heads exactly
     } else {
       (void)hipGetLastError();
     }
@@ -2558,7 +2623,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   }
   if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
   mark_phase(3, stream);
-  launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, stream);
+  launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, ea, stream);
   mark_phase(4, stream);
   return KVC_OK;
 }

@@ -140,12 +140,13 @@ def test_no_optional_outputs(L, w, pool, schedule):
     print(f"[snapkv] {wl.name}: {kinds.count('exact')} exact, {kinds.count('near-tie')} near-tie heads", flush=True)
 
 
-def test_single_pass_residency_fallback():
+@pytest.mark.parametrize("pool", [7, 17])
+def test_single_pass_residency_fallback(pool):
     """The score kernel's residency check forced to fail from the host (it waits
     for one workgroup more than its grid has, briefly): the kernel flags every
-    head, the exact fixup computes all votes, and the results still match the
-    oracle."""
-    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=1, H=2, L=70000, budget=1200)
+    head, the pooling kernel (register windows for p = 7, the LDS path for
+    p = 17) computes all votes exactly, and the results still match the oracle."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=1, H=2, L=70000, budget=1200, pool_kernel=pool)
     lib = kvc.library()
     prev = lib.kvc_snapkv_force_residency_fallback(1)
     try:
