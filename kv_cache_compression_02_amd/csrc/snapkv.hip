@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     qs[rr][d] = rr < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rr) * qst + d] : 0.f;
   }
   merge_stats_to_lds(bh, nchunk, part, st);
-  if (threadIdx.x < kMaxWindow && threadIdx.x >= w) st[threadIdx.x] = make_float2(0.f, 0.f);
+  if (threadIdx.x < kMaxWindow && static_cast<int>(threadIdx.x) >= w) st[threadIdx.x] = make_float2(0.f, 0.f);
   __syncthreads();
   const int c0 = chunk * kChunkF32, c1 = min(t0, c0 + kChunkF32);
   const int e0 = max(0, c0 - r), e1 = min(t0, c1 + r);
@@ -426,6 +426,7 @@ constexpr int kCoopRowWords = 544;           // row stride in 64-bit words: 4 KB
                                              // rows' atomics spread over memory channels
 constexpr int kCoopHeadWords = 32 * kCoopRowWords;
 constexpr int kCoopFinWords = 24;            // words per row the finisher stages (room for the carries)
+static_assert(kCoopWords < kCoopFinWords, "the staged words must hold every term's word and its carries");
 constexpr int kCoopCtrWords = 32;            // per head: [0] unit count, [16] overflow flag
 constexpr float kCoopOvfGap = 150.f;
 constexpr unsigned kCoopSpin = 1u << 22;
@@ -439,10 +440,6 @@ __device__ __forceinline__ uint2 ld_agent_u2(const uint2* p) {
   const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
   return make_uint2(static_cast<unsigned>(u), static_cast<unsigned>(u >> 32));
-}
-
-__device__ __forceinline__ unsigned long long ld_agent_u64(const unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -748,7 +745,7 @@ __device__ __forceinline__ void coop_bookkeeping(const CoopCtx& c, CoopPipe& p, 
   // (b) the count raised last round: the last contribution makes this
   // workgroup the finisher; stage the head's words in LDS
   if (p.cnt_head >= 0) {
-    if (__builtin_amdgcn_readfirstlane(p.cnt_ret) == static_cast<unsigned>(c.cnt_target - 1)) {
+    if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(p.cnt_ret)) == static_cast<unsigned>(c.cnt_target - 1)) {
       const unsigned long long* a = c.acc + static_cast<int64_t>(p.cnt_head) * kCoopHeadWords;
       constexpr int kPieces = 32 * kCoopFinWords / 2;  // 16-byte pieces
 #pragma unroll
@@ -1312,7 +1309,7 @@ __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane
 // waits for something it owes itself.
 __device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane) {
   if (p.cnt_head >= 0) {
-    if (__builtin_amdgcn_readfirstlane(p.cnt_ret) == static_cast<unsigned>(c.G - 1))
+    if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(p.cnt_ret)) == static_cast<unsigned>(c.G - 1))
       wv_publish(c, p, p.cnt_head, lane);
     p.cnt_head = -1;
   }
