@@ -1882,6 +1882,7 @@ __global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vo
 //     positions.
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+static_assert(kHistBins >= kSelThreads, "the compaction keeps one run start per thread in the histogram's LDS");
 constexpr int kSelPer = 4;                            // 16-byte score pieces per thread
 constexpr int kSelChunk = kSelThreads * kSelPer * 4;  // positions per workgroup
 constexpr int kCandLds = 4096;                        // candidates a workgroup holds in LDS
@@ -2230,11 +2231,12 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
   }
   __syncthreads();
 
-  // ordered compaction of the bitmap into ascending positions: prefix counts
-  // of each thread's run of words, then (bitmap in LDS) every output slot t
-  // finds its word by binary search over the words' prefix counts and its bit
-  // by halving popcounts, so that all lanes do the same work; else each
-  // thread writes its own words' positions
+  // ordered compaction of the bitmap into ascending positions: each thread
+  // counts a run of wpt consecutive words and a block scan gives every run's
+  // first output slot. With the bitmap in LDS, every output slot t then finds
+  // its run by binary search over the runs' first slots, its word by a scan of
+  // at most wpt popcounts and its bit by halving popcounts, so that all lanes
+  // do the same work; else each thread writes its own run's positions.
   int* out = idx_out + static_cast<int64_t>(bh) * kk;
   const int wpt = (words + kSelThreads - 1) / kSelThreads;
   const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
@@ -2242,24 +2244,27 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
   for (int i = w0; i < w1; ++i) cnt += __popc(lds_bm ? s.bm[i] : load_word(&bm_g[i]));
   unsigned total;
   unsigned run = sel_block_scan(cnt, s.wsum, &total);
-  if (lds_bm && words <= 2 * kCandLds) {
-    unsigned* pre = reinterpret_cast<unsigned*>(s.cand);  // the candidates are no longer needed
-    for (int i = w0; i < w1; ++i) {
-      pre[i] = run;
-      run += __popc(s.bm[i]);
-    }
+  if (lds_bm) {
+    unsigned* first = s.sh;  // kSelThreads run starts (the histogram is no longer needed)
+    first[tid] = run;
     __syncthreads();
     const unsigned n_out = min(total, static_cast<unsigned>(kk));
     for (unsigned t = tid; t < n_out; t += kSelThreads) {
-      int lo = 0, hi = words;  // pre[lo] <= t < pre[hi], pre[words] standing for the total
+      int lo = 0, hi = kSelThreads;  // first[lo] <= t < first[hi], first[kSelThreads] standing for the total
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (pre[mid] <= t)
+        if (first[mid] <= t)
           lo = mid;
         else
           hi = mid;
       }
-      unsigned x = s.bm[lo], r = t - pre[lo];
+      unsigned r = t - first[lo];
+      int wi = lo * wpt;  // run lo's words (a run with no set bit is never found)
+      unsigned x = s.bm[wi];
+      for (unsigned c = __popc(x); r >= c; c = __popc(x)) {
+        r -= c;
+        x = s.bm[++wi];
+      }
       int pos = 0;
 #pragma unroll
       for (int sh = 16; sh; sh >>= 1) {
@@ -2270,11 +2275,11 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
           pos += sh;
         }
       }
-      out[t] = lo * 32 + pos;
+      out[t] = wi * 32 + pos;
     }
   } else {
     for (int i = w0; i < w1; ++i) {
-      unsigned x = lds_bm ? s.bm[i] : load_word(&bm_g[i]);
+      unsigned x = load_word(&bm_g[i]);
       while (x) {
         if (run < static_cast<unsigned>(kk)) out[run] = i * 32 + __ffs(x) - 1;
         ++run;
