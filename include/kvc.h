@@ -175,7 +175,7 @@ int kvc_snapkv_force_residency_fallback(int on);
  * first kernel, then after the workspace clear (1; the single pass's
  * preparation kernel under SINGLE_PASS), the row-statistics pass (2; the
  * single score kernel under SINGLE_PASS), the row-statistics merge (3; nothing
- * separate under either schedule), the vote + pooling + histogram pass (4;
+ * under SINGLE_PASS), the vote + pooling + histogram pass (4;
  * pooling + histogram under SINGLE_PASS), the per-head selection (5) and the
  * gather (6). The events are created and owned by the caller; pass NULL or 0
  * to stop recording. */

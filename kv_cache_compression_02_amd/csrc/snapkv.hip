@@ -115,6 +115,15 @@ __device__ void merge_stats_to_lds(int bh, int nchunk, const float2* __restrict_
   __syncthreads();
 }
 
+// Each window row's (m2, 1/l) of head blockIdx.x from its per-chunk partials,
+// once per head between the two passes.
+__global__ __launch_bounds__(kThreads) void snap_stats_merge(const float2* __restrict__ part, int nchunk,
+                                                             float2* __restrict__ rowstat) {
+  __shared__ float2 st[32];
+  merge_stats_to_lds(blockIdx.x, nchunk, part, st);
+  if (threadIdx.x < 32) rowstat[blockIdx.x * 32 + threadIdx.x] = st[threadIdx.x];
+}
+
 // Max-pool and histogram of one chunk: sv holds the votes of prefix keys
 // [e0, e1) = [c0 - r, c1 + r) clipped to [0, t0); pooled[j] for j in [c0, c1)
 // is the max over the neighbours that exist, and each pooled value's top 12
@@ -270,14 +279,15 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
-    float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
-    float* __restrict__ pooled, unsigned* __restrict__ hist) {
+    float scale_log2, const float2* __restrict__ rowstat, float* __restrict__ vote, float* __restrict__ pooled,
+    unsigned* __restrict__ hist) {
   constexpr int KS = D / 16;
   __shared__ float sv[kChunkMfma + 2 * kMaxPoolRadius];
   __shared__ unsigned sh[kHistBins];
   __shared__ float2 stat[32];
   const int chunk = blockIdx.x, bh = blockIdx.y;
-  merge_stats_to_lds(bh, nchunk, part, stat);
+  if (threadIdx.x < 32) stat[threadIdx.x] = rowstat[bh * 32 + threadIdx.x];
+  __syncthreads();
   const int b = bh / H, h = bh - b * H;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int col = lane & 31, half = lane >> 5;
@@ -343,8 +353,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
-    float scale_log2, int nchunk, const float2* __restrict__ part, float* __restrict__ vote,
-    float* __restrict__ pooled, unsigned* __restrict__ hist) {
+    float scale_log2, const float2* __restrict__ rowstat, float* __restrict__ vote, float* __restrict__ pooled,
+    unsigned* __restrict__ hist) {
   __shared__ float qs[kMaxWindow][D];
   __shared__ float2 st[kMaxWindow];
   __shared__ float sv[kChunkF32 + 2 * kMaxPoolRadius];
@@ -357,8 +367,8 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const int rr = i / D, d = i - rr * D;
     qs[rr][d] = rr < w ? q[b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rr) * qst + d] : 0.f;
   }
-  merge_stats_to_lds(bh, nchunk, part, st);
-  if (threadIdx.x < kMaxWindow && static_cast<int>(threadIdx.x) >= w) st[threadIdx.x] = make_float2(0.f, 0.f);
+  if (threadIdx.x < kMaxWindow)
+    st[threadIdx.x] = static_cast<int>(threadIdx.x) < w ? rowstat[bh * 32 + threadIdx.x] : make_float2(0.f, 0.f);
   __syncthreads();
   const int c0 = chunk * kChunkF32, c1 = min(t0, c0 + kChunkF32);
   const int e0 = max(0, c0 - r), e1 = min(t0, c1 + r);
@@ -2337,7 +2347,7 @@ struct SnapLayout {
   int64_t BH;
   int N, kk, nchunk, words, nunit;
   size_t hist, sel_ctr;
-  size_t part, pooled, cand, bitmap;
+  size_t part, rowstat, pooled, cand, bitmap;
   size_t cref, cacc, ccnt, cstat, cpart, cstatus;  // single pass (bf16)
   size_t total;
 };
@@ -2361,6 +2371,7 @@ bool snap_layout(int B, int H, int L, int D, int w, int budget, kvc_dtype dt, Sn
   o->hist = take(static_cast<size_t>(BH) * kHistBins * 4);
   o->sel_ctr = take(static_cast<size_t>(BH) * kSelCtrWords * 4);
   o->part = take(static_cast<size_t>(BH) * o->nchunk * 32 * 8);
+  o->rowstat = take(static_cast<size_t>(BH) * 32 * 8);
   o->pooled = take(static_cast<size_t>(BH) * o->N * 4);
   o->cand = take(static_cast<size_t>(BH) * o->N * 8);
   o->bitmap = take(static_cast<size_t>(BH) * o->words * 4);
@@ -2412,7 +2423,7 @@ void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int 
                   float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
   snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
-                                                scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
+                                                scale_log2, reinterpret_cast<const float2*>(ws + lay.rowstat),
                                                 vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
@@ -2422,12 +2433,12 @@ void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
                   float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
   snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
-                                               scale_log2, lay.nchunk, reinterpret_cast<const float2*>(ws + lay.part),
+                                               scale_log2, reinterpret_cast<const float2*>(ws + lay.rowstat),
                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
-// Pass 1 (row statistics; it also clears the histograms and counters), then
-// pass 2 (merge of the statistics in its prologue, votes, pooling and the
+// Pass 1 (row statistics; it also clears the histograms and counters), the
+// merge of each head's statistics, then pass 2 (votes, pooling and the
 // histogram), with phase marks 2, 3 and 4.
 template <typename T>
 void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int qrow0, const T* k,
@@ -2438,7 +2449,9 @@ void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int 
   else
     launch_stats<64>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
   mark_phase(2, stream);
-  mark_phase(3, stream);  // no separate merge launch
+  snap_stats_merge<<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
+      reinterpret_cast<const float2*>(ws + lay.part), lay.nchunk, reinterpret_cast<float2*>(ws + lay.rowstat));
+  mark_phase(3, stream);
   if (D == 128)
     launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, r, scale_log2, ws, vote, pooled, stream);
   else
