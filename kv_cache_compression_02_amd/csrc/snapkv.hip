@@ -42,7 +42,7 @@ namespace {
 constexpr int kTile = 32;            // keys per MFMA tile (the 32x32 output's N or M side)
 constexpr int kThreads = 256;        // workgroup size of the streaming kernels
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunkMfma = 1024;     // keys per workgroup, bf16 MFMA vote pass
+constexpr int kChunkMfma = 2048;     // keys per workgroup, bf16 MFMA vote pass
 constexpr int kStatChunkMfma = 2048; // keys per workgroup, bf16 MFMA statistics pass
 constexpr int kChunkF32 = 256;       // keys per workgroup, fp32 path (a key per thread)
 constexpr int kMaxWindow = 32;
