@@ -2303,7 +2303,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
 
 // kGatherPer 16-byte pieces of output rows per thread, K and V together; all
 // loads are issued before the stores.
-constexpr int kGatherPer = 4;
+constexpr int kGatherPer = 2;
 
 __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__ k,
                                                         const char* __restrict__ v, int64_t sb,
