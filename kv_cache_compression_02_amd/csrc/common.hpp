@@ -83,6 +83,12 @@ __device__ __forceinline__ float lane_xor(float x) {
   return __uint_as_float(lane_xor_u<K>(__float_as_uint(x)));
 }
 
+template <int K>
+__device__ __forceinline__ unsigned long long lane_xor_u64(unsigned long long x) {
+  return (static_cast<unsigned long long>(lane_xor_u<K>(static_cast<unsigned>(x >> 32))) << 32) |
+         lane_xor_u<K>(static_cast<unsigned>(x));
+}
+
 // lane_xor for a stride that is a constant only once the caller's loop is
 // unrolled; any other stride goes through __shfl_xor.
 __device__ __forceinline__ float lane_xor_n(float x, int k) {
@@ -124,15 +130,19 @@ __device__ __forceinline__ unsigned wave_sum_u(unsigned x) {
   return x + lane_xor_u<1>(x);
 }
 
-// Inclusive prefix sum across the wave (Hillis-Steele over 64 lanes).
+// Inclusive prefix sum across the wave: Hillis-Steele shifts within each
+// 16-lane row (DPP row_shr, lanes past the row's start adding zero), then the
+// row totals carried into the rows above (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3).
 __device__ __forceinline__ unsigned wave_incl_scan(unsigned x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    unsigned y = __shfl_up(x, o);
-    if (l >= o) x += y;
-  }
-  return x;
+  int v = static_cast<int>(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return static_cast<unsigned>(v);
 }
 
 // Exclusive prefix sum over the whole block. `scratch` must hold one unsigned

@@ -51,6 +51,29 @@ __device__ __forceinline__ unsigned long long evict_key(float acc, int pos) {
   return (static_cast<unsigned long long>(__float_as_uint(acc)) << 32) | static_cast<unsigned>(pos);
 }
 
+// The smallest (score, position) key among slots j < N whose position is
+// below rthr: evict_threshold for E = 1 (the usual decode step), by one
+// block-wide minimum. red: kWaves words of LDS. Every thread calls it.
+__device__ unsigned long long evict_min(const float* s_val, const int* s_pos, int N, int rthr,
+                                        unsigned long long* red) {
+  unsigned long long m = ~0ull;
+  for (int j = threadIdx.x; j < N; j += blockDim.x)
+    if (s_pos[j] < rthr) m = min(m, evict_key(s_val[j], s_pos[j]));
+  m = min(m, lane_xor_u64<32>(m));
+  m = min(m, lane_xor_u64<16>(m));
+  m = min(m, lane_xor_u64<8>(m));
+  m = min(m, lane_xor_u64<4>(m));
+  m = min(m, lane_xor_u64<2>(m));
+  m = min(m, lane_xor_u64<1>(m));
+  if (lane_id() == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  unsigned long long r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = min(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
 // Key of the E-th smallest (score, position) among slots j < N whose position
 // is below rthr (the non-recent tokens): radix select, 8 bits at a time from the
 // top. Slots with a key <= the result are exactly the E to evict (keys are
@@ -225,7 +248,9 @@ __global__ __launch_bounds__(kThreads, 8) void h2o_step_kernel(
     const int rthr = length - n_recent;  // positions >= rthr are recent
     const int E = N - budget;
     n_keep = budget;
-    const unsigned long long prefix = evict_threshold(s_val, s_pos, N, rthr, static_cast<unsigned>(E), dh);
+    __shared__ unsigned long long red64[kWaves];
+    const unsigned long long prefix = E == 1 ? evict_min(s_val, s_pos, N, rthr, red64)
+                                             : evict_threshold(s_val, s_pos, N, rthr, static_cast<unsigned>(E), dh);
     // prefix = key of the last evicted token. Holes: evicted slots below
     // n_keep; movers: kept slots at or above n_keep. Pair them by rank.
     const int seg = (N + kThreads - 1) / kThreads;

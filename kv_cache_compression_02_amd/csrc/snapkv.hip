@@ -1920,24 +1920,11 @@ __device__ __forceinline__ unsigned lds_add_rtn(unsigned* p, unsigned v) {
   return r;
 }
 
-// Inclusive prefix sum over the wave: shifts within each 16-lane row, then the
-// row totals carried into the rows above.
-__device__ __forceinline__ unsigned wave_scan_dpp(unsigned x) {
-  int v = static_cast<int>(x);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
-  return static_cast<unsigned>(v);
-}
-
 // Exclusive prefix sum over the block with one barrier; *total gets the block
 // sum. `wsum` (kSelWaves words) may be written again only after a barrier.
 __device__ __forceinline__ unsigned sel_block_scan(unsigned x, unsigned* wsum, unsigned* total) {
   const int w = static_cast<int>(threadIdx.x) / kWave;
-  const unsigned incl = wave_scan_dpp(x);
+  const unsigned incl = wave_incl_scan(x);
   if (lane_id() == kWave - 1) wsum[w] = incl;
   __syncthreads();
   unsigned before = 0, all = 0;
