@@ -159,10 +159,21 @@ __global__ __launch_bounds__(kThreads, 8) void h2o_step_kernel(
   }
   float qv[VE];
   Vec16<T>::load(q + static_cast<int64_t>(bh) * RB + sub * 16, qv);
+  // The slots' positions and running scores, loaded now so that they arrive
+  // while the scores are computed (the first kPre * kThreads slots).
+  constexpr int kPre = 4;
+  int pre_pos[kPre];
+  float pre_acc[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int j = threadIdx.x + u * kThreads;
+    pre_pos[u] = j < n ? pos_g[slot0 + j] : new_pos;
+    pre_acc[u] = j < n ? acc_g[slot0 + j] : 0.f;
+  }
 
   // Scores of all N slots; the new token's key is read from k_new. kStepRows
   // row groups per iteration, their loads all issued before any is used.
-  constexpr int kStepRows = D >= 128 ? 4 : 2;
+  constexpr int kStepRows = D >= 128 ? 3 : 2;
   float lmax = -INFINITY;
   for (int j0 = wave * RPW; j0 < N; j0 += kWaves * RPW * kStepRows) {
     float kx[kStepRows][VE];
@@ -188,7 +199,21 @@ __global__ __launch_bounds__(kThreads, 8) void h2o_step_kernel(
       }
     }
   }
-  for (int j = threadIdx.x; j < N; j += kThreads) s_pos[j] = j < n ? pos_g[slot0 + j] : new_pos;
+  // positions to LDS, running scores parked in the eviction list's space
+  // until the update below
+  float* s_acc = reinterpret_cast<float*>(s_list);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int j = threadIdx.x + u * kThreads;
+    if (j < N) {
+      s_pos[j] = pre_pos[u];
+      s_acc[j] = pre_acc[u];
+    }
+  }
+  for (int j = threadIdx.x + kPre * kThreads; j < N; j += kThreads) {
+    s_pos[j] = j < n ? pos_g[slot0 + j] : new_pos;
+    s_acc[j] = j < n ? acc_g[slot0 + j] : 0.f;
+  }
   __syncthreads();
   const float m2 = block_max(lmax, red);
   float lsum = 0.f;
@@ -236,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 8) void h2o_step_kernel(
   // Running scores: acc += p (the new token starts from 0).
   for (int j = threadIdx.x; j < N; j += kThreads) {
     const float p = fast_exp2(s_val[j] - m2) * inv;
-    s_val[j] = (j < n ? acc_g[slot0 + j] : 0.f) + p;
+    s_val[j] = s_acc[j] + p;
   }
   __syncthreads();
 
