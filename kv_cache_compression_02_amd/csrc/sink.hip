@@ -15,30 +15,31 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One 16-byte piece of one head's new K and V row per thread.
-__global__ __launch_bounds__(kThreads) void sink_write(char* __restrict__ rk, char* __restrict__ rv,
-                                                       const char* __restrict__ kn,
-                                                       const char* __restrict__ vn, int64_t n_pieces,
-                                                       int pieces_per_row, int n_slots, int slot) {
+// One launch per token: thread t copies 16-byte piece t of the heads' new K
+// and V rows into the token's slot (t < n_pieces), writes entry t of the
+// ascending list of held positions (t < n_kept, when asked for), and thread 0
+// records the slot's new position.
+__global__ __launch_bounds__(kThreads) void sink_update(char* __restrict__ rk, char* __restrict__ rv,
+                                                        const char* __restrict__ kn, const char* __restrict__ vn,
+                                                        int64_t n_pieces, int pieces_per_row, int n_slots, int slot,
+                                                        int* __restrict__ slot_pos, int pos,
+                                                        int* __restrict__ kept, int n_sinks_held, int n_kept,
+                                                        int recent_from) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (t >= n_pieces) return;
-  const int64_t bh = t / pieces_per_row;
-  const int c = static_cast<int>(t - bh * pieces_per_row);
-  const int64_t row_bytes = static_cast<int64_t>(pieces_per_row) * 16;
-  const int64_t dst = (bh * n_slots + slot) * row_bytes + c * 16;
-  const int64_t src = bh * row_bytes + c * 16;
-  *reinterpret_cast<u32x4_t*>(rk + dst) = *reinterpret_cast<const u32x4_t*>(kn + src);
-  *reinterpret_cast<u32x4_t*>(rv + dst) = *reinterpret_cast<const u32x4_t*>(vn + src);
-}
-
-// Slot map update and the ascending list of held positions.
-__global__ __launch_bounds__(kThreads) void sink_map(int* __restrict__ slot_pos, int slot, int pos,
-                                                     int* __restrict__ kept, int n_sinks_held,
-                                                     int n_kept, int recent_from) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) slot_pos[slot] = pos;
-  if (!kept) return;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n_kept; i += gridDim.x * kThreads)
+  if (t < n_pieces) {
+    const int64_t bh = t / pieces_per_row;
+    const int c = static_cast<int>(t - bh * pieces_per_row);
+    const int64_t row_bytes = static_cast<int64_t>(pieces_per_row) * 16;
+    const int64_t dst = (bh * n_slots + slot) * row_bytes + c * 16;
+    const int64_t src = bh * row_bytes + c * 16;
+    *reinterpret_cast<u32x4_t*>(rk + dst) = *reinterpret_cast<const u32x4_t*>(kn + src);
+    *reinterpret_cast<u32x4_t*>(rv + dst) = *reinterpret_cast<const u32x4_t*>(vn + src);
+  }
+  if (kept && t < n_kept) {
+    const int i = static_cast<int>(t);
     kept[i] = i < n_sinks_held ? i : recent_from + (i - n_sinks_held);
+  }
+  if (t == 0) slot_pos[slot] = pos;
 }
 
 }  // namespace
@@ -67,15 +68,13 @@ extern "C" kvc_status kvc_sink_recent(void* ring_k, void* ring_v, int32_t* slot_
   const int es = dt == KVC_BF16 ? 2 : 4;
   const int ppr = D * es / 16;
   const int64_t pieces = static_cast<int64_t>(B) * H * ppr;
-  sink_write<<<static_cast<unsigned>((pieces + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
-      static_cast<char*>(ring_k), static_cast<char*>(ring_v), static_cast<const char*>(k_new),
-      static_cast<const char*>(v_new), pieces, ppr, n_slots, slot);
   const int64_t held_sinks = len < n_sink ? len : n_sink;
   const int64_t n_kept = len < n_slots ? len : n_slots;
   const int64_t recent_from = len - n_recent > n_sink ? len - n_recent : n_sink;
-  const unsigned gm = static_cast<unsigned>(n_kept / kThreads + 1 < 64 ? n_kept / kThreads + 1 : 64);
-  sink_map<<<gm, kThreads, 0, stream>>>(slot_pos, slot, static_cast<int>(pos), kept_idx_out,
-                                        static_cast<int>(held_sinks), static_cast<int>(n_kept),
-                                        static_cast<int>(recent_from));
+  const int64_t threads = pieces > n_kept ? pieces : n_kept;
+  sink_update<<<static_cast<unsigned>((threads + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+      static_cast<char*>(ring_k), static_cast<char*>(ring_v), static_cast<const char*>(k_new),
+      static_cast<const char*>(v_new), pieces, ppr, n_slots, slot, slot_pos, static_cast<int>(pos), kept_idx_out,
+      static_cast<int>(held_sinks), static_cast<int>(n_kept), static_cast<int>(recent_from));
   return check_launch("sink_recent");
 }
