@@ -355,107 +355,195 @@ __device__ __forceinline__ void load_frag(const uint16_t* p, bf16x8_t (&f)[D / 1
 
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
-// bf16, MFMA 32x32x16, output S^T (lane = query row): per-row running max/sum.
+// bf16 passes: a workgroup owns kWaves consecutive 32-row tiles (one per wave)
+// of its head and streams the other operand's tiles through a double-buffered
+// LDS ring, so each streamed tile is read from L2 once per workgroup instead of
+// once per wave. Rows in LDS are padded by 16 bytes: a wave's 16-byte fragment
+// reads (32 rows at one column offset) then spread over all LDS banks.
 template <int D>
-__global__ __launch_bounds__(kThreads) void h2o_prefill_stats_bf16(
-    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ k,
-    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, float scale_log2, float2* __restrict__ stat) {
-  constexpr int KS = D / 16;
-  __shared__ float2 wred[kWaves][32];
-  const int qt = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / H, h = bh - b * H;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int col = lane & 31, half = lane >> 5;
-  const int qi = qt * kPTile + col;
-  bf16x8_t qf[KS];
-  if (qi < Lp) {
-    load_frag<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qi) * qst + half * (D / 2), qf);
-  } else {
+constexpr int kPRow = D + 8;  // LDS row stride in bf16 elements
+
+// Block id -> (head, group) so that the groups of one head run on one XCD
+// (workgroups are dealt to the 8 XCDs round-robin by linear id): a head's K and
+// Q stay in that XCD's L2 while its groups run. Heavier groups (more tiles in
+// the causal triangle) are issued first. Any bijection is correct.
+__device__ __forceinline__ void xcd_group(int64_t id, int64_t total, int nb, bool heavy_last, int& bh, int& g) {
+  const int64_t x = id & 7, slot = id >> 3, q = total >> 3, r = total & 7;
+  const int64_t lin = x * q + (x < r ? x : r) + slot;
+  bh = static_cast<int>(lin / nb);
+  const int i = static_cast<int>(lin - static_cast<int64_t>(bh) * nb);
+  g = heavy_last ? nb - 1 - i : i;
+}
+
+// Global -> registers part of staging one 32-row tile (rows clamped to Lp - 1):
+// 16-byte pieces, consecutive threads on consecutive pieces of a row.
+template <int D>
+__device__ __forceinline__ void tile_load(const uint16_t* base, int64_t st, int row0, int Lp,
+                                          u32x4_t (&r)[D / 64]) {
+  constexpr int kChunks = D / 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
-  }
-  const uint16_t* kb = k + b * ksb + h * ksh + half * (D / 2);
-  float m_run = kNegBig, l_run = 0.f;
-  for (int kt = wave; kt <= qt; kt += kWaves) {
-    bf16x8_t kf[KS];
-    load_frag<D>(kb + static_cast<int64_t>(min(kt * kPTile + col, Lp - 1)) * kst, kf);
-    f32x16_t acc = {};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
-    float sv[16], tmax = kNegBig;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = kt * kPTile + acc_row(r, half);
-      sv[r] = (j <= qi && j < Lp) ? acc[r] * scale_log2 : kNegBig;
-      tmax = fmaxf(tmax, sv[r]);
-    }
-    const float mnew = fmaxf(m_run, tmax);
-    float add = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) add += fast_exp2(sv[r] - mnew);
-    l_run = l_run * fast_exp2(m_run - mnew) + add;
-    m_run = mnew;
-  }
-  lse2_merge(m_run, l_run, lane_xor<32>(m_run), lane_xor<32>(l_run));
-  if (half == 0) wred[wave][col] = make_float2(m_run, l_run);
-  __syncthreads();
-  if (threadIdx.x < 32 && qt * kPTile + static_cast<int>(threadIdx.x) < Lp) {
-    float m = wred[0][threadIdx.x].x, l = wred[0][threadIdx.x].y;
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) lse2_merge(m, l, wred[i][threadIdx.x].x, wred[i][threadIdx.x].y);
-    stat[static_cast<int64_t>(bh) * Lp + qt * kPTile + threadIdx.x] = make_float2(m, 1.f / l);
+  for (int i = 0; i < D / 64; ++i) {
+    const int p = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int row = p / kChunks, c = p - row * kChunks;
+    r[i] = *reinterpret_cast<const u32x4_t*>(base + static_cast<int64_t>(min(row0 + row, Lp - 1)) * st + c * 8);
   }
 }
 
-// bf16, MFMA, output S (lane = key column): column sums of the normalised weights.
 template <int D>
-__global__ __launch_bounds__(kThreads) void h2o_prefill_colsum_bf16(
+__device__ __forceinline__ void tile_store(uint16_t* t, const u32x4_t (&r)[D / 64]) {
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int p = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int row = p / kChunks, c = p - row * kChunks;
+    *reinterpret_cast<u32x4_t*>(t + row * kPRow<D> + c * 8) = r[i];
+  }
+}
+
+// MFMA operand of lane (col, half): row col, elements [half*D/2, half*D/2 + D/2)
+// (the same permutation of the head dimension on both operands).
+template <int D>
+__device__ __forceinline__ void frag_lds(const uint16_t* t, int col, int half, bf16x8_t (&f)[D / 16]) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(t + col * kPRow<D> + half * (D / 2));
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, src[s]);
+}
+
+// Pass 1, output S^T (lane = query row): per-row running max/sum over the key
+// tiles up to the row's own (the diagonal tile is the only one that needs the
+// causal mask; rows past Lp in the last tile are not written).
+template <int D>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_stats_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ k,
-    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, float scale_log2, const float2* __restrict__ stat,
-    float* __restrict__ colsum) {
+    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, int nb, float scale_log2, float2* __restrict__ stat) {
   constexpr int KS = D / 16;
-  __shared__ float wsum[kWaves][32];
-  const int kt = blockIdx.x, bh = blockIdx.y;
+  __shared__ __align__(16) uint16_t ring[2][kPTile * kPRow<D>];
+  int bh, g;
+  xcd_group(blockIdx.x, gridDim.x, nb, true, bh, g);
   const int b = bh / H, h = bh - b * H;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int col = lane & 31, half = lane >> 5;
+  const int nqt = (Lp + kPTile - 1) / kPTile;
+  const int qt = g * kWaves + wave;
+  const int qi = qt * kPTile + col;
+  const int last = min(g * kWaves + kWaves - 1, nqt - 1);
+  bf16x8_t qf[KS];
+  load_frag<D>(q + b * qsb + h * qsh + static_cast<int64_t>(min(qi, Lp - 1)) * qst + half * (D / 2), qf);
+  const uint16_t* kb = k + b * ksb + h * ksh;
+  u32x4_t stage[D / 64];
+  tile_load<D>(kb, kst, 0, Lp, stage);
+  tile_store<D>(ring[0], stage);
+  __syncthreads();
+  float m_run = kNegBig, l_run = 0.f;
+  for (int kt = 0; kt <= last; ++kt) {
+    if (kt < last) tile_load<D>(kb, kst, (kt + 1) * kPTile, Lp, stage);
+    if (kt <= qt && qt < nqt) {
+      bf16x8_t kf[KS];
+      frag_lds<D>(ring[kt & 1], col, half, kf);
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+      if (kt == qt) {
+        // -inf, not a large finite value: a half-wave whose rows are all masked
+        // then adds exactly 0 (fma(-big, scale, -m) can round to a large positive).
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * kPTile + acc_row(r, half) > qi) acc[r] = -__builtin_inff();
+      }
+      float tmax = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+      const float mnew = fmaxf(m_run, tmax * scale_log2);
+      float add = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add += fast_exp2(fmaf(acc[r], scale_log2, -mnew));
+      l_run = l_run * fast_exp2(m_run - mnew) + add;
+      m_run = mnew;
+    }
+    if (kt < last) tile_store<D>(ring[(kt + 1) & 1], stage);
+    __syncthreads();
+  }
+  lse2_merge(m_run, l_run, lane_xor<32>(m_run), lane_xor<32>(l_run));
+  if (half == 0 && qi < Lp) stat[static_cast<int64_t>(bh) * Lp + qi] = make_float2(m_run, 1.f / l_run);
+}
+
+// Pass 2, output S (lane = key column): column sums of the normalised weights
+// over the query tiles from the column's own to the last. With
+// c_i = m_i + log2(l_i), each weight is 2^(s*scale - c_i); rows past Lp get
+// c = +1e30 (weight 0), so only the diagonal tile needs a mask.
+template <int D>
+__global__ __launch_bounds__(kThreads) void h2o_prefill_colsum_bf16(
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, const uint16_t* __restrict__ k,
+    int64_t ksb, int64_t ksh, int64_t kst, int H, int Lp, int nb, float scale_log2,
+    const float2* __restrict__ stat, float* __restrict__ colsum) {
+  constexpr int KS = D / 16;
+  __shared__ __align__(16) uint16_t ring[2][kPTile * kPRow<D>];
+  __shared__ __align__(16) float cring[2][kPTile];
+  int bh, g;
+  xcd_group(blockIdx.x, gridDim.x, nb, false, bh, g);
+  const int b = bh / H, h = bh - b * H;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 31, half = lane >> 5;
+  const int nqt = (Lp + kPTile - 1) / kPTile;
+  const int kt = g * kWaves + wave;
   const int kj = kt * kPTile + col;
+  const int first = g * kWaves;
   bf16x8_t kf[KS];
   load_frag<D>(k + b * ksb + h * ksh + static_cast<int64_t>(min(kj, Lp - 1)) * kst + half * (D / 2), kf);
-  const uint16_t* qb = q + b * qsb + h * qsh + half * (D / 2);
+  const uint16_t* qb = q + b * qsb + h * qsh;
   const float2* sb = stat + static_cast<int64_t>(bh) * Lp;
-  const int nqt = (Lp + kPTile - 1) / kPTile;
-  float csum = 0.f;
-  for (int qt = kt + wave; qt < nqt; qt += kWaves) {
-    bf16x8_t qf[KS];
-    const int qrow = qt * kPTile + col;
-    if (qrow < Lp) {
-      load_frag<D>(qb + static_cast<int64_t>(qrow) * qst, qf);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
-    }
-    f32x16_t acc = {};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = qt * kPTile + acc_row(r, half);
-      if (i < Lp && i >= kj) {
-        const float2 st = sb[i];
-        csum += fast_exp2(acc[r] * scale_log2 - st.x) * st.y;
+  u32x4_t stage[D / 64];
+  float cst = 0.f;
+  auto load_c = [&](int qt) {
+    if (threadIdx.x < kPTile) {
+      const int i = qt * kPTile + static_cast<int>(threadIdx.x);
+      cst = 1.0e30f;
+      if (i < Lp) {
+        const float2 v = sb[i];
+        cst = v.x - __builtin_amdgcn_logf(v.y);
       }
     }
+  };
+  tile_load<D>(qb, qst, first * kPTile, Lp, stage);
+  load_c(first);
+  tile_store<D>(ring[0], stage);
+  if (threadIdx.x < kPTile) cring[0][threadIdx.x] = cst;
+  __syncthreads();
+  float csum = 0.f;
+  for (int qt = first; qt < nqt; ++qt) {
+    const int cur = (qt - first) & 1;
+    if (qt + 1 < nqt) {
+      tile_load<D>(qb, qst, (qt + 1) * kPTile, Lp, stage);
+      load_c(qt + 1);
+    }
+    if (qt >= kt) {
+      bf16x8_t qf[KS];
+      frag_lds<D>(ring[cur], col, half, qf);
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
+      float cr[16];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&cring[cur][8 * gq + 4 * half]);
+        cr[4 * gq] = c4.x; cr[4 * gq + 1] = c4.y; cr[4 * gq + 2] = c4.z; cr[4 * gq + 3] = c4.w;
+      }
+      if (qt == kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (acc_row(r, half) < col) cr[r] = 1.0e30f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) csum += fast_exp2(fmaf(acc[r], scale_log2, -cr[r]));
+    }
+    if (qt + 1 < nqt) {
+      tile_store<D>(ring[cur ^ 1], stage);
+      if (threadIdx.x < kPTile) cring[cur ^ 1][threadIdx.x] = cst;
+    }
+    __syncthreads();
   }
   csum += lane_xor<32>(csum);
-  if (half == 0) wsum[wave][col] = csum;
-  __syncthreads();
-  if (threadIdx.x < 32 && kt * kPTile + static_cast<int>(threadIdx.x) < Lp) {
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) t += wsum[i][threadIdx.x];
-    colsum[static_cast<int64_t>(bh) * Lp + kt * kPTile + threadIdx.x] = t;
-  }
+  if (half == 0 && kj < Lp) colsum[static_cast<int64_t>(bh) * Lp + kj] = csum;
 }
 
 // fp32, VALU: a query row (pass 1) or a key column (pass 2) per thread.
@@ -555,10 +643,12 @@ __global__ __launch_bounds__(kThreads) void h2o_prefill_evict(
 template <int D>
 void launch_prefill_passes(const uint16_t* q, kvc_strides qs, const uint16_t* k, kvc_strides kvs, int H,
                            int64_t BH, int Lp, float scale_log2, float2* stat, float* colsum, hipStream_t stream) {
-  const dim3 g((Lp + kPTile - 1) / kPTile, static_cast<unsigned>(BH));
-  h2o_prefill_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp,
+  const int nqt = (Lp + kPTile - 1) / kPTile;
+  const int nb = (nqt + kWaves - 1) / kWaves;
+  const unsigned g = static_cast<unsigned>(BH * nb);
+  h2o_prefill_stats_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp, nb,
                                                        scale_log2, stat);
-  h2o_prefill_colsum_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp,
+  h2o_prefill_colsum_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, k, kvs.b, kvs.h, kvs.t, H, Lp, nb,
                                                         scale_log2, stat, colsum);
 }
 

@@ -222,6 +222,19 @@ def test_h2o_prefill_fp32_d64():
                  20)
 
 
+def test_h2o_prefill_bf16_d64_ragged():
+    """bf16, head_dim 64, 161-token prompt: 6 row tiles, so the head's second workgroup has two tiles past
+    the end and the last tile holds one row."""
+    _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=5, D=64, prompt_len=161, seed=21), 24)
+
+
+def test_h2o_prefill_short_prompts():
+    """Prompts of 1 and 33 tokens (a single row; one full tile plus one row), budget 2 + 2."""
+    for lp in (1, 33):
+        _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=3, prompt_len=lp, seed=lp), 8,
+                     policy=lambda t: (2, 2))
+
+
 def test_h2o_prefill_budget_never_binds():
     """No eviction: every prompt token is kept with its full causal column sum."""
     lf = _prefill_run(syn.H2O_WORKLOADS["opt6.7b-decode"].with_(B=1, H=2, prompt_len=300), 0,
