@@ -358,6 +358,36 @@ def bench_h2o(args, ev):
     }
 
 
+def stream_peak():
+    """What this GPU streams with plain library kernels: a 1 GiB device copy (bytes read plus
+    bytes written; the stream-copy peak) and a 1 GiB sum (a library reduction: bytes read), each
+    timed over 10 launches with torch events on torch's own stream."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+        torch.sum(a)
+    torch.cuda.synchronize()
+    reps = 10
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * n), ("read", lambda: torch.sum(a), n)):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        e.synchronize()
+        out[f"{name}_gbps"] = nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    out["bytes"] = n
+    out["kernels"] = "torch copy_ (read + write counted) and torch.sum (a reduction; read), 10 launches each"
+    return out
+
+
 def calibrate_copy():
     import torch
 
@@ -410,6 +440,10 @@ def main():
         "phase_ms": res["phase_ms"],
         "decode_attention_compressed": res["decode_attention"],
     }
+    sp = stream_peak()
+    sp["score_kernel_frac_of_copy"] = res["roofline"]["achieved"] / sp["copy_gbps"]
+    line["measured_stream"] = sp
+    log(f"stream peak: copy {sp['copy_gbps']:.0f} GB/s, read {sp['read_gbps']:.0f} GB/s")
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
     else:
