@@ -29,6 +29,19 @@ constexpr int kChunk = 256;       // rows per workgroup
 constexpr int kChunkSmall = 128;  // rows per workgroup when kChunk would leave the chip underfilled
 constexpr int kFillGroups = 512;  // workgroups below which the small chunk is used
 
+// A 16-byte piece as float lanes (bf16: 8 widened by a shift; fp32: 4).
+__device__ __forceinline__ void widen16(const u32x4_t& u, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(u[i] << 16);
+    x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen16(const u32x4_t& u, float (&x)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(u[i]);
+}
+
 template <typename T, int D, int CH>
 __global__ __launch_bounds__(kDecThreads) void decode_partial(const T* __restrict__ q, int64_t qsb, int64_t qsh,
                                                                const T* __restrict__ k, const T* __restrict__ v,
@@ -51,12 +64,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(const T* __restric
   float qv[VE];
   Vec16<T>::load(q + b * qsb + h * qsh + pc * VE, qv);
 
+  // every K and V piece of the wave's rows is requested before any is used:
+  // the chunk then costs one memory round trip, not one per load group
+  u32x4_t kr[S], vr[S];
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    kr[st] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(row0 + st * RPW, n - 1)) * kst);
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    vr[st] = *reinterpret_cast<const u32x4_t*>(vb + static_cast<int64_t>(min(row0 + st * RPW, n - 1)) * kst);
+  __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise sink the loads to their uses)
   float sc[S];
 #pragma unroll
   for (int st = 0; st < S; ++st) {
     const int row = row0 + st * RPW;
     float kv[VE];
-    Vec16<T>::load(kb + static_cast<int64_t>(min(row, n - 1)) * kst, kv);
+    widen16(kr[st], kv);
     float d = 0.f;
 #pragma unroll
     for (int e = 0; e < VE; ++e) d = fmaf(qv[e], kv[e], d);
@@ -77,7 +100,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(const T* __restric
   for (int st = 0; st < S; ++st) {
     const int row = row0 + st * RPW;
     float vv[VE];
-    Vec16<T>::load(vb + static_cast<int64_t>(min(row, n - 1)) * kst, vv);
+    widen16(vr[st], vv);
     const float p = row < n ? fast_exp2(sc[st] - m) : 0.f;
     l += p;
 #pragma unroll
