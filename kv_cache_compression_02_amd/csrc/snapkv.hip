@@ -1458,9 +1458,9 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   // the tile whose votes come next round: tile r - 7 (tile 0 before round 8)
   int vn_head = p.vhead, vn_t = p.vtile;
   if (r >= kWvBanks) wv_next_ht(c, vn_head, vn_t);
-  wv_prefetch<PAR>(c, p, min(vn_head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
   // this tile's MFMAs first, then the next head's Q loads (which then have the
-  // votes and the row sums to land behind), then the votes of round r - 8
+  // votes and the row sums to land behind), then the votes of round r - 8,
+  // then the next round's prefetches
   f32x16_t acc = {};
   if (do_a) {
     const int col = lane & 31, half = lane >> 5;
@@ -1484,6 +1484,11 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     p.vhead = vn_head;
     p.vtile = vn_t;
   }
+  // Issued after this round's votes rather than at its start, the weights
+  // are read half a round later, so that fewer votes find them not yet
+  // published and poll (every head needs every workgroup's contribution);
+  // the rest of the round still covers the load before the next round's wait.
+  wv_prefetch<PAR>(c, p, min(vn_head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
   if (do_a) {
     const int col = lane & 31, half = lane >> 5;
     float* rs = c.sh->s_r[c.wave];
