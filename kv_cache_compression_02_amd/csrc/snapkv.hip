@@ -1075,8 +1075,8 @@ struct WvCtx {
 
 // A wave's state carried from round to round.
 struct WvPipe {
-  int cnt_head;      // head whose count this wave raised (its return is looked at after a full wait)
-  unsigned cnt_ret;  // that count's value before the increment
+  int fin_head;      // the next head this wave finishes (heads g + G * wave + W * i), >= BH: none left
+  unsigned fin_cnt;  // that head's contribution count, read (agent scope) last round
   int merge_head;    // head this wave merges for its workgroup once all its waves have stored their sums
   uint2 pre[2];      // vote weights prefetched for the votes of the rounds of each parity
   float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
@@ -1282,12 +1282,12 @@ __device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int
 // The merge of head h for this workgroup, by its designated wave, once all
 // kWvWaves waves have stored their row sums in slot h & 1: the sums added in
 // wave order, the slot reopened for head h + 2, the result added to the
-// head's accumulators, and the head's count raised. The workgroup whose
-// increment is the last stages and converts the words (which carry their own
-// contribution counts, so the increment need not wait for the contributions
-// to land). Skipped while the previous count's return has not been looked at.
+// head's accumulators, and the head's count raised (no return is waited for).
+// The head's finisher, fixed in advance, reads the count and, once all G
+// workgroups have counted, stages and converts the words (which carry their
+// own contribution counts, so an increment need not wait for its
+// contributions to land).
 __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane) {
-  if (p.cnt_head >= 0) return;
   WvShared* sh = c.sh;
   const int h = p.merge_head, sl = h & 1, ln = opaque(lane), col = ln & 31;
   asm volatile("" ::: "memory");
@@ -1303,27 +1303,38 @@ __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane
   }
   asm volatile("" ::: "memory");
   if (ln < 32 && col < c.w) wv_add_sum(c.acc + static_cast<int64_t>(h) * kCoopHeadWords, col, L);
-  // (an address the compiler cannot prove uniform: its atomic optimizer would
-  // otherwise broadcast the return at once, waiting for the next tile too)
-  unsigned ret = 0;
-  if (ln == 0) ret = atomicAdd(&c.cnt[h * kCoopCtrWords] + opaque(0), 1u);
-  p.cnt_ret = ret;
-  p.cnt_head = h;
+  if (ln == 0) atomicAdd(&c.cnt[h * kCoopCtrWords] + opaque(0), 1u);
   p.merge_head = -1;
 }
 
+// Finishers. Head h is finished by wave (h / G) % kWvWaves of workgroup
+// h % G, so that the finishing work (a staging round trip and the
+// conversion) is spread over the workgroups rather than given to the last
+// one to count, which is the one furthest behind: as finisher it would fall
+// further behind and stay last. A finisher reads its head's count (agent
+// scope) every round once it has reached the head, and publishes at the start
+// of the round after the count shows all G workgroups.
+__device__ __forceinline__ void wv_finish(const WvCtx& c, WvPipe& p, int lane) {
+  wv_publish(c, p, p.fin_head, lane);
+  p.fin_head += c.W;
+  p.fin_cnt = 0u;
+}
+
+// The same inside a bounded wait: the count read now, after the full wait.
+__device__ __forceinline__ void wv_finish_poll(const WvCtx& c, WvPipe& p, int lane) {
+  if (p.fin_head >= c.BH) return;
+  const unsigned n = __hip_atomic_load(&c.cnt[p.fin_head * kCoopCtrWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(n)) == static_cast<unsigned>(c.G)) wv_finish(c, p, lane);
+}
+
 // Work this wave owes other waves, done after a full wait (every memory
-// operation it issued before is complete): publish the head whose count this
-// wave's increment completed, merge its workgroup's sums of a head it is
-// designated for. Every bounded wait of the kernel calls it, so that no wave
-// waits for something it owes itself.
+// operation it issued before is complete): merge its workgroup's sums of a
+// head it is designated for, and (in a bounded wait) finish its head if that
+// head's count is complete. Every bounded wait of the kernel calls it, so
+// that no wave waits for something it owes itself.
 __device__ __forceinline__ void wv_service(const WvCtx& c, WvPipe& p, int lane) {
-  if (p.cnt_head >= 0) {
-    if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(p.cnt_ret)) == static_cast<unsigned>(c.G - 1))
-      wv_publish(c, p, p.cnt_head, lane);
-    p.cnt_head = -1;
-  }
   if (p.merge_head >= 0) wv_try_merge(c, p, lane);
+  wv_finish_poll(c, p, lane);
 }
 
 // The next round's prefetches: the vote weights for its votes (head
@@ -1452,6 +1463,10 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   // this round's tile, Q and reference score, and everything issued last round
   wait_vm_all();
   const int lane = opaque(lane_id());
+  if (__builtin_expect(p.fin_head < c.BH &&
+                           static_cast<unsigned>(__builtin_amdgcn_readfirstlane(p.fin_cnt)) ==
+                               static_cast<unsigned>(c.G), 0))
+    wv_finish(c, p, lane);
   const WvPos nxt = wv_next(c, pos);
   const bool more = r + 1 < c.rounds;
   if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
@@ -1489,6 +1504,9 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   // published and poll (every head needs every workgroup's contribution);
   // the rest of the round still covers the load before the next round's wait.
   wv_prefetch<PAR>(c, p, min(vn_head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
+  // the count of the head this wave finishes, once the wave has reached it
+  if (p.fin_head < c.BH && (pos.head >= p.fin_head || !do_a))
+    p.fin_cnt = __hip_atomic_load(&c.cnt[p.fin_head * kCoopCtrWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (do_a) {
     const int col = lane & 31, half = lane >> 5;
     float* rs = c.sh->s_r[c.wave];
@@ -1514,12 +1532,11 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     if (!more || nxt.head != pos.head) wv_head_end(c, p, pos.head, ls, lane);
   }
   pos = nxt;
-  // owed work after a full wait (the next round starts with that wait anyway:
-  // it only comes earlier): a count raised this round is looked at, so the
-  // head a merge completes is published within the round
-  if (__builtin_expect(p.cnt_head >= 0 || p.merge_head >= 0, 0)) {
+  // a merge still owed after a full wait (the next round starts with that
+  // wait anyway: it only comes earlier)
+  if (__builtin_expect(p.merge_head >= 0, 0)) {
     wait_vm_all();
-    wv_service(c, p, lane);
+    wv_try_merge(c, p, lane);
   }
 }
 
@@ -1563,8 +1580,9 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   }
   if (threadIdx.x < kWvFinBufs) sh.fin_owner[threadIdx.x] = -1;
   WvPipe p;
-  p.cnt_head = p.merge_head = -1;
-  p.cnt_ret = 0;
+  p.merge_head = -1;
+  p.fin_head = c.g + c.G * c.wave;
+  p.fin_cnt = 0u;
   p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
   p.rref[0] = p.rref[1] = 0.f;
   p.gave_up = false;
@@ -1627,12 +1645,15 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     wv_round<D, 6>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 6);
     wv_round<D, 7>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 7);
   }
-  // work still owed after the last round: a pending merge or election (bounded)
-  for (unsigned t = 0; (p.cnt_head >= 0 || p.merge_head >= 0) && t < kWvSpin; ++t) {
+  // work still owed after the last round: a pending merge, heads still to
+  // finish (bounded)
+  for (unsigned t = 0; (p.merge_head >= 0 || p.fin_head < c.BH) && !p.gave_up && t < kWvSpin; ++t) {
     wait_vm_all();
     __builtin_amdgcn_s_sleep(2);
     wv_service(c, p, lane_id());
   }
+  if (p.fin_head < c.BH && lane_id() == 0)  // a finisher that ran out of time: a protocol failure
+    __hip_atomic_store(status, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Exact votes of the heads the single pass flagged (a score more than 2^127
