@@ -1016,10 +1016,10 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
 constexpr int kWvWaves = 8;
 constexpr unsigned kWvGateSpin = 1u << 14;  // residency-check polls (~1 ms) before the exact fallback
 constexpr int kWvThreads = kWvWaves * kWave;
-constexpr int kWvBanks = 8;
+constexpr int kWvBanks = 9;
 constexpr int kWvRowWords = 24;  // accumulator words per row a finisher stages (values in words 0..19)
 constexpr int kWvFinBufs = 4;    // finisher staging buffers, by head mod 4
-constexpr int kWvMaxSpan = 5;    // a head spans at most this many rounds after its first
+constexpr int kWvMaxSpan = kWvBanks - 3;  // a head spans at most this many rounds after its first
 constexpr unsigned kWvSpin = 1u << 18;  // polls before a wait gives up (far beyond any legitimate wait)
 constexpr int kWvOvfWord = 20;   // a non-finite row sum adds its count here (the head is then flagged)
 constexpr unsigned long long kWvCountOne = 1ull << 48;
@@ -1451,13 +1451,14 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f3
   }
 }
 
-template <int D, int BANK>
+template <int D, int BANK, int PAR>
 __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, f32x16_t (&sc)[kWvBanks],
                                          f32x16_t& ls, bf16x8_t (&qf)[D / 16], unsigned char* ring0,
                                          unsigned char* ring1, int r) {
   using Ly = WvLayout<D>;
   constexpr int KS = D / 16;
-  constexpr int PAR = BANK & 1;  // ring slot and prefetch parity of round r (kWvBanks is even)
+  // BANK = r % kWvBanks, PAR = r % 2 (the ring slot and prefetch parity)
+  if (r >= c.rounds + kWvBanks) return;  // past the last votes
   const bool do_a = r < c.rounds;
   const bool do_b = r >= kWvBanks && r - kWvBanks < c.rounds;
   // this round's tile, Q and reference score, and everything issued last round
@@ -1470,14 +1471,24 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   const WvPos nxt = wv_next(c, pos);
   const bool more = r + 1 < c.rounds;
   if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
-  // the tile whose votes come next round: tile r - 7 (tile 0 before round 8)
+  // the tile whose votes come next round: tile r - 8 (tile 0 before round 9)
   int vn_head = p.vhead, vn_t = p.vtile;
   if (r >= kWvBanks) wv_next_ht(c, vn_head, vn_t);
-  // this tile's MFMAs first, then the next head's Q loads (which then have the
-  // votes and the row sums to land behind), then the votes of round r - 8,
-  // then the next round's prefetches
-  f32x16_t acc = {};
+  // the votes of the tile of round r - 9 first, from the bank this round's
+  // MFMAs then write; then the next round's prefetches (the weights read a
+  // whole round before their votes); then this tile's MFMAs, the next head's
+  // Q loads, the e_ij and the row sums
+  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
+  if (r >= kWvBanks) {
+    p.vhead = vn_head;
+    p.vtile = vn_t;
+  }
+  wv_prefetch<PAR>(c, p, min(vn_head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
+  // the count of the head this wave finishes, once the wave has reached it
+  if (p.fin_head < c.BH && (pos.head >= p.fin_head || !do_a))
+    p.fin_cnt = __hip_atomic_load(&c.cnt[p.fin_head * kCoopCtrWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (do_a) {
+    f32x16_t acc = {};
     const int col = lane & 31, half = lane >> 5;
     // fragment k-step s of row col: piece half*kP/2 + s at slot piece ^ (col & (kP-1)),
     // i.e. address A ^ (s << 4) (the tile's rows start at multiples of 256 bytes)
@@ -1493,22 +1504,6 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     }
     // Q of the next tile's head into the registers just read (a head's tiles share Q)
     if (more && nxt.head != pos.head) wv_load_q<D>(c, nxt, qf, lane);
-  }
-  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
-  if (r >= kWvBanks) {
-    p.vhead = vn_head;
-    p.vtile = vn_t;
-  }
-  // Issued after this round's votes rather than at its start, the weights
-  // are read half a round later, so that fewer votes find them not yet
-  // published and poll (every head needs every workgroup's contribution);
-  // the rest of the round still covers the load before the next round's wait.
-  wv_prefetch<PAR>(c, p, min(vn_head, c.BH - 1), min(more ? nxt.head : pos.head, c.BH - 1), lane);
-  // the count of the head this wave finishes, once the wave has reached it
-  if (p.fin_head < c.BH && (pos.head >= p.fin_head || !do_a))
-    p.fin_cnt = __hip_atomic_load(&c.cnt[p.fin_head * kCoopCtrWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (do_a) {
-    const int col = lane & 31, half = lane >> 5;
     float* rs = c.sh->s_r[c.wave];
     if (half == 0) rs[col] = p.rref[PAR];  // R_i of this tile's head, read back per register below
     // e_ij = 2^(s_ij - R_i) for key j = key0 + col and the lane's 16 rows i
@@ -1632,18 +1627,29 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
 
   f32x16_t sc[kWvBanks];
   f32x16_t ls = {};
-  static_assert(kWvBanks == 8, "the round loop below is unrolled over the register banks");
+  static_assert(kWvBanks == 9, "the round loop below is unrolled over the register banks and ring slots");
   // the last tile's votes fall in round rounds - 1 + kWvBanks, and the last
-  // head's publication a few rounds after its last tile
-  for (int r0 = 0; r0 < c.rounds + kWvBanks; r0 += kWvBanks) {
-    wv_round<D, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0);
-    wv_round<D, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 1);
-    wv_round<D, 2>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 2);
-    wv_round<D, 3>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 3);
-    wv_round<D, 4>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 4);
-    wv_round<D, 5>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 5);
-    wv_round<D, 6>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 6);
-    wv_round<D, 7>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 7);
+  // head's publication a few rounds after its last tile; the loop body is
+  // 18 rounds (bank r % 9, ring slot r % 2)
+  for (int r0 = 0; r0 < c.rounds + kWvBanks; r0 += 2 * kWvBanks) {
+    wv_round<D, 0, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0);
+    wv_round<D, 1, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 1);
+    wv_round<D, 2, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 2);
+    wv_round<D, 3, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 3);
+    wv_round<D, 4, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 4);
+    wv_round<D, 5, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 5);
+    wv_round<D, 6, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 6);
+    wv_round<D, 7, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 7);
+    wv_round<D, 8, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 8);
+    wv_round<D, 0, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 9);
+    wv_round<D, 1, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 10);
+    wv_round<D, 2, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 11);
+    wv_round<D, 3, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 12);
+    wv_round<D, 4, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 13);
+    wv_round<D, 5, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 14);
+    wv_round<D, 6, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 15);
+    wv_round<D, 7, 0>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 16);
+    wv_round<D, 8, 1>(c, p, pos, sc, ls, qf, ring0, ring1, r0 + 17);
   }
   // work still owed after the last round: a pending merge, heads still to
   // finish (bounded)
@@ -2543,9 +2549,9 @@ int64_t wave_tiles(int L) { return ((L + kTile - 1) / kTile + kWvWaves - 1) / kW
 // workgroup must have tiles in every head (a head's padded tile count is at
 // least the worker count W), and a head may span at most kWvMaxSpan rounds
 // beyond its first: a vote waits (in round r) for the normaliser of a tile
-// of round r - kWvBanks, which its finisher publishes three rounds after the
-// head's last tile, so every such wait then depends only on heads that
-// started earlier and all of them end.
+// of round r - kWvBanks, whose head's last tile was then scored by round
+// r - 3 at the latest, so every such wait depends only on heads that every
+// wave has finished, and all of them end.
 int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
   const CoopCaps& c = coop_caps();
   if (c.cus <= 0) return 0;

@@ -290,8 +290,10 @@ def test_single_pass_kernel_choice():
         assert kvc.snapkv_last_score_kernel() == kernel, (L, kvc.snapkv_last_score_kernel())
     _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_TWO_PASS)
     assert kvc.snapkv_last_score_kernel() == "snap_stats_bf16+snap_votes_bf16"
-    # AUTO: the independent-wave kernel where it runs, else two passes
-    for L, kernel in ((3000, "snap_stats_bf16+snap_votes_bf16"), (131072, "snap_wave_bf16")):
+    # AUTO: the independent-wave kernel where it runs, else two passes (380000 keys: a head
+    # spans six rounds, the most the nine-round vote lag allows)
+    for L, kernel in ((3000, "snap_stats_bf16+snap_votes_bf16"), (131072, "snap_wave_bf16"),
+                      (380000, "snap_wave_bf16")):
         q = torch.zeros((1, 2, 32, 128), dtype=torch.bfloat16, device="cuda")
         k = torch.zeros((1, 2, L, 128), dtype=torch.bfloat16, device="cuda")
         _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_AUTO)
