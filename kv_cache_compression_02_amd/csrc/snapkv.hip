@@ -1020,6 +1020,7 @@ constexpr int kWvBanks = 9;
 constexpr int kWvRowWords = 24;  // accumulator words per row a finisher stages (values in words 0..19)
 constexpr int kWvFinBufs = 4;    // finisher staging buffers, by head mod 4
 constexpr int kWvMaxSpan = kWvBanks - 3;  // a head spans at most this many rounds after its first
+constexpr int kWvMinRounds = 8;            // rounds a layer of heads shorter than a round must fill
 constexpr unsigned kWvSpin = 1u << 18;  // polls before a wait gives up (far beyond any legitimate wait)
 constexpr int kWvOvfWord = 20;   // a non-finite row sum adds its count here (the head is then flagged)
 constexpr unsigned long long kWvCountOne = 1ull << 48;
@@ -1060,6 +1061,8 @@ struct WvCtx {
   const uint16_t* k;
   int64_t ksb, ksh, kst;
   int H, L, w, t0, nt, BH, G, g, W, rounds, wave;
+  int tgt;     // workgroups that contribute to each head: G, or nt / kWvWaves when a head is shorter than a round
+  bool small;  // a head is shorter than a round: every workgroup takes a new head every round
   int64_t dk_tile, dk_head, dk_batch, dq_head, dq_batch;  // byte steps of WvPos::kt and WvPos::qb
   float scale_log2;
   const float* ref;
@@ -1078,6 +1081,7 @@ struct WvPipe {
   int fin_head;      // the next head this wave finishes (heads g + G * wave + W * i), >= BH: none left
   unsigned fin_cnt;  // that head's contribution count, read (agent scope) last round
   int merge_head;    // head this wave merges for its workgroup once all its waves have stored their sums
+  int merge_idx;     // that head's index in the workgroup's sequence of heads (its slot is merge_idx & 1)
   uint2 pre[2];      // vote weights prefetched for the votes of the rounds of each parity
   float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
   int vhead, vtile;  // the tile whose votes are next (round r - kWvBanks in round r)
@@ -1089,6 +1093,18 @@ struct WvPipe {
 __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
   p.t += c.W;
   p.kt += c.dk_tile;
+  if (c.small) {  // heads shorter than a round: several head boundaries, pointers recomputed
+    if (p.t >= c.nt) {
+      const int adv = p.t / c.nt;
+      p.t -= adv * c.nt;
+      p.head += adv;
+      const int b = p.head / c.H;
+      p.h = p.head - b * c.H;
+      p.kt = reinterpret_cast<const char*>(c.k + b * c.ksb + p.h * c.ksh + static_cast<int64_t>(p.t) * kTile * c.kst);
+      p.qb = reinterpret_cast<const char*>(c.q + b * c.qsb + p.h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst);
+    }
+    return p;
+  }
   if (p.t >= c.nt) {
     p.t -= c.nt;
     ++p.head;
@@ -1107,8 +1123,9 @@ __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
 __device__ __forceinline__ void wv_next_ht(const WvCtx& c, int& head, int& t) {
   t += c.W;
   if (t >= c.nt) {
-    t -= c.nt;
-    ++head;
+    const int adv = t / c.nt;
+    t -= adv * c.nt;
+    head += adv;
   }
 }
 
@@ -1265,7 +1282,7 @@ __device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int
     unsigned count;
     bool ovf;
     float wv = wv_words_to_w(f, ln, count, ovf);
-    if (__ballot(row < c.w && count != static_cast<unsigned>(c.G)) == 0ull) {
+    if (__ballot(row < c.w && count != static_cast<unsigned>(c.tgt)) == 0ull) {
       if (__ballot(ovf) != 0ull) wv = 0.f;
       if (ln < 32 && row < c.w) st_agent_u2(&c.stat[h * 32 + row], make_uint2(__float_as_uint(wv), 1u));
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer read before it is released
@@ -1289,7 +1306,7 @@ __device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int
 // contributions to land).
 __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane) {
   WvShared* sh = c.sh;
-  const int h = p.merge_head, sl = h & 1, ln = opaque(lane), col = ln & 31;
+  const int h = p.merge_head, sl = p.merge_idx & 1, ln = opaque(lane), col = ln & 31;
   asm volatile("" ::: "memory");
   if (__builtin_amdgcn_readfirstlane(sh->mcnt[sl]) != kWvWaves) return;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1299,7 +1316,7 @@ __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sums read before the slot reopens
   if (ln == 0) {
     sh->mcnt[sl] = 0;
-    sh->mtag[sl] = h + 2;
+    sh->mtag[sl] = p.merge_idx + 2;
   }
   asm volatile("" ::: "memory");
   if (ln < 32 && col < c.w) wv_add_sum(c.acc + static_cast<int64_t>(h) * kCoopHeadWords, col, L);
@@ -1324,7 +1341,7 @@ __device__ __forceinline__ void wv_finish(const WvCtx& c, WvPipe& p, int lane) {
 __device__ __forceinline__ void wv_finish_poll(const WvCtx& c, WvPipe& p, int lane) {
   if (p.fin_head >= c.BH) return;
   const unsigned n = __hip_atomic_load(&c.cnt[p.fin_head * kCoopCtrWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(n)) == static_cast<unsigned>(c.G)) wv_finish(c, p, lane);
+  if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(n)) == static_cast<unsigned>(c.tgt)) wv_finish(c, p, lane);
 }
 
 // Work this wave owes other waves, done after a full wait (every memory
@@ -1400,7 +1417,7 @@ __device__ __forceinline__ float lane_pick(float a, float b, unsigned m) {
   return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
 }
 
-__device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f32x16_t& ls, int lane) {
+__device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, int idx, f32x16_t& ls, int lane) {
   const int ln = opaque(lane);
   // step over lane bit k: a lane with the bit set keeps the upper half of its
   // registers and sends the lower half (masks opaque, all ones where the bit is set)
@@ -1421,12 +1438,12 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f3
   const int row = acc_row(r, ln >> 5);
   if (__builtin_expect(__ballot(!(x1 <= 3.0e38f)) != 0ull, 0) && ln == 0) atomicOr(&c.cnt[h * kCoopCtrWords + 16], 1u);
   WvShared* sh = c.sh;
-  const int sl = h & 1;
+  const int sl = idx & 1;
   // plain LDS reads behind compiler barriers: an atomic load here would make
   // the compiler wait for the direct loads in flight into the tile ring
   asm volatile("" ::: "memory");
-  if (__builtin_expect(!p.gave_up && sh->mtag[sl] != h, 0)) {
-    // the slot still holds head h - 2 (its merge is pending)
+  if (__builtin_expect(!p.gave_up && sh->mtag[sl] != idx, 0)) {
+    // the slot still holds the workgroup's head before last (its merge is pending)
     unsigned polls = 0;
     bool late;
     do {
@@ -1434,7 +1451,7 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f3
       wait_vm_all();
       wv_service(c, p, ln);
       asm volatile("" ::: "memory");
-      late = sh->mtag[sl] != h;
+      late = sh->mtag[sl] != idx;
     } while (late && ++polls < kWvSpin);
     if (late) {
       p.gave_up = true;
@@ -1447,6 +1464,7 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, f3
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (c.wave == ((h + c.g) & (kWvWaves - 1))) {
     p.merge_head = h;
+    p.merge_idx = idx;
     wv_try_merge(c, p, ln);
   }
 }
@@ -1466,7 +1484,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   const int lane = opaque(lane_id());
   if (__builtin_expect(p.fin_head < c.BH &&
                            static_cast<unsigned>(__builtin_amdgcn_readfirstlane(p.fin_cnt)) ==
-                               static_cast<unsigned>(c.G), 0))
+                               static_cast<unsigned>(c.tgt), 0))
     wv_finish(c, p, lane);
   const WvPos nxt = wv_next(c, pos);
   const bool more = r + 1 < c.rounds;
@@ -1524,7 +1542,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
         ls[i] += x;
       }
     }
-    if (!more || nxt.head != pos.head) wv_head_end(c, p, pos.head, ls, lane);
+    if (!more || nxt.head != pos.head) wv_head_end(c, p, pos.head, c.small ? r : pos.head, ls, lane);
   }
   pos = nxt;
   // a merge still owed after a full wait (the next round starts with that
@@ -1556,6 +1574,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.H = H; c.L = L; c.w = w; c.t0 = L - w; c.nt = nt; c.BH = BH;
   c.fin = fin;
   c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x); c.W = c.G * kWvWaves;
+  c.small = nt < c.W;
+  c.tgt = c.small ? nt / kWvWaves : c.G;
   c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
   c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   c.dk_tile = static_cast<int64_t>(c.W) * kTile * kst * 2;
@@ -1570,29 +1590,36 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   unsigned char* ring1 = ring_odd + c.wave * Ly::kTileB;
   if (threadIdx.x == 0) {
     sh.mcnt[0] = sh.mcnt[1] = 0;
-    sh.mtag[0] = 0;  // every workgroup has tiles in every head, starting with head 0
+    sh.mtag[0] = 0;  // a workgroup's heads in order (all heads, or one per round for short heads)
     sh.mtag[1] = 1;
   }
   if (threadIdx.x < kWvFinBufs) sh.fin_owner[threadIdx.x] = -1;
   WvPipe p;
-  p.merge_head = -1;
+  p.merge_head = p.merge_idx = -1;
   p.fin_head = c.g + c.G * c.wave;
   p.fin_cnt = 0u;
   p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
   p.rref[0] = p.rref[1] = 0.f;
   p.gave_up = false;
-  // round 0: tile v of head 0 (v < W <= tiles per head)
-  WvPos pos{0, 0, c.g * kWvWaves + c.wave, nullptr, nullptr};
-  pos.kt = reinterpret_cast<const char*>(k + static_cast<int64_t>(pos.t) * kTile * kst);
-  pos.qb = reinterpret_cast<const char*>(q + static_cast<int64_t>(qrow0) * qst);
-  p.vhead = 0;
+  // round 0: tile v (of head 0 unless heads are shorter than a round)
+  WvPos pos;
+  {
+    const int v = c.g * kWvWaves + c.wave;
+    pos.head = v / nt;
+    pos.t = v - pos.head * nt;
+    const int b = pos.head / H;
+    pos.h = pos.head - b * H;
+    pos.kt = reinterpret_cast<const char*>(k + b * ksb + pos.h * ksh + static_cast<int64_t>(pos.t) * kTile * kst);
+    pos.qb = reinterpret_cast<const char*>(q + b * qsb + pos.h * qsh + static_cast<int64_t>(qrow0) * qst);
+  }
+  p.vhead = pos.head;
   p.vtile = pos.t;
   bf16x8_t qf[D / 16];
   if (c.rounds > 0) {
     const int lane = lane_id();
     wv_issue_k<D>(c, pos, ring0, lane);
     wv_load_q<D>(c, pos, qf, lane);
-    p.rref[0] = ref[lane & 31];
+    p.rref[0] = ref[pos.head * 32 + (lane & 31)];
   }
   // Residency check, in place of a launch that guarantees it (its wait
   // overlaps the first tile's loads): the waits below need every workgroup
@@ -2545,9 +2572,11 @@ int coop_grid(const SnapLayout& lay, int D) {
 int64_t wave_tiles(int L) { return ((L + kTile - 1) / kTile + kWvWaves - 1) / kWvWaves * kWvWaves; }
 
 // Grid of the independent-wave single pass (one workgroup per resident slot,
-// which the kernel checks at its start), 0 when it cannot run. Every
-// workgroup must have tiles in every head (a head's padded tile count is at
-// least the worker count W), and a head may span at most kWvMaxSpan rounds
+// which the kernel checks at its start), 0 when it cannot run. Either every
+// workgroup has tiles in every head (a head's padded tile count is at least
+// the worker count W), or heads are shorter than a round and each workgroup
+// takes one head per round (nt / kWvWaves workgroups contribute to each);
+// a head may span at most kWvMaxSpan rounds
 // beyond its first: a vote waits (in round r) for the normaliser of a tile
 // of round r - kWvBanks, whose head's last tile was then scored by round
 // r - 3 at the latest, so every such wait depends only on heads that every
@@ -2558,7 +2587,10 @@ int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
   const int per_cu = c.wv_per_cu[D == 128 ? 1 : 0];
   if (per_cu <= 0) return 0;
   const int64_t G = static_cast<int64_t>(per_cu) * c.cus, W = G * kWvWaves, nt = wave_tiles(L);
-  if (nt < W || lay.BH * nt > INT32_MAX) return 0;
+  if (lay.BH * nt > INT32_MAX) return 0;
+  // heads shorter than a round: each workgroup takes one head per round, so
+  // only when the layer fills enough rounds for the votes' lag to pay off
+  if (nt < W && lay.BH * nt < static_cast<int64_t>(kWvMinRounds) * W) return 0;
   if (kst * 2 * 8 >= (int64_t(1) << 32) || qst * 2 * 32 >= (int64_t(1) << 32)) return 0;  // 32-bit lane offsets
   for (int64_t bh = 0; bh < lay.BH; ++bh) {
     const int64_t r0 = bh * nt / W, r1 = ((bh + 1) * nt - 1) / W;
