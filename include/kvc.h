@@ -127,7 +127,9 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
  *                once. snap_wave_bf16, whose waves work independently on
  *                32-key tiles, runs where every workgroup has tiles in every
  *                head and a head spans at most seven of its rounds (on MI355X:
- *                about 64K to 390K keys per head); it is launched like any
+ *                about 64K to 390K keys per head), or where heads are shorter
+ *                than one of its rounds (2048 tiles) and the layer fills at
+ *                least eight rounds (e.g. 64 heads of 16K keys); it is launched like any
  *                kernel and checks residency at its start: if its workgroups
  *                cannot all start within about a millisecond (other work
  *                holding the compute units), it flags every head and the
