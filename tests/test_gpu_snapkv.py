@@ -298,6 +298,13 @@ def test_single_pass_kernel_choice():
         k = torch.zeros((1, 2, L, 128), dtype=torch.bfloat16, device="cuda")
         _run(q, k, k, 32, 256, 7, "bf16", kvc.SNAPKV_AUTO)
         assert kvc.snapkv_last_score_kernel() == kernel, (L, kvc.snapkv_last_score_kernel())
+    # heads shorter than a round of the independent-wave kernel (512 tiles against 2048 workers):
+    # its short-head form once the layer fills eight rounds (32 heads of 16K keys), else two passes
+    for H, kernel in ((32, "snap_wave_bf16"), (8, "snap_stats_bf16+snap_votes_bf16")):
+        q = torch.zeros((1, H, 32, 128), dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros((1, H, 16384, 128), dtype=torch.bfloat16, device="cuda")
+        _run(q, k, k, 32, 1024, 7, "bf16", kvc.SNAPKV_AUTO)
+        assert kvc.snapkv_last_score_kernel() == kernel, (H, kvc.snapkv_last_score_kernel())
 
 
 def test_schedule_setting_rejects_unknown():
