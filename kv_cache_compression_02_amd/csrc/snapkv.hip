@@ -1123,9 +1123,14 @@ __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
 __device__ __forceinline__ void wv_next_ht(const WvCtx& c, int& head, int& t) {
   t += c.W;
   if (t >= c.nt) {
-    const int adv = t / c.nt;
-    t -= adv * c.nt;
-    head += adv;
+    if (c.small) {
+      const int adv = t / c.nt;
+      t -= adv * c.nt;
+      head += adv;
+    } else {
+      t -= c.nt;
+      ++head;
+    }
   }
 }
 
@@ -1306,7 +1311,7 @@ __device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int
 // contributions to land).
 __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane) {
   WvShared* sh = c.sh;
-  const int h = p.merge_head, sl = p.merge_idx & 1, ln = opaque(lane), col = ln & 31;
+  const int h = p.merge_head, idx = c.small ? p.merge_idx : h, sl = idx & 1, ln = opaque(lane), col = ln & 31;
   asm volatile("" ::: "memory");
   if (__builtin_amdgcn_readfirstlane(sh->mcnt[sl]) != kWvWaves) return;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1316,7 +1321,7 @@ __device__ __forceinline__ void wv_try_merge(const WvCtx& c, WvPipe& p, int lane
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sums read before the slot reopens
   if (ln == 0) {
     sh->mcnt[sl] = 0;
-    sh->mtag[sl] = p.merge_idx + 2;
+    sh->mtag[sl] = idx + 2;
   }
   asm volatile("" ::: "memory");
   if (ln < 32 && col < c.w) wv_add_sum(c.acc + static_cast<int64_t>(h) * kCoopHeadWords, col, L);
@@ -1553,7 +1558,9 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   }
 }
 
-template <int D>
+// SHORT: heads shorter than a round (a compile-time choice, so that the
+// long-head kernel carries none of the short-head code)
+template <int D, bool SHORT>
 __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int nt,
@@ -1574,8 +1581,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.H = H; c.L = L; c.w = w; c.t0 = L - w; c.nt = nt; c.BH = BH;
   c.fin = fin;
   c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x); c.W = c.G * kWvWaves;
-  c.small = nt < c.W;
-  c.tgt = c.small ? nt / kWvWaves : c.G;
+  c.small = SHORT;
+  c.tgt = SHORT ? nt / kWvWaves : c.G;
   c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
   c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   c.dk_tile = static_cast<int64_t>(c.W) * kTile * kst * 2;
@@ -1605,7 +1612,7 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   WvPos pos;
   {
     const int v = c.g * kWvWaves + c.wave;
-    pos.head = v / nt;
+    pos.head = SHORT ? v / nt : 0;
     pos.t = v - pos.head * nt;
     const int b = pos.head / H;
     pos.h = pos.head - b * H;
@@ -2532,8 +2539,8 @@ const CoopCaps& coop_caps() {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&n64, snap_coop_bf16<64>, kCoopThreads, 0) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&n128, snap_coop_bf16<128>, kCoopThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w64, snap_wave_bf16<64>, kWvThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w128, snap_wave_bf16<128>, kWvThreads, 0) == hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w64, snap_wave_bf16<64, false>, kWvThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w128, snap_wave_bf16<128, false>, kWvThreads, 0) == hipSuccess) {
       c.coop = coop != 0;
       c.cus = cus;
       c.per_cu[0] = n64;
@@ -2664,9 +2671,14 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
     const int nt = static_cast<int>(wave_tiles(L)), total = static_cast<int>(lay.BH * nt);
     const unsigned target = static_cast<unsigned>(Gw) + (g_force_residency_fail ? 1u : 0u);
     const unsigned spin = g_force_residency_fail ? 16u : kWvGateSpin;
-    snap_wave_bf16<D><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
-        q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref, acc,
-        cnt, stat, status, vote, gate, target, spin);
+    if (nt < Gw * kWvWaves)
+      snap_wave_bf16<D, true><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
+          q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref,
+          acc, cnt, stat, status, vote, gate, target, spin);
+    else
+      snap_wave_bf16<D, false><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
+          q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref,
+          acc, cnt, stat, status, vote, gate, target, spin);
     e = hipGetLastError();
     if (e == hipSuccess) {
       g_last_kernel = "snap_wave_bf16";
