@@ -102,6 +102,16 @@ def test_380k_full_sampled_heads(schedule):
     _workload(syn.SNAPKV_WORKLOADS["380k-bf16"], heads=[(0, 5), (0, 30)], schedule=schedule)
 
 
+def test_short_heads_d64_sampled_heads(schedule):
+    """32 heads of 16K keys at head dim 64: under the single pass, the independent-wave kernel's
+    short-head form at D = 64 (each workgroup one head per round)."""
+    wl = syn.SnapKVWorkload(name="short-d64", B=1, H=32, D=64, L=16384, window=32, budget=1024, pool_kernel=7,
+                            dtype="bf16", n_spans=12, span_len=8, span_boost=1.5, seed=1664)
+    _workload(wl, heads=[(0, 0), (0, 13), (0, 31)], schedule=schedule)
+    if schedule == kvc.SNAPKV_SINGLE_PASS:
+        assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
+
+
 EDGE = [
     # dtype, D, window, L, budget, pool
     ("bf16", 64, 1, 100, 2, 1),
