@@ -197,6 +197,9 @@ def bench_snapkv(args, ev):
     dec_att = time_decode(kvc, ev, q[:, :, -1].contiguous(), out.k, out.v, wl.budget, 200,
                           f"SnapKV-compressed {wl.name} layer B{B} H{H} {wl.budget} rows")
     phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / args.steps for j, p in enumerate(phases)}
+    # (single pass: nothing runs between marks 2 and 3; that interval is the events' own cost)
+    phase_ms.pop("none", None)
+    phases = [p for p in phases if p != "none"]
     step_ms = elapsed / args.steps * 1e3
     nbytes = snapkv_bytes(wl)
     dominant = "score" if single else max(("stats", "votes"), key=lambda p: kern_ms[p])

@@ -102,6 +102,17 @@ def test_380k_full_sampled_heads(schedule):
     _workload(syn.SNAPKV_WORKLOADS["380k-bf16"], heads=[(0, 5), (0, 30)], schedule=schedule)
 
 
+def test_short_heads_straddling_rounds(schedule):
+    """52 heads of 10000 keys (40 tile groups each, not a divisor of a round's 256): heads such as
+    head 6 start at the end of one round and finish at the start of the next, so two ranges of
+    workgroups count for them; the layer ends in a partial round."""
+    wl = syn.SnapKVWorkload(name="short-straddle", B=1, H=52, D=128, L=10000, window=32, budget=512,
+                            pool_kernel=7, dtype="bf16", n_spans=8, span_len=6, span_boost=1.5, seed=5252)
+    _workload(wl, heads=[(0, 0), (0, 6), (0, 32), (0, 51)], schedule=schedule)
+    if schedule == kvc.SNAPKV_SINGLE_PASS:
+        assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
+
+
 def test_short_heads_d64_sampled_heads(schedule):
     """32 heads of 16K keys at head dim 64: under the single pass, the independent-wave kernel's
     short-head form at D = 64 (each workgroup one head per round)."""
