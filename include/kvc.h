@@ -170,6 +170,18 @@ const char* kvc_snapkv_last_score_kernel(void);
  * workgroups cannot all be resident at once. Returns the previous setting. */
 int kvc_snapkv_force_residency_fallback(int on);
 
+/* Testing (not part of the method): while `on` is non-zero, the calling
+ * thread's single-pass calls run the independent-wave score kernel with a
+ * limit of zero polls on its cross-worker waits (vote weights, merge slots,
+ * a head's publication, the work owed after the last round): every wait that
+ * would have to wait gives up at once and records a failure code in the
+ * status word, exactly as a wait whose normal limit (2^18 polls) runs out.
+ * The kernel still exits normally. The pooling kernel reads the status word
+ * and recomputes every head's votes exactly, so the results are the same as
+ * without the knob (the votes may differ in the last bits). Returns the
+ * previous setting. */
+int kvc_snapkv_force_wait_timeout(int on);
+
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its
  * stream at phase boundary i, for i < n_events (at most 7) and events[i] not

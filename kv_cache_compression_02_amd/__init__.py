@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "kvc_last_error", "kvc_version", "kvc_snapkv_workspace_bytes", "kvc_snapkv_compress",
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
-    "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback",
+    "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback", "kvc_snapkv_force_wait_timeout",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention",
 )
 
@@ -135,6 +135,19 @@ def _dev(t, name):
     return t
 
 
+def _check_out(t, name, shape, dtype, device):
+    """A caller-supplied output: contiguous, of the documented shape and dtype, on the inputs' device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -199,14 +212,30 @@ def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, 
     B, H, L, D = k.shape
     dt = _dtype_code(k)
     dev = k.device
+    if q.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on one device")
+    if (q.shape[0], q.shape[1], q.shape[3]) != (B, H, D):
+        raise ValueError(f"q must be [B, H, q_len, D] = [{B}, {H}, *, {D}], got {tuple(q.shape)}")
+    if q.shape[2] < window:
+        raise ValueError(f"q holds {q.shape[2]} rows, fewer than the window {window}")
+    n_keep, n_pre = max(budget - window, 0), max(L - window, 0)
     if out is None:
         k_out = torch.empty((B, H, budget, D), dtype=k.dtype, device=dev)
         v_out = torch.empty_like(k_out)
-        idx = torch.empty((B, H, max(budget - window, 0)), dtype=torch.int32, device=dev)
-        pooled = torch.empty((B, H, L - window), dtype=torch.float32, device=dev) if want_pooled else None
-        vote = torch.empty((B, H, L - window), dtype=torch.float32, device=dev) if want_vote else None
+        idx = torch.empty((B, H, n_keep), dtype=torch.int32, device=dev)
+        pooled = torch.empty((B, H, n_pre), dtype=torch.float32, device=dev) if want_pooled else None
+        vote = torch.empty((B, H, n_pre), dtype=torch.float32, device=dev) if want_vote else None
     else:
         k_out, v_out, idx, pooled, vote = out
+        _check_out(k_out, "out.k", (B, H, budget, D), k.dtype, dev)
+        _check_out(v_out, "out.v", (B, H, budget, D), k.dtype, dev)
+        _check_out(idx, "out.idx", (B, H, n_keep), torch.int32, dev)
+        if pooled is not None:
+            _check_out(pooled, "out.pooled", (B, H, n_pre), torch.float32, dev)
+        if vote is not None:
+            _check_out(vote, "out.vote", (B, H, n_pre), torch.float32, dev)
+    if workspace is not None:
+        _check_out(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
     if workspace is None:
         nbytes = snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, k.dtype)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -238,8 +267,14 @@ def decode_attention(q, k, v, n=None, *, workspace=None, out=None):
     if tuple(q.shape) != (B, H, D):
         raise ValueError("q must be [B, H, D] matching k")
     n = N if n is None else int(n)
+    if not 1 <= n <= N:
+        raise ValueError(f"n = {n} must lie in 1 .. {N}")
+    if q.device != k.device or v.device != k.device:
+        raise ValueError("q, k, v must be on one device")
     if out is None:
         out = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    else:
+        _check_out(out, "out", (B, H, D), torch.float32, k.device)
     if workspace is None:
         nbytes = decode_attention_workspace_bytes(B, H, n, D)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=k.device)
@@ -277,6 +312,9 @@ class H2OCache:
         if k.shape != v.shape or k.stride() != v.stride() or q.shape != k.shape:
             raise ValueError("q, k, v must share one shape, and k, v one set of strides")
         B, H, Lp, D = k.shape
+        if (B, H, D) != (self.k.shape[0], self.k.shape[1], self.k.shape[3]) or k.device != self.k.device:
+            raise ValueError(f"prompt [B, H, *, D] = {tuple(k.shape)} does not match the cache "
+                             f"{tuple(self.k.shape)} on {self.k.device}")
         if workspace is None:
             nbytes = int(library().kvc_h2o_prefill_workspace_bytes(B, H, Lp))
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
@@ -286,10 +324,14 @@ class H2OCache:
 
     def step(self, q, k_new, v_new, n_heavy, n_recent, attn_out=None):
         """One decode step for every head; q, k_new, v_new: [B, H, D] contiguous."""
+        B, H, _, D = self.k.shape
         for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
             _dev(t, n)
             if not t.is_contiguous() or t.dtype != self.k.dtype:
                 raise ValueError(f"{n} must be contiguous with the cache's dtype")
+            _check_out(t, n, (B, H, D), self.k.dtype, self.k.device)
+        if attn_out is not None:
+            _check_out(attn_out, "attn_out", (B, H, D), torch.float32, self.k.device)
         _check(library().kvc_h2o_step(ctypes.byref(self._c), _ptr(q), _ptr(k_new), _ptr(v_new),
                                       n_heavy, n_recent, _ptr(attn_out), _stream()))
         return attn_out
@@ -310,6 +352,9 @@ class SinkCache:
 
     def append(self, k_new, v_new):
         """Write one new token ([B, H, D] contiguous); return the held positions, ascending."""
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _dev(t, n)
+            _check_out(t, n, (self.B, self.H, self.D), self.k.dtype, self.k.device)
         self.length += 1
         n_kept = min(self.length, self.n_sink + self.n_recent)
         _check(library().kvc_sink_recent(

@@ -8,23 +8,38 @@
 // top-scoring prefix positions and their K/V rows are concatenated with the
 // window's own rows.
 //
-// Kernel sequence per call (all on the caller's stream, no host sync):
-//   zero      clear per-head counters and histograms in the workspace
-//   stats     window scores q.k/sqrt(D) on MFMA (bf16) or VALU (fp32) for a
-//             chunk of keys; per-row running max / sum of 2^(s - m) (two-pass
-//             softmax, pass 1)
-//   merge     combine the chunk partials into each row's max and 1/sum
-//   votes     recompute the scores of the prefix keys, normalise with the merged
-//             row statistics and sum over the window rows (pass 2); max-pool
-//             the chunk (its halo keys are recomputed) and histogram the top 12
-//             bits of the pooled values per head
-//   classify  find the histogram bin that holds the k-th largest pooled score;
-//             emit positions above that bin (kept for sure) and the bin's
-//             members (candidates) to per-head lists
-//   finalize  radix-select the remaining picks among the candidates on the key
-//             (score desc, position asc); mark the kept positions in a bitmap
-//             and compact it into ascending positions
-//   gather    copy the kept K/V rows and the window rows into the outputs
+// Kernel sequence per call (all on the caller's stream, no host sync). Two
+// score schedules share the selection and the gather:
+//
+// single pass (bf16, the default where it runs):
+//   snap_coop_prep   per head: clear the workspace state; each window row's
+//                    reference score R_i (its largest score against the
+//                    window keys it sees) from one wave of MFMA
+//   snap_wave_bf16   persistent grid of independent waves over 32-key tiles:
+//                    MFMA scores, e_ij = 2^(s_ij - R_i) kept in registers,
+//                    row sums merged exactly in fixed point across the grid,
+//                    votes once the head's normaliser is published (K read
+//                    once); snap_coop_bf16 is the lockstep form for shorter
+//                    heads
+//   snap_pool        max-pool of the votes and the per-head 12-bit histogram
+//                    of pooled scores (exact votes recomputed first for any
+//                    head the score kernel flagged, or every head if its
+//                    status word reports a wait that ran out)
+// two passes (fp32, or where the single pass cannot run):
+//   snap_stats_*     per chunk of keys: each window row's max and sum of
+//                    2^(s - m) (softmax pass 1); clears the counters
+//   snap_stats_merge each row's (max, 1/sum) from the chunk partials
+//   snap_votes_*     scores again, normalised and summed over the window rows
+//                    (pass 2), max-pooled in LDS with a recomputed halo, and
+//                    the histogram of pooled scores
+// then, for both:
+//   snap_select      per head: the histogram bin holding the k-th largest
+//                    pooled score; positions above it go straight to a
+//                    bitmap, the bin's members are ranked by (score desc,
+//                    position asc); the head's last workgroup compacts the
+//                    bitmap into ascending positions (pooling the raw votes
+//                    itself for radii up to 4 under the single pass)
+//   snap_gather      copy the kept K/V rows and the window rows to the outputs
 //
 // Scores live in the base-2 domain: s2 = (q.k) * log2(e)/sqrt(D), so the
 // softmax is 2^(s2 - m2) / sum; it equals exp(s - m)/sum exactly in real
@@ -543,9 +558,11 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, float scale_log2,
     float* __restrict__ ref, unsigned long long* __restrict__ acc, unsigned* __restrict__ cnt,
-    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ sel_ctr, unsigned* __restrict__ gate) {
+    uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ sel_ctr,
+    unsigned* __restrict__ status) {
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
-  if (bh == 0 && threadIdx.x < 2) gate[threadIdx.x] = 0;
+  // status[0]: the score kernel's failure code; status[1], status[2]: its residency gate
+  if (bh == 0 && threadIdx.x < 3) status[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
@@ -1022,6 +1039,7 @@ constexpr int kWvFinBufs = 4;    // finisher staging buffers, by head mod 4
 constexpr int kWvMaxSpan = kWvBanks - 3;  // a head spans at most this many rounds after its first
 constexpr int kWvMinRounds = 8;            // rounds a layer of heads shorter than a round must fill
 constexpr unsigned kWvSpin = 1u << 18;  // polls before a wait gives up (far beyond any legitimate wait)
+constexpr unsigned kWvSpinForced = 0u;   // the testing limit: every wait that has to wait gives up
 constexpr int kWvOvfWord = 20;   // a non-finite row sum adds its count here (the head is then flagged)
 constexpr unsigned long long kWvCountOne = 1ull << 48;
 
@@ -1064,6 +1082,7 @@ struct WvCtx {
   int tgt;     // workgroups that contribute to each head: G, or nt / kWvWaves when a head is shorter than a round
   bool small;  // a head is shorter than a round: every workgroup takes a new head every round
   int64_t dk_tile, dk_head, dk_batch, dq_head, dq_batch;  // byte steps of WvPos::kt and WvPos::qb
+  unsigned spin;  // polls before a cross-worker wait gives up (kWvSpin; kWvSpinForced for tests)
   float scale_log2;
   const float* ref;
   unsigned long long* acc;
@@ -1281,7 +1300,7 @@ __device__ __forceinline__ void wv_stage(const WvCtx& c, int h, int lane) {
 __device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int lane) {
   const int ln = opaque(lane), row = ln & 31;
   const WvFin& f = c.fin[h & (kWvFinBufs - 1)];
-  for (unsigned t = 0; t < kWvSpin; ++t) {
+  for (unsigned t = 0; t < c.spin; ++t) {
     wv_stage(c, h, ln);
     wait_vm_all();
     unsigned count;
@@ -1386,7 +1405,7 @@ __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, c
       wait_vm_all();  // every exit from here has its load back
       wv_service(c, p, lane);  // what this wave owes others may be what it waits for
       late = __ballot(row < c.w && pre.y != 1u) != 0ull;
-    } while (late && ++polls < kWvSpin);
+    } while (late && ++polls < c.spin);
     if (late) {  // a protocol failure: record it and never wait again
       p.gave_up = true;
       if (lane == 0) __hip_atomic_store(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1457,7 +1476,7 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, in
       wv_service(c, p, ln);
       asm volatile("" ::: "memory");
       late = sh->mtag[sl] != idx;
-    } while (late && ++polls < kWvSpin);
+    } while (late && ++polls < c.spin);
     if (late) {
       p.gave_up = true;
       if (ln == 0) __hip_atomic_store(c.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1566,7 +1585,7 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int nt,
     int total_tiles, int BH, float scale_log2, const float* __restrict__ ref, unsigned long long* __restrict__ acc,
     unsigned* __restrict__ cnt, uint2* __restrict__ stat, unsigned* __restrict__ status, float* __restrict__ vote,
-    unsigned* __restrict__ gate, unsigned gate_target, unsigned gate_spin) {
+    unsigned* __restrict__ gate, unsigned gate_target, unsigned gate_spin, unsigned wait_spin) {
   using Ly = WvLayout<D>;
   // the two tile slots of every wave's ring, as two arrays: the reads of one
   // slot are then known not to alias the direct loads in flight into the other
@@ -1590,6 +1609,7 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.dk_batch = (ksb - H * ksh) * 2;
   c.dq_head = qsh * 2;
   c.dq_batch = (qsb - H * qsh) * 2;
+  c.spin = wait_spin;
   c.scale_log2 = scale_log2;
   c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.status = status; c.vote = vote;
   c.sh = &sh;
@@ -1687,7 +1707,7 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   }
   // work still owed after the last round: a pending merge, heads still to
   // finish (bounded)
-  for (unsigned t = 0; (p.merge_head >= 0 || p.fin_head < c.BH) && !p.gave_up && t < kWvSpin; ++t) {
+  for (unsigned t = 0; (p.merge_head >= 0 || p.fin_head < c.BH) && !p.gave_up && t < c.spin; ++t) {
     wait_vm_all();
     __builtin_amdgcn_s_sleep(2);
     wv_service(c, p, lane_id());
@@ -1697,8 +1717,9 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
 }
 
 // Exact votes of the heads the single pass flagged (a score more than 2^127
-// above its row's reference, or every head when the independent-wave kernel's
-// workgroups could not all be resident), recomputed in fp32 by the pooling
+// above its row's reference; every head when the independent-wave kernel's
+// workgroups could not all be resident, or when a bounded wait of a score
+// kernel ran out, which leaves a non-zero status word), recomputed in fp32 by the pooling
 // kernel's workgroups, each for the positions it pools: one plain pass over
 // the head's keys gives every window row's (max, sum of 2^(s - m)), then the
 // vote of a position is sum_i 2^(s_i - c_i) with c_i = m_i + log2 sum_i.
@@ -1712,7 +1733,8 @@ struct ExactArgs {
   int64_t ksb, ksh, kst;
   int H, L, w, D;
   float scale_log2;
-  const unsigned* flags;  // per head at word 16 of its counters; NULL: no head is flagged
+  const unsigned* flags;   // per head at word 16 of its counters; NULL: no head is flagged
+  const unsigned* status;  // the score kernel's failure code (non-zero: every head flagged); NULL: none
 };
 
 struct ExactShared {
@@ -1729,7 +1751,7 @@ union PoolShared {
 };
 
 __device__ __forceinline__ bool exact_flagged(const ExactArgs& a, int bh) {
-  return a.flags && a.flags[bh * kCoopCtrWords + 16] != 0u;
+  return (a.status && a.status[0] != 0u) || (a.flags && a.flags[bh * kCoopCtrWords + 16] != 0u);
 }
 
 // Rows 8g .. 8g+7 of the window's fp32 scores against key j (rows past w
@@ -2608,6 +2630,7 @@ int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
 
 thread_local const char* g_last_kernel = "";
 thread_local bool g_force_residency_fail = false;
+thread_local bool g_force_wait_timeout = false;
 
 template <int R>
 void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, const ExactArgs& ea,
@@ -2659,26 +2682,30 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   unsigned* gate = status + 1;
   snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
       q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist,
-      reinterpret_cast<unsigned*>(ws + lay.sel_ctr), gate);
+      reinterpret_cast<unsigned*>(ws + lay.sel_ctr), status);
   mark_phase(1, stream);
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
   hipError_t e = hipErrorInvalidValue;
-  ExactArgs ea{q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, D, scale_log2, nullptr};
+  // the pooling kernel reads the status word after either score kernel: a
+  // wait that ran out leaves it non-zero, and every head's votes are then
+  // recomputed exactly
+  ExactArgs ea{q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, D, scale_log2, nullptr, status};
   if (Gw > 0) {
     // an ordinary launch: the kernel checks residency itself (a cooperative
     // launch would guarantee it, at ~10 us of extra queue work on each side)
     const int nt = static_cast<int>(wave_tiles(L)), total = static_cast<int>(lay.BH * nt);
     const unsigned target = static_cast<unsigned>(Gw) + (g_force_residency_fail ? 1u : 0u);
     const unsigned spin = g_force_residency_fail ? 16u : kWvGateSpin;
+    const unsigned wait_spin = g_force_wait_timeout ? kWvSpinForced : kWvSpin;
     if (nt < Gw * kWvWaves)
       snap_wave_bf16<D, true><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
           q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref,
-          acc, cnt, stat, status, vote, gate, target, spin);
+          acc, cnt, stat, status, vote, gate, target, spin, wait_spin);
     else
       snap_wave_bf16<D, false><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
           q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref,
-          acc, cnt, stat, status, vote, gate, target, spin);
+          acc, cnt, stat, status, vote, gate, target, spin, wait_spin);
     e = hipGetLastError();
     if (e == hipSuccess) {
       g_last_kernel = "snap_wave_bf16";
@@ -2726,6 +2753,12 @@ extern "C" const char* kvc_snapkv_last_score_kernel(void) { return g_last_kernel
 extern "C" int kvc_snapkv_force_residency_fallback(int on) {
   const int prev = g_force_residency_fail ? 1 : 0;
   g_force_residency_fail = on != 0;
+  return prev;
+}
+
+extern "C" int kvc_snapkv_force_wait_timeout(int on) {
+  const int prev = g_force_wait_timeout ? 1 : 0;
+  g_force_wait_timeout = on != 0;
   return prev;
 }
 

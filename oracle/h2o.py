@@ -26,6 +26,8 @@ Readings adopted where the page is silent (each is listed in the design notes):
 """
 import numpy as np
 
+from .snapkv import to_f64
+
 
 class HeadState:
     """Cached tokens of one head: positions, cumulative scores, raw key/value rows."""
@@ -41,15 +43,6 @@ class HeadState:
 
     def __len__(self):
         return self.pos.shape[0]
-
-
-def _to_f64(x, dtype):
-    if dtype == "fp64":
-        return np.asarray(x, dtype=np.float64)
-    if dtype == "bf16":
-        return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
-            np.float32).astype(np.float64)
-    return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
 def evict(pos, acc, length, n_heavy, n_recent):
@@ -86,11 +79,11 @@ def step_head(st, q, k_new, v_new, length, n_heavy, n_recent, dtype):
     K = np.concatenate([st.k, np.asarray(k_new)[None]], axis=0)
     V = np.concatenate([st.v, np.asarray(v_new)[None]], axis=0)
     D = K.shape[1]
-    s = _to_f64(K, dtype) @ _to_f64(q, dtype) / np.sqrt(D)
+    s = to_f64(K, dtype) @ to_f64(q, dtype) / np.sqrt(D)
     e = np.exp(s - s.max())
     p = e / e.sum()
     acc = acc + p
-    o = p @ _to_f64(V, dtype)
+    o = p @ to_f64(V, dtype)
     keep = evict(pos, acc, length, n_heavy, n_recent)
     return HeadState(pos[keep], acc[keep], K[keep], V[keep]), p, o
 
@@ -102,7 +95,7 @@ def prefill_head(q, k, v, n_heavy, n_recent, dtype):
     softmax weight P[i, j]; then the eviction rule at length = prompt length.
     Returns (state, colsum) where colsum [Lp] is the score before eviction.
     """
-    qf, kf = _to_f64(q, dtype), _to_f64(k, dtype)
+    qf, kf = to_f64(q, dtype), to_f64(k, dtype)
     Lp, D = kf.shape
     S = qf @ kf.T / np.sqrt(D)
     S[np.triu_indices(Lp, 1)] = -np.inf

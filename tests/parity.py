@@ -21,6 +21,12 @@ REL = 1e-3
 VOTE_ABS = 2e-3
 VOTE_REL = 1e-4
 VOTE_FLOOR = 1e-9
+# A tighter band for the kept set, implied by the bound above: when every GPU
+# pooled score is within VOTE_REL |ref| + VOTE_FLOOR of the oracle's, two
+# positions whose oracle scores differ by more than ~2 VOTE_REL relative (plus
+# the floor over scores near 1e-5) keep their order on the GPU, so only
+# positions within REL_TIGHT of the threshold may be chosen differently.
+REL_TIGHT = 3e-4
 
 
 def to_device(arr, dtype):
@@ -91,3 +97,24 @@ def check_gather(k_out, v_out, k_in, v_in, idx_gpu, t0):
     np.testing.assert_array_equal(v_out[:kk], v_in[idx_gpu])
     np.testing.assert_array_equal(k_out[kk:], k_in[t0:])
     np.testing.assert_array_equal(v_out[kk:], v_in[t0:])
+
+
+def check_topk_self(pooled_gpu, idx_gpu, kk):
+    """The GPU's kept list is exactly the top-kk of the GPU's own pooled scores under the tie rule
+    (larger score first, equal scores: lower position first), ascending. Integer work on the GPU's
+    float32 values, so it must hold bit for bit at any size, near-ties and plateaus included."""
+    p = np.asarray(pooled_gpu, np.float32)
+    idx_gpu = np.asarray(idx_gpu, np.int64)
+    n = p.shape[0]
+    assert idx_gpu.shape == (kk,), f"expected {kk} indices, got {idx_gpu.shape}"
+    assert np.all(np.diff(idx_gpu) > 0), "indices must be strictly ascending"
+    assert idx_gpu[0] >= 0 and idx_gpu[-1] < n, "index out of range"
+    # the kk-th largest key (score desc, position asc): everything strictly above
+    # the threshold score is kept, and among positions equal to it the lowest ones
+    thr = np.partition(p, n - kk)[n - kk]
+    above = np.flatnonzero(p > thr)
+    equal = np.flatnonzero(p == thr)
+    want = np.sort(np.concatenate([above, equal[:kk - above.size]]))
+    assert np.array_equal(idx_gpu, want), (
+        f"not the top-{kk} of the GPU's own scores: {np.setdiff1d(want, idx_gpu)[:8]} missing, "
+        f"{np.setdiff1d(idx_gpu, want)[:8]} extra")

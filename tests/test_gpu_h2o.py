@@ -259,3 +259,72 @@ def test_h2o_error_statuses():
     with pytest.raises(kvc.KvcError) as e:
         c.step(x, x, x, -1, 2)
     assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_h2o_decode_full_loop_sampled_heads():
+    """The whole decode workload: GPU prefill of the 2048-token prompt of all 64 x 32 heads, then all
+    2048 decode steps. The oracle steps six sampled heads through every step from its own prefill;
+    every 64th step and the last, the sampled heads' kept positions, scores and attention output are
+    sliced on the GPU and compared. A head whose set differs is dropped only if the oracle saw a
+    near-tie eviction (within REL) since the last check; at most a quarter of the heads may end so."""
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"]
+    heads = [(0, 0), (7, 19), (21, 5), (38, 31), (50, 12), (63, 27)]
+    steps, every = wl.steps, 64
+    print(f"[h2o-loop] B{wl.B} H{wl.H} prompt {wl.prompt_len} + {steps} steps, heads {heads}", flush=True)
+    cache = kvc.H2OCache(wl.B, wl.H, wl.D, wl.cap)
+    qn, kn, vn = syn.h2o_prompt_batch(wl)
+    Lp = wl.prompt_len
+    q, k, v = (par.to_device(x, wl.dtype) for x in (qn, kn, vn))
+    cache.prefill(q, k, v, wl.n_heavy(Lp), wl.n_recent(Lp))
+    del q, k, v
+    states = {}
+    for b, h in heads:
+        states[(b, h)], _ = ref.prefill_head(qn[b, h], kn[b, h], vn[b, h], wl.n_heavy(Lp), wl.n_recent(Lp), wl.dtype)
+    del qn, kn, vn
+    bi = torch.tensor([b for b, _ in heads], device="cuda")
+    hi = torch.tensor([h for _, h in heads], device="cuda")
+    out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.float32, device="cuda")
+    live = set(heads)
+    tie_since_check = set()
+    diverged = {}
+    checks = 0
+    for s_ in range(steps):
+        length = Lp + s_ + 1
+        hh, r = wl.n_heavy(length), wl.n_recent(length)
+        x = syn.h2o_step_inputs(wl, s_)
+        cache.step(*(par.to_device(a, wl.dtype) for a in x), hh, r, attn_out=out)
+        outs = {}
+        for bh in live:
+            b, h = bh
+            pre = states[bh]
+            st, p, o = ref.step_head(pre, x[0][b, h], x[1][b, h], x[2][b, h], length, hh, r, wl.dtype)
+            gap = _eviction_gap(pre, p, length, hh, r)
+            if gap is not None and gap[0] - gap[1] <= par.REL * abs(gap[0]):
+                tie_since_check.add(bh)
+            states[bh] = st
+            outs[bh] = (o, p @ np.abs(_widen(np.concatenate([pre.v, x[2][b, h][None]]), wl.dtype)))
+        if (s_ + 1) % every and s_ + 1 != steps:
+            continue
+        checks += 1
+        n = cache.n
+        pos_g = cache.pos[bi, hi, :n].cpu().numpy()
+        acc_g = cache.acc[bi, hi, :n].cpu().numpy()
+        out_g = out[bi, hi].cpu().numpy()
+        for i, bh in enumerate(heads):
+            if bh not in live:
+                continue
+            st = states[bh]
+            assert len(st) == n, f"{bh} step {length}: oracle holds {len(st)}, GPU {n}"
+            if set(pos_g[i].tolist()) != set(st.pos.tolist()):
+                assert bh in tie_since_check, f"{bh} step {length}: kept sets differ with no near-tie eviction"
+                diverged[bh] = length
+                live.discard(bh)
+                continue
+            o, scale = outs[bh]
+            par.assert_close_votes(out_g[i], o, f"o{bh}@{length}", scale=scale)
+            par.assert_close_votes(acc_g[i][np.argsort(pos_g[i])], st.acc[np.argsort(st.pos)], f"acc{bh}@{length}")
+        tie_since_check.clear()
+    print(f"[h2o-loop] {checks} checks; compared to the end: {len(live)} heads; diverged after near-ties: "
+          f"{diverged}", flush=True)
+    assert checks == steps // every
+    assert len(diverged) <= len(heads) // 4

@@ -153,3 +153,66 @@ def test_prefill_equals_stepping_from_empty():
     assert set(range(Lp - 4, Lp)) <= set(st3.pos.tolist()) and len(st3) == 8
     rest = [j for j in np.argsort(-colsum, kind="stable") if j < Lp - 4][:4]
     assert set(rest) <= set(st3.pos.tolist())
+
+
+def _bf16_bits_via_torch(x32):
+    """bf16 bit patterns of float32 values, rounded by torch (a library the oracle does not call)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def test_widening_matches_torch_and_known_encodings():
+    """The oracle's exact widening of stored inputs: bf16 bit patterns against torch's own widening and
+    a few encodings fixed by the bfloat16 format (sign, 8-bit exponent, 7-bit fraction), fp32 unchanged."""
+    import torch
+
+    from oracle.snapkv import to_f64
+
+    known = {0x3F80: 1.0, 0xC000: -2.0, 0x3F81: 1.0 + 2.0 ** -7, 0x0000: 0.0, 0x8000: -0.0,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x0001: 2.0 ** -133, 0x4049: 3.140625}
+    bits = np.array(list(known), np.uint16)
+    got = to_f64(bits, "bf16")
+    np.testing.assert_array_equal(got, np.array(list(known.values())))
+    rng = np.random.default_rng(3)
+    x = _bf16_bits_via_torch(rng.standard_normal(4096).astype(np.float32) * 10)
+    via_torch = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(to_f64(x, "bf16"), via_torch)
+    f = rng.standard_normal(100).astype(np.float32)
+    np.testing.assert_array_equal(to_f64(f, "fp32"), f.astype(np.float64))
+    assert to_f64(f, "fp32").dtype == np.float64
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_step_and_prefill_on_stored_types_equal_fp64_on_widened_values(dtype):
+    """step_head / prefill_head on bf16 bit patterns or fp32 arrays give exactly what the fp64 run gives on
+    the same values widened by torch (so the stored-type branch neither drops, shifts nor masks bits)."""
+    import torch
+
+    rng = np.random.default_rng(11 if dtype == "bf16" else 12)
+    Lp, D, steps = 40, 64, 12
+    x = rng.standard_normal((3, Lp + steps, D)).astype(np.float32)
+    if dtype == "bf16":
+        stored = _bf16_bits_via_torch(x)
+        wide = torch.from_numpy(stored.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    else:
+        stored = x
+        wide = torch.from_numpy(x).to(torch.float64).numpy()
+    q, k, v = stored
+    qw, kw, vw = wide
+    st_s, col_s = ref.prefill_head(q[:Lp], k[:Lp], v[:Lp], 6, 5, dtype)
+    st_w, col_w = ref.prefill_head(qw[:Lp], kw[:Lp], vw[:Lp], 6, 5, "fp64")
+    np.testing.assert_array_equal(col_s, col_w)
+    np.testing.assert_array_equal(st_s.pos, st_w.pos)
+    np.testing.assert_array_equal(st_s.acc, st_w.acc)
+    for t in range(steps):
+        length = Lp + t + 1
+        st_s, p_s, o_s = ref.step_head(st_s, q[length - 1], k[length - 1], v[length - 1], length, 6, 5, dtype)
+        st_w, p_w, o_w = ref.step_head(st_w, qw[length - 1], kw[length - 1], vw[length - 1], length, 6, 5, "fp64")
+        np.testing.assert_array_equal(p_s, p_w)
+        np.testing.assert_array_equal(o_s, o_w)
+        np.testing.assert_array_equal(st_s.pos, st_w.pos)
+        np.testing.assert_array_equal(st_s.acc, st_w.acc)
+    # the kept rows are the stored rows themselves (raw bits), not widened copies
+    assert st_s.k.dtype == stored.dtype
