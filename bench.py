@@ -4,12 +4,16 @@
 Default run (N = 1 GPU):
   * SnapKV compression of one 131K-token layer (B1 H32 D128 L131072, window 32,
     budget 2048, max-pool 7, bf16): a step is one full kvc_snapkv_compress call
-    (window scores, two-pass softmax, vote, pool, top-k, gather) over inputs
+    (window scores, softmax normalisers, vote, pool, top-k, gather) over inputs
     already resident in HBM. value = prompt tokens compressed per second.
+  * The other SnapKV layers (tiny fp32, 16K batch 2, 380K) are timed the same
+    way and reported under "workloads", each with its own roofline.
+  * Consecutive steps rotate over enough device copies of K and V that a step
+    never finds the previous step's K in the 256 MB infinity cache (MALL).
   * The H2O + StreamingLLM decode loop of an OPT-6.7B-shaped layer (B64 H32
     D128, 2048-token prompt then 2048 decode steps, budget len//10 heavy +
     len//10 recent, sink 4 + recent 1020 ring) is measured as a second object.
-  * The CPU oracle is timed on a bounded sample of the same SnapKV workload.
+  * The CPU oracle is timed on bounded samples of the same workloads.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -49,6 +53,8 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-h2o", action="store_true")
     ap.add_argument("--h2o-steps", type=int, default=2048, help="timed decode steps (<= 2048)")
+    ap.add_argument("--skip-extra", action="store_true", help="only the 131K layer (no tiny / 16K / 380K lines)")
+    ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of each extra SnapKV layer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     return ap.parse_args()
@@ -113,94 +119,121 @@ def snapkv_bytes(wl):
     q_read = BH * wl.window * wl.D * es
     gather = 4 * BH * wl.budget * wl.D * es
     idx = 4 * BH * (wl.budget - wl.window)
-    votes_out = 4 * BH * (wl.L - wl.window)
+    # a score kernel's share: K once and the window queries (votes and row
+    # statistics are workspace and not counted); the two-pass vote pass reads
+    # the prefix keys again
     return dict(total=k_read + q_read + gather + idx, stats=k_read + q_read,
                 votes=BH * (wl.L - wl.window) * wl.D * es + q_read,
-                score=k_read + q_read + votes_out, gather=gather + idx)
+                score=k_read + q_read, gather=gather + idx)
 
 
-def bench_snapkv(args, ev):
+MALL_BYTES = 256 << 20
+
+
+def n_copies(wl):
+    """Device copies of K and V the timed steps rotate over: enough that at least twice the MALL's
+    256 MB of other keys is read between two reads of one copy."""
+    es = 2 if wl.dtype == "bf16" else 4
+    k_bytes = wl.B * wl.H * wl.L * wl.D * es
+    return 1 + -(-2 * MALL_BYTES // k_bytes)
+
+
+def put_host(x, dtype):
     import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
+    """Time kvc_snapkv_compress on one layer: `steps` calls back to back with no events in the stream
+    (the step time), the same calls again with events around the score kernel(s) only (the dominant
+    kernel's launch time) and, with `detail`, once more with every phase boundary marked."""
     import torch
 
     import kv_cache_compression_02_amd as kvc
     import synthetic as syn
 
-    wl = syn.SNAPKV_WORKLOADS[args.workload]
     log(f"generating {wl.name}: B{wl.B} H{wl.H} D{wl.D} L{wl.L} w{wl.window} C{wl.budget} p{wl.pool_kernel}")
     t = time.time()
     qn, kn, vn = syn.snapkv_batch(wl)
     log(f"generated in {time.time() - t:.1f}s")
-
-    def put(x):
-        if wl.dtype == "bf16":
-            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(x).cuda()
-
-    q, k, v = put(qn), put(kn), put(vn)
-    B, H, L, D = k.shape
-    out = kvc.SnapKVResult(torch.empty((B, H, wl.budget, D), dtype=k.dtype, device="cuda"),
-                           torch.empty((B, H, wl.budget, D), dtype=k.dtype, device="cuda"),
+    ncp = n_copies(wl)
+    q = put_host(qn, wl.dtype)
+    k0, v0 = put_host(kn, wl.dtype), put_host(vn, wl.dtype)
+    if not keep_host:
+        del kn, vn
+        kn = vn = None
+    ks, vs = [k0], [v0]
+    for _ in range(ncp - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    log(f"{ncp} device copies of K and V ({ncp * 2 * k0.numel() * k0.element_size() / 2**30:.2f} GiB)")
+    B, H, L, D = k0.shape
+    out = kvc.SnapKVResult(torch.empty((B, H, wl.budget, D), dtype=k0.dtype, device="cuda"),
+                           torch.empty((B, H, wl.budget, D), dtype=k0.dtype, device="cuda"),
                            torch.empty((B, H, wl.budget - wl.window), dtype=torch.int32, device="cuda"),
                            None, None)
-    ws = torch.empty(kvc.snapkv_workspace_bytes(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k.dtype),
+    ws = torch.empty(kvc.snapkv_workspace_bytes(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k0.dtype),
                      dtype=torch.uint8, device="cuda")
     lib = kvc.library()
     n_ev = len(PHASES) + 1
 
-    def call():
-        kvc.snapkv_compress(q, k, v, wl.window, wl.budget, wl.pool_kernel, workspace=ws, out=out)
+    def call(i):
+        kvc.snapkv_compress(q, ks[i % ncp], vs[i % ncp], wl.window, wl.budget, wl.pool_kernel, workspace=ws,
+                            out=out)
 
     def set_events(arr):
         lib.kvc_snapkv_set_phase_events(ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
                                         n_ev if arr is not None else 0)
 
     lib.kvc_snapkv_set_schedule(SCHEDULES[args.schedule])
-    for _ in range(args.warmup):
-        call()
+    for i in range(warmup):
+        call(i)
     torch.cuda.synchronize()
     single = kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
     score_kernel = kvc.snapkv_last_score_kernel()
     phases = PHASES_SINGLE if single else PHASES
     passes = ("score", "pool") if single else ("stats", "votes")
     log(f"schedule: {'single pass' if single else 'two passes'} ({score_kernel})")
-    # Timed region: K steps back to back with no events in the stream (a
+    # Timed region: the steps back to back with no events in the stream (a
     # recorded event between two kernels costs the GPU several microseconds).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        call()
+    for i in range(steps):
+        call(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # The same K steps again with events around the score passes only
+    # The same steps again with events around the score passes only
     # (boundaries 1 to 4): 1 -> 2 is the statistics pass or the single score
     # kernel, 3 -> 4 the vote pass or the pooling kernel.
-    timed = [ev.create(4) for _ in range(args.steps)]
+    timed = [ev.create(4) for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         arr = (ctypes.c_void_p * n_ev)()
         arr[1], arr[2], arr[3], arr[4] = timed[i]
         set_events(arr)
-        call()
+        call(i)
     torch.cuda.synchronize()
     set_events(None)
-    kern_ms = {passes[0]: sum(ev.ms(e[0], e[1]) for e in timed) / args.steps,
-               passes[1]: sum(ev.ms(e[2], e[3]) for e in timed) / args.steps}
-    # Untimed instrumented pass: every phase boundary, for the breakdown only.
-    events = [ev.create(n_ev) for _ in range(args.steps)]
-    for i in range(args.steps):
-        set_events(events[i])
-        call()
-    torch.cuda.synchronize()
-    set_events(None)
+    kern_ms = {passes[0]: sum(ev.ms(e[0], e[1]) for e in timed) / steps,
+               passes[1]: sum(ev.ms(e[2], e[3]) for e in timed) / steps}
+    phase_ms = None
+    if detail:
+        # Untimed instrumented pass: every phase boundary, for the breakdown only.
+        events = [ev.create(n_ev) for _ in range(steps)]
+        for i in range(steps):
+            set_events(events[i])
+            call(i)
+        torch.cuda.synchronize()
+        set_events(None)
+        phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / steps for j, p in enumerate(phases)}
+        # (single pass: nothing runs between marks 2 and 3; that interval is the events' own cost)
+        phase_ms.pop("none", None)
     lib.kvc_snapkv_set_schedule(0)
-    dec_att = time_decode(kvc, ev, q[:, :, -1].contiguous(), out.k, out.v, wl.budget, 200,
-                          f"SnapKV-compressed {wl.name} layer B{B} H{H} {wl.budget} rows")
-    phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / args.steps for j, p in enumerate(phases)}
-    # (single pass: nothing runs between marks 2 and 3; that interval is the events' own cost)
-    phase_ms.pop("none", None)
-    phases = [p for p in phases if p != "none"]
-    step_ms = elapsed / args.steps * 1e3
+    step_ms = elapsed / steps * 1e3
     nbytes = snapkv_bytes(wl)
     dominant = "score" if single else max(("stats", "votes"), key=lambda p: kern_ms[p])
     dom_bytes = nbytes[dominant]
@@ -208,47 +241,133 @@ def bench_snapkv(args, ev):
     suffix = "bf16" if wl.dtype == "bf16" else "f32"
     kernel_name = score_kernel if single else f"snap_{dominant}_{suffix}"
     traffic = load_traffic(kernel_name, ["snapkv.hip", "common.hpp"])
-    log(f"step {step_ms:.3f} ms; phases (ms): " + ", ".join(f"{p} {phase_ms[p]:.4f}" for p in phases))
-    return dict(
-        wl=wl, qn=qn, kn=kn, vn=vn, step_ms=step_ms, elapsed=elapsed,
-        value=B * L * args.steps / elapsed,
+    log(f"{wl.name}: step {step_ms:.4f} ms, {nbytes['total'] / (step_ms * 1e-3) / PEAK_HBM:.3f} of HBM peak; "
+        f"{kernel_name} {kern_ms[dominant] * 1e3:.1f} us" +
+        ("; phases (ms): " + ", ".join(f"{p} {v:.4f}" for p, v in phase_ms.items()) if phase_ms else ""))
+    res = dict(
+        wl=wl, step_ms=step_ms, elapsed=elapsed, steps=steps, copies=ncp,
+        value=B * L * steps / elapsed,
         path_gbps=nbytes["total"] / (step_ms * 1e-3) / 1e9,
         roofline={"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                   "frac": achieved / PEAK_HBM, "traffic": traffic, "kernel": kernel_name,
                   "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": kern_ms[dominant],
                   "score_pass_ms": kern_ms},
         phase_ms=phase_ms, alg_bytes=nbytes["total"], schedule="single-pass" if single else "two-pass",
-        decode_attention=dec_att)
+        host=(qn, kn, vn) if keep_host else None)
+    if detail:
+        # decode attention over the compressed cache, rotated over enough copies of it (K' and V')
+        # that the calls do not re-read it from the L2 / MALL
+        res["decode_attention"] = time_decode(
+            kvc, ev, q[:, :, -1].contiguous(), out.k, out.v, wl.budget, 200,
+            f"SnapKV-compressed {wl.name} layer B{B} H{H} {wl.budget} rows")
+    del ks, vs, q, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
-def cpu_baseline(res, seconds):
-    """The oracle on a bounded sample of the same workload (whole heads, in order)."""
-    from oracle import snapkv as ref
-
+def workload_line(res):
+    """The JSON object of one SnapKV layer."""
     wl = res["wl"]
+    return {
+        "config": {"workload": f"snapkv-{wl.name}", "batch": wl.B, "heads": wl.H, "head_dim": wl.D,
+                   "prompt_len": wl.L, "window": wl.window, "budget": wl.budget, "pool_kernel": wl.pool_kernel,
+                   "dtype": wl.dtype, "schedule": res["schedule"]},
+        "value": res["value"], "unit": "tokens/s", "ms_per_step": res["step_ms"], "steps": res["steps"],
+        "kv_copies_rotated": res["copies"],
+        "hbm_gbps_path": res["path_gbps"], "hbm_frac_path": res["path_gbps"] * 1e9 / PEAK_HBM,
+        "algorithmic_bytes_per_step": res["alg_bytes"], "roofline": res["roofline"],
+    }
+
+
+def blas_threads():
     try:
         import threadpoolctl
-        blas = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+
+        return max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     except Exception:  # threadpoolctl missing: report the affinity only
-        blas = None
-    cores = len(os.sched_getaffinity(0))
+        return None
+
+
+def cpu_snapkv(wl, seconds, host=None, threads=None):
+    """The oracle on a bounded sample of a SnapKV layer: whole heads, in order, cycling over the
+    layer until `seconds` have passed; scaled to one layer. `threads` caps the BLAS threads."""
+    import contextlib
+
+    import synthetic as syn
+    from oracle import snapkv as ref
+
+    ctx = contextlib.nullcontext()
+    if threads is not None:
+        import threadpoolctl
+
+        ctx = threadpoolctl.threadpool_limits(limits=threads)
     heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
     done = 0
-    t0 = time.perf_counter()
-    # whole heads, cycling over the layer, until the time budget is spent
-    while True:
-        b, h = heads[done % len(heads)]
-        ref.compress_head(res["qn"][b, h], res["kn"][b, h], res["vn"][b, h], wl.budget, wl.pool_kernel, wl.dtype)
-        done += 1
-        if time.perf_counter() - t0 > seconds:
-            break
-    t = time.perf_counter() - t0
+    with ctx:
+        used = blas_threads()
+        t0 = time.perf_counter()
+        while True:
+            b, h = heads[done % len(heads)]
+            if host is not None:
+                qh, kh, vh = host[0][b, h], host[1][b, h], host[2][b, h]
+            else:
+                tg = time.perf_counter()
+                qh, kh, vh = syn.snapkv_head(wl, b, h)
+                t0 += time.perf_counter() - tg  # generation is not the oracle's time
+            ref.compress_head(qh, kh, vh, wl.budget, wl.pool_kernel, wl.dtype)
+            done += 1
+            if time.perf_counter() - t0 > seconds or (done >= len(heads) and done >= 3 * len(heads)):
+                break
+        t = time.perf_counter() - t0
     full_layer_s = t * len(heads) / done
-    log(f"cpu oracle: {done} head compressions ({done / len(heads):.2f} layers) in {t:.1f}s")
-    return {"value": wl.B * wl.L / full_layer_s, "unit": "tokens/s", "cores": blas or cores,
-            "kind": "oracle", "affinity_cores": cores,
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu oracle {wl.name}: {done} head compressions ({done / len(heads):.2f} layers) in {t:.1f}s, "
+        f"{used} BLAS threads")
+    return {"value": wl.B * wl.L / full_layer_s, "unit": "tokens/s", "cores": used or cores, "kind": "oracle",
+            "affinity_cores": cores,
             "sample": f"{done} whole-head compressions cycling over the {len(heads)} heads of the {wl.name} "
-                      f"layer (fp64 numpy, BLAS threads as reported), {t:.1f}s; scaled to one layer"}
+                      f"layer (fp64 numpy, {used} BLAS threads), {t:.1f}s; scaled to one layer"}
+
+
+def cpu_h2o(seconds, n_heads=4, steps=256):
+    """The H2O oracle on a sample of the decode workload: `n_heads` heads from their own prompt
+    prefill, then up to `steps` decode steps each (bounded by `seconds`); per-step time scaled to
+    all B x H heads. Labelled per step: the sample covers the first decode steps only."""
+    import numpy as np
+
+    import synthetic as syn
+    from oracle import h2o as ref
+
+    wl = syn.H2O_WORKLOADS["opt6.7b-decode"]
+    Lp = wl.prompt_len
+    heads = [(b, (7 * b) % wl.H) for b in range(0, wl.B, wl.B // n_heads)][:n_heads]
+    used = blas_threads()
+    t_pf = 0.0
+    states = {}
+    for b, h in heads:
+        q, k, v, _ = syn.h2o_prompt_head(wl, b, h)
+        t = time.perf_counter()
+        states[(b, h)], _ = ref.prefill_head(q, k, v, wl.n_heavy(Lp), wl.n_recent(Lp), wl.dtype)
+        t_pf += time.perf_counter() - t
+    t_steps, done = 0.0, 0
+    for s_ in range(steps):
+        x = syn.h2o_step_inputs(wl, s_)
+        length = Lp + s_ + 1
+        t = time.perf_counter()
+        for b, h in heads:
+            states[(b, h)], _, _ = ref.step_head(states[(b, h)], x[0][b, h], x[1][b, h], x[2][b, h], length,
+                                                 wl.n_heavy(length), wl.n_recent(length), wl.dtype)
+        t_steps += time.perf_counter() - t
+        done += 1
+        if t_steps + t_pf > seconds:
+            break
+    per_step_all = t_steps / done * (wl.B * wl.H) / len(heads)
+    log(f"cpu oracle h2o: {len(heads)} heads, prefill {t_pf:.1f}s, {done} steps {t_steps:.2f}s")
+    return {"value": wl.B / per_step_all, "unit": "decode tokens/s (per step)", "cores": used,
+            "kind": "oracle", "prefill_s_all_heads": t_pf * wl.B * wl.H / len(heads),
+            "sample": f"{len(heads)} of the {wl.B * wl.H} heads of {wl.name}: the oracle's prompt prefill, then the "
+                      f"first {done} decode steps; per-step time scaled to all heads (per step, not the whole "
+                      f"2048-step loop)"}
 
 
 def time_decode(kvc, ev, q, k, v, n, reps, label):

@@ -311,6 +311,20 @@ kvc_status kvc_decode_attention(const void* q, kvc_strides qs, const void* k,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* Instrumentation (not part of the method).                                  */
+/* ------------------------------------------------------------------------- */
+
+/* A plain streaming read of `bytes` bytes at `buf` (device memory, 16-byte
+ * aligned, a positive multiple of 16): blocks_per_cu (1..64) workgroups of 256
+ * threads per compute unit, each thread reading four 16-byte pieces per step
+ * of a grid-stride loop. Its time against `bytes` is what the device streams
+ * with a read-only kernel, the reference for the library's HBM-bound kernels.
+ * sink: device buffer of 256 words, written only in the unlikely case the
+ * data's folded value hits a fixed pattern (it keeps the loads live). */
+kvc_status kvc_measure_stream_read(const void* buf, size_t bytes, int blocks_per_cu, unsigned* sink,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

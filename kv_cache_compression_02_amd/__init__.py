@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
     "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback", "kvc_snapkv_force_wait_timeout",
-    "kvc_decode_attention_workspace_bytes", "kvc_decode_attention",
+    "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +108,8 @@ def library():
     L.kvc_snapkv_last_schedule.argtypes = []
     L.kvc_snapkv_last_score_kernel.restype = ctypes.c_char_p
     L.kvc_snapkv_last_score_kernel.argtypes = []
+    L.kvc_measure_stream_read.restype = i32
+    L.kvc_measure_stream_read.argtypes = [vp, sz, i32, vp, vp]
     L.kvc_sink_recent.restype = i32
     L.kvc_sink_recent.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
     _lib = L
@@ -267,8 +269,8 @@ def decode_attention(q, k, v, n=None, *, workspace=None, out=None):
     if tuple(q.shape) != (B, H, D):
         raise ValueError("q must be [B, H, D] matching k")
     n = N if n is None else int(n)
-    if not 1 <= n <= N:
-        raise ValueError(f"n = {n} must lie in 1 .. {N}")
+    if n > N:  # (n < 1 is the library's INVALID_ARG)
+        raise ValueError(f"n = {n} exceeds the {N} rows of k and v")
     if q.device != k.device or v.device != k.device:
         raise ValueError("q, k, v must be on one device")
     if out is None:
