@@ -316,7 +316,7 @@ def cpu_snapkv(wl, seconds, host=None, threads=None):
                 t0 += time.perf_counter() - tg  # generation is not the oracle's time
             ref.compress_head(qh, kh, vh, wl.budget, wl.pool_kernel, wl.dtype)
             done += 1
-            if time.perf_counter() - t0 > seconds or (done >= len(heads) and done >= 3 * len(heads)):
+            if time.perf_counter() - t0 > seconds:
                 break
         t = time.perf_counter() - t0
     full_layer_s = t * len(heads) / done
@@ -373,28 +373,36 @@ def cpu_h2o(seconds, n_heads=4, steps=256):
 def time_decode(kvc, ev, q, k, v, n, reps, label):
     """kvc_decode_attention over the first n rows of k/v: average time of `reps` back-to-back
     calls bracketed by two events on the library's stream, and its HBM roofline (K and V rows
-    read once, q read, the fp32 output written)."""
+    read once, q read, the fp32 output written). The calls rotate over enough copies of the
+    cache that at least twice the MALL's 256 MB of other rows is read between two reads of one
+    copy, so that the figure is an HBM one even for a small (compressed) cache."""
     import torch
 
     B, H, _, D = k.shape
     es = k.element_size()
+    cache_bytes = 2 * B * H * n * D * es
+    ncp = 1 + -(-2 * MALL_BYTES // cache_bytes)
+    ks = [k] + [k[:, :, :n].clone() for _ in range(ncp - 1)]
+    vs = [v] + [v[:, :, :n].clone() for _ in range(ncp - 1)]
     ws = torch.empty(max(kvc.decode_attention_workspace_bytes(B, H, n, D), 16), dtype=torch.uint8, device="cuda")
     out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        kvc.decode_attention(q, k, v, n, workspace=ws, out=out)
+    for i in range(3):
+        kvc.decode_attention(q, ks[i % ncp], vs[i % ncp], n, workspace=ws, out=out)
     torch.cuda.synchronize()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     e = ev.create(2)
     ev.record(e[0], stream)
-    for _ in range(reps):
-        kvc.decode_attention(q, k, v, n, workspace=ws, out=out)
+    for i in range(reps):
+        kvc.decode_attention(q, ks[i % ncp], vs[i % ncp], n, workspace=ws, out=out)
     ev.record(e[1], stream)
     torch.cuda.synchronize()
     ms = ev.ms(e[0], e[1]) / reps
     nbytes = B * H * (2 * n * D * es + D * es + D * 4)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    log(f"decode attention, {label}: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s")
+    log(f"decode attention, {label}: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s ({ncp} cache copies rotated)")
+    del ks, vs
     return {"cache": label, "ms_per_call": ms, "calls": reps, "algorithmic_bytes": nbytes,
+            "cache_copies_rotated": ncp,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": gbps * 1e9 / PEAK_HBM, "kernel": "decode_partial + decode_merge"}}
 
@@ -480,33 +488,49 @@ def bench_h2o(args, ev):
     }
 
 
-def stream_peak():
-    """What this GPU streams with plain library kernels: a 1 GiB device copy (bytes read plus
-    bytes written; the stream-copy peak) and a 1 GiB sum (a library reduction: bytes read), each
-    timed over 10 launches with torch events on torch's own stream."""
+def stream_peak(ev):
+    """What this GPU streams over a 1 GiB buffer (4x the MALL): a torch device copy (bytes read plus
+    bytes written; the stream-copy peak), and the library's plain streaming-read kernel
+    (kvc_measure_stream_read: bytes read; the best of a few workgroups-per-CU settings), each
+    over 10 launches bracketed by events on the stream they run on."""
     import torch
+
+    import kv_cache_compression_02_amd as kvc
 
     n = 1 << 30
     a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
-    for _ in range(2):
-        b.copy_(a)
-        torch.sum(a)
-    torch.cuda.synchronize()
-    reps = 10
-    out = {}
-    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * n), ("read", lambda: torch.sum(a), n)):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    lib = kvc.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def read(per_cu):
+        st = lib.kvc_measure_stream_read(ctypes.c_void_p(a.data_ptr()), n, per_cu, ctypes.c_void_p(sink.data_ptr()),
+                                         stream)
+        assert st == 0, lib.kvc_last_error().decode()
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e = ev.create(2)
+        ev.record(e[0], stream)
         for _ in range(reps):
             fn()
-        e.record()
-        e.synchronize()
-        out[f"{name}_gbps"] = nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+        ev.record(e[1], stream)
+        torch.cuda.synchronize()
+        return ev.ms(e[0], e[1]) / reps * 1e-3
+
+    out = {"copy_gbps": 2 * n / timed(lambda: b.copy_(a)) / 1e9}
+    reads = {per_cu: n / timed(lambda: read(per_cu)) / 1e9 for per_cu in (2, 4, 8, 16)}
+    best = max(reads, key=reads.get)
+    out["read_gbps"] = reads[best]
+    out["read_gbps_by_workgroups_per_cu"] = reads
     del a, b
     torch.cuda.empty_cache()
     out["bytes"] = n
-    out["kernels"] = "torch copy_ (read + write counted) and torch.sum (a reduction; read), 10 launches each"
+    out["kernels"] = ("torch copy_ (read + write counted); kvc_measure_stream_read (plain 16-byte nontemporal "
+                      "loads, grid-stride, 4 in flight per thread; read only), 10 launches each")
     return out
 
 
@@ -537,8 +561,10 @@ def main():
         calibrate_copy()
         return
     ev = HipEvents()
-    res = bench_snapkv(args, ev)
-    wl = res["wl"]
+    import synthetic as syn
+
+    wl = syn.SNAPKV_WORKLOADS[args.workload]
+    res = bench_snapkv(wl, args, ev, args.steps, args.warmup, detail=True, keep_host=not args.skip_cpu)
     line = {
         "metric": "prompt tokens compressed/s per layer (all heads); HBM GB/s as % of peak",
         "value": res["value"],
@@ -558,19 +584,40 @@ def main():
         "hbm_gbps_path": res["path_gbps"],
         "hbm_frac_path": res["path_gbps"] * 1e9 / PEAK_HBM,
         "algorithmic_bytes_per_step": res["alg_bytes"],
+        "kv_copies_rotated": res["copies"],
         "roofline": res["roofline"],
         "phase_ms": res["phase_ms"],
         "decode_attention_compressed": res["decode_attention"],
     }
-    sp = stream_peak()
-    sp["score_kernel_frac_of_copy"] = res["roofline"]["achieved"] / sp["copy_gbps"]
+    sp = stream_peak(ev)
+    sp["score_kernel_frac_of_read"] = res["roofline"]["achieved"] / sp["read_gbps"]
+    sp["path_frac_of_read"] = res["path_gbps"] / sp["read_gbps"]
     line["measured_stream"] = sp
     log(f"stream peak: copy {sp['copy_gbps']:.0f} GB/s, read {sp['read_gbps']:.0f} GB/s")
+    host = res.pop("host")
+    extra = {}
+    if not args.skip_extra:
+        for name in ("tiny-fp32", "16k-bf16", "380k-bf16"):
+            if name == wl.name:
+                continue
+            r = bench_snapkv(syn.SNAPKV_WORKLOADS[name], args, ev, args.extra_steps, 2, detail=False,
+                             keep_host=not args.skip_cpu and name != "380k-bf16")
+            extra[name] = r
+        line["workloads"] = {n: workload_line(r) for n, r in extra.items()}
     if not args.skip_cpu:
-        line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_snapkv(wl, args.cpu_seconds, host)
+        cpu = {}
+        short = min(args.cpu_seconds, 6.0)
+        for name, r in extra.items():
+            cpu[name] = cpu_snapkv(r["wl"], short, r["host"])
+            if name in ("tiny-fp32", "16k-bf16"):
+                cpu[name + " (1 thread)"] = cpu_snapkv(r["wl"], short, r["host"], threads=1)
+        if not args.skip_h2o:
+            cpu["opt6.7b-decode"] = cpu_h2o(short)
+        line["cpu_baselines"] = cpu
     else:
         line["cpu_baseline"] = None
-    del res
+    del res, host, extra
     if not args.skip_h2o:
         line["h2o_sink"] = bench_h2o(args, ev)
     print(json.dumps(line), flush=True)
