@@ -311,6 +311,23 @@ kvc_status kvc_decode_attention(const void* q, kvc_strides qs, const void* k,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* The same attention for callers that cannot allocate or bring device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument, and the call allocates nothing. Where the
+ * rows are split over several workgroups per head, the partials go to a static
+ * device array of the library (8 MiB on each GPU it runs on, held until the
+ * process ends); sizes whose partials exceed it (kvc_decode_attention_workspace_bytes
+ * > 8 MiB, e.g. B*H*ceil(n/256) > 16131 at D = 128) return KVC_ERR_WORKSPACE
+ * and leave `out` untouched. Every call on one GPU shares that array: calls
+ * that overlap on one GPU (on different streams, or from several threads)
+ * race. The array needs no clearing: every partial is written before it is
+ * read. Arguments, results and errors are otherwise those of
+ * kvc_decode_attention (the same kernels compute the same values). */
+kvc_status kvc_decode_attention_noalloc(const void* q, kvc_strides qs, const void* k,
+                                        const void* v, kvc_strides kvs, int B, int H,
+                                        int n, int D, kvc_dtype dt, float* out,
+                                        hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Instrumentation (not part of the method).                                  */
 /* ------------------------------------------------------------------------- */

@@ -25,7 +25,7 @@ __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
     "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS",
     "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
-    "decode_attention_workspace_bytes", "decode_attention",
+    "decode_attention_workspace_bytes", "decode_attention", "decode_attention_noalloc",
 ]
 
 KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
     "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback", "kvc_snapkv_force_wait_timeout",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
+    "kvc_decode_attention_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +109,8 @@ def library():
     L.kvc_snapkv_last_schedule.argtypes = []
     L.kvc_snapkv_last_score_kernel.restype = ctypes.c_char_p
     L.kvc_snapkv_last_score_kernel.argtypes = []
+    L.kvc_decode_attention_noalloc.restype = i32
+    L.kvc_decode_attention_noalloc.argtypes = [vp, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, vp, vp]
     L.kvc_measure_stream_read.restype = i32
     L.kvc_measure_stream_read.argtypes = [vp, sz, i32, vp, vp]
     L.kvc_sink_recent.restype = i32
@@ -283,6 +286,29 @@ def decode_attention(q, k, v, n=None, *, workspace=None, out=None):
     _check(library().kvc_decode_attention(
         _ptr(q), Strides(q.stride(0), q.stride(1), 0), _ptr(k), _ptr(v), _strides4(k), B, H, n, D,
         _dtype_code(k), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def decode_attention_noalloc(q, k, v, n, out):
+    """decode_attention without a workspace (kvc_decode_attention_noalloc): the library's static
+    scratch holds the partials, so neither this call nor the library allocates; ``out`` (float32
+    [B, H, D], contiguous) is the caller's. Overlapping calls on one GPU race on that scratch."""
+    _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, H, D] and k, v [B, H, N, D]")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, D = k.shape
+    if tuple(q.shape) != (B, H, D) or q.device != k.device or v.device != k.device:
+        raise ValueError("q must be [B, H, D] matching k, on k's device")
+    if int(n) > N:
+        raise ValueError(f"n = {n} exceeds the {N} rows of k and v")
+    _check_out(out, "out", (B, H, D), torch.float32, k.device)
+    _check(library().kvc_decode_attention_noalloc(
+        _ptr(q), Strides(q.stride(0), q.stride(1), 0), _ptr(k), _ptr(v), _strides4(k), B, H, int(n), D,
+        _dtype_code(k), _ptr(out), _stream()))
     return out
 
 

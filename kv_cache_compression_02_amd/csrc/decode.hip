@@ -18,6 +18,8 @@
 // merges by log-sum-exp; a head of a single chunk writes its output directly.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace kvc {
@@ -190,6 +192,71 @@ void launch_decode(const void* q, kvc_strides qs, const void* k, const void* v, 
     launch_decode_ch<T, D, kChunkSmall>(q, qs, k, v, kvs, B, H, n, out, part, stream);
 }
 
+// The allocation-free variant's partials: a file-scope array in device memory
+// (each GPU the library runs on holds its own copy until the process ends).
+// In host code `scratch` names a host-side stand-in, not a device address:
+// kernels get the per-device address from scratch_ptr() instead.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current; NULL (and *err set) if the lookup fails.
+float* scratch_ptr(hipError_t* err) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return static_cast<float*>(ptrs[dev]);
+}
+
+// Validation shared by both entry points; on success *split says whether the
+// rows are split over several workgroups per head (partials then merged).
+kvc_status decode_check(const void* q, kvc_strides qs, const void* k, const void* v, kvc_strides kvs, int B, int H,
+                        int n, int D, kvc_dtype dt, float* out, bool* split) {
+  if (!q || !k || !v || !out) return fail(KVC_ERR_INVALID_ARG, "decode_attention: q, k, v and out must be non-NULL");
+  if (dt != KVC_BF16 && dt != KVC_F32) return fail(KVC_ERR_INVALID_ARG, "decode_attention: unknown dtype %d", (int)dt);
+  if (B <= 0 || H <= 0 || n <= 0) return fail(KVC_ERR_INVALID_ARG, "decode_attention: B, H and n must be positive");
+  if (static_cast<int64_t>(B) * H > 65535) return fail(KVC_ERR_UNSUPPORTED, "decode_attention: B*H must be <= 65535");
+  if (D != 64 && D != 128) return fail(KVC_ERR_UNSUPPORTED, "decode_attention: head_dim %d not in {64, 128}", D);
+  const int64_t es = dt == KVC_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(KVC_ERR_INVALID_ARG, "decode_attention: device pointers must be 16-byte aligned");
+  const int64_t strides[5] = {qs.b, qs.h, kvs.b, kvs.h, kvs.t};
+  for (int64_t s : strides)
+    if (s < 0 || (s * es) % 16 != 0)
+      return fail(KVC_ERR_INVALID_ARG, "decode_attention: strides must be non-negative and multiples of 16 bytes");
+  if (kvs.t < D) return fail(KVC_ERR_INVALID_ARG, "decode_attention: row stride must be >= head_dim");
+  *split = n > decode_chunk(B, H, n);
+  return KVC_OK;
+}
+
+void launch_decode_any(const void* q, kvc_strides qs, const void* k, const void* v, kvc_strides kvs, int B, int H,
+                       int n, int D, kvc_dtype dt, float* out, float* part, hipStream_t stream) {
+  if (dt == KVC_BF16) {
+    if (D == 128)
+      launch_decode<uint16_t, 128>(q, qs, k, v, kvs, B, H, n, out, part, stream);
+    else
+      launch_decode<uint16_t, 64>(q, qs, k, v, kvs, B, H, n, out, part, stream);
+  } else {
+    if (D == 128)
+      launch_decode<float, 128>(q, qs, k, v, kvs, B, H, n, out, part, stream);
+    else
+      launch_decode<float, 64>(q, qs, k, v, kvs, B, H, n, out, part, stream);
+  }
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -206,37 +273,38 @@ extern "C" kvc_status kvc_decode_attention(const void* q, kvc_strides qs, const 
                                            kvc_strides kvs, int B, int H, int n, int D, kvc_dtype dt, float* out,
                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
-  if (!q || !k || !v || !out) return fail(KVC_ERR_INVALID_ARG, "decode_attention: q, k, v and out must be non-NULL");
-  if (dt != KVC_BF16 && dt != KVC_F32) return fail(KVC_ERR_INVALID_ARG, "decode_attention: unknown dtype %d", (int)dt);
-  if (B <= 0 || H <= 0 || n <= 0) return fail(KVC_ERR_INVALID_ARG, "decode_attention: B, H and n must be positive");
-  if (static_cast<int64_t>(B) * H > 65535) return fail(KVC_ERR_UNSUPPORTED, "decode_attention: B*H must be <= 65535");
-  if (D != 64 && D != 128) return fail(KVC_ERR_UNSUPPORTED, "decode_attention: head_dim %d not in {64, 128}", D);
-  const int64_t es = dt == KVC_BF16 ? 2 : 4;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(KVC_ERR_INVALID_ARG, "decode_attention: device pointers must be 16-byte aligned");
-  const int64_t strides[5] = {qs.b, qs.h, kvs.b, kvs.h, kvs.t};
-  for (int64_t s : strides)
-    if (s < 0 || (s * es) % 16 != 0)
-      return fail(KVC_ERR_INVALID_ARG, "decode_attention: strides must be non-negative and multiples of 16 bytes");
-  if (kvs.t < D) return fail(KVC_ERR_INVALID_ARG, "decode_attention: row stride must be >= head_dim");
+  bool split = false;
+  const kvc_status st = decode_check(q, qs, k, v, kvs, B, H, n, D, dt, out, &split);
+  if (st != KVC_OK) return st;
   const size_t need = kvc_decode_attention_workspace_bytes(B, H, n, D);
-  const bool split = n > decode_chunk(B, H, n);
   if (split && (!workspace || workspace_bytes < need))
     return fail(KVC_ERR_WORKSPACE, "decode_attention: workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (split && !aligned16(workspace))
     return fail(KVC_ERR_INVALID_ARG, "decode_attention: workspace must be 16-byte aligned");
-  float* part = static_cast<float*>(workspace);
-  if (dt == KVC_BF16) {
-    if (D == 128)
-      launch_decode<uint16_t, 128>(q, qs, k, v, kvs, B, H, n, out, part, stream);
-    else
-      launch_decode<uint16_t, 64>(q, qs, k, v, kvs, B, H, n, out, part, stream);
-  } else {
-    if (D == 128)
-      launch_decode<float, 128>(q, qs, k, v, kvs, B, H, n, out, part, stream);
-    else
-      launch_decode<float, 64>(q, qs, k, v, kvs, B, H, n, out, part, stream);
-  }
+  launch_decode_any(q, qs, k, v, kvs, B, H, n, D, dt, out, static_cast<float*>(workspace), stream);
   return check_launch("decode_attention");
+}
+
+extern "C" kvc_status kvc_decode_attention_noalloc(const void* q, kvc_strides qs, const void* k, const void* v,
+                                                   kvc_strides kvs, int B, int H, int n, int D, kvc_dtype dt,
+                                                   float* out, hipStream_t stream) {
+  clear_error();
+  bool split = false;
+  const kvc_status st = decode_check(q, qs, k, v, kvs, B, H, n, D, dt, out, &split);
+  if (st != KVC_OK) return st;
+  float* part = nullptr;
+  if (split) {
+    const size_t need = kvc_decode_attention_workspace_bytes(B, H, n, D);
+    if (need > kScratchBytes)
+      return fail(KVC_ERR_WORKSPACE,
+                  "decode_attention_noalloc: these sizes need %zu bytes of partials, beyond the %zu-byte static "
+                  "scratch; use kvc_decode_attention with a workspace",
+                  need, kScratchBytes);
+    hipError_t e = hipSuccess;
+    part = scratch_ptr(&e);
+    if (!part) return fail(KVC_ERR_HIP, "decode_attention_noalloc: scratch address: %s", hipGetErrorString(e));
+  }
+  launch_decode_any(q, qs, k, v, kvs, B, H, n, D, dt, out, part, stream);
+  return check_launch("decode_attention_noalloc");
 }
