@@ -112,6 +112,54 @@ kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Pooling operators of the vote smoothing (SnapKV page, processing flow step
+ * 3 says only "1D pooling"):
+ *   KVC_POOL_MAX  max over the in-range neighbours j-p/2 .. j+p/2 (the default
+ *                 of kvc_snapkv_compress);
+ *   KVC_POOL_AVG  their mean: the sum of the in-range neighbours' votes,
+ *                 divided by how many are in range (neighbours beyond either end
+ *                 of the prefix are ignored, as for the max). */
+typedef enum { KVC_POOL_MAX = 0, KVC_POOL_AVG = 1 } kvc_pool_type;
+
+/* Workspace bytes kvc_snapkv_compress_ex needs for these sizes (0 if they are
+ * invalid); `ragged` non-zero when a lengths array will be passed. */
+size_t kvc_snapkv_workspace_bytes_ex(int n_layers, int B, int H, int L, int D, int window, int budget,
+                                     int pool_kernel, kvc_dtype dt, int ragged);
+
+/* kvc_snapkv_compress with three extensions for serving stacks (SnapKV page,
+ * limits: per-head selection and gather-based KV reconstruction inside the
+ * serving engine; processing flow step 3 for the pooling operator):
+ *   - pool_type: KVC_POOL_MAX or KVC_POOL_AVG (see kvc_pool_type);
+ *   - n_layers >= 1 layers of one prompt in one call: layer l's queries start
+ *     q_layer_stride elements after layer l-1's, its keys and values
+ *     kv_layer_stride elements after; each layer is compressed independently
+ *     (the method is per layer and per head). Outputs are contiguous over
+ *     [n_layers, B, H, ...]. When q_layer_stride == B * qs.b and
+ *     kv_layer_stride == B * kvs.b (layers stacked in front of the batch axis)
+ *     the layers run as one batch of n_layers * B sequences, which fills the
+ *     device for short prompts; otherwise layer by layer;
+ *   - lengths: optional HOST array [B] of prompt lengths (a ragged batch
+ *     padded to L): sequence b uses keys and values 0 .. lengths[b]-1, its
+ *     window is its last `window` positions lengths[b]-window .. lengths[b]-1,
+ *     whose queries are q's rows q_len-window .. q_len-1 (the same rows for
+ *     every sequence: each sequence's own window queries, aligned at the end
+ *     of q); every length must satisfy budget < lengths[b] <= L. Each (layer,
+ *     sequence) then runs as its own launch sequence. k_out / v_out / idx_out
+ *     keep their fixed shapes; pooled_out and vote_out are packed: for each
+ *     layer, then each sequence, H rows of lengths[b] - window values.
+ *     NULL lengths: every sequence has length L (pooled / vote
+ *     [n_layers, B, H, L - window]).
+ * Everything else (arguments, rules, errors, asynchrony) is as in
+ * kvc_snapkv_compress; the workspace is sized by kvc_snapkv_workspace_bytes_ex
+ * and reused across the launch sequences in stream order. */
+kvc_status kvc_snapkv_compress_ex(const void* q, int q_len, kvc_strides qs, int64_t q_layer_stride,
+                                  const void* k, const void* v, kvc_strides kvs, int64_t kv_layer_stride,
+                                  int n_layers, int B, int H, int L, int D, const int32_t* lengths,
+                                  int window, int budget, int pool_kernel, int pool_type, kvc_dtype dt,
+                                  void* k_out, void* v_out, int32_t* idx_out, float* pooled_out,
+                                  float* vote_out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Score schedules of kvc_snapkv_compress. Both compute every score in fp32
  * from the same bf16 / fp32 inputs and select by the same rule; they differ in
  * how often K is read and in how each window row's softmax normaliser is

@@ -23,13 +23,16 @@ import torch
 
 __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
-    "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS",
+    "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS", "KVC_POOL_MAX",
+    "KVC_POOL_AVG", "snapkv_workspace_bytes_ex", "snapkv_compress_ex",
     "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
     "decode_attention_workspace_bytes", "decode_attention", "decode_attention_noalloc",
 ]
 
 KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
 KVC_F32, KVC_BF16 = 0, 1
+KVC_POOL_MAX, KVC_POOL_AVG = 0, 1
+_POOLS = {"max": KVC_POOL_MAX, "avg": KVC_POOL_AVG}
 SNAPKV_AUTO, SNAPKV_TWO_PASS, SNAPKV_SINGLE_PASS = 0, 1, 2
 _STATUS_NAMES = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
@@ -39,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
     "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback", "kvc_snapkv_force_wait_timeout",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
-    "kvc_decode_attention_noalloc",
+    "kvc_decode_attention_noalloc", "kvc_snapkv_workspace_bytes_ex", "kvc_snapkv_compress_ex",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +92,12 @@ def library():
     L.kvc_snapkv_compress.restype = i32
     L.kvc_snapkv_compress.argtypes = [
         vp, i32, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kvc_snapkv_workspace_bytes_ex.restype = sz
+    L.kvc_snapkv_workspace_bytes_ex.argtypes = [i32] * 8 + [i32, i32]
+    L.kvc_snapkv_compress_ex.restype = i32
+    L.kvc_snapkv_compress_ex.argtypes = [
+        vp, i32, Strides, i64, vp, vp, Strides, i64, i32, i32, i32, i32, i32, vp, i32, i32, i32, i32, i32,
         vp, vp, vp, vp, vp, vp, sz, vp]
     L.kvc_h2o_step.restype = i32
     L.kvc_h2o_step.argtypes = [ctypes.POINTER(_H2OCacheC), vp, vp, vp, i32, i32, vp, vp]
@@ -248,6 +257,87 @@ def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, 
         _ptr(q), q.shape[2], _strides4(q), _ptr(k), _ptr(v), _strides4(k), B, H, L, D,
         window, budget, pool_kernel, dt, _ptr(k_out), _ptr(v_out), _ptr(idx), _ptr(pooled),
         _ptr(vote), _ptr(workspace), workspace.numel(), _stream()))
+    return SnapKVResult(k_out, v_out, idx, pooled, vote)
+
+
+def snapkv_workspace_bytes_ex(n_layers, B, H, L, D, window, budget, pool_kernel, dtype, ragged=False):
+    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    return int(library().kvc_snapkv_workspace_bytes_ex(n_layers, B, H, L, D, window, budget, pool_kernel, code,
+                                                       int(bool(ragged))))
+
+
+def snapkv_compress_ex(q, k, v, window, budget, pool_kernel, *, pool="max", lengths=None, want_pooled=False,
+                       want_vote=False, workspace=None, out=None):
+    """kvc_snapkv_compress_ex: the pooling operator ("max" or "avg"), all layers of a prompt in one call and
+    ragged batches.
+
+    q: [B, H, q_len, D] or [n_layers, B, H, q_len, D] (the last ``window`` rows of each sequence's q are its
+    window queries); k, v: [B, H, L, D] or [n_layers, B, H, L, D] with the same strides. ``lengths``: optional
+    sequence of B prompt lengths (budget < length <= L). Returns SnapKVResult with k, v [n_layers, B, H,
+    budget, D], idx [n_layers, B, H, budget - window] (the layer axis dropped for 4-D inputs) and pooled /
+    vote float32: [n_layers, B, H, L - window] without lengths, else packed 1-D (per layer, per sequence,
+    H rows of lengths[b] - window).
+    """
+    if pool not in _POOLS:
+        raise ValueError(f"pool must be one of {sorted(_POOLS)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    layered = k.dim() == 5
+    if q.dim() != k.dim() or k.dim() not in (4, 5):
+        raise ValueError("q, k, v must all be 4-D [B, H, T, D] or all 5-D [n_layers, B, H, T, D]")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.device != k.device or v.device != k.device:
+        raise ValueError("q, k, v must be on one device")
+    q5, k5 = (q, k) if layered else (q.unsqueeze(0), k.unsqueeze(0))
+    NL, B, H, L, D = k5.shape
+    if (q5.shape[0], q5.shape[1], q5.shape[2], q5.shape[4]) != (NL, B, H, D):
+        raise ValueError(f"q must be [{NL}, {B}, {H}, *, {D}] like k, got {tuple(q.shape)}")
+    if q5.shape[3] < window:
+        raise ValueError(f"q holds {q5.shape[3]} rows, fewer than the window {window}")
+    dt = _dtype_code(k)
+    dev = k.device
+    lens = None
+    if lengths is not None:
+        lengths = [int(x) for x in lengths]
+        if len(lengths) != B:
+            raise ValueError(f"lengths must hold {B} values")
+        lens = (ctypes.c_int32 * B)(*lengths)
+        n_pre = NL * H * sum(max(x - window, 0) for x in lengths)
+        pv_shape = (n_pre,)
+    else:
+        pv_shape = (NL, B, H, max(L - window, 0)) if layered else (B, H, max(L - window, 0))
+    lead = (NL, B, H) if layered else (B, H)
+    n_keep = max(budget - window, 0)
+    if out is None:
+        k_out = torch.empty(lead + (budget, D), dtype=k.dtype, device=dev)
+        v_out = torch.empty_like(k_out)
+        idx = torch.empty(lead + (n_keep,), dtype=torch.int32, device=dev)
+        pooled = torch.empty(pv_shape, dtype=torch.float32, device=dev) if want_pooled else None
+        vote = torch.empty(pv_shape, dtype=torch.float32, device=dev) if want_vote else None
+    else:
+        k_out, v_out, idx, pooled, vote = out
+        _check_out(k_out, "out.k", lead + (budget, D), k.dtype, dev)
+        _check_out(v_out, "out.v", lead + (budget, D), k.dtype, dev)
+        _check_out(idx, "out.idx", lead + (n_keep,), torch.int32, dev)
+        if pooled is not None:
+            _check_out(pooled, "out.pooled", pv_shape, torch.float32, dev)
+        if vote is not None:
+            _check_out(vote, "out.vote", pv_shape, torch.float32, dev)
+    if workspace is None:
+        nbytes = snapkv_workspace_bytes_ex(NL, B, H, L, D, window, budget, pool_kernel, k.dtype, lens is not None)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_out(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    qs = Strides(q5.stride(1), q5.stride(2), q5.stride(3))
+    ks = Strides(k5.stride(1), k5.stride(2), k5.stride(3))
+    _check(library().kvc_snapkv_compress_ex(
+        _ptr(q), q5.shape[3], qs, q5.stride(0), _ptr(k), _ptr(v), ks, k5.stride(0), NL, B, H, L, D,
+        ctypes.cast(lens, ctypes.c_void_p) if lens is not None else None, window, budget, pool_kernel, _POOLS[pool],
+        dt, _ptr(k_out), _ptr(v_out), _ptr(idx), _ptr(pooled), _ptr(vote), _ptr(workspace), workspace.numel(),
+        _stream()))
     return SnapKVResult(k_out, v_out, idx, pooled, vote)
 
 

@@ -143,12 +143,18 @@ __global__ __launch_bounds__(kThreads) void snap_stats_merge(const float2* __res
 // [e0, e1) = [c0 - r, c1 + r) clipped to [0, t0); pooled[j] for j in [c0, c1)
 // is the max over the neighbours that exist, and each pooled value's top 12
 // bits are counted in the LDS histogram sh (merged into hist by the caller).
-__device__ void pool_and_count(const float* sv, int e0, int e1, int c0, int c1, int r, float* pooled_row,
+__device__ void pool_and_count(const float* sv, int e0, int e1, int c0, int c1, int r, int avg, float* pooled_row,
                                unsigned* sh) {
   for (int j = c0 + static_cast<int>(threadIdx.x); j < c1; j += kThreads) {
+    // the in-range neighbours j-r .. j+r (e0 and e1 clip at the prefix's ends)
     const int lo = max(j - r, e0) - e0, hi = min(j + r, e1 - 1) - e0;
     float m = sv[lo];
-    for (int d = lo + 1; d <= hi; ++d) m = fmaxf(m, sv[d]);
+    if (avg) {  // their mean, summed in position order
+      for (int d = lo + 1; d <= hi; ++d) m += sv[d];
+      m /= static_cast<float>(hi - lo + 1);
+    } else {  // their maximum
+      for (int d = lo + 1; d <= hi; ++d) m = fmaxf(m, sv[d]);
+    }
     pooled_row[j] = m;
     atomicAdd(&sh[(__float_as_uint(m) >> kHistShift) & (kHistBins - 1)], 1u);
   }
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void snap_stats_f32(
 template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
-    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r, int avg,
     float scale_log2, const float2* __restrict__ rowstat, float* __restrict__ vote, float* __restrict__ pooled,
     unsigned* __restrict__ hist) {
   constexpr int KS = D / 16;
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
     }
   }
   __syncthreads();
-  pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
+  pool_and_count(sv, e0, e1, c0, c1, r, avg, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
 }
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
 template <int D>
 __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     const float* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qst, int qrow0,
-    const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r,
+    const float* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst, int H, int L, int w, int r, int avg,
     float scale_log2, const float2* __restrict__ rowstat, float* __restrict__ vote, float* __restrict__ pooled,
     unsigned* __restrict__ hist) {
   __shared__ float qs[kMaxWindow][D];
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void snap_votes_f32(
     if (vote && j >= c0 && j < c1) vote[static_cast<int64_t>(bh) * t0 + j] = v;
   }
   __syncthreads();
-  pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * t0, sh);
+  pool_and_count(sv, e0, e1, c0, c1, r, avg, pooled + static_cast<int64_t>(bh) * t0, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
 }
@@ -1837,8 +1843,8 @@ __device__ float exact_vote(const ExactShared& e, const ExactArgs& a, int bh, in
   return v;
 }
 
-// Max-pool of raw votes (neighbours beyond the prefix ignored) and the
-// per-head 12-bit histogram of the pooled scores, after the single pass. A
+// Max- or average-pool of raw votes (neighbours beyond the prefix ignored) and
+// the per-head 12-bit histogram of the pooled scores, after the single pass. A
 // thread pools kPoolPer consecutive positions from a register window of their
 // votes with a halo of R on each side (rounded up to whole 16-byte pieces);
 // neighbouring pooled scores often share a histogram bin, so each run of equal
@@ -1849,7 +1855,8 @@ constexpr int kPoolRegRadius = 7;  // larger radii pool from LDS (snap_pool_lds)
 
 template <int R, bool VEC>
 __global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, float* __restrict__ pooled,
-                                                      unsigned* __restrict__ hist, int N, const ExactArgs ea) {
+                                                      unsigned* __restrict__ hist, int N, int avg,
+                                                      const ExactArgs ea) {
   // pooled may be NULL: then only the histogram is produced
   constexpr int kHalo = (R + 3) / 4 * 4;
   constexpr int kX = kPoolPer + 2 * kHalo;
@@ -1886,12 +1893,27 @@ __global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, 
   }
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
   float o[kPoolPer];
+  if (avg) {
+    // the mean of the in-range neighbours j-R .. j+R (summed in position order)
 #pragma unroll
-  for (int i = 0; i < kPoolPer; ++i) {
-    float m = x[i + kHalo - R];
+    for (int i = 0; i < kPoolPer; ++i) {
+      const int j = j0 + i;
+      float m = 0.f;
 #pragma unroll
-    for (int d = 1; d <= 2 * R; ++d) m = fmaxf(m, x[i + kHalo - R + d]);
-    o[i] = m;
+      for (int d = 0; d <= 2 * R; ++d) {
+        const int jd = j - R + d;
+        m += jd >= 0 && jd < N ? x[i + kHalo - R + d] : 0.f;
+      }
+      o[i] = m / static_cast<float>(min(j + R, N - 1) - max(j - R, 0) + 1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPoolPer; ++i) {
+      float m = x[i + kHalo - R];
+#pragma unroll
+      for (int d = 1; d <= 2 * R; ++d) m = fmaxf(m, x[i + kHalo - R + d]);
+      o[i] = m;
+    }
   }
   if (pooled) {  // the pooled scores are stored only when something reads them
     float* pr = pooled + static_cast<int64_t>(bh) * N + j0;
@@ -1931,7 +1953,7 @@ __global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, 
 // The same for pooling radii beyond kPoolRegRadius: the chunk's votes and halo
 // staged in LDS, one output position per thread and step.
 __global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vote, float* __restrict__ pooled,
-                                                          unsigned* __restrict__ hist, int N, int r,
+                                                          unsigned* __restrict__ hist, int N, int r, int avg,
                                                           const ExactArgs ea) {
   __shared__ float sv[kPoolChunk + 2 * kMaxPoolRadius];
   __shared__ PoolShared ps;
@@ -1952,7 +1974,7 @@ __global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vo
   }
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
   __syncthreads();
-  pool_and_count(sv, e0, e1, c0, c1, r, pooled + static_cast<int64_t>(bh) * N, sh);
+  pool_and_count(sv, e0, e1, c0, c1, r, avg, pooled + static_cast<int64_t>(bh) * N, sh);
   __syncthreads();
   flush_hist(sh, hist + static_cast<int64_t>(bh) * kHistBins);
 }
@@ -2494,20 +2516,20 @@ void launch_stats(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
 
 template <int D>
 void launch_votes(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int qrow0, const uint16_t* k,
-                  kvc_strides kvs, int H, int L, int w, int r, float scale_log2, char* ws, float* vote,
+                  kvc_strides kvs, int H, int L, int w, int r, int avg, float scale_log2, char* ws, float* vote,
                   float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkMfma - 1) / kChunkMfma, static_cast<unsigned>(lay.BH));
-  snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
+  snap_votes_bf16<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r, avg,
                                                 scale_log2, reinterpret_cast<const float2*>(ws + lay.rowstat),
                                                 vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
 
 template <int D>
 void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qrow0, const float* k,
-                  kvc_strides kvs, int H, int L, int w, int r, float scale_log2, char* ws, float* vote,
+                  kvc_strides kvs, int H, int L, int w, int r, int avg, float scale_log2, char* ws, float* vote,
                   float* pooled, hipStream_t stream) {
   const dim3 g((lay.N + kChunkF32 - 1) / kChunkF32, static_cast<unsigned>(lay.BH));
-  snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r,
+  snap_votes_f32<D><<<g, kThreads, 0, stream>>>(q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, r, avg,
                                                scale_log2, reinterpret_cast<const float2*>(ws + lay.rowstat),
                                                vote, pooled, reinterpret_cast<unsigned*>(ws + lay.hist));
 }
@@ -2517,7 +2539,7 @@ void launch_votes(const SnapLayout& lay, const float* q, kvc_strides qs, int qro
 // histogram), with phase marks 2, 3 and 4.
 template <typename T>
 void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int qrow0, const T* k,
-                         kvc_strides kvs, int H, int L, int D, int w, int r, float scale_log2, char* ws,
+                         kvc_strides kvs, int H, int L, int D, int w, int r, int avg, float scale_log2, char* ws,
                          float* vote, float* pooled, hipStream_t stream) {
   if (D == 128)
     launch_stats<128>(lay, q, qs, qrow0, k, kvs, H, L, w, scale_log2, ws, stream);
@@ -2528,9 +2550,9 @@ void launch_score_passes(const SnapLayout& lay, const T* q, kvc_strides qs, int 
       reinterpret_cast<const float2*>(ws + lay.part), lay.nchunk, reinterpret_cast<float2*>(ws + lay.rowstat));
   mark_phase(3, stream);
   if (D == 128)
-    launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, r, scale_log2, ws, vote, pooled, stream);
+    launch_votes<128>(lay, q, qs, qrow0, k, kvs, H, L, w, r, avg, scale_log2, ws, vote, pooled, stream);
   else
-    launch_votes<64>(lay, q, qs, qrow0, k, kvs, H, L, w, r, scale_log2, ws, vote, pooled, stream);
+    launch_votes<64>(lay, q, qs, qrow0, k, kvs, H, L, w, r, avg, scale_log2, ws, vote, pooled, stream);
   mark_phase(4, stream);
 }
 
@@ -2633,32 +2655,32 @@ thread_local bool g_force_residency_fail = false;
 thread_local bool g_force_wait_timeout = false;
 
 template <int R>
-void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, const ExactArgs& ea,
+void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, int avg, const ExactArgs& ea,
                    hipStream_t stream) {
   const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
   if (N % 4 == 0 && aligned16(vote) && (!pooled || aligned16(pooled)))
-    snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, ea);
+    snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
   else
-    snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, ea);
+    snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
 }
 
 // Max-pool of the raw votes with the histogram of the results (pooled scores
 // stored if `pooled` is not NULL; radii beyond kPoolRegRadius always store them).
-void launch_pool(float* vote, float* pooled, unsigned* hist, int BH, int N, int r, const ExactArgs& ea,
+void launch_pool(float* vote, float* pooled, unsigned* hist, int BH, int N, int r, int avg, const ExactArgs& ea,
                  hipStream_t stream) {
   static_assert(kPoolRegRadius == 7, "the cases below cover radii 0 .. kPoolRegRadius");
   switch (r) {
-    case 0: return launch_pool_r<0>(vote, pooled, hist, BH, N, ea, stream);
-    case 1: return launch_pool_r<1>(vote, pooled, hist, BH, N, ea, stream);
-    case 2: return launch_pool_r<2>(vote, pooled, hist, BH, N, ea, stream);
-    case 3: return launch_pool_r<3>(vote, pooled, hist, BH, N, ea, stream);
-    case 4: return launch_pool_r<4>(vote, pooled, hist, BH, N, ea, stream);
-    case 5: return launch_pool_r<5>(vote, pooled, hist, BH, N, ea, stream);
-    case 6: return launch_pool_r<6>(vote, pooled, hist, BH, N, ea, stream);
-    case 7: return launch_pool_r<7>(vote, pooled, hist, BH, N, ea, stream);
+    case 0: return launch_pool_r<0>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 1: return launch_pool_r<1>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 2: return launch_pool_r<2>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 3: return launch_pool_r<3>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 4: return launch_pool_r<4>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 5: return launch_pool_r<5>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 6: return launch_pool_r<6>(vote, pooled, hist, BH, N, avg, ea, stream);
+    case 7: return launch_pool_r<7>(vote, pooled, hist, BH, N, avg, ea, stream);
     default: {
       const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
-      snap_pool_lds<<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, r, ea);
+      snap_pool_lds<<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, r, avg, ea);
     }
   }
 }
@@ -2670,8 +2692,8 @@ void launch_pool(float* vote, float* pooled, unsigned* hist, int BH, int N, int 
 // flagged head first). Phase marks 1 to 4.
 template <int D>
 kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint16_t* q, kvc_strides qs, int qrow0,
-                              const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, float scale_log2,
-                              char* ws, float* vote, float* pooled, hipStream_t stream) {
+                              const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, int avg,
+                              float scale_log2, char* ws, float* vote, float* pooled, hipStream_t stream) {
   float* ref = reinterpret_cast<float*>(ws + lay.cref);
   unsigned long long* acc = reinterpret_cast<unsigned long long*>(ws + lay.cacc);
   unsigned* cnt = reinterpret_cast<unsigned*>(ws + lay.ccnt);
@@ -2728,7 +2750,7 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   }
   if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
   mark_phase(3, stream);
-  launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, ea, stream);
+  launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, avg, ea, stream);
   mark_phase(4, stream);
   return KVC_OK;
 }
@@ -2770,13 +2792,13 @@ extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int win
   return lay.total;
 }
 
-extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs, const void* k,
-                                          const void* v, kvc_strides kvs, int B, int H, int L, int D,
-                                          int window, int budget, int pool_kernel, kvc_dtype dt,
-                                          void* k_out, void* v_out, int32_t* idx_out,
-                                          float* pooled_out, float* vote_out, void* workspace,
-                                          size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
+namespace kvc {
+namespace {
+
+// Host checks of one layer's arguments (everything but the workspace).
+kvc_status snap_validate(const void* q, int q_len, kvc_strides qs, const void* k, const void* v, kvc_strides kvs,
+                         int B, int H, int L, int D, int window, int budget, int pool_kernel, int pool_type,
+                         kvc_dtype dt, const void* k_out, const void* v_out, const int32_t* idx_out) {
   if (!q || !k || !v || !k_out || !v_out || !idx_out)
     return fail(KVC_ERR_INVALID_ARG, "snapkv: q, k, v, k_out, v_out and idx_out must be non-NULL");
   if (dt != KVC_BF16 && dt != KVC_F32) return fail(KVC_ERR_INVALID_ARG, "snapkv: unknown dtype %d", (int)dt);
@@ -2790,25 +2812,31 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
     return fail(KVC_ERR_INVALID_ARG, "snapkv: pool_kernel must be odd and >= 1 (got %d)", pool_kernel);
   if (pool_kernel / 2 > kMaxPoolRadius)
     return fail(KVC_ERR_UNSUPPORTED, "snapkv: pool_kernel %d > %d", pool_kernel, 2 * kMaxPoolRadius + 1);
+  if (pool_type != KVC_POOL_MAX && pool_type != KVC_POOL_AVG)
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: unknown pool type %d", pool_type);
   if (q_len < window) return fail(KVC_ERR_INVALID_ARG, "snapkv: q_len %d < window %d", q_len, window);
   if (D != 64 && D != 128) return fail(KVC_ERR_UNSUPPORTED, "snapkv: head_dim %d not in {64, 128}", D);
   const int64_t es = dt == KVC_BF16 ? 2 : 4;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
     return fail(KVC_ERR_INVALID_ARG, "snapkv: device pointers must be 16-byte aligned");
   const int64_t strides[6] = {qs.b, qs.h, qs.t, kvs.b, kvs.h, kvs.t};
-  for (int64_t s : strides)
-    if (s < 0 || (s * es) % 16 != 0)
+  for (int64_t st : strides)
+    if (st < 0 || (st * es) % 16 != 0)
       return fail(KVC_ERR_INVALID_ARG, "snapkv: strides must be non-negative and multiples of 16 bytes");
   if (kvs.t < D || qs.t < D)
     return fail(KVC_ERR_INVALID_ARG, "snapkv: row strides must be >= head_dim (D axis contiguous)");
+  return KVC_OK;
+}
+
+// One validated launch sequence over B*H heads of length L: the score
+// schedule, the selection and the gather.
+kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, const void* v, kvc_strides kvs,
+                     int B, int H, int L, int D, int window, int budget, int pool_kernel, int avg, kvc_dtype dt,
+                     void* k_out, void* v_out, int32_t* idx_out, float* pooled_out, float* vote_out, char* ws,
+                     hipStream_t stream) {
   SnapLayout lay;
   snap_layout(B, H, L, D, window, budget, dt, &lay);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(KVC_ERR_WORKSPACE, "snapkv: workspace of %zu bytes needed, got %zu", lay.total,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(KVC_ERR_INVALID_ARG, "snapkv: workspace must be 16-byte aligned");
-
-  char* ws = static_cast<char*>(workspace);
+  const int64_t es = dt == KVC_BF16 ? 2 : 4;
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D)));
   float* vote = vote_out;  // votes are written only when asked for
   unsigned* hist = reinterpret_cast<unsigned*>(ws + lay.hist);
@@ -2826,8 +2854,8 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   const int Gc = try_single && (g_schedule == KVC_SNAPKV_SINGLE_PASS || Gw > 0) ? coop_grid(lay, D) : 0;
   int schedule = KVC_SNAPKV_TWO_PASS;
   mark_phase(0, stream);
-  // what the selection reads: the pooled scores, or (single pass, small
-  // pooling radius) the raw votes, which it then pools itself
+  // what the selection reads: the pooled scores, or (single pass, max-pool of
+  // a small radius) the raw votes, which it then pools itself
   const float* sel_src = pooled;
   int sel_rad = 0;
   if (Gw > 0 || Gc > 0) {
@@ -2837,14 +2865,14 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
     // pooling kernel has read them by then). The pooling kernel stores pooled
     // scores only if the caller asked for them or the selection reads them.
     const int r = pool_kernel / 2;
-    const bool sel_pools = r <= kSelMaxRad;
+    const bool sel_pools = !avg && r <= kSelMaxRad;
     float* vraw = vote ? vote : reinterpret_cast<float*>(ws + (sel_pools ? lay.pooled : lay.cand));
     float* pooled_dst = pooled_out ? pooled_out : sel_pools ? nullptr : pooled;
     const uint16_t* qb = static_cast<const uint16_t*>(q);
     const uint16_t* kb = static_cast<const uint16_t*>(k);
-    kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r,
+    kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r, avg,
                                                        scale_log2, ws, vraw, pooled_dst, stream)
-                             : launch_single_pass<64>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r,
+                             : launch_single_pass<64>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r, avg,
                                                       scale_log2, ws, vraw, pooled_dst, stream);
     if (st == KVC_OK) {
       schedule = KVC_SNAPKV_SINGLE_PASS;
@@ -2864,11 +2892,11 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
     g_last_kernel = dt == KVC_BF16 ? "snap_stats_bf16+snap_votes_bf16" : "snap_stats_f32+snap_votes_f32";
     if (dt == KVC_BF16)
       launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0,
-                                    static_cast<const uint16_t*>(k), kvs, H, L, D, window, pool_kernel / 2,
+                                    static_cast<const uint16_t*>(k), kvs, H, L, D, window, pool_kernel / 2, avg,
                                     scale_log2, ws, vote, pooled, stream);
     else
       launch_score_passes<float>(lay, static_cast<const float*>(q), qs, qrow0, static_cast<const float*>(k), kvs, H,
-                                 L, D, window, pool_kernel / 2, scale_log2, ws, vote, pooled, stream);
+                                 L, D, window, pool_kernel / 2, avg, scale_log2, ws, vote, pooled, stream);
   }
   kvc_status st = check_launch("snapkv score passes");
   if (st != KVC_OK) return st;
@@ -2895,6 +2923,121 @@ extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides 
   st = check_launch("snapkv gather");
   if (st == KVC_OK) g_last_schedule = schedule;
   return st;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_snapkv_compress(const void* q, int q_len, kvc_strides qs, const void* k,
+                                          const void* v, kvc_strides kvs, int B, int H, int L, int D,
+                                          int window, int budget, int pool_kernel, kvc_dtype dt,
+                                          void* k_out, void* v_out, int32_t* idx_out,
+                                          float* pooled_out, float* vote_out, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  kvc_status st = snap_validate(q, q_len, qs, k, v, kvs, B, H, L, D, window, budget, pool_kernel, KVC_POOL_MAX, dt,
+                                k_out, v_out, idx_out);
+  if (st != KVC_OK) return st;
+  SnapLayout lay;
+  snap_layout(B, H, L, D, window, budget, dt, &lay);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(KVC_ERR_WORKSPACE, "snapkv: workspace of %zu bytes needed, got %zu", lay.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(KVC_ERR_INVALID_ARG, "snapkv: workspace must be 16-byte aligned");
+  return snap_core(q, q_len, qs, k, v, kvs, B, H, L, D, window, budget, pool_kernel, 0, dt, k_out, v_out, idx_out,
+                   pooled_out, vote_out, static_cast<char*>(workspace), stream);
+}
+
+extern "C" size_t kvc_snapkv_workspace_bytes_ex(int n_layers, int B, int H, int L, int D, int window, int budget,
+                                                int pool_kernel, kvc_dtype dt, int ragged) {
+  (void)pool_kernel;
+  if (n_layers < 1 || B < 1) return 0;
+  // a ragged batch runs one sequence of one layer per launch sequence; else
+  // the layers run together as one batch of n_layers * B (or one by one)
+  const int64_t Bc = ragged ? 1 : static_cast<int64_t>(n_layers) * B;
+  if (Bc > INT32_MAX) return 0;
+  SnapLayout lay;
+  if (!snap_layout(static_cast<int>(Bc), H, L, D, window, budget, dt, &lay)) return 0;
+  return lay.total;
+}
+
+extern "C" kvc_status kvc_snapkv_compress_ex(const void* q, int q_len, kvc_strides qs, int64_t q_layer_stride,
+                                             const void* k, const void* v, kvc_strides kvs,
+                                             int64_t kv_layer_stride, int n_layers, int B, int H, int L, int D,
+                                             const int32_t* lengths, int window, int budget, int pool_kernel,
+                                             int pool_type, kvc_dtype dt, void* k_out, void* v_out,
+                                             int32_t* idx_out, float* pooled_out, float* vote_out,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (n_layers < 1) return fail(KVC_ERR_INVALID_ARG, "snapkv: n_layers must be >= 1 (got %d)", n_layers);
+  kvc_status st = snap_validate(q, q_len, qs, k, v, kvs, B, H, L, D, window, budget, pool_kernel, pool_type, dt,
+                                k_out, v_out, idx_out);
+  if (st != KVC_OK) return st;
+  const int64_t es = dt == KVC_BF16 ? 2 : 4;
+  if (n_layers > 1 && (q_layer_stride < 0 || kv_layer_stride < 0 || (q_layer_stride * es) % 16 != 0 ||
+                       (kv_layer_stride * es) % 16 != 0))
+    return fail(KVC_ERR_INVALID_ARG, "snapkv: layer strides must be non-negative and multiples of 16 bytes");
+  if (static_cast<int64_t>(n_layers) * B * H > INT32_MAX)
+    return fail(KVC_ERR_UNSUPPORTED, "snapkv: n_layers * B * H too large");
+  if (lengths)
+    for (int b = 0; b < B; ++b)
+      if (lengths[b] <= budget || lengths[b] > L)
+        return fail(KVC_ERR_INVALID_ARG, "snapkv: lengths[%d] = %d must satisfy budget (%d) < length <= L (%d)", b,
+                    lengths[b], budget, L);
+  const size_t need = kvc_snapkv_workspace_bytes_ex(n_layers, B, H, L, D, window, budget, pool_kernel, dt,
+                                                    lengths != nullptr);
+  if (need == 0) return fail(KVC_ERR_UNSUPPORTED, "snapkv: sizes out of range");
+  if (!workspace || workspace_bytes < need)
+    return fail(KVC_ERR_WORKSPACE, "snapkv: workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(KVC_ERR_INVALID_ARG, "snapkv: workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const int avg = pool_type == KVC_POOL_AVG;
+  const int kk = budget - window;
+  const int64_t out_bh = static_cast<int64_t>(budget) * D * es;  // output bytes per head
+  char* ko = static_cast<char*>(k_out);
+  char* vo = static_cast<char*>(v_out);
+  const char* qc = static_cast<const char*>(q);
+  const char* kc = static_cast<const char*>(k);
+  const char* vc = static_cast<const char*>(v);
+  if (!lengths) {
+    const int64_t N = L - window;
+    const bool fold = n_layers == 1 || (q_layer_stride == static_cast<int64_t>(B) * qs.b &&
+                                        kv_layer_stride == static_cast<int64_t>(B) * kvs.b);
+    if (fold) {  // the layers are one batch of n_layers * B sequences
+      if (static_cast<int64_t>(n_layers) * B * H > 65535)
+        return fail(KVC_ERR_UNSUPPORTED, "snapkv: n_layers * B * H must be <= 65535");
+      return snap_core(q, q_len, qs, k, v, kvs, n_layers * B, H, L, D, window, budget, pool_kernel, avg, dt, k_out,
+                       v_out, idx_out, pooled_out, vote_out, ws, stream);
+    }
+    for (int l = 0; l < n_layers; ++l) {  // layer by layer, one workspace reused in stream order
+      const int64_t bh0 = static_cast<int64_t>(l) * B * H;
+      st = snap_core(qc + l * q_layer_stride * es, q_len, qs, kc + l * kv_layer_stride * es,
+                     vc + l * kv_layer_stride * es, kvs, B, H, L, D, window, budget, pool_kernel, avg, dt,
+                     ko + bh0 * out_bh, vo + bh0 * out_bh, idx_out + bh0 * kk, pooled_out ? pooled_out + bh0 * N : nullptr,
+                     vote_out ? vote_out + bh0 * N : nullptr, ws, stream);
+      if (st != KVC_OK) return st;
+    }
+    return KVC_OK;
+  }
+  // ragged: sequence b of layer l is its own launch sequence over its
+  // lengths[b] keys; pooled / vote rows are packed per (l, b) in that order,
+  // H rows of lengths[b] - window each
+  int64_t packed = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    for (int b = 0; b < B; ++b) {
+      const int Lb = lengths[b];
+      const int64_t bh0 = (static_cast<int64_t>(l) * B + b) * H;
+      st = snap_core(qc + (l * q_layer_stride + b * qs.b) * es, q_len, qs,
+                     kc + (l * kv_layer_stride + b * kvs.b) * es, vc + (l * kv_layer_stride + b * kvs.b) * es, kvs, 1,
+                     H, Lb, D, window, budget, pool_kernel, avg, dt, ko + bh0 * out_bh, vo + bh0 * out_bh,
+                     idx_out + bh0 * kk, pooled_out ? pooled_out + packed : nullptr,
+                     vote_out ? vote_out + packed : nullptr, ws, stream);
+      if (st != KVC_OK) return st;
+      packed += static_cast<int64_t>(H) * (Lb - window);
+    }
+  }
+  return KVC_OK;
 }
 
 extern "C" void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events) {

@@ -17,7 +17,8 @@ Readings adopted where the page is silent (each is listed in the design notes):
     window); only prefix columns are voted on;
   * the vote of a prefix position is the plain sum over the window queries;
   * the pooling is a max-pool of odd width p, stride 1, over the prefix vote
-    vector only, with out-of-range neighbours ignored;
+    vector only, with out-of-range neighbours ignored; the averaging variant
+    takes the mean of the same in-range neighbours;
   * the budget counts the window, so budget - window prefix positions are kept;
     equal pooled scores are broken toward the lower position; kept positions
     come out in ascending order, followed by the window.
@@ -73,6 +74,22 @@ def max_pool(v, p):
     return np.lib.stride_tricks.sliding_window_view(padded, p).max(axis=1)
 
 
+def avg_pool(v, p):
+    """Processing flow step 3 with an averaging 1D pooling of odd width p, stride 1.
+
+    pooled[j] = mean(v[j + d]) over |d| <= p // 2 with 0 <= j + d < len(v): the
+    out-of-range neighbours are ignored (not counted), as for the max-pool, so a
+    window at either end averages fewer votes.
+    """
+    r = p // 2
+    # Out-of-range neighbours are ignored: pad with NaN and take the mean of the rest.
+    padded = np.concatenate([np.full(r, np.nan), v, np.full(r, np.nan)])
+    return np.nanmean(np.lib.stride_tricks.sliding_window_view(padded, p), axis=1)
+
+
+POOLS = {"max": max_pool, "avg": avg_pool}
+
+
 def top_positions(pooled, n_keep):
     """Choose the ``n_keep`` prefix positions with the largest pooled score.
 
@@ -101,10 +118,11 @@ def to_f64(x, dtype):
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
-def compress_head(q_win, k, v, budget, pool_kernel, dtype):
+def compress_head(q_win, k, v, budget, pool_kernel, dtype, pool_type="max"):
     """SnapKV compression of one head.
 
-    q_win: [w, D] window queries; k, v: [L, D]; values stored as ``dtype``.
+    q_win: [w, D] window queries; k, v: [L, D]; values stored as ``dtype``;
+    ``pool_type`` "max" (max_pool) or "avg" (avg_pool).
     Returns a dict with scores-derived intermediates and the compacted cache:
       P [w, L], m [w], l [w]   softmax of the window rows (natural-exp domain)
       vote [t0], pooled [t0]   float64
@@ -121,23 +139,33 @@ def compress_head(q_win, k, v, budget, pool_kernel, dtype):
     S = window_scores(to_f64(q_win, dtype), to_f64(k, dtype))
     P, m, l = row_softmax(S)
     vt = vote(P, t0)
-    pooled = max_pool(vt, pool_kernel)
+    pooled = POOLS[pool_type](vt, pool_kernel)
     idx = top_positions(pooled, budget - w)
     return dict(P=P, m=m, l=l, vote=vt, pooled=pooled, idx=idx,
                 k_out=gather_concat(k, idx, t0), v_out=gather_concat(v, idx, t0))
 
 
-def compress(q, k, v, window, budget, pool_kernel, dtype, heads=None):
+def compress(q, k, v, window, budget, pool_kernel, dtype, heads=None, pool_type="max", lengths=None):
     """SnapKV compression of a whole layer; every (batch, head) is independent.
 
     q: [B, H, q_len, D] (its last ``window`` rows are the observation window);
     k, v: [B, H, L, D]. ``heads`` optionally restricts the work to a list of
-    (b, h) pairs. Returns {(b, h): compress_head(...)}.
+    (b, h) pairs. ``lengths`` (optional, [B]) makes the batch ragged: sequence
+    b is the prompt k[b, :, :lengths[b]], v[b, :, :lengths[b]], and its window
+    queries are still q's last ``window`` rows. Returns {(b, h): compress_head(...)}.
     """
-    B, H = k.shape[:2]
+    B, H, L = k.shape[:3]
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     out = {}
     for b, h in pairs:
+        Lb = L if lengths is None else int(lengths[b])
         qw = q[b, h, q.shape[2] - window:]
-        out[(b, h)] = compress_head(qw, k[b, h], v[b, h], budget, pool_kernel, dtype)
+        out[(b, h)] = compress_head(qw, k[b, h, :Lb], v[b, h, :Lb], budget, pool_kernel, dtype, pool_type)
     return out
+
+
+def compress_layers(q, k, v, window, budget, pool_kernel, dtype, pool_type="max", lengths=None):
+    """All layers of one prompt: q [n_layers, B, H, q_len, D], k and v [n_layers, B, H, L, D]; each layer
+    is compressed on its own (the method runs once per attention layer). Returns a list of compress(...)."""
+    return [compress(q[l], k[l], v[l], window, budget, pool_kernel, dtype, pool_type=pool_type, lengths=lengths)
+            for l in range(k.shape[0])]

@@ -205,3 +205,103 @@ def test_rejects_bad_arguments():
         ref.compress_head(q, k, v, budget=20, pool_kernel=3, dtype="fp64")  # budget >= L
     with pytest.raises(ValueError):
         ref.compress_head(q, k, v, budget=10, pool_kernel=4, dtype="fp64")  # even kernel
+
+
+def test_worked_example_average_pooling():
+    """Hand-worked means over in-range neighbours (tests/golden/snapkv_worked.txt) and the kept sets
+    they give."""
+    g, q, k, v = _worked()
+    t0 = k.shape[0] - q.shape[0]
+    vt = ref.vote(ref.row_softmax(ref.window_scores(q, k))[0], t0)
+    for p in (1, 3, 5):
+        np.testing.assert_allclose(ref.avg_pool(vt, p), gio.nums(g[f"pooled_avg_p{p}"]), atol=1e-14)
+    n = 0
+    for key, toks in g.items():
+        if key.startswith("idxavg_"):
+            _, pk, bk = key.split("_")
+            out = ref.compress_head(q, k, v, int(bk[1:]), int(pk[1:]), "fp64", pool_type="avg")
+            assert out["idx"].tolist() == gio.ints(toks), key
+            n += 1
+    assert n == 8
+
+
+@pytest.mark.parametrize("p", [1, 3, 5, 7, 9, 17, 65])
+def test_avg_pool_matches_torch(p):
+    """Same as torch's avg_pool1d with zero padding left out of the count (count_include_pad=False)."""
+    rng = np.random.default_rng(p)
+    for n in (1, 2, p // 2, p, 3 * p + 1, 200):
+        if n < 1:
+            continue
+        v = rng.random(n)
+        want = torch.nn.functional.avg_pool1d(torch.from_numpy(v)[None, None], kernel_size=p, stride=1,
+                                              padding=p // 2, count_include_pad=False)[0, 0].numpy()
+        if p // 2 > 0 and n < p // 2:  # torch needs at least one in-range value per window, as we do
+            continue
+        np.testing.assert_allclose(ref.avg_pool(v, p), want, rtol=1e-12, atol=0)
+
+
+def test_avg_pool_closed_forms():
+    rng = np.random.default_rng(0)
+    v = rng.random(50)
+    np.testing.assert_array_equal(ref.avg_pool(v, 1), v)                     # width 1: identity
+    np.testing.assert_allclose(ref.avg_pool(np.full(30, 0.3), 7), 0.3)        # constant stays constant
+    spike = np.zeros(40)
+    spike[20] = 7.0                                                           # interior spike: 7 / p around it
+    np.testing.assert_allclose(ref.avg_pool(spike, 5)[18:23], 7.0 / 5)
+    assert np.all(ref.avg_pool(spike, 5)[:18] == 0) and np.all(ref.avg_pool(spike, 5)[23:] == 0)
+    edge = np.zeros(40)
+    edge[0] = 6.0                                                             # edge spike: fewer neighbours
+    np.testing.assert_allclose(ref.avg_pool(edge, 5)[:3], [6.0 / 3, 6.0 / 4, 6.0 / 5])
+    assert ref.avg_pool(v, 5).sum() <= v.sum() * 1.0000001 * 5 / 3            # a mean never exceeds the max
+    assert np.all(ref.avg_pool(v, 9) <= ref.max_pool(v, 9) + 1e-15)
+
+
+def test_zero_queries_average_pooling_ties():
+    """Q = 0 gives equal votes, so the averages are equal too (up to rounding of equal sums) and the
+    kept set is decided by the positions: with exactly equal votes every mean is the same value."""
+    w, L, D, budget = 4, 60, 8, 20
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((L, D))
+    out = ref.compress_head(np.zeros((w, D)), k, k, budget, 5, "fp64", pool_type="avg")
+    np.testing.assert_allclose(out["pooled"], out["vote"][0], rtol=1e-14)
+
+
+def test_ragged_lengths_ignore_padding():
+    """A ragged batch: sequence b sees only its first lengths[b] keys; whatever lies in the padding
+    beyond does not change its result, and the result is that of the truncated prompt."""
+    B, H, L, D, w, budget = 3, 2, 90, 16, 4, 20
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((B, H, w, D))
+    k = rng.standard_normal((B, H, L, D))
+    v = rng.standard_normal((B, H, L, D))
+    lengths = [90, 41, 64]
+    a = ref.compress(q, k, v, w, budget, 5, "fp64", lengths=lengths)
+    k2, v2 = k.copy(), v.copy()
+    for b, n in enumerate(lengths):
+        k2[b, :, n:] = 50.0 * rng.standard_normal((H, L - n, D))  # loud padding
+        v2[b, :, n:] = -9.0
+    c = ref.compress(q, k2, v2, w, budget, 5, "fp64", lengths=lengths)
+    for b, n in enumerate(lengths):
+        for h in range(H):
+            assert a[(b, h)]["idx"].tolist() == c[(b, h)]["idx"].tolist()
+            np.testing.assert_array_equal(a[(b, h)]["vote"], c[(b, h)]["vote"])
+            assert a[(b, h)]["vote"].shape == (n - w,)
+            np.testing.assert_array_equal(a[(b, h)]["k_out"][-w:], k[b, h, n - w:n])  # its own window
+            t = ref.compress_head(q[b, h], k[b, h, :n], v[b, h, :n], budget, 5, "fp64")
+            assert t["idx"].tolist() == a[(b, h)]["idx"].tolist()
+
+
+def test_layers_are_independent():
+    """compress_layers runs every layer on its own: permuting the layers permutes the results."""
+    NL, B, H, L, D, w, budget = 3, 2, 2, 70, 8, 4, 16
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((NL, B, H, w, D))
+    k = rng.standard_normal((NL, B, H, L, D))
+    v = rng.standard_normal((NL, B, H, L, D))
+    out = ref.compress_layers(q, k, v, w, budget, 3, "fp64", pool_type="avg")
+    perm = [2, 0, 1]
+    outp = ref.compress_layers(q[perm], k[perm], v[perm], w, budget, 3, "fp64", pool_type="avg")
+    for i, l in enumerate(perm):
+        for bh in out[l]:
+            assert out[l][bh]["idx"].tolist() == outp[i][bh]["idx"].tolist()
+            np.testing.assert_array_equal(out[l][bh]["pooled"], outp[i][bh]["pooled"])
