@@ -324,6 +324,23 @@ kvc_status kvc_sink_recent(void* ring_k, void* ring_v, int32_t* slot_pos,
                            int n_sink, int n_recent, int B, int H, int D,
                            kvc_dtype dt, int32_t* kept_idx_out, hipStream_t stream);
 
+/* Positions inside the cache (StreamingLLM page, cache structure and inference
+ * flow; the page does not say which positions the model uses while streaming):
+ * after `len` tokens, cache_pos_out[slot] is the rank of the token the slot
+ * holds among the held tokens, sinks first (in arrival order), then the recent
+ * window from oldest to newest, i.e. min(n_sink, len) + (p - max(n_sink,
+ * len - n_recent)) for a recent token at position p and p for a sink; -1 for a
+ * slot that holds no token yet. These stay below n_sink + n_recent however long
+ * the stream runs, and the newest token takes the last one: the positions a
+ * positional encoding would give the cached keys and the next query (which
+ * takes min(len, n_sink + n_recent)). slot_pos: the [n_sink + n_recent] slot
+ * map kept by kvc_sink_recent (read on the stream, after the calls before it);
+ * cache_pos_out: [n_sink + n_recent] int32, device. Requires len >= 1,
+ * n_sink >= 0, n_recent >= 1, and slot_pos as kvc_sink_recent leaves it after
+ * `len` tokens. */
+kvc_status kvc_sink_cache_positions(const int32_t* slot_pos, int64_t len, int n_sink, int n_recent,
+                                    int32_t* cache_pos_out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Decode attention over a compacted or windowed cache.                       */
 /* ------------------------------------------------------------------------- */

@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback", "kvc_snapkv_force_wait_timeout",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
     "kvc_decode_attention_noalloc", "kvc_snapkv_workspace_bytes_ex", "kvc_snapkv_compress_ex",
+    "kvc_sink_cache_positions",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -122,6 +123,8 @@ def library():
     L.kvc_decode_attention_noalloc.argtypes = [vp, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, vp, vp]
     L.kvc_measure_stream_read.restype = i32
     L.kvc_measure_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    L.kvc_sink_cache_positions.restype = i32
+    L.kvc_sink_cache_positions.argtypes = [vp, i64, i32, i32, vp, vp]
     L.kvc_sink_recent.restype = i32
     L.kvc_sink_recent.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
     _lib = L
@@ -480,3 +483,17 @@ class SinkCache:
             self.length, self.n_sink, self.n_recent, self.B, self.H, self.D,
             _dtype_code(self.k), _ptr(self.kept), _stream()))
         return self.kept[:n_kept]
+
+    def cache_positions(self, out=None):
+        """Position inside the cache of each slot's token ([n_sink + n_recent] int32, -1 for an empty slot;
+        kvc_sink_cache_positions): the positions a positional encoding would give the cached keys."""
+        if self.length < 1:
+            raise ValueError("the cache holds no token yet")
+        slots = self.n_sink + self.n_recent
+        if out is None:
+            out = torch.empty((slots,), dtype=torch.int32, device=self.k.device)
+        else:
+            _check_out(out, "out", (slots,), torch.int32, self.k.device)
+        _check(library().kvc_sink_cache_positions(_ptr(self.slot_pos), self.length, self.n_sink, self.n_recent,
+                                                  _ptr(out), _stream()))
+        return out

@@ -42,10 +42,37 @@ __global__ __launch_bounds__(kThreads) void sink_update(char* __restrict__ rk, c
   if (t == 0) slot_pos[slot] = pos;
 }
 
+// Position inside the cache of each slot's token (its rank among the held
+// tokens: sinks first, then the recent window oldest to newest), one slot per
+// thread; -1 for a slot that holds no token yet.
+__global__ __launch_bounds__(kThreads) void sink_positions(const int* __restrict__ slot_pos, int n_slots, int n_sink,
+                                                           int n_sinks_held, int recent_from,
+                                                           int* __restrict__ cache_pos) {
+  const int t = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
+  if (t >= n_slots) return;
+  const int p = slot_pos[t];
+  cache_pos[t] = p < 0 ? -1 : p < n_sink ? p : n_sinks_held + (p - recent_from);
+}
+
 }  // namespace
 }  // namespace kvc
 
 using namespace kvc;
+
+extern "C" kvc_status kvc_sink_cache_positions(const int32_t* slot_pos, int64_t len, int n_sink, int n_recent,
+                                               int32_t* cache_pos_out, hipStream_t stream) {
+  clear_error();
+  if (!slot_pos || !cache_pos_out) return fail(KVC_ERR_INVALID_ARG, "sink positions: NULL pointer");
+  if (len < 1 || len > INT32_MAX) return fail(KVC_ERR_INVALID_ARG, "sink positions: len must be in [1, 2^31-1]");
+  if (n_sink < 0 || n_recent < 1 || static_cast<int64_t>(n_sink) + n_recent > INT32_MAX)
+    return fail(KVC_ERR_INVALID_ARG, "sink positions: need n_sink >= 0 and n_recent >= 1");
+  const int n_slots = n_sink + n_recent;
+  const int64_t held_sinks = len < n_sink ? len : n_sink;
+  const int64_t recent_from = len - n_recent > n_sink ? len - n_recent : n_sink;
+  sink_positions<<<static_cast<unsigned>((n_slots + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+      slot_pos, n_slots, n_sink, static_cast<int>(held_sinks), static_cast<int>(recent_from), cache_pos_out);
+  return check_launch("sink_cache_positions");
+}
 
 extern "C" kvc_status kvc_sink_recent(void* ring_k, void* ring_v, int32_t* slot_pos, const void* k_new,
                                       const void* v_new, int64_t len, int n_sink, int n_recent, int B, int H,

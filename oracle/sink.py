@@ -11,9 +11,18 @@ the start of the stream plus a recent window of fixed length) and æŽ¨è«–ã®æµã‚
 (inference flow: each new token enters the recent region, the oldest recent
 token leaves once the window is full, sink tokens never leave).
 
-Reading adopted where the page is silent: the cache stores the sinks in slots
-0 .. s-1 and the recent window as a ring of r slots after them, so the
-position p >= s lives in slot s + (p - s) mod r.
+Readings adopted where the page is silent:
+  * the cache stores the sinks in slots 0 .. s-1 and the recent window as a
+    ring of r slots after them, so the position p >= s lives in slot
+    s + (p - s) mod r;
+  * the position a held token takes inside the cache (the position the model's
+    positional encoding would use while streaming) is its rank among the held
+    tokens in the order the inference flow keeps them: the sinks in arrival
+    order, then the recent window from oldest to newest. Positions then stay
+    below s + r however long the stream runs, which is what a cache of constant
+    size (cache structure subsection) streaming millions of tokens (section
+    å®Ÿé¨“ã¨çµæžœ, the 4M-token result) needs; the newest token always takes the
+    last position.
 """
 from collections import deque
 
@@ -64,3 +73,12 @@ def ring_after(rows, n_sink, n_recent):
         slot_rows[s] = row
         slot_pos[s] = p
     return slot_rows, slot_pos
+
+
+def cache_positions(length, n_sink, n_recent):
+    """Position inside the cache of the token each slot holds after ``length`` tokens, slot by slot
+    (-1 for a slot not yet written): the token's rank in the held order, sinks first, then the recent
+    tokens oldest to newest. The slots are filled by writing the tokens in order (ring_after)."""
+    _, slot_pos = ring_after(list(range(length)), n_sink, n_recent)
+    rank = {p: i for i, p in enumerate(kept_positions(length, n_sink, n_recent))}
+    return [rank[p] if p >= 0 else -1 for p in slot_pos]

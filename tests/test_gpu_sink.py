@@ -34,6 +34,7 @@ def test_sink_ring_matches_oracle(s, r, n, dtype, D, check_every):
         kept = cache.append(dev[t - 1, 0].contiguous(), dev[t - 1, 1].contiguous())
         if t in samples:
             assert kept.cpu().tolist() == ref.kept_positions(t, s, r), f"len {t}"
+            assert cache.cache_positions().cpu().tolist() == ref.cache_positions(t, s, r), f"positions, len {t}"
     rows_k = [toks[p, 0] for p in range(n)]
     rows_v = [toks[p, 1] for p in range(n)]
     exp_k, exp_pos = ref.ring_after(rows_k, s, r)
@@ -54,3 +55,19 @@ def test_sink_error_statuses():
     with pytest.raises(kvc.KvcError) as e:
         c.append(x, x)
     assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_cache_positions_long_stream():
+    """Positions inside a 4 + 1020 cache over a stream of 5000 tokens (the ring wrapped four times),
+    checked every 97 tokens: a permutation of 0 .. 1023 once full, the newest token last."""
+    B, H, D, s, r = 1, 2, 64, 4, 1020
+    cache = kvc.SinkCache(B, H, D, s, r)
+    x = torch.zeros((B, H, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((s + r,), dtype=torch.int32, device="cuda")
+    for t in range(1, 5001):
+        cache.append(x, x)
+        if t % 97 == 0 or t in (1, 4, 5, 1024, 1025, 5000):
+            got = cache.cache_positions(out).cpu().tolist()
+            assert got == ref.cache_positions(t, s, r), f"len {t}"
+            if t >= s + r:
+                assert sorted(got) == list(range(s + r))
