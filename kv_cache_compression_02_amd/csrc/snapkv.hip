@@ -475,6 +475,11 @@ __device__ __forceinline__ uint2 ld_agent_u2(const uint2* p) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Cache-policy bits of a direct-to-LDS load that streams data read once (the
+// nontemporal bit): on this device such a stream of K tiles moves measurably
+// more bytes per second than with the default policy.
+constexpr int kNtLoad = 2;
+
 // LDS row layout shared by K tiles and Q: a row is D*2 bytes of kP 16-byte
 // pieces; piece p of row R sits in slot p ^ (R & (kP-1)), so the 32 rows a
 // wave reads for one MFMA k-step hit distinct banks.
@@ -521,7 +526,7 @@ __device__ __forceinline__ void coop_issue_k_full(const char* rows, int64_t row_
   for (int i = wave; i < kWaves * Ly::kInstPerTile; i += 3) {
     const unsigned b16 = static_cast<unsigned>((i * Ly::kRowsPerInst) & (Ly::kP - 1)) << 4;
     const char* base = rows + static_cast<int64_t>(i * Ly::kRowsPerInst) * row_bytes;
-    __builtin_amdgcn_global_load_lds(base + (lrow + (x16 ^ b16)), (lds_void*)(kbuf + i * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + (lrow + (x16 ^ b16)), (lds_void*)(kbuf + i * 1024), 16, 0, kNtLoad);
   }
 }
 
@@ -1176,7 +1181,7 @@ __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsig
     for (int i = 0; i < Ly::kInst; ++i) {
       const unsigned b16 = static_cast<unsigned>((i * Ly::kRowsPerInst) & (Ly::kP - 1)) << 4;
       __builtin_amdgcn_global_load_lds(rows + static_cast<int64_t>(i * Ly::kRowsPerInst) * rb + (lrow + (x16 ^ b16)),
-                                       (lds_void*)(slot + i * 1024), 16, 0, 0);
+                                       (lds_void*)(slot + i * 1024), 16, 0, kNtLoad);
     }
   } else {  // the head's last, ragged tile or a padding tile: rows clamped to the data
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.kt) - static_cast<int64_t>(key0) * c.kst;
@@ -1186,7 +1191,7 @@ __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsig
       const int piece = (lane % Ly::kP) ^ (row & (Ly::kP - 1));
       const int key = min(key0 + row, c.L - 1);
       __builtin_amdgcn_global_load_lds(kb + static_cast<int64_t>(key) * c.kst + piece * 8,
-                                       (lds_void*)(slot + i * 1024), 16, 0, 0);
+                                       (lds_void*)(slot + i * 1024), 16, 0, kNtLoad);
     }
   }
 }
@@ -2426,15 +2431,15 @@ __global__ __launch_bounds__(kThreads) void snap_gather(const char* __restrict__
     int src = row < kk ? idx[static_cast<int64_t>(bh) * kk + row] : (L - w + (row - kk));
     src = min(max(src, 0), L - 1);
     const int64_t so = b * sb + h * sh + static_cast<int64_t>(src) * st + static_cast<int64_t>(vc) * 16;
-    kx[u] = *reinterpret_cast<const u32x4_t*>(k + so);
-    vx[u] = *reinterpret_cast<const u32x4_t*>(v + so);
+    kx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k + so));
+    vx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v + so));
     dst[u] = (static_cast<int64_t>(bh) * C + row) * row_bytes + static_cast<int64_t>(vc) * 16;
   }
 #pragma unroll
   for (int u = 0; u < kGatherPer; ++u) {
     if (dst[u] < 0) continue;
-    *reinterpret_cast<u32x4_t*>(k_out + dst[u]) = kx[u];
-    *reinterpret_cast<u32x4_t*>(v_out + dst[u]) = vx[u];
+    __builtin_nontemporal_store(kx[u], reinterpret_cast<u32x4_t*>(k_out + dst[u]));
+    __builtin_nontemporal_store(vx[u], reinterpret_cast<u32x4_t*>(v_out + dst[u]));
   }
 }
 
