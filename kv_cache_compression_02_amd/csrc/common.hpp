@@ -172,12 +172,13 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned* scratc
 }
 
 template <typename T>
-struct Vec16;  // a 16-byte piece of a row as float lanes
+struct Vec16;  // a 16-byte piece of a row as float lanes (loaded with the nontemporal bit:
+               // the kernels that use it stream rows they read once per call)
 template <>
 struct Vec16<uint16_t> {
   static constexpr int kN = 8;
   __device__ static void load(const void* p, float (&x)[8]) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[2 * i] = __uint_as_float(u[i] << 16);
@@ -189,7 +190,7 @@ template <>
 struct Vec16<float> {
   static constexpr int kN = 4;
   __device__ static void load(const void* p, float (&x)[4]) {
-    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = u[i];
   }

@@ -71,10 +71,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(const T* __restric
   u32x4_t kr[S], vr[S];
 #pragma unroll
   for (int st = 0; st < S; ++st)
-    kr[st] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(row0 + st * RPW, n - 1)) * kst);
+    kr[st] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(row0 + st * RPW, n - 1)) * kst));
 #pragma unroll
   for (int st = 0; st < S; ++st)
-    vr[st] = *reinterpret_cast<const u32x4_t*>(vb + static_cast<int64_t>(min(row0 + st * RPW, n - 1)) * kst);
+    vr[st] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_t*>(vb + static_cast<int64_t>(min(row0 + st * RPW, n - 1)) * kst));
   __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise sink the loads to their uses)
   float sc[S];
 #pragma unroll

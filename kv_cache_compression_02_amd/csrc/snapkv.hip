@@ -81,6 +81,15 @@ __device__ __forceinline__ void load_half_row(const uint16_t* p, bf16x8_t (&f)[D
   for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, src[s]);
 }
 
+// The same for a row streamed once (the keys of a score pass): loaded with the
+// nontemporal bit. The window queries, which many waves read again, are not.
+template <int D>
+__device__ __forceinline__ void load_half_row_nt(const uint16_t* p, bf16x8_t (&f)[D / 16]) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(src + s));
+}
+
 template <int D>
 __device__ __forceinline__ void zero_frag(bf16x8_t (&f)[D / 16]) {
 #pragma unroll
@@ -198,11 +207,11 @@ __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
 
   int tile = key0 + wave * kTile;
   bf16x8_t kf[KS];
-  if (tile < key1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, L - 1)) * kst, kf);
+  if (tile < key1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(tile + col, L - 1)) * kst, kf);
   for (; tile < key1; tile += kStep) {
     bf16x8_t kn[KS];
     const int nt = tile + kStep;
-    if (nt < key1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, L - 1)) * kst, kn);
+    if (nt < key1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(nt + col, L - 1)) * kst, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
@@ -341,11 +350,11 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
 
   int tile = e0 + wave * kTile;
   bf16x8_t kf[KS];
-  if (tile < e1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
+  if (tile < e1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
   for (; tile < e1; tile += kStep) {
     bf16x8_t kn[KS];
     const int nt = tile + kStep;
-    if (nt < e1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
+    if (nt < e1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
@@ -1748,9 +1757,11 @@ struct ExactArgs {
   const unsigned* status;  // the score kernel's failure code (non-zero: every head flagged); NULL: none
 };
 
+constexpr int kExactMaxWaves = 16;  // the largest workgroup that computes exact votes (1024 threads)
+
 struct ExactShared {
   float qs[kMaxWindow][128];
-  float red_m[kWaves][kMaxWindow], red_l[kWaves][kMaxWindow];
+  float red_m[kExactMaxWaves][kMaxWindow], red_l[kExactMaxWaves][kMaxWindow];
   float cst[kMaxWindow];
 };
 
@@ -1784,8 +1795,10 @@ __device__ __forceinline__ void exact_scores(const ExactShared& e, const ExactAr
 // The head's window rows into LDS, then c_i from one pass over its keys per
 // group of rows (every thread of the workgroup calls it).
 __device__ void exact_prepare(ExactShared& e, const ExactArgs& a, int bh) {
+  // any workgroup of whole waves up to kExactMaxWaves of them
+  const int nthreads = static_cast<int>(blockDim.x), nwaves = nthreads / kWave;
   const int b = bh / a.H, h = bh - b * a.H, t0 = a.L - a.w, wave = threadIdx.x / kWave;
-  for (int i = threadIdx.x; i < kMaxWindow * a.D; i += kThreads) {
+  for (int i = threadIdx.x; i < kMaxWindow * a.D; i += nthreads) {
     const int rr = i / a.D, d = i - rr * a.D;
     e.qs[rr][d] = rr < a.w ? bf16_to_f32(a.q[b * a.qsb + h * a.qsh + static_cast<int64_t>(a.qrow0 + rr) * a.qst + d])
                            : 0.f;
@@ -1800,7 +1813,7 @@ __device__ void exact_prepare(ExactShared& e, const ExactArgs& a, int bh) {
       m[i] = kNegBig;
       l[i] = 0.f;
     }
-    for (int j = threadIdx.x; j < a.L; j += kThreads) {
+    for (int j = threadIdx.x; j < a.L; j += nthreads) {
       float s[kExactRows];
       exact_scores(e, a, kb, j, g, s);
 #pragma unroll
@@ -1826,7 +1839,7 @@ __device__ void exact_prepare(ExactShared& e, const ExactArgs& a, int bh) {
   __syncthreads();
   if (threadIdx.x < kMaxWindow) {
     float mm = e.red_m[0][threadIdx.x], ll = e.red_l[0][threadIdx.x];
-    for (int wv = 1; wv < kWaves; ++wv) lse2_merge(mm, ll, e.red_m[wv][threadIdx.x], e.red_l[wv][threadIdx.x]);
+    for (int wv = 1; wv < nwaves; ++wv) lse2_merge(mm, ll, e.red_m[wv][threadIdx.x], e.red_l[wv][threadIdx.x]);
     e.cst[threadIdx.x] = mm + __builtin_amdgcn_logf(ll);
   }
   __syncthreads();
@@ -2007,6 +2020,7 @@ __global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vo
 //     positions.
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+static_assert(kSelWaves <= kExactMaxWaves, "exact votes may be computed by a workgroup of the selection's size");
 static_assert(kHistBins >= kSelThreads, "the compaction keeps one run start per thread in the histogram's LDS");
 constexpr int kSelPer = 4;                            // 16-byte score pieces per thread
 constexpr int kSelChunk = kSelThreads * kSelPer * 4;  // positions per workgroup
@@ -2190,6 +2204,141 @@ __device__ __forceinline__ float sel_pool_at(const float* pb, int j, int N, int 
   return m;
 }
 
+// The head's kk kept positions once all its positions are classified: the
+// bitmap holds the positions above the threshold bin bstar (in LDS s.bm when
+// lds_bm, else bm_g), the bin's n_cand members are candidates (s.cand when
+// in_lds, else cand_g), of which the rem with the largest keys are kept. One
+// workgroup: the rem-th largest candidate key (12-bit radix passes below the
+// bits bstar fixes while more than a wave's worth share the prefix, then a
+// direct rank in one wave), the kept candidates' bits added, and the bitmap
+// compacted into ascending positions.
+__device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, unsigned n_cand, bool in_lds,
+                                 const uint2* __restrict__ cand_g, unsigned* __restrict__ bm_g, bool lds_bm,
+                                 int words, int N, int kk, int* __restrict__ out) {
+  constexpr int kHistPer = kHistBins / kSelThreads;
+  const int tid = threadIdx.x;
+  unsigned long long prefix = static_cast<unsigned long long>(bstar) << kKeyFixed;
+  unsigned long long pmask = ~0ull << kKeyFixed;
+  unsigned long long thr = prefix;  // candidate keys >= thr are kept
+  unsigned members = n_cand;        // candidates whose key matches prefix under pmask
+  __syncthreads();
+  for (int lo = kKeyFixed; members != rem && lo > 0;) {
+    if (members <= static_cast<unsigned>(kWave)) {
+      // direct rank of the few members left, by one wave
+      if (tid == 0) {
+        s.nmem = 0;
+        s.thr = prefix;
+      }
+      __syncthreads();
+      for (unsigned i = tid; i < n_cand; i += kSelThreads) {
+        const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
+        const unsigned long long key = sel_key(c.x, c.y);
+        if ((key & pmask) == prefix) {
+          const unsigned slot = lds_add_rtn(&s.nmem, 1u);
+          if (slot < static_cast<unsigned>(kWave)) s.mem[slot] = key;
+        }
+      }
+      __syncthreads();
+      const unsigned nm = min(s.nmem, static_cast<unsigned>(kWave));
+      if (static_cast<unsigned>(tid) < nm) {
+        const unsigned long long mine = s.mem[tid];
+        unsigned greater = 0;
+        for (unsigned i = 0; i < nm; ++i) greater += s.mem[i] > mine;
+        if (greater + 1u == rem) s.thr = mine;  // keys are distinct: one lane at most
+      }
+      __syncthreads();
+      thr = s.thr;
+      break;
+    }
+    const int nb = lo >= 12 ? 12 : lo;
+    lo -= nb;
+    const unsigned dmask = (1u << nb) - 1u;
+#pragma unroll
+    for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = 0;
+    if (tid == 0) {
+      s.bin = 0;
+      s.above = 0;
+    }
+    __syncthreads();
+    for (unsigned i = tid; i < n_cand; i += kSelThreads) {
+      const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
+      const unsigned long long key = sel_key(c.x, c.y);
+      if ((key & pmask) == prefix) atomicAdd(&s.sh[static_cast<unsigned>(key >> lo) & dmask], 1u);
+    }
+    __syncthreads();
+    sel_find_bin(s.sh, rem, s.wsum, &s.bin, &s.above);
+    const unsigned d = s.bin;
+    rem -= s.above;
+    members = s.sh[d];
+    prefix |= static_cast<unsigned long long>(d) << lo;
+    pmask |= static_cast<unsigned long long>(dmask) << lo;
+    thr = prefix;
+    __syncthreads();  // every thread has read the digit before the next pass clears it
+  }
+  unsigned* bm = lds_bm ? s.bm : bm_g;
+  for (unsigned i = tid; i < n_cand; i += kSelThreads) {
+    const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
+    if (sel_key(c.x, c.y) >= thr && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
+  }
+  __syncthreads();
+
+  // ordered compaction of the bitmap into ascending positions: each thread
+  // counts a run of wpt consecutive words and a block scan gives every run's
+  // first output slot. With the bitmap in LDS, every output slot t then finds
+  // its run by binary search over the runs' first slots, its word by a scan of
+  // at most wpt popcounts and its bit by halving popcounts, so that all lanes
+  // do the same work; else each thread writes its own run's positions.
+  const int wpt = (words + kSelThreads - 1) / kSelThreads;
+  const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
+  unsigned cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(lds_bm ? s.bm[i] : load_word(&bm_g[i]));
+  unsigned total;
+  unsigned run = sel_block_scan(cnt, s.wsum, &total);
+  if (lds_bm) {
+    unsigned* first = s.sh;  // kSelThreads run starts (the histogram is no longer needed)
+    first[tid] = run;
+    __syncthreads();
+    const unsigned n_out = min(total, static_cast<unsigned>(kk));
+    for (unsigned t = tid; t < n_out; t += kSelThreads) {
+      int lo = 0, hi = kSelThreads;  // first[lo] <= t < first[hi], first[kSelThreads] standing for the total
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (first[mid] <= t)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      unsigned r = t - first[lo];
+      int wi = lo * wpt;  // run lo's words (a run with no set bit is never found)
+      unsigned x = s.bm[wi];
+      for (unsigned c = __popc(x); r >= c; c = __popc(x)) {
+        r -= c;
+        x = s.bm[++wi];
+      }
+      int pos = 0;
+#pragma unroll
+      for (int sh = 16; sh; sh >>= 1) {
+        const unsigned c = __popc(x & ((1u << sh) - 1u));
+        if (r >= c) {
+          r -= c;
+          x >>= sh;
+          pos += sh;
+        }
+      }
+      out[t] = wi * 32 + pos;
+    }
+  } else {
+    for (int i = w0; i < w1; ++i) {
+      unsigned x = load_word(&bm_g[i]);
+      while (x) {
+        if (run < static_cast<unsigned>(kk)) out[run] = i * 32 + __ffs(x) - 1;
+        ++run;
+        x &= x - 1;
+      }
+    }
+  }
+}
+
 // src: per head N pooled scores (rad = 0) or raw votes (pooled here with radius rad)
 __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ src, int vec, int rad,
                                                            const unsigned* __restrict__ hist, int N, int kk,
@@ -2278,127 +2427,8 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
     for (unsigned i = tid; i < n_cand; i += kSelThreads) s.cand[i] = ld_agent_u2(&cand_g[i]);
   if (lds_bm)
     for (int i = tid; i < words; i += kSelThreads) s.bm[i] = load_word(&bm_g[i]);
-  unsigned long long prefix = static_cast<unsigned long long>(bstar) << kKeyFixed;
-  unsigned long long pmask = ~0ull << kKeyFixed;
-  unsigned long long thr = prefix;  // candidate keys >= thr are kept
-  unsigned members = n_cand;        // candidates whose key matches prefix under pmask
-  __syncthreads();
-  for (int lo = kKeyFixed; members != rem && lo > 0;) {
-    if (members <= static_cast<unsigned>(kWave)) {
-      // direct rank of the few members left, by one wave
-      if (tid == 0) {
-        s.nmem = 0;
-        s.thr = prefix;
-      }
-      __syncthreads();
-      for (unsigned i = tid; i < n_cand; i += kSelThreads) {
-        const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
-        const unsigned long long key = sel_key(c.x, c.y);
-        if ((key & pmask) == prefix) {
-          const unsigned slot = lds_add_rtn(&s.nmem, 1u);
-          if (slot < static_cast<unsigned>(kWave)) s.mem[slot] = key;
-        }
-      }
-      __syncthreads();
-      const unsigned nm = min(s.nmem, static_cast<unsigned>(kWave));
-      if (static_cast<unsigned>(tid) < nm) {
-        const unsigned long long mine = s.mem[tid];
-        unsigned greater = 0;
-        for (unsigned i = 0; i < nm; ++i) greater += s.mem[i] > mine;
-        if (greater + 1u == rem) s.thr = mine;  // keys are distinct: one lane at most
-      }
-      __syncthreads();
-      thr = s.thr;
-      break;
-    }
-    const int nb = lo >= 12 ? 12 : lo;
-    lo -= nb;
-    const unsigned dmask = (1u << nb) - 1u;
-#pragma unroll
-    for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = 0;
-    if (tid == 0) {
-      s.bin = 0;
-      s.above = 0;
-    }
-    __syncthreads();
-    for (unsigned i = tid; i < n_cand; i += kSelThreads) {
-      const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
-      const unsigned long long key = sel_key(c.x, c.y);
-      if ((key & pmask) == prefix) atomicAdd(&s.sh[static_cast<unsigned>(key >> lo) & dmask], 1u);
-    }
-    __syncthreads();
-    sel_find_bin(s.sh, rem, s.wsum, &s.bin, &s.above);
-    const unsigned d = s.bin;
-    rem -= s.above;
-    members = s.sh[d];
-    prefix |= static_cast<unsigned long long>(d) << lo;
-    pmask |= static_cast<unsigned long long>(dmask) << lo;
-    thr = prefix;
-    __syncthreads();  // every thread has read the digit before the next pass clears it
-  }
-  unsigned* bm = lds_bm ? s.bm : bm_g;
-  for (unsigned i = tid; i < n_cand; i += kSelThreads) {
-    const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
-    if (sel_key(c.x, c.y) >= thr && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
-  }
-  __syncthreads();
-
-  // ordered compaction of the bitmap into ascending positions: each thread
-  // counts a run of wpt consecutive words and a block scan gives every run's
-  // first output slot. With the bitmap in LDS, every output slot t then finds
-  // its run by binary search over the runs' first slots, its word by a scan of
-  // at most wpt popcounts and its bit by halving popcounts, so that all lanes
-  // do the same work; else each thread writes its own run's positions.
-  int* out = idx_out + static_cast<int64_t>(bh) * kk;
-  const int wpt = (words + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
-  unsigned cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(lds_bm ? s.bm[i] : load_word(&bm_g[i]));
-  unsigned total;
-  unsigned run = sel_block_scan(cnt, s.wsum, &total);
-  if (lds_bm) {
-    unsigned* first = s.sh;  // kSelThreads run starts (the histogram is no longer needed)
-    first[tid] = run;
-    __syncthreads();
-    const unsigned n_out = min(total, static_cast<unsigned>(kk));
-    for (unsigned t = tid; t < n_out; t += kSelThreads) {
-      int lo = 0, hi = kSelThreads;  // first[lo] <= t < first[hi], first[kSelThreads] standing for the total
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (first[mid] <= t)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      unsigned r = t - first[lo];
-      int wi = lo * wpt;  // run lo's words (a run with no set bit is never found)
-      unsigned x = s.bm[wi];
-      for (unsigned c = __popc(x); r >= c; c = __popc(x)) {
-        r -= c;
-        x = s.bm[++wi];
-      }
-      int pos = 0;
-#pragma unroll
-      for (int sh = 16; sh; sh >>= 1) {
-        const unsigned c = __popc(x & ((1u << sh) - 1u));
-        if (r >= c) {
-          r -= c;
-          x >>= sh;
-          pos += sh;
-        }
-      }
-      out[t] = wi * 32 + pos;
-    }
-  } else {
-    for (int i = w0; i < w1; ++i) {
-      unsigned x = load_word(&bm_g[i]);
-      while (x) {
-        if (run < static_cast<unsigned>(kk)) out[run] = i * 32 + __ffs(x) - 1;
-        ++run;
-        x &= x - 1;
-      }
-    }
-  }
+  sel_rank_compact(s, bstar, rem, n_cand, in_lds, cand_g, bm_g, lds_bm, words, N, kk,
+                   idx_out + static_cast<int64_t>(bh) * kk);
 }
 
 // -------------------------------------------------------------- gather
@@ -2870,6 +2900,8 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
     // pooling kernel has read them by then). The pooling kernel stores pooled
     // scores only if the caller asked for them or the selection reads them.
     const int r = pool_kernel / 2;
+    // the selection pools the raw votes itself (max-pool of a small radius),
+    // else it reads the pooling kernel's stored scores
     const bool sel_pools = !avg && r <= kSelMaxRad;
     float* vraw = vote ? vote : reinterpret_cast<float*>(ws + (sel_pools ? lay.pooled : lay.cand));
     float* pooled_dst = pooled_out ? pooled_out : sel_pools ? nullptr : pooled;
