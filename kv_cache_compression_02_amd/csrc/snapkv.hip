@@ -1125,6 +1125,7 @@ struct WvPipe {
   float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
   int vhead, vtile;  // the tile whose votes are next (round r - kWvBanks in round r)
   bool gave_up;      // a bounded wait has run out: no further waits (the results are invalid)
+  bool q_lds;        // the next head's queries wait in the ring slot the coming tile is issued into
 };
 
 // The next round's tile: W tiles on (W <= tiles per head, so at most one
@@ -1213,6 +1214,26 @@ __device__ __forceinline__ void wv_load_q(const WvCtx& c, const WvPos& p, bf16x8
   const unsigned off = static_cast<unsigned>(min(lane & 31, c.w - 1)) * static_cast<unsigned>(c.qst * 2) +
                        static_cast<unsigned>((lane >> 5) * D);
   load_half_row<D>(reinterpret_cast<const uint16_t*>(base + off), qf);
+}
+
+// Direct-to-LDS loads of the head's window queries into `slot`, laid out as
+// a K tile (32 rows, XOR-swizzled; rows past the window repeat its last row),
+// so that the MFMA fragments of the queries are read with the same addresses
+// as a tile's. Four rows per instruction: each reads whole rows, where loading
+// the fragments straight into registers takes 16 bytes from each of 64 rows
+// per instruction (the loads of every head change then measured ~15 us of
+// the 131K layer's score kernel).
+template <int D>
+__device__ __forceinline__ void wv_issue_q(const WvCtx& c, const WvPos& p, unsigned char* slot, int lane) {
+  using Ly = WvLayout<D>;
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.qb);
+#pragma unroll
+  for (int i = 0; i < Ly::kInst; ++i) {
+    const int row = i * Ly::kRowsPerInst + lane / Ly::kP;
+    const int piece = (lane % Ly::kP) ^ (row & (Ly::kP - 1));
+    __builtin_amdgcn_global_load_lds(qb + static_cast<int64_t>(min(row, c.w - 1)) * c.qst + piece * 8,
+                                     (lds_void*)(slot + i * 1024), 16, 0, 0);
+  }
 }
 
 // s_waitcnt vmcnt(0), as the builtin (so that the compiler's own wait
@@ -1532,6 +1553,20 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     wv_finish(c, p, lane);
   const WvPos nxt = wv_next(c, pos);
   const bool more = r + 1 < c.rounds;
+  if (p.q_lds) {
+    // this tile's head changed last round: its queries wait in the slot the
+    // next tile goes to; their fragments (addressed as a tile's) into the
+    // registers, read before the slot is refilled
+    const unsigned char* qt = PAR ? ring0 : ring1;
+    const int col = lane & 31, half = lane >> 5;
+    const unsigned A = static_cast<unsigned>(col * Ly::kRowB) +
+                       (static_cast<unsigned>((half * (Ly::kP / 2)) ^ (col & (Ly::kP - 1))) << 4);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qt + (A ^ static_cast<unsigned>(s << 4))));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    p.q_lds = false;
+  }
   if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
   // the tile whose votes come next round: tile r - 8 (tile 0 before round 9)
   int vn_head = p.vhead, vn_t = p.vtile;
@@ -1564,8 +1599,13 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf, acc, 0, 0, 0);
       if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight
     }
-    // Q of the next tile's head into the registers just read (a head's tiles share Q)
-    if (more && nxt.head != pos.head) wv_load_q<D>(c, nxt, qf, lane);
+    // the next tile's head changes: its queries into the slot just read (its
+    // fragments go to the registers at the start of the next round)
+    if (more && nxt.head != pos.head) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile's fragments have been read
+      wv_issue_q<D>(c, nxt, PAR ? ring1 : ring0, lane);
+      p.q_lds = true;
+    }
     float* rs = c.sh->s_r[c.wave];
     if (half == 0) rs[col] = p.rref[PAR];  // R_i of this tile's head, read back per register below
     // e_ij = 2^(s_ij - R_i) for key j = key0 + col and the lane's 16 rows i
@@ -1648,6 +1688,7 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
   p.rref[0] = p.rref[1] = 0.f;
   p.gave_up = false;
+  p.q_lds = false;
   // round 0: tile v (of head 0 unless heads are shorter than a round)
   WvPos pos;
   {
