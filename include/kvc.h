@@ -230,6 +230,20 @@ int kvc_snapkv_force_residency_fallback(int on);
  * previous setting. */
 int kvc_snapkv_force_wait_timeout(int on);
 
+/* Testing (not part of the method): while `on` is non-zero, the calling
+ * thread's kvc_snapkv_compress calls run the top-k selection as several
+ * workgroups per head that classify ranges of the head's positions and leave
+ * the ranking and compaction to the head's last workgroup (the form used for
+ * heads of more than 524288 positions or rows that are not 16-byte aligned),
+ * instead of one workgroup per head. The kept positions are the same either
+ * way. Returns the previous setting. */
+int kvc_snapkv_force_split_select(int on);
+
+/* Name of the selection kernel the last kvc_snapkv_compress call on the
+ * calling thread launched ("snap_select_head" or "snap_select"): a static
+ * string, "" if none. For reports and tests. */
+const char* kvc_snapkv_last_select_kernel(void);
+
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its
  * stream at phase boundary i, for i < n_events (at most 7) and events[i] not

@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "kvc_h2o_step", "kvc_sink_recent", "kvc_snapkv_set_phase_events", "kvc_h2o_prefill",
     "kvc_h2o_prefill_workspace_bytes", "kvc_snapkv_set_schedule", "kvc_snapkv_last_schedule",
     "kvc_snapkv_last_score_kernel", "kvc_snapkv_force_residency_fallback", "kvc_snapkv_force_wait_timeout",
+    "kvc_snapkv_force_split_select", "kvc_snapkv_last_select_kernel",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
     "kvc_decode_attention_noalloc", "kvc_snapkv_workspace_bytes_ex", "kvc_snapkv_compress_ex",
     "kvc_sink_cache_positions",
@@ -119,6 +120,10 @@ def library():
     L.kvc_snapkv_last_schedule.argtypes = []
     L.kvc_snapkv_last_score_kernel.restype = ctypes.c_char_p
     L.kvc_snapkv_last_score_kernel.argtypes = []
+    L.kvc_snapkv_force_split_select.restype = i32
+    L.kvc_snapkv_force_split_select.argtypes = [i32]
+    L.kvc_snapkv_last_select_kernel.restype = ctypes.c_char_p
+    L.kvc_snapkv_last_select_kernel.argtypes = []
     L.kvc_decode_attention_noalloc.restype = i32
     L.kvc_decode_attention_noalloc.argtypes = [vp, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, vp, vp]
     L.kvc_measure_stream_read.restype = i32
@@ -206,6 +211,11 @@ def snapkv_last_schedule():
 def snapkv_last_score_kernel():
     """Kernel name(s) that computed the scores in the last successful snapkv_compress call."""
     return library().kvc_snapkv_last_score_kernel().decode()
+
+
+def snapkv_last_select_kernel():
+    """Selection kernel the last snapkv_compress call launched."""
+    return library().kvc_snapkv_last_select_kernel().decode()
 
 
 def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,

@@ -1925,6 +1925,17 @@ __global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, 
   const int j0 = (static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x)) * kPoolPer;
   float* vb = vote + static_cast<int64_t>(bh) * N;
   float x[kX];
+  // the votes are loaded before the head's flag is known (its load would
+  // otherwise delay theirs); a flagged head's exact votes replace them
+  const bool vec_body = VEC && j0 >= kHalo && j0 + kPoolPer + kHalo <= N;
+  if (vec_body) {
+#pragma unroll
+    for (int p = 0; p < kX / 4; ++p) {
+      const f32x4_t f = *reinterpret_cast<const f32x4_t*>(vb + j0 - kHalo + 4 * p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * p + e] = f[e];
+    }
+  }
   if (exact_flagged(ea, bh)) {
     // exact votes (halo included) for a flagged head; the thread's own
     // positions go back to the vote buffer, where the selection and the
@@ -1936,14 +1947,7 @@ __global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, 
       if (i >= kHalo && i < kHalo + kPoolPer && j < N) vb[j] = x[i];
     }
     __syncthreads();  // the rows are read before the histogram reuses their LDS
-  } else if (VEC && j0 >= kHalo && j0 + kPoolPer + kHalo <= N) {
-#pragma unroll
-    for (int p = 0; p < kX / 4; ++p) {
-      const f32x4_t f = *reinterpret_cast<const f32x4_t*>(vb + j0 - kHalo + 4 * p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * p + e] = f[e];
-    }
-  } else {
+  } else if (!vec_body) {
 #pragma unroll
     for (int i = 0; i < kX; ++i) {
       const int j = j0 - kHalo + i;
@@ -2059,6 +2063,9 @@ __global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vo
 //     share the prefix, then a direct rank within one wave), adds the bits of
 //     the candidates at or above it and compacts the bitmap into ascending
 //     positions.
+// A head of at most one range is selected by one workgroup alone
+// (snap_select_head): the same steps with the bitmap and candidates in LDS
+// throughout, and no exchange through device memory.
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 static_assert(kSelWaves <= kExactMaxWaves, "exact votes may be computed by a workgroup of the selection's size");
@@ -2143,7 +2150,7 @@ struct SelShared {
   unsigned bm[kBitmapLds];
   uint2 cand[kCandLds];
   unsigned sh[kHistBins];
-  unsigned long long mem[kWave];
+  alignas(16) unsigned long long mem[kWave];
   unsigned wsum[kSelWaves];
   unsigned long long thr;
   unsigned bin, above, nloc, base, last, nmem;
@@ -2265,11 +2272,14 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
   __syncthreads();
   for (int lo = kKeyFixed; members != rem && lo > 0;) {
     if (members <= static_cast<unsigned>(kWave)) {
-      // direct rank of the few members left, by one wave
+      // direct rank of the few members left, by one wave: each lane counts
+      // the members above its own, reading 16 keys per step (the unused slots
+      // hold 0, below every key)
       if (tid == 0) {
         s.nmem = 0;
         s.thr = prefix;
       }
+      if (tid < kWave) s.mem[tid] = 0ull;
       __syncthreads();
       for (unsigned i = tid; i < n_cand; i += kSelThreads) {
         const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
@@ -2284,7 +2294,13 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
       if (static_cast<unsigned>(tid) < nm) {
         const unsigned long long mine = s.mem[tid];
         unsigned greater = 0;
-        for (unsigned i = 0; i < nm; ++i) greater += s.mem[i] > mine;
+        for (unsigned i = 0; i < nm; i += 16) {
+          u64x2_t kv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[e] = *reinterpret_cast<const u64x2_t*>(&s.mem[i + 2 * e]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) greater += (kv[e][0] > mine) + (kv[e][1] > mine);
+        }
         if (greater + 1u == rem) s.thr = mine;  // keys are distinct: one lane at most
       }
       __syncthreads();
@@ -2316,10 +2332,14 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
     thr = prefix;
     __syncthreads();  // every thread has read the digit before the next pass clears it
   }
-  unsigned* bm = lds_bm ? s.bm : bm_g;
   for (unsigned i = tid; i < n_cand; i += kSelThreads) {
     const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
-    if (sel_key(c.x, c.y) >= thr && c.y < static_cast<unsigned>(N)) atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
+    if (sel_key(c.x, c.y) >= thr && c.y < static_cast<unsigned>(N)) {
+      if (lds_bm)
+        atomicOr(&s.bm[c.y >> 5], 1u << (c.y & 31));
+      else
+        atomicOr(&bm_g[c.y >> 5], 1u << (c.y & 31));
+    }
   }
   __syncthreads();
 
@@ -2469,6 +2489,100 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
   if (lds_bm)
     for (int i = tid; i < words; i += kSelThreads) s.bm[i] = load_word(&bm_g[i]);
   sel_rank_compact(s, bstar, rem, n_cand, in_lds, cand_g, bm_g, lds_bm, words, N, kk,
+                   idx_out + static_cast<int64_t>(bh) * kk);
+}
+
+// The classification of sel_piece with the bitmap word kept in LDS.
+__device__ __forceinline__ void sel_piece_lds(SelShared& s, unsigned* ctr_head, uint2* cand_g, int N, f32x4_t x,
+                                              int f, bool valid, unsigned bstar) {
+  const int lane = lane_id();
+  unsigned m = 0, nc = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned bin = (__float_as_uint(x[e]) >> kHistShift) & (kHistBins - 1);
+    m |= static_cast<unsigned>(valid && bin > bstar) << e;
+    nc += valid && bin == bstar;
+  }
+  m = octet_or(m << (4 * (lane & 7)));
+  if (valid && (lane & 7) == 0) s.bm[f >> 3] = m;
+  if (nc != 0u) {
+    unsigned slot = lds_add_rtn(&s.nloc, nc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned u = __float_as_uint(x[e]);
+      if (valid && ((u >> kHistShift) & (kHistBins - 1)) == bstar) {
+        sel_add_cand(s, ctr_head, cand_g, N, u, static_cast<unsigned>(4 * f + e), slot);
+        ++slot;
+      }
+    }
+  }
+}
+
+// The whole selection of one head in one workgroup, for heads of at most
+// kSelChunk positions (one workgroup's range; N % 4 == 0, 16-byte aligned
+// rows): the same threshold bin, classification, ranking and compaction as
+// snap_select, with the head's bitmap and candidates in LDS from the start,
+// so that no workgroup waits for another's results through device memory.
+// Longer heads go to snap_select: one workgroup walking them range by range
+// would wait for each range's loads in turn.
+__global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __restrict__ src, int rad,
+                                                                const unsigned* __restrict__ hist, int N, int kk,
+                                                                unsigned* __restrict__ ctr,
+                                                                uint2* __restrict__ cand_ws,
+                                                                int* __restrict__ idx_out) {
+  __shared__ SelShared s;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = lane_id();
+  const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(bh) * N);
+  const int nf = N >> 2;
+  const int words = (N + 31) >> 5;
+  uint2* cand_g = cand_ws + static_cast<int64_t>(bh) * N;
+  unsigned* ctr_head = ctr + bh * kSelCtrWords;
+  const unsigned* hb = hist + static_cast<int64_t>(bh) * kHistBins;
+
+  // the histogram row and the head's pieces in flight together
+  constexpr int kHistPer = kHistBins / kSelThreads;
+  unsigned hv[kHistPer];
+#pragma unroll
+  for (int r = 0; r < kHistPer; ++r) hv[r] = hb[tid + r * kSelThreads];
+  f32x4_t xb[kSelPer], xe[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int f = tid + k * kSelThreads;
+    xb[k] = pv[min(f, nf - 1)];
+    // the piece just beyond the wave, for lanes 0 and 63 (a clamped copy for the others)
+    xe[k] = pv[min(max(lane == 0 ? f - 1 : f + 1, 0), nf - 1)];
+  }
+#pragma unroll
+  for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = hv[r];
+  if (tid == 0) {
+    s.bin = 0;
+    s.above = 0;
+    s.nloc = 0;
+  }
+  __syncthreads();
+  sel_find_bin(s.sh, static_cast<unsigned>(kk), s.wsum, &s.bin, &s.above);
+  const unsigned bstar = s.bin;
+  const unsigned rem = static_cast<unsigned>(kk) - s.above;
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int f = tid + k * kSelThreads;
+    sel_piece_lds(s, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+  }
+  __syncthreads();
+  // candidates past the LDS list went to the head's workspace list as they
+  // were found; then the LDS ones join them there
+  const unsigned nloc = s.nloc;
+  const bool in_lds = nloc <= static_cast<unsigned>(kCandLds);
+  unsigned n_cand = nloc;
+  if (!in_lds) {
+    if (tid == 0) s.base = atomicAdd(&ctr_head[0], static_cast<unsigned>(kCandLds));
+    __syncthreads();
+    for (unsigned i = tid; i < static_cast<unsigned>(kCandLds); i += kSelThreads)
+      if (s.base + i < static_cast<unsigned>(N)) st_agent_u2(&cand_g[s.base + i], s.cand[i]);
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before any thread reads the list
+    n_cand = min(nloc, static_cast<unsigned>(N));
+  }
+  sel_rank_compact(s, bstar, rem, n_cand, in_lds, cand_g, nullptr, true, words, N, kk,
                    idx_out + static_cast<int64_t>(bh) * kk);
 }
 
@@ -2729,6 +2843,8 @@ int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
 thread_local const char* g_last_kernel = "";
 thread_local bool g_force_residency_fail = false;
 thread_local bool g_force_wait_timeout = false;
+thread_local bool g_force_split_select = false;
+thread_local const char* g_last_select = "";
 
 template <int R>
 void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, int avg, const ExactArgs& ea,
@@ -2860,6 +2976,14 @@ extern "C" int kvc_snapkv_force_wait_timeout(int on) {
   return prev;
 }
 
+extern "C" int kvc_snapkv_force_split_select(int on) {
+  const int prev = g_force_split_select ? 1 : 0;
+  g_force_split_select = on != 0;
+  return prev;
+}
+
+extern "C" const char* kvc_snapkv_last_select_kernel(void) { return g_last_select; }
+
 extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
                                              int pool_kernel, kvc_dtype dt) {
   (void)pool_kernel;
@@ -2980,11 +3104,21 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
   if (st != KVC_OK) return st;
 
   const int vec = lay.N % 4 == 0 && aligned16(sel_src);
-  const dim3 gs((lay.N + kSelChunk - 1) / kSelChunk, static_cast<unsigned>(lay.BH));
-  snap_select<<<gs, kSelThreads, 0, stream>>>(sel_src, vec, sel_rad, hist, lay.N, lay.kk,
-                                              reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
-                                              reinterpret_cast<uint2*>(ws + lay.cand),
-                                              reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
+  if (vec && lay.N <= kSelChunk && !g_force_split_select) {
+    // one workgroup per head (a head of at most one workgroup's range): no
+    // exchange between workgroups
+    snap_select_head<<<static_cast<unsigned>(lay.BH), kSelThreads, 0, stream>>>(
+        sel_src, sel_rad, hist, lay.N, lay.kk, reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
+        reinterpret_cast<uint2*>(ws + lay.cand), idx_out);
+    g_last_select = "snap_select_head";
+  } else {
+    const dim3 gs((lay.N + kSelChunk - 1) / kSelChunk, static_cast<unsigned>(lay.BH));
+    snap_select<<<gs, kSelThreads, 0, stream>>>(sel_src, vec, sel_rad, hist, lay.N, lay.kk,
+                                                reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
+                                                reinterpret_cast<uint2*>(ws + lay.cand),
+                                                reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
+    g_last_select = "snap_select";
+  }
   mark_phase(5, stream);
   st = check_launch("snapkv selection");
   if (st != KVC_OK) return st;

@@ -121,6 +121,7 @@ def test_16k_shape_ragged_small(schedule):
 
 def test_16k_full_all_heads(schedule):
     _workload(syn.SNAPKV_WORKLOADS["16k-bf16"], schedule=schedule)
+    assert kvc.snapkv_last_select_kernel() == "snap_select_head"
     if schedule == kvc.SNAPKV_SINGLE_PASS:
         assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
 
@@ -134,6 +135,7 @@ def test_131k_full_all_heads(schedule):
 def test_131k_no_optional_outputs_all_heads(schedule):
     """No vote or pooled output (the benchmark's call): raw votes live in the workspace only."""
     _workload(syn.SNAPKV_WORKLOADS["131k-bf16"], want_vote=False, want_pooled=False, schedule=schedule)
+    assert kvc.snapkv_last_select_kernel() == "snap_select"
 
 
 def test_380k_full_all_heads(schedule):
@@ -263,13 +265,14 @@ def test_single_pass_many_heads_unaligned():
     assert kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
 
 
-@pytest.mark.parametrize("L,C", [(2000, 300), (70000, 2048), (600000, 1024)])
+@pytest.mark.parametrize("L,C", [(2000, 300), (12000, 1024), (70000, 2048), (600000, 1024)])
 def test_zero_queries_exact_ties(L, C, schedule):
     """Q = 0 makes every vote equal: the tie rule alone decides, so the kept set is 0..k-1.
-    Every prefix position then shares the threshold bin: at L = 70000 the candidates overflow
-    the workgroups' LDS lists into the head's device list and the rank takes several radix
-    passes over the position bits before the direct rank; at L = 600000 the bitmap also
-    lives in device memory (N > 524288)."""
+    Every prefix position then shares the threshold bin. At L = 12000 one workgroup selects each
+    head and its 11968 candidates overflow its LDS list into the head's device list; at
+    L = 70000 several workgroups select each head and their lists overflow the same way; both
+    rank with several radix passes over the position bits before the direct rank. At
+    L = 600000 the bitmap also lives in device memory (N > 524288)."""
     B, H, D, w = 1, 2, 128, 32
     print(f"[snapkv] zero queries L{L} C{C} schedule {schedule}", flush=True)
     rng = np.random.default_rng(L)
@@ -283,6 +286,62 @@ def test_zero_queries_exact_ties(L, C, schedule):
     vote = res.vote.cpu().numpy()
     assert np.all(vote == vote[:, :, :1]), "equal votes expected bit for bit"
     _report(f"zero-queries-{L}", _compare(qn, kn, kn, res, w, C, 7, "bf16"), B * H)
+
+
+class _SplitSelect:
+    """Forces the several-workgroups-per-head selection while active."""
+
+    def __enter__(self):
+        self.prev = kvc.library().kvc_snapkv_force_split_select(1)
+
+    def __exit__(self, *exc):
+        kvc.library().kvc_snapkv_force_split_select(self.prev)
+
+
+@pytest.mark.parametrize("L,C", [(2000, 300), (70000, 2048)])
+def test_zero_queries_exact_ties_split_select(L, C):
+    """The tie rule through the split selection (at L = 70000 the candidates overflow each
+    workgroup's LDS list into the head's device list)."""
+    B, H, D, w = 1, 2, 128, 32
+    print(f"[snapkv] zero queries, split selection, L{L} C{C}", flush=True)
+    rng = np.random.default_rng(L + 1)
+    kn = syn.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32))
+    qn = np.zeros((B, H, w, D), np.uint16)
+    q, k = par.to_device(qn, "bf16"), par.to_device(kn, "bf16")
+    with _SplitSelect():
+        res = _run(q, k, k, w, C, 7, "bf16")
+        assert kvc.snapkv_last_select_kernel() == "snap_select"
+    idx = res.idx.cpu().numpy()
+    for h in range(H):
+        assert idx[0, h].tolist() == list(range(C - w))
+
+
+@pytest.mark.parametrize("name,L,pool", [("16k-bf16", None, 7), ("16k-bf16", None, 13), ("131k-bf16", 16416, 7),
+                                          ("16k-bf16", 9000, 5)])
+def test_select_forms_agree(name, L, pool):
+    """One workgroup per head (heads of at most 16384 prefix positions) and several per head keep
+    the same positions, bit for bit, on the same votes (both schedules' votes: the selection reads
+    raw votes and pools them itself for a max-pool of radius <= 4, else the pooling kernel's
+    stored scores)."""
+    wl = syn.SNAPKV_WORKLOADS[name].with_(pool_kernel=pool)
+    if L is not None:
+        wl = wl.with_(L=L, name=f"{name}-L{L}")
+    print(f"[snapkv] selection forms on {name} p{pool}", flush=True)
+    qn, kn, vn = _batch(wl.with_(pool_kernel=syn.SNAPKV_WORKLOADS[name].pool_kernel))
+    q, k, v = (par.to_device(x, wl.dtype) for x in (qn, kn, vn))
+    for schedule in (kvc.SNAPKV_SINGLE_PASS, kvc.SNAPKV_TWO_PASS):
+        a = _run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True, want_pooled=True)
+        assert kvc.snapkv_last_select_kernel() == "snap_select_head"
+        with _SplitSelect():
+            b = _run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True, want_pooled=True)
+            assert kvc.snapkv_last_select_kernel() == "snap_select"
+        assert torch.equal(a.vote, b.vote) and torch.equal(a.pooled, b.pooled)  # deterministic votes
+        assert torch.equal(a.idx, b.idx)
+        assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+        pooled, idx = a.pooled.cpu().numpy(), a.idx.cpu().numpy()
+        for bb in range(wl.B):
+            for h in range(wl.H):
+                par.check_topk_self(pooled[bb, h], idx[bb, h], wl.budget - wl.window)
 
 
 def test_planted_spike_neighbourhood(schedule):
