@@ -1055,7 +1055,7 @@ constexpr unsigned kWvGateSpin = 1u << 14;  // residency-check polls (~1 ms) bef
 constexpr int kWvThreads = kWvWaves * kWave;
 constexpr int kWvBanks = 9;
 constexpr int kWvRowWords = 24;  // accumulator words per row a finisher stages (values in words 0..19)
-constexpr int kWvFinBufs = 4;    // finisher staging buffers, by head mod 4
+constexpr int kWvFinBufs = 2;    // finisher staging buffers, by head mod 2
 constexpr int kWvMaxSpan = kWvBanks - 3;  // a head spans at most this many rounds after its first
 constexpr int kWvMinRounds = 8;            // rounds a layer of heads shorter than a round must fill
 constexpr unsigned kWvSpin = 1u << 18;  // polls before a wait gives up (far beyond any legitimate wait)
@@ -1079,17 +1079,18 @@ struct WvFin {
 
 struct WvShared {
   float lslot[2][kWvWaves][32];  // the waves' row sums of head h, in slot h & 1
-  float s_w[kWvWaves][32];       // each wave's vote weights w_i for its votes
-  float s_r[kWvWaves][32];       // each wave's reference scores R_i for its tile
+  float s_wr[kWvWaves][32];      // each wave's vote weights w_i for its votes, then (later in
+                                 // the same round) the reference scores R_i of its tile
   int fin_owner[kWvFinBufs];     // head staged in a finisher buffer, -1 if free
   int mcnt[2];                   // waves that have stored their sums in a slot
   int mtag[2];                   // the head a slot is open for
+  int qtag[2];                   // workgroup head sequence index whose queries have landed in query slot s
+  int qreads[2];                 // waves that have read the queries in query slot s
 };
 
 struct WvPos {
   int head, h, t;      // tile t of head `head` (h = head % H)
   const char* kt;      // K row 32 t of that head
-  const char* qb;      // the head's first window query row
 };
 
 struct WvCtx {
@@ -1101,7 +1102,7 @@ struct WvCtx {
   int H, L, w, t0, nt, BH, G, g, W, rounds, wave;
   int tgt;     // workgroups that contribute to each head: G, or nt / kWvWaves when a head is shorter than a round
   bool small;  // a head is shorter than a round: every workgroup takes a new head every round
-  int64_t dk_tile, dk_head, dk_batch, dq_head, dq_batch;  // byte steps of WvPos::kt and WvPos::qb
+  int64_t dk_tile, dk_head, dk_batch;  // byte steps of WvPos::kt
   unsigned spin;  // polls before a cross-worker wait gives up (kWvSpin; kWvSpinForced for tests)
   float scale_log2;
   const float* ref;
@@ -1113,7 +1114,21 @@ struct WvCtx {
   WvShared* sh;
   WvFin* fin;  // the finisher buffers: an array of their own, so that LDS accesses to the
                // workgroup's other shared state are known not to alias their direct loads
+  unsigned char* qs;  // the workgroup's two query slots, a tile each
+  int wq, wr;        // heads shorter than a round: W / nt and W % nt
+  unsigned h_rcp;    // min(ceil(2^32 / H), 2^32 - 1), for head / H without a division
 };
+
+// head / H for 0 <= head < 2^31: for H >= 2 the high word of head * h_rcp is
+// the quotient or one more (the product overshoots head / H by less than
+// head / 2^32 < 1/2); for H = 1 it is the quotient or one less; one compare
+// in each direction corrects it.
+__device__ __forceinline__ int wv_batch_of(const WvCtx& c, int head) {
+  int b = static_cast<int>(__umulhi(static_cast<unsigned>(head), c.h_rcp));
+  if (b * c.H > head) --b;
+  if ((b + 1) * c.H <= head) ++b;
+  return b;
+}
 
 // A wave's state carried from round to round.
 struct WvPipe {
@@ -1125,35 +1140,32 @@ struct WvPipe {
   float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
   int vhead, vtile;  // the tile whose votes are next (round r - kWvBanks in round r)
   bool gave_up;      // a bounded wait has run out: no further waits (the results are invalid)
-  bool q_lds;        // the next head's queries wait in the ring slot the coming tile is issued into
+  int qhead;         // head whose query fragments are in the registers, -1: none
+  int qpub;          // workgroup head sequence index of the queries this wave loaded into a
+                     // query slot last round (marked landed at the next round's start), -1: none
 };
 
 // The next round's tile: W tiles on (W <= tiles per head, so at most one
-// head boundary); the K and Q pointers move by precomputed byte steps.
+// head boundary); the K pointer moves by precomputed byte steps.
 __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
-  p.t += c.W;
-  p.kt += c.dk_tile;
-  if (c.small) {  // heads shorter than a round: several head boundaries, pointers recomputed
-    if (p.t >= c.nt) {
-      const int adv = p.t / c.nt;
-      p.t -= adv * c.nt;
-      p.head += adv;
-      const int b = p.head / c.H;
-      p.h = p.head - b * c.H;
-      p.kt = reinterpret_cast<const char*>(c.k + b * c.ksb + p.h * c.ksh + static_cast<int64_t>(p.t) * kTile * c.kst);
-      p.qb = reinterpret_cast<const char*>(c.q + b * c.qsb + p.h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst);
-    }
+  if (c.small) {  // heads shorter than a round: W / nt or one more heads on, pointers recomputed
+    const int carry = p.t + c.wr >= c.nt ? 1 : 0;  // t < nt and W % nt < nt: at most one more
+    p.t += c.wr - carry * c.nt;
+    p.head += c.wq + carry;
+    const int b = wv_batch_of(c, p.head);
+    p.h = p.head - b * c.H;
+    p.kt = reinterpret_cast<const char*>(c.k + b * c.ksb + p.h * c.ksh + static_cast<int64_t>(p.t) * kTile * c.kst);
     return p;
   }
+  p.t += c.W;
+  p.kt += c.dk_tile;
   if (p.t >= c.nt) {
     p.t -= c.nt;
     ++p.head;
     p.kt += c.dk_head;
-    p.qb += c.dq_head;
     if (++p.h == c.H) {
       p.h = 0;
       p.kt += c.dk_batch;
-      p.qb += c.dq_batch;
     }
   }
   return p;
@@ -1161,16 +1173,16 @@ __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
 
 // The tile after t for the vote tracker (head and tile only).
 __device__ __forceinline__ void wv_next_ht(const WvCtx& c, int& head, int& t) {
+  if (c.small) {
+    const int carry = t + c.wr >= c.nt ? 1 : 0;
+    t += c.wr - carry * c.nt;
+    head += c.wq + carry;
+    return;
+  }
   t += c.W;
   if (t >= c.nt) {
-    if (c.small) {
-      const int adv = t / c.nt;
-      t -= adv * c.nt;
-      head += adv;
-    } else {
-      t -= c.nt;
-      ++head;
-    }
+    t -= c.nt;
+    ++head;
   }
 }
 
@@ -1206,27 +1218,22 @@ __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsig
   }
 }
 
-// The lane's Q fragments (window row lane & 31, rows past the window repeat
-// its last row; half lane >> 5 of the contraction) for the tile at p.
-template <int D>
-__device__ __forceinline__ void wv_load_q(const WvCtx& c, const WvPos& p, bf16x8_t (&qf)[D / 16], int lane) {
-  const char* base = p.qb;
-  const unsigned off = static_cast<unsigned>(min(lane & 31, c.w - 1)) * static_cast<unsigned>(c.qst * 2) +
-                       static_cast<unsigned>((lane >> 5) * D);
-  load_half_row<D>(reinterpret_cast<const uint16_t*>(base + off), qf);
+// The first window query row of head `head`.
+__device__ __forceinline__ const uint16_t* wv_q_base(const WvCtx& c, int head) {
+  const int b = wv_batch_of(c, head), h = head - b * c.H;
+  return c.q + b * c.qsb + h * c.qsh + static_cast<int64_t>(c.qrow0) * c.qst;
 }
 
-// Direct-to-LDS loads of the head's window queries into `slot`, laid out as
-// a K tile (32 rows, XOR-swizzled; rows past the window repeat its last row),
-// so that the MFMA fragments of the queries are read with the same addresses
-// as a tile's. Four rows per instruction: each reads whole rows, where loading
-// the fragments straight into registers takes 16 bytes from each of 64 rows
-// per instruction (the loads of every head change then measured ~15 us of
-// the 131K layer's score kernel).
+// Direct-to-LDS loads of a head's window queries (first row qb) into a query
+// slot, laid out as a K tile (32 rows, XOR-swizzled; rows past the window
+// repeat its last row), so that the MFMA fragments of the queries are read
+// with the same addresses as a tile's. Four rows per instruction: each reads
+// whole rows, where loading the fragments straight into registers takes 16
+// bytes from each of 64 rows per instruction (the loads of every head change
+// then measured ~15 us of the 131K layer's score kernel).
 template <int D>
-__device__ __forceinline__ void wv_issue_q(const WvCtx& c, const WvPos& p, unsigned char* slot, int lane) {
+__device__ __forceinline__ void wv_issue_q(const WvCtx& c, const uint16_t* qb, unsigned char* slot, int lane) {
   using Ly = WvLayout<D>;
-  const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.qb);
 #pragma unroll
   for (int i = 0; i < Ly::kInst; ++i) {
     const int row = i * Ly::kRowsPerInst + lane / Ly::kP;
@@ -1252,6 +1259,14 @@ __device__ __forceinline__ void wait_vm_all() {
 __device__ __forceinline__ void lds_add(int* p, int v) {
   const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
   asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
+// The same, returning the value before the add (its LDS wait included).
+__device__ __forceinline__ int lds_add_rtn_i(int* p, int v) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p));
+  int r;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a), "v"(v) : "memory");
+  return r;
 }
 
 // Adds a workgroup's row sum L (of e_ij = 2^(s_ij - R_i)) to row `row` of a
@@ -1452,7 +1467,7 @@ __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, c
       if (lane == 0) __hip_atomic_store(c.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  float* ws = c.sh->s_w[c.wave];
+  float* ws = c.sh->s_wr[c.wave];
   if (half == 0) ws[row] = __uint_as_float(pre.x);
   float v = 0.f;
 #pragma unroll
@@ -1534,6 +1549,65 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, in
   }
 }
 
+// A wave's first tile of a head: the head's query fragments from query slot
+// seq & 1, once the queries have landed there (bounded wait), where seq is the
+// head's index in the workgroup's sequence of heads (every head in order, or
+// one head per round when heads are shorter than a round). Every wave of a
+// workgroup works on the same head in a round (tile counts are padded to
+// whole groups of kWvWaves), so a workgroup loads each head's queries once;
+// the last of its waves to read them loads, into the same slot, the queries
+// of the head two on in the sequence, and marks them landed at the start of
+// its next round.
+template <int D>
+__device__ __forceinline__ void wv_take_q(const WvCtx& c, WvPipe& p, const WvPos& pos, const WvPos& nxt, int r,
+                                          bf16x8_t (&qf)[D / 16], int lane) {
+  using Ly = WvLayout<D>;
+  constexpr int KS = D / 16;
+  const int seq = c.small ? r : pos.head;
+  const int sl = seq & 1;
+  WvShared* sh = c.sh;
+  // plain LDS reads behind compiler barriers (see wv_head_end)
+  asm volatile("" ::: "memory");
+  if (__builtin_expect(!p.gave_up && sh->qtag[sl] != seq, 0)) {
+    unsigned polls = 0;
+    bool late;
+    do {
+      __builtin_amdgcn_s_sleep(1);
+      wait_vm_all();
+      wv_service(c, p, lane);
+      asm volatile("" ::: "memory");
+      late = sh->qtag[sl] != seq;
+    } while (late && ++polls < c.spin);
+    if (late) {
+      p.gave_up = true;
+      if (lane == 0) __hip_atomic_store(c.status, 5u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const unsigned char* qt = c.qs + sl * Ly::kTileB;
+  const int col = lane & 31, half = lane >> 5;
+  const unsigned A = static_cast<unsigned>(col * Ly::kRowB) +
+                     (static_cast<unsigned>((half * (Ly::kP / 2)) ^ (col & (Ly::kP - 1))) << 4);
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qt + (A ^ static_cast<unsigned>(s << 4))));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the slot can be refilled
+  p.qhead = pos.head;
+  int before = 0;
+  if (lane == 0) before = lds_add_rtn_i(&sh->qreads[sl], 1);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before == kWvWaves - 1) {
+    // every wave has read them: the slot takes the queries of sequence index seq + 2
+    if (lane == 0) sh->qreads[sl] = 0;
+    const int nseq = seq + 2;
+    if (c.small ? r + 2 < c.rounds : nseq < c.BH) {
+      // heads shorter than a round: the head of round r + 2, one round past nxt
+      const int nhead = c.small ? nxt.head + c.wq + (nxt.t + c.wr >= c.nt ? 1 : 0) : nseq;
+      wv_issue_q<D>(c, wv_q_base(c, nhead), c.qs + sl * Ly::kTileB, lane);
+      p.qpub = nseq;
+    }
+  }
+}
+
 template <int D, int BANK, int PAR>
 __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, f32x16_t (&sc)[kWvBanks],
                                          f32x16_t& ls, bf16x8_t (&qf)[D / 16], unsigned char* ring0,
@@ -1553,28 +1627,21 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     wv_finish(c, p, lane);
   const WvPos nxt = wv_next(c, pos);
   const bool more = r + 1 < c.rounds;
-  if (p.q_lds) {
-    // this tile's head changed last round: its queries wait in the slot the
-    // next tile goes to; their fragments (addressed as a tile's) into the
-    // registers, read before the slot is refilled
-    const unsigned char* qt = PAR ? ring0 : ring1;
-    const int col = lane & 31, half = lane >> 5;
-    const unsigned A = static_cast<unsigned>(col * Ly::kRowB) +
-                       (static_cast<unsigned>((half * (Ly::kP / 2)) ^ (col & (Ly::kP - 1))) << 4);
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qt + (A ^ static_cast<unsigned>(s << 4))));
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    p.q_lds = false;
+  if (p.qpub >= 0) {
+    // the queries this wave loaded into a query slot last round have landed
+    // (the wait above): mark them for the workgroup
+    if (lane == 0) c.sh->qtag[p.qpub & 1] = p.qpub;
+    p.qpub = -1;
   }
   if (more) wv_issue_k<D>(c, nxt, PAR ? ring0 : ring1, lane);
+  if (do_a && pos.head != p.qhead) wv_take_q<D>(c, p, pos, nxt, r, qf, lane);
   // the tile whose votes come next round: tile r - 8 (tile 0 before round 9)
   int vn_head = p.vhead, vn_t = p.vtile;
   if (r >= kWvBanks) wv_next_ht(c, vn_head, vn_t);
   // the votes of the tile of round r - 9 first, from the bank this round's
   // MFMAs then write; then the next round's prefetches (the weights read a
-  // whole round before their votes); then this tile's MFMAs, the next head's
-  // Q loads, the e_ij and the row sums
+  // whole round before their votes); then this tile's MFMAs, the e_ij and the
+  // row sums
   if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
   if (r >= kWvBanks) {
     p.vhead = vn_head;
@@ -1599,14 +1666,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf, acc, 0, 0, 0);
       if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight
     }
-    // the next tile's head changes: its queries into the slot just read (its
-    // fragments go to the registers at the start of the next round)
-    if (more && nxt.head != pos.head) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this tile's fragments have been read
-      wv_issue_q<D>(c, nxt, PAR ? ring1 : ring0, lane);
-      p.q_lds = true;
-    }
-    float* rs = c.sh->s_r[c.wave];
+    float* rs = c.sh->s_wr[c.wave];  // the votes above have read their weights
     if (half == 0) rs[col] = p.rref[PAR];  // R_i of this tile's head, read back per register below
     // e_ij = 2^(s_ij - R_i) for key j = key0 + col and the lane's 16 rows i
     const int key0 = pos.t * kTile;
@@ -1651,6 +1711,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   // slot are then known not to alias the direct loads in flight into the other
   __shared__ __attribute__((aligned(1024))) unsigned char ring_even[kWvWaves * Ly::kTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char ring_odd[kWvWaves * Ly::kTileB];
+  // the workgroup's two query slots (slot s at s * kTileB), an array of their own
+  __shared__ __attribute__((aligned(1024))) unsigned char qslot[2 * Ly::kTileB];
   __shared__ __attribute__((aligned(16))) WvShared sh;
   __shared__ __attribute__((aligned(16))) WvFin fin[kWvFinBufs];
 
@@ -1661,24 +1723,30 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.fin = fin;
   c.G = static_cast<int>(gridDim.x); c.g = static_cast<int>(blockIdx.x); c.W = c.G * kWvWaves;
   c.small = SHORT;
+  c.wq = SHORT ? c.W / nt : 0;
+  c.wr = SHORT ? c.W - c.wq * nt : 0;
+  c.h_rcp = static_cast<unsigned>(
+      min((0x100000000ull + static_cast<unsigned long long>(H) - 1) / static_cast<unsigned long long>(H),
+          0xFFFFFFFFull));
   c.tgt = SHORT ? nt / kWvWaves : c.G;
   c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
   c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   c.dk_tile = static_cast<int64_t>(c.W) * kTile * kst * 2;
   c.dk_head = ksh * 2 - static_cast<int64_t>(nt) * kTile * kst * 2;
   c.dk_batch = (ksb - H * ksh) * 2;
-  c.dq_head = qsh * 2;
-  c.dq_batch = (qsb - H * qsh) * 2;
   c.spin = wait_spin;
   c.scale_log2 = scale_log2;
   c.ref = ref; c.acc = acc; c.cnt = cnt; c.stat = stat; c.status = status; c.vote = vote;
   c.sh = &sh;
+  c.qs = qslot;
   unsigned char* ring0 = ring_even + c.wave * Ly::kTileB;
   unsigned char* ring1 = ring_odd + c.wave * Ly::kTileB;
   if (threadIdx.x == 0) {
     sh.mcnt[0] = sh.mcnt[1] = 0;
     sh.mtag[0] = 0;  // a workgroup's heads in order (all heads, or one per round for short heads)
     sh.mtag[1] = 1;
+    sh.qtag[0] = sh.qtag[1] = -1;
+    sh.qreads[0] = sh.qreads[1] = 0;
   }
   if (threadIdx.x < kWvFinBufs) sh.fin_owner[threadIdx.x] = -1;
   WvPipe p;
@@ -1688,7 +1756,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   p.pre[0] = p.pre[1] = make_uint2(0u, 0u);
   p.rref[0] = p.rref[1] = 0.f;
   p.gave_up = false;
-  p.q_lds = false;
+  p.qhead = -1;
+  p.qpub = -1;
   // round 0: tile v (of head 0 unless heads are shorter than a round)
   WvPos pos;
   {
@@ -1698,7 +1767,6 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     const int b = pos.head / H;
     pos.h = pos.head - b * H;
     pos.kt = reinterpret_cast<const char*>(k + b * ksb + pos.h * ksh + static_cast<int64_t>(pos.t) * kTile * kst);
-    pos.qb = reinterpret_cast<const char*>(q + b * qsb + pos.h * qsh + static_cast<int64_t>(qrow0) * qst);
   }
   p.vhead = pos.head;
   p.vtile = pos.t;
@@ -1706,7 +1774,13 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   if (c.rounds > 0) {
     const int lane = lane_id();
     wv_issue_k<D>(c, pos, ring0, lane);
-    wv_load_q<D>(c, pos, qf, lane);
+    // the queries of the workgroup's first two heads (sequence indices 0 and
+    // 1) into the query slots, by waves 0 and 1
+    if (c.wave < 2 && (SHORT ? c.wave < c.rounds : c.wave < BH)) {
+      const int head = SHORT ? (c.g * kWvWaves + c.wave * c.W) / nt : c.wave;
+      wv_issue_q<D>(c, wv_q_base(c, head), qslot + c.wave * Ly::kTileB, lane);
+      p.qpub = c.wave;
+    }
     p.rref[0] = ref[pos.head * 32 + (lane & 31)];
   }
   // Residency check, in place of a launch that guarantees it (its wait
