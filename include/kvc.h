@@ -221,7 +221,8 @@ int kvc_snapkv_force_residency_fallback(int on);
 /* Testing (not part of the method): while `on` is non-zero, the calling
  * thread's single-pass calls run the independent-wave score kernel with a
  * limit of zero polls on its cross-worker waits (vote weights, merge slots,
- * a head's publication, the work owed after the last round): every wait that
+ * a head's queries, a head's publication, the work owed after the last
+ * round): every wait that
  * would have to wait gives up at once and records a failure code in the
  * status word, exactly as a wait whose normal limit (2^18 polls) runs out.
  * The kernel still exits normally. The pooling kernel reads the status word

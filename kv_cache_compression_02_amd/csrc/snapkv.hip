@@ -38,7 +38,9 @@
 //                    bitmap, the bin's members are ranked by (score desc,
 //                    position asc); the head's last workgroup compacts the
 //                    bitmap into ascending positions (pooling the raw votes
-//                    itself for radii up to 4 under the single pass)
+//                    itself for radii up to 4 under the single pass);
+//                    snap_select_head does the same in one workgroup per
+//                    head for heads of at most 16384 prefix positions
 //   snap_gather      copy the kept K/V rows and the window rows to the outputs
 //
 // Scores live in the base-2 domain: s2 = (q.k) * log2(e)/sqrt(D), so the
@@ -1023,9 +1025,12 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
 // workers; tiles numbered head by head, a head's tile count padded to a
 // multiple of kWvWaves, so that the tiles of one workgroup in one round share
 // a head). A wave keeps its next tile in flight while it works on the
-// current one: K by direct-to-LDS loads into a private two-slot ring, Q (when
-// the head changes) by plain loads into the registers the MFMAs have just
-// read. One MFMA orientation serves both uses: lane = key, registers = rows.
+// current one: K by direct-to-LDS loads into a private two-slot ring. The
+// workgroup's waves share two query slots in LDS: a head's window queries
+// are loaded once per workgroup, two heads ahead, by the last wave to read
+// the slot's previous head (wv_take_q), and each wave reads them into its
+// registers at its first tile of the head. One MFMA orientation serves both
+// uses: lane = key, registers = rows.
 // Round r's e_ij wait in register bank r % kWvBanks and each lane adds them
 // into per-row partial sums; just before round r's values replace them, the
 // bank's previous contents (the tile of round r - kWvBanks) become votes.
@@ -1045,7 +1050,7 @@ __global__ __launch_bounds__(kCoopThreads, 2) void snap_coop_bf16(
 // head is flagged and the pooling kernel recomputes its votes exactly (the
 // usual path's votes of that head are discarded).
 //
-// Registers: the eight banks (128), Q (32), the MFMA accumulator and the row
+// Registers: the nine banks (144), Q (32), the MFMA accumulator and the row
 // sums fill most of the 256 a wave has at two waves per SIMD, so every
 // per-lane value a round needs is derived inside the round from one opaque
 // lane index instead of being kept live across the loop (a spilled value's
