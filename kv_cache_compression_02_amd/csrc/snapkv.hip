@@ -1094,8 +1094,10 @@ struct WvShared {
 };
 
 struct WvPos {
-  int head, h, t;      // tile t of head `head` (h = head % H)
-  const char* kt;      // K row 32 t of that head
+  int head, h, t;      // processing index t of head `head` (h = head % H)
+  int a;               // the head's tile it scores (wv_rot)
+  const char* kh;      // K row 0 of that head
+  const char* kt;      // K row 32 a of that head
 };
 
 struct WvCtx {
@@ -1107,7 +1109,7 @@ struct WvCtx {
   int H, L, w, t0, nt, BH, G, g, W, rounds, wave;
   int tgt;     // workgroups that contribute to each head: G, or nt / kWvWaves when a head is shorter than a round
   bool small;  // a head is shorter than a round: every workgroup takes a new head every round
-  int64_t dk_tile, dk_head, dk_batch;  // byte steps of WvPos::kt
+  int64_t tile_b, dk_head, dk_batch;  // bytes per K tile; steps of WvPos::kh to the next head, batch
   unsigned spin;  // polls before a cross-worker wait gives up (kWvSpin; kWvSpinForced for tests)
   float scale_log2;
   const float* ref;
@@ -1143,15 +1145,25 @@ struct WvPipe {
   int merge_idx;     // that head's index in the workgroup's sequence of heads (its slot is merge_idx & 1)
   uint2 pre[2];      // vote weights prefetched for the votes of the rounds of each parity
   float rref[2];     // reference score of row lane & 31 for the tiles of each round parity
-  int vhead, vtile;  // the tile whose votes are next (round r - kWvBanks in round r)
+  int vhead, vtile;  // head and processing index of the tile whose votes are next (round r - kWvBanks)
   bool gave_up;      // a bounded wait has run out: no further waits (the results are invalid)
   int qhead;         // head whose query fragments are in the registers, -1: none
   int qpub;          // workgroup head sequence index of the queries this wave loaded into a
                      // query slot last round (marked landed at the next round's start), -1: none
 };
 
+// The tile of head `head` that processing index t scores: t rotated by
+// head % kWvWaves within the head's nt tiles. Without it the head's last
+// tiles (the window's own keys, whose scores are masked) would fall to the
+// same wave in every head, which then trails the others by that extra work
+// more with each head; rotated, they go to a different wave each time.
+__device__ __forceinline__ int wv_rot(const WvCtx& c, int head, int t) {
+  const int a = t + (head & (kWvWaves - 1));
+  return a >= c.nt ? a - c.nt : a;
+}
+
 // The next round's tile: W tiles on (W <= tiles per head, so at most one
-// head boundary); the K pointer moves by precomputed byte steps.
+// head boundary); the head's K base moves by precomputed byte steps.
 __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
   if (c.small) {  // heads shorter than a round: W / nt or one more heads on, pointers recomputed
     const int carry = p.t + c.wr >= c.nt ? 1 : 0;  // t < nt and W % nt < nt: at most one more
@@ -1159,20 +1171,21 @@ __device__ __forceinline__ WvPos wv_next(const WvCtx& c, WvPos p) {
     p.head += c.wq + carry;
     const int b = wv_batch_of(c, p.head);
     p.h = p.head - b * c.H;
-    p.kt = reinterpret_cast<const char*>(c.k + b * c.ksb + p.h * c.ksh + static_cast<int64_t>(p.t) * kTile * c.kst);
-    return p;
-  }
-  p.t += c.W;
-  p.kt += c.dk_tile;
-  if (p.t >= c.nt) {
-    p.t -= c.nt;
-    ++p.head;
-    p.kt += c.dk_head;
-    if (++p.h == c.H) {
-      p.h = 0;
-      p.kt += c.dk_batch;
+    p.kh = reinterpret_cast<const char*>(c.k + b * c.ksb + p.h * c.ksh);
+  } else {
+    p.t += c.W;
+    if (p.t >= c.nt) {
+      p.t -= c.nt;
+      ++p.head;
+      p.kh += c.dk_head;
+      if (++p.h == c.H) {
+        p.h = 0;
+        p.kh += c.dk_batch;
+      }
     }
   }
+  p.a = wv_rot(c, p.head, p.t);
+  p.kt = p.kh + static_cast<int64_t>(p.a) * c.tile_b;
   return p;
 }
 
@@ -1196,7 +1209,7 @@ __device__ __forceinline__ void wv_next_ht(const WvCtx& c, int& head, int& t) {
 template <int D>
 __device__ __forceinline__ void wv_issue_k(const WvCtx& c, const WvPos& p, unsigned char* slot, int lane) {
   using Ly = WvLayout<D>;
-  const int key0 = p.t * kTile;
+  const int key0 = p.a * kTile;
   if (__builtin_expect(key0 + kTile <= c.L, 1)) {
     // instruction i covers rows i*kRowsPerInst + lane/kP: a uniform row base plus
     // the per-lane 32-bit offset (lane/kP) * row_bytes + 16 * piece
@@ -1647,7 +1660,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
   // MFMAs then write; then the next round's prefetches (the weights read a
   // whole round before their votes); then this tile's MFMAs, the e_ij and the
   // row sums
-  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, p.vtile, lane);
+  if (do_b) wv_votes(c, p, p.pre[PAR], sc[BANK], p.vhead, wv_rot(c, p.vhead, p.vtile), lane);
   if (r >= kWvBanks) {
     p.vhead = vn_head;
     p.vtile = vn_t;
@@ -1674,7 +1687,7 @@ __device__ __forceinline__ void wv_round(const WvCtx& c, WvPipe& p, WvPos& pos, 
     float* rs = c.sh->s_wr[c.wave];  // the votes above have read their weights
     if (half == 0) rs[col] = p.rref[PAR];  // R_i of this tile's head, read back per register below
     // e_ij = 2^(s_ij - R_i) for key j = key0 + col and the lane's 16 rows i
-    const int key0 = pos.t * kTile;
+    const int key0 = pos.a * kTile;
     const bool full = key0 + kTile <= c.t0;  // every row sees every key of the tile
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -1736,8 +1749,8 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
   c.tgt = SHORT ? nt / kWvWaves : c.G;
   c.rounds = (total_tiles - c.g * kWvWaves + c.W - 1) / c.W;  // the same for the workgroup's waves
   c.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  c.dk_tile = static_cast<int64_t>(c.W) * kTile * kst * 2;
-  c.dk_head = ksh * 2 - static_cast<int64_t>(nt) * kTile * kst * 2;
+  c.tile_b = static_cast<int64_t>(kTile) * kst * 2;
+  c.dk_head = ksh * 2;
   c.dk_batch = (ksb - H * ksh) * 2;
   c.spin = wait_spin;
   c.scale_log2 = scale_log2;
@@ -1771,7 +1784,9 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     pos.t = v - pos.head * nt;
     const int b = pos.head / H;
     pos.h = pos.head - b * H;
-    pos.kt = reinterpret_cast<const char*>(k + b * ksb + pos.h * ksh + static_cast<int64_t>(pos.t) * kTile * kst);
+    pos.kh = reinterpret_cast<const char*>(k + b * ksb + pos.h * ksh);
+    pos.a = wv_rot(c, pos.head, pos.t);
+    pos.kt = pos.kh + static_cast<int64_t>(pos.a) * c.tile_b;
   }
   p.vhead = pos.head;
   p.vtile = pos.t;
