@@ -172,7 +172,7 @@ __device__ void pool_and_count(const float* sv, int e0, int e1, int c0, int c1, 
 }
 
 __device__ void flush_hist(const unsigned* sh, unsigned* hist_row) {
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+  for (int i = threadIdx.x; i < kHistBins; i += static_cast<int>(blockDim.x))
     if (sh[i]) atomicAdd(&hist_row[i], sh[i]);
 }
 
@@ -2004,19 +2004,21 @@ __device__ float exact_vote(const ExactShared& e, const ExactArgs& a, int bh, in
 // bins is one LDS add.
 constexpr int kPoolPer = 16;
 constexpr int kPoolChunk = kThreads * kPoolPer;
+constexpr int kPoolBigThreads = 1024;  // the large-layer form: 4x the positions per histogram
+constexpr int kPoolBigChunk = kPoolBigThreads * kPoolPer;
 constexpr int kPoolRegRadius = 7;  // larger radii pool from LDS (snap_pool_lds)
 
-template <int R, bool VEC>
-__global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, float* __restrict__ pooled,
-                                                      unsigned* __restrict__ hist, int N, int avg,
-                                                      const ExactArgs ea) {
+template <int R, bool VEC, int THREADS>
+__global__ __launch_bounds__(THREADS) void snap_pool(float* __restrict__ vote, float* __restrict__ pooled,
+                                                     unsigned* __restrict__ hist, int N, int avg,
+                                                     const ExactArgs ea) {
   // pooled may be NULL: then only the histogram is produced
   constexpr int kHalo = (R + 3) / 4 * 4;
   constexpr int kX = kPoolPer + 2 * kHalo;
   __shared__ PoolShared ps;
   unsigned* sh = ps.sh;
   const int bh = blockIdx.y;
-  const int j0 = (static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x)) * kPoolPer;
+  const int j0 = (static_cast<int>(blockIdx.x) * THREADS + static_cast<int>(threadIdx.x)) * kPoolPer;
   float* vb = vote + static_cast<int64_t>(bh) * N;
   float x[kX];
   // the votes are loaded before the head's flag is known (its load would
@@ -2048,7 +2050,7 @@ __global__ __launch_bounds__(kThreads) void snap_pool(float* __restrict__ vote, 
       x[i] = j >= 0 && j < N ? vb[j] : -__builtin_huge_valf();
     }
   }
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sh[i] = 0;
+  for (int i = threadIdx.x; i < kHistBins; i += THREADS) sh[i] = 0;
   float o[kPoolPer];
   if (avg) {
     // the mean of the in-range neighbours j-R .. j+R (summed in position order)
@@ -2943,11 +2945,21 @@ thread_local const char* g_last_select = "";
 template <int R>
 void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, int avg, const ExactArgs& ea,
                    hipStream_t stream) {
+  const bool vec = N % 4 == 0 && aligned16(vote) && (!pooled || aligned16(pooled));
+  // a layer that fills the GPU with workgroups of 16384 positions takes those:
+  // the histogram's clear and its flush into the head's row (device atomics)
+  // are then paid once per 16384 positions instead of once per 4096
+  const int64_t big_groups = static_cast<int64_t>(BH) * ((N + kPoolBigChunk - 1) / kPoolBigChunk);
+  if (vec && big_groups >= coop_caps().cus) {
+    const dim3 g((N + kPoolBigChunk - 1) / kPoolBigChunk, static_cast<unsigned>(BH));
+    snap_pool<R, true, kPoolBigThreads><<<g, kPoolBigThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
+    return;
+  }
   const dim3 g((N + kPoolChunk - 1) / kPoolChunk, static_cast<unsigned>(BH));
-  if (N % 4 == 0 && aligned16(vote) && (!pooled || aligned16(pooled)))
-    snap_pool<R, true><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
+  if (vec)
+    snap_pool<R, true, kThreads><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
   else
-    snap_pool<R, false><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
+    snap_pool<R, false, kThreads><<<g, kThreads, 0, stream>>>(vote, pooled, hist, N, avg, ea);
 }
 
 // Max-pool of the raw votes with the histogram of the results (pooled scores
