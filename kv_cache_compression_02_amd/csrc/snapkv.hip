@@ -1497,7 +1497,9 @@ __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, c
   v += lane_xor<32>(v);
   const int j = tv * kTile + row;
   float* vrow = c.vote + static_cast<int64_t>(hv) * c.t0 + tv * kTile;  // uniform
-  if (half == 0 && j < c.t0) *reinterpret_cast<float*>(reinterpret_cast<char*>(vrow) + static_cast<unsigned>(row) * 4u) = v;
+  // nontemporal: the K stream reads faster beside streaming stores than beside plain ones
+  if (half == 0 && j < c.t0)
+    __builtin_nontemporal_store(v, reinterpret_cast<float*>(reinterpret_cast<char*>(vrow) + static_cast<unsigned>(row) * 4u));
 }
 
 // This wave has scored its last tile of head h: its per-lane row sums are
@@ -2301,6 +2303,24 @@ __device__ __forceinline__ void sel_piece(SelShared& s, unsigned* bm_g, unsigned
   }
 }
 
+// Whether a wave's 64 consecutive pieces can hold anything in bin b* or above:
+// the largest raw vote (or pooled score) among its pieces and the pieces either
+// side of each (`edge` holds a neighbouring piece for every lane) bounds every
+// pooled score of the wave's positions, since pooling reaches at most
+// kSelMaxRad <= 4 positions, one piece, away. A wave below b* has no bitmap bit
+// and no candidate, so its classification reduces to storing zero words.
+__device__ __forceinline__ bool sel_wave_reaches(f32x4_t cur, f32x4_t edge, unsigned bstar) {
+  float m = fmaxf(fmaxf(fmaxf(cur[0], cur[1]), fmaxf(cur[2], cur[3])),
+                  fmaxf(fmaxf(edge[0], edge[1]), fmaxf(edge[2], edge[3])));
+  m = fmaxf(m, lane_xor<1>(m));
+  m = fmaxf(m, lane_xor<2>(m));
+  m = fmaxf(m, lane_xor<4>(m));
+  m = fmaxf(m, lane_xor<8>(m));
+  m = fmaxf(m, lane_xor<16>(m));
+  m = fmaxf(m, lane_xor<32>(m));
+  return ((__float_as_uint(m) >> kHistShift) & (kHistBins - 1)) >= bstar;
+}
+
 // The max-pool (radius rad <= kSelMaxRad, neighbours past the prefix ignored)
 // of piece f of a row of raw votes, from the lane's piece `cur`, its wave
 // neighbours' pieces (DPP wave shifts) and, for the wave's first and last lane,
@@ -2497,7 +2517,7 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
 }
 
 // src: per head N pooled scores (rad = 0) or raw votes (pooled here with radius rad)
-__global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ src, int vec, int rad,
+__global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ src, int vec, int rad, int skip,
                                                            const unsigned* __restrict__ hist, int N, int kk,
                                                            unsigned* __restrict__ ctr, uint2* __restrict__ cand_ws,
                                                            unsigned* __restrict__ bitmap_ws,
@@ -2546,7 +2566,10 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
 #pragma unroll
     for (int k = 0; k < kSelPer; ++k) {
       const int f = fb + tid + k * kSelThreads;
-      sel_piece(s, bm_g, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+      if (!skip || sel_wave_reaches(xb[k], xe[k], bstar))
+        sel_piece(s, bm_g, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+      else if (f < nf && (lane_id() & 7) == 0)
+        store_word(&bm_g[f >> 3], 0u);
     }
   } else {
     for (int w = (c0 >> 5) + tid; w < ((c1 + 31) >> 5); w += kSelThreads) {
@@ -2621,7 +2644,7 @@ __device__ __forceinline__ void sel_piece_lds(SelShared& s, unsigned* ctr_head, 
 // so that no workgroup waits for another's results through device memory.
 // Longer heads go to snap_select: one workgroup walking them range by range
 // would wait for each range's loads in turn.
-__global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __restrict__ src, int rad,
+__global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __restrict__ src, int rad, int skip,
                                                                 const unsigned* __restrict__ hist, int N, int kk,
                                                                 unsigned* __restrict__ ctr,
                                                                 uint2* __restrict__ cand_ws,
@@ -2662,7 +2685,10 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __r
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
     const int f = tid + k * kSelThreads;
-    sel_piece_lds(s, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+    if (!skip || sel_wave_reaches(xb[k], xe[k], bstar))
+      sel_piece_lds(s, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+    else if (f < nf && (lane & 7) == 0)
+      s.bm[f >> 3] = 0u;
   }
   __syncthreads();
   // candidates past the LDS list went to the head's workspace list as they
@@ -3210,16 +3236,20 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
   if (st != KVC_OK) return st;
 
   const int vec = lay.N % 4 == 0 && aligned16(sel_src);
+  // a wave checks whether its range can reach the threshold bin before it
+  // classifies only where few positions are kept (the check costs more than
+  // it saves where most waves hold a kept position)
+  const int skip = static_cast<int64_t>(lay.kk) * 128 < lay.N ? 1 : 0;
   if (vec && lay.N <= kSelChunk && !g_force_split_select) {
     // one workgroup per head (a head of at most one workgroup's range): no
     // exchange between workgroups
     snap_select_head<<<static_cast<unsigned>(lay.BH), kSelThreads, 0, stream>>>(
-        sel_src, sel_rad, hist, lay.N, lay.kk, reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
+        sel_src, sel_rad, skip, hist, lay.N, lay.kk, reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
         reinterpret_cast<uint2*>(ws + lay.cand), idx_out);
     g_last_select = "snap_select_head";
   } else {
     const dim3 gs((lay.N + kSelChunk - 1) / kSelChunk, static_cast<unsigned>(lay.BH));
-    snap_select<<<gs, kSelThreads, 0, stream>>>(sel_src, vec, sel_rad, hist, lay.N, lay.kk,
+    snap_select<<<gs, kSelThreads, 0, stream>>>(sel_src, vec, sel_rad, skip, hist, lay.N, lay.kk,
                                                 reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
                                                 reinterpret_cast<uint2*>(ws + lay.cand),
                                                 reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
