@@ -2156,11 +2156,11 @@ __global__ __launch_bounds__(kThreads) void snap_pool_lds(float* __restrict__ vo
 //     stored at device scope and complete before the workgroup counts itself
 //     finished;
 //  3. the head's last workgroup to finish loads the bitmap and the
-//     candidates, finds the rem-th largest candidate key (12-bit radix passes
+//     candidates, finds the rem-th largest candidate key (8-bit radix passes
 //     below the bits b* fixes while more than a wave's worth of candidates
-//     share the prefix, then a direct rank within one wave), adds the bits of
-//     the candidates at or above it and compacts the bitmap into ascending
-//     positions.
+//     share the prefix, each digit found by one wave, then a direct rank
+//     within one wave), adds the bits of the candidates at or above it and
+//     compacts the bitmap into ascending positions.
 // A head of at most one range is selected by one workgroup alone
 // (snap_select_head): the same steps with the bitmap and candidates in LDS
 // throughout, and no exchange through device memory.
@@ -2372,19 +2372,19 @@ __device__ __forceinline__ float sel_pool_at(const float* pb, int j, int N, int 
 // bitmap holds the positions above the threshold bin bstar (in LDS s.bm when
 // lds_bm, else bm_g), the bin's n_cand members are candidates (s.cand when
 // in_lds, else cand_g), of which the rem with the largest keys are kept. One
-// workgroup: the rem-th largest candidate key (12-bit radix passes below the
+// workgroup: the rem-th largest candidate key (8-bit radix passes below the
 // bits bstar fixes while more than a wave's worth share the prefix, then a
 // direct rank in one wave), the kept candidates' bits added, and the bitmap
 // compacted into ascending positions.
 __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, unsigned n_cand, bool in_lds,
                                  const uint2* __restrict__ cand_g, unsigned* __restrict__ bm_g, bool lds_bm,
                                  int words, int N, int kk, int* __restrict__ out) {
-  constexpr int kHistPer = kHistBins / kSelThreads;
   const int tid = threadIdx.x;
   unsigned long long prefix = static_cast<unsigned long long>(bstar) << kKeyFixed;
   unsigned long long pmask = ~0ull << kKeyFixed;
   unsigned long long thr = prefix;  // candidate keys >= thr are kept
   unsigned members = n_cand;        // candidates whose key matches prefix under pmask
+  unsigned pass = 0;
   __syncthreads();
   for (int lo = kKeyFixed; members != rem && lo > 0;) {
     if (members <= static_cast<unsigned>(kWave)) {
@@ -2423,11 +2423,14 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
       thr = s.thr;
       break;
     }
-    const int nb = lo >= 12 ? 12 : lo;
+    // an 8-bit digit: 256 bins, which one wave scans (4 per lane); the
+    // passes alternate between two bin arrays, so that a pass's clear needs no
+    // barrier after the previous pass's reads
+    const int nb = lo >= 8 ? 8 : lo;
     lo -= nb;
     const unsigned dmask = (1u << nb) - 1u;
-#pragma unroll
-    for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = 0;
+    unsigned* hb = s.sh + (pass++ & 1) * 256;
+    if (tid < 256) hb[tid] = 0;
     if (tid == 0) {
       s.bin = 0;
       s.above = 0;
@@ -2436,17 +2439,39 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
     for (unsigned i = tid; i < n_cand; i += kSelThreads) {
       const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
       const unsigned long long key = sel_key(c.x, c.y);
-      if ((key & pmask) == prefix) atomicAdd(&s.sh[static_cast<unsigned>(key >> lo) & dmask], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&hb[static_cast<unsigned>(key >> lo) & dmask], 1u);
     }
     __syncthreads();
-    sel_find_bin(s.sh, rem, s.wsum, &s.bin, &s.above);
+    if (tid < kWave) {  // wave 0: the digit holding the rem-th largest member
+      unsigned c[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hb[4 * tid + i];
+        sum += c[i];
+      }
+      const unsigned incl = wave_incl_scan(sum);
+      const unsigned higher =
+          static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1)) - incl;
+      if (higher < rem && higher + sum >= rem) {
+        unsigned run = higher;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          if (run + c[i] >= rem) {
+            s.bin = 4 * tid + i;
+            s.above = run;
+            break;
+          }
+          run += c[i];
+        }
+      }
+    }
+    __syncthreads();
     const unsigned d = s.bin;
     rem -= s.above;
-    members = s.sh[d];
+    members = hb[d];
     prefix |= static_cast<unsigned long long>(d) << lo;
     pmask |= static_cast<unsigned long long>(dmask) << lo;
     thr = prefix;
-    __syncthreads();  // every thread has read the digit before the next pass clears it
   }
   for (unsigned i = tid; i < n_cand; i += kSelThreads) {
     const uint2 c = in_lds ? s.cand[i] : ld_agent_u2(&cand_g[i]);
@@ -2462,9 +2487,10 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
   // ordered compaction of the bitmap into ascending positions: each thread
   // counts a run of wpt consecutive words and a block scan gives every run's
   // first output slot. With the bitmap in LDS, every output slot t then finds
-  // its run by binary search over the runs' first slots, its word by a scan of
-  // at most wpt popcounts and its bit by halving popcounts, so that all lanes
-  // do the same work; else each thread writes its own run's positions.
+  // its wave from the waves' first slots, its run by binary search over that
+  // wave's 64 runs, its word by a scan of at most wpt popcounts and its bit by
+  // halving popcounts, so that all lanes do the same work; else each thread
+  // writes its own run's positions.
   const int wpt = (words + kSelThreads - 1) / kSelThreads;
   const int w0 = min(words, tid * wpt), w1 = min(words, w0 + wpt);
   unsigned cnt = 0;
@@ -2474,10 +2500,27 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
   if (lds_bm) {
     unsigned* first = s.sh;  // kSelThreads run starts (the histogram is no longer needed)
     first[tid] = run;
+    // the waves' first output slots: wave w's runs start at wstart[w] (wsum
+    // holds the waves' totals after the scan)
+    unsigned wstart[kSelWaves];
+    {
+      unsigned acc = 0;
+#pragma unroll
+      for (int i = 0; i < kSelWaves; ++i) {
+        wstart[i] = acc;
+        acc += s.wsum[i];
+      }
+    }
     __syncthreads();
     const unsigned n_out = min(total, static_cast<unsigned>(kk));
     for (unsigned t = tid; t < n_out; t += kSelThreads) {
-      int lo = 0, hi = kSelThreads;  // first[lo] <= t < first[hi], first[kSelThreads] standing for the total
+      // the last wave starting at or before t holds slot t (an empty wave
+      // shares its start with the next one), then its 64 runs by halving:
+      // first[lo] <= t < first[hi], first[kSelThreads] standing for the total
+      int w = 0;
+#pragma unroll
+      for (int i = 1; i < kSelWaves; ++i) w += wstart[i] <= t ? 1 : 0;
+      int lo = w * kWave, hi = lo + kWave;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (first[mid] <= t)
