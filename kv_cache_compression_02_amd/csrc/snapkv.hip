@@ -75,7 +75,10 @@ constexpr float kNegBig = -1.0e30f;  // "no score" sentinel: 2^(kNegBig - m) == 
 // The lane's contiguous half row: elements [half*D/2, half*D/2 + D/2) as D/16
 // MFMA k-step fragments of 8 bf16. The contraction index is permuted the same
 // way for Q and K, so the dot product is unchanged while each lane reads one
-// contiguous 64/128-byte run.
+// contiguous 64/128-byte run. Plain loads, also for keys streamed once: a
+// row's cache lines are read by D/16 separate instructions of the wave, and
+// with the nontemporal bit they were evicted between those reads (the two
+// score passes then fetched 23-28% more than K and ran 2.4x slower).
 template <int D>
 __device__ __forceinline__ void load_half_row(const uint16_t* p, bf16x8_t (&f)[D / 16]) {
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p);
@@ -83,14 +86,6 @@ __device__ __forceinline__ void load_half_row(const uint16_t* p, bf16x8_t (&f)[D
   for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, src[s]);
 }
 
-// The same for a row streamed once (the keys of a score pass): loaded with the
-// nontemporal bit. The window queries, which many waves read again, are not.
-template <int D>
-__device__ __forceinline__ void load_half_row_nt(const uint16_t* p, bf16x8_t (&f)[D / 16]) {
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p);
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) f[s] = __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(src + s));
-}
 
 template <int D>
 __device__ __forceinline__ void zero_frag(bf16x8_t (&f)[D / 16]) {
@@ -209,11 +204,11 @@ __global__ __launch_bounds__(kThreads) void snap_stats_bf16(
 
   int tile = key0 + wave * kTile;
   bf16x8_t kf[KS];
-  if (tile < key1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(tile + col, L - 1)) * kst, kf);
+  if (tile < key1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, L - 1)) * kst, kf);
   for (; tile < key1; tile += kStep) {
     bf16x8_t kn[KS];
     const int nt = tile + kStep;
-    if (nt < key1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(nt + col, L - 1)) * kst, kn);
+    if (nt < key1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, L - 1)) * kst, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
@@ -352,11 +347,11 @@ __global__ __launch_bounds__(kThreads) void snap_votes_bf16(
 
   int tile = e0 + wave * kTile;
   bf16x8_t kf[KS];
-  if (tile < e1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
+  if (tile < e1) load_half_row<D>(kb + static_cast<int64_t>(min(tile + col, t0 - 1)) * kst, kf);
   for (; tile < e1; tile += kStep) {
     bf16x8_t kn[KS];
     const int nt = tile + kStep;
-    if (nt < e1) load_half_row_nt<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
+    if (nt < e1) load_half_row<D>(kb + static_cast<int64_t>(min(nt + col, t0 - 1)) * kst, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
