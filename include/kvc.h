@@ -231,11 +231,24 @@ int kvc_snapkv_force_residency_fallback(int on);
  * previous setting. */
 int kvc_snapkv_force_wait_timeout(int on);
 
+/* Testing (not part of the method): byte offset, inside a workspace sized by
+ * kvc_snapkv_workspace_bytes for the same arguments, of the single pass's
+ * three 32-bit status words, or -1 if that layout has none (fp32, or
+ * arguments it rejects). After a single-pass kvc_snapkv_compress call has
+ * completed, word 0 is 0 when every bounded wait of the score kernel ended
+ * in time, else the code of the wait that ran out (1 vote weights, 2 merge
+ * slot, 3 a head's publication, 4 a head left unfinished, 5 a head's
+ * queries), in which case every
+ * head's votes were recomputed exactly; words 1 and 2 are the residency
+ * gate's count and state (1: passed). Reading them is the caller's copy. */
+int64_t kvc_snapkv_status_offset(int B, int H, int L, int D, int window, int budget, int pool_kernel,
+                                 kvc_dtype dt);
+
 /* Testing (not part of the method): while `on` is non-zero, the calling
  * thread's kvc_snapkv_compress calls run the top-k selection as several
  * workgroups per head that classify ranges of the head's positions and leave
  * the ranking and compaction to the head's last workgroup (the form used for
- * heads of more than 524288 positions or rows that are not 16-byte aligned),
+ * heads of more than 16384 prefix positions or rows that are not 16-byte aligned),
  * instead of one workgroup per head. The kept positions are the same either
  * way. Returns the previous setting. */
 int kvc_snapkv_force_split_select(int on);

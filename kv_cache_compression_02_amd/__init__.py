@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
     "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS", "KVC_POOL_MAX",
-    "KVC_POOL_AVG", "snapkv_workspace_bytes_ex", "snapkv_compress_ex",
+    "KVC_POOL_AVG", "snapkv_workspace_bytes_ex", "snapkv_compress_ex", "snapkv_status_offset",
     "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
     "decode_attention_workspace_bytes", "decode_attention", "decode_attention_noalloc",
 ]
@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "kvc_snapkv_force_split_select", "kvc_snapkv_last_select_kernel",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
     "kvc_decode_attention_noalloc", "kvc_snapkv_workspace_bytes_ex", "kvc_snapkv_compress_ex",
-    "kvc_sink_cache_positions",
+    "kvc_sink_cache_positions", "kvc_snapkv_status_offset",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -124,6 +124,8 @@ def library():
     L.kvc_snapkv_force_split_select.argtypes = [i32]
     L.kvc_snapkv_last_select_kernel.restype = ctypes.c_char_p
     L.kvc_snapkv_last_select_kernel.argtypes = []
+    L.kvc_snapkv_status_offset.restype = i64
+    L.kvc_snapkv_status_offset.argtypes = [i32] * 7 + [i32]
     L.kvc_decode_attention_noalloc.restype = i32
     L.kvc_decode_attention_noalloc.argtypes = [vp, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, vp, vp]
     L.kvc_measure_stream_read.restype = i32
@@ -185,6 +187,13 @@ def _strides4(t):
 def snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, dtype):
     code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
     return int(library().kvc_snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, code))
+
+
+def snapkv_status_offset(B, H, L, D, window, budget, pool_kernel, dtype):
+    """Byte offset of the single pass's three status words in a workspace of
+    snapkv_workspace_bytes(...) bytes, -1 if that layout has none (testing)."""
+    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    return int(library().kvc_snapkv_status_offset(B, H, L, D, window, budget, pool_kernel, code))
 
 
 SnapKVResult = namedtuple("SnapKVResult", "k v idx pooled vote")

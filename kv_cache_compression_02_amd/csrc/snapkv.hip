@@ -578,7 +578,10 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
     uint2* __restrict__ stat, unsigned* __restrict__ hist, unsigned* __restrict__ sel_ctr,
     unsigned* __restrict__ status) {
   const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
-  // status[0]: the score kernel's failure code; status[1], status[2]: its residency gate
+  // status[0]: the score kernel's failure code (0 none; a bounded wait that
+  // ran out: 1 vote weights, 2 merge slot, 3 a head's publication, 4 a head
+  // still unfinished after the last round, 5 a head's queries); status[1],
+  // status[2]: its residency gate
   if (bh == 0 && threadIdx.x < 3) status[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
@@ -1389,9 +1392,10 @@ __device__ __forceinline__ void wv_publish(const WvCtx& c, WvPipe& p, int h, int
   if (ln == 0) __hip_atomic_store(c.status, 3u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The merge of head h for this workgroup, by its designated wave, once all
-// kWvWaves waves have stored their row sums in slot h & 1: the sums added in
-// wave order, the slot reopened for head h + 2, the result added to the
+// The merge of head h (sequence index idx) for this workgroup, by its
+// designated wave, once all kWvWaves waves have stored their row sums in slot
+// idx & 1: the sums added in wave order, the slot reopened for sequence index
+// idx + 2, the result added to the
 // head's accumulators, and the head's count raised (no return is waited for).
 // The head's finisher, fixed in advance, reads the count and, once all G
 // workgroups have counted, stages and converts the words (which carry their
@@ -1500,10 +1504,11 @@ __device__ __forceinline__ void wv_votes(const WvCtx& c, WvPipe& p, uint2 pre, c
 // This wave has scored its last tile of head h: its per-lane row sums are
 // reduced across the lanes of each half (a transposing butterfly: after the
 // steps over lane bits 0..3 a lane keeps register bitrev4(lane & 15); a last
-// step adds the partner across bit 4), the results go to slot h & 1 of the
-// workgroup (once the slot is open for h), and the designated wave
-// (h + g) % kWvWaves merges them when all waves have stored theirs (now if it
-// is the last, else at a later service). A non-finite sum flags the head.
+// step adds the partner across bit 4), the results go to slot idx & 1 of the
+// workgroup (idx: the head's index in the workgroup's sequence of heads; once
+// the slot is open for idx), and the designated wave (idx + g) % kWvWaves
+// merges them when all waves have stored theirs (now if it is the last, else
+// at a later service). A non-finite sum flags the head.
 // (a & m) | (b & ~m) for a mask m that is all ones or all zeros per lane: the
 // lane-dependent choice between two registers, written so that the compiler
 // cannot turn it into an indexed read of the register array (which it lowers
@@ -1557,7 +1562,12 @@ __device__ __forceinline__ void wv_head_end(const WvCtx& c, WvPipe& p, int h, in
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the sums are in LDS before the count says so
   if (ln == 0) lds_add(&sh->mcnt[sl], 1);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (c.wave == ((h + c.g) & (kWvWaves - 1))) {
+  // the merging wave is (idx + g) % kWvWaves: a wave merges sequence index
+  // idx again only at idx + kWvWaves, and before that, at idx + 2, its
+  // slot's wait has needed the merge of idx done, so a wave never owes two
+  // merges (with the head in place of idx, a head that advances by a multiple
+  // of kWvWaves from one round to the next would give one wave both merges)
+  if (c.wave == ((idx + c.g) & (kWvWaves - 1))) {
     p.merge_head = h;
     p.merge_idx = idx;
     wv_try_merge(c, p, ln);
@@ -1864,7 +1874,9 @@ __global__ __launch_bounds__(kWvThreads, 1) void snap_wave_bf16(
     __builtin_amdgcn_s_sleep(2);
     wv_service(c, p, lane_id());
   }
-  if (p.fin_head < c.BH && lane_id() == 0)  // a finisher that ran out of time: a protocol failure
+  // a finisher that ran out of time here (a wait that gave up earlier has
+  // recorded its own code already)
+  if (p.fin_head < c.BH && !p.gave_up && lane_id() == 0)
     __hip_atomic_store(status, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -3160,6 +3172,14 @@ extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int win
   SnapLayout lay;
   if (!snap_layout(B, H, L, D, window, budget, dt, &lay)) return 0;
   return lay.total;
+}
+
+extern "C" int64_t kvc_snapkv_status_offset(int B, int H, int L, int D, int window, int budget, int pool_kernel,
+                                           kvc_dtype dt) {
+  (void)pool_kernel;
+  SnapLayout lay;
+  if (!snap_layout(B, H, L, D, window, budget, dt, &lay) || lay.cstatus == 0) return -1;
+  return static_cast<int64_t>(lay.cstatus);
 }
 
 namespace kvc {

@@ -36,6 +36,18 @@ def test_workspace_query():
     assert lib.kvc_snapkv_workspace_bytes(1, 32, 100, 128, 32, 32, 7, kvc.KVC_BF16) == 0   # budget == window
 
 
+def test_status_offset_query():
+    """The single pass's status words lie inside the workspace of a bf16 layer, 4-byte aligned, and
+    a layout without them (fp32) or a rejected shape answers -1."""
+    lib = kvc.library()
+    for B, H, L in [(1, 32, 131072), (2, 32, 9000), (2, 26, 10000)]:
+        n = lib.kvc_snapkv_workspace_bytes(B, H, L, 128, 32, 2048, 7, kvc.KVC_BF16)
+        off = lib.kvc_snapkv_status_offset(B, H, L, 128, 32, 2048, 7, kvc.KVC_BF16)
+        assert 0 < off and off % 4 == 0 and off + 12 <= n
+    assert lib.kvc_snapkv_status_offset(1, 32, 131072, 128, 32, 2048, 7, kvc.KVC_F32) == -1
+    assert lib.kvc_snapkv_status_offset(1, 32, 100, 128, 32, 200, 7, kvc.KVC_BF16) == -1
+
+
 def _snap(lib, **over):
     a = dict(q=16, q_len=32, qs=kvc.Strides(32 * 32 * 128, 32 * 128, 128), k=16, v=16,
              kvs=kvc.Strides(32 * 4096 * 128, 4096 * 128, 128), B=1, H=32, L=4096, D=128, window=32,

@@ -258,6 +258,36 @@ def test_single_pass_wait_timeout(pool):
                                               cache_key=wl), wl.B * wl.H)
 
 
+@pytest.mark.parametrize("name,H,L", [("16k-bf16", 32, 8000), ("16k-bf16", 32, 9000), ("16k-bf16", 26, 10000),
+                                      ("16k-bf16", 32, 16384), ("131k-bf16", 32, 131072)])
+def test_single_pass_waits_end_in_time(name, H, L):
+    """Every bounded wait of the independent-wave kernel ends in time on ordinary inputs: the status
+    word reads 0 after the call and the residency gate passed, so the votes come from the single
+    pass itself, not from the exact fallback (which would give the same kept positions, only
+    slower). With 256 workgroups of 8 waves, 64 heads of 8000 keys (256 tiles) put 8 whole heads
+    in each round, so a workgroup's head advances by 8 from round to round and one wave merges
+    every round's sums; at 9000 keys (288 tiles) the advance is 7 or 8; at 10000 keys (320 tiles)
+    6 or 7; the 16K and 131K layers have other step patterns (4 heads a round, and heads longer
+    than a round). Two heads of the short-head shapes are also checked against the oracle."""
+    wl = syn.SNAPKV_WORKLOADS[name].with_(H=H, L=L)
+    qn, kn, vn = _batch(wl)
+    q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
+    B, _, _, D = k.shape
+    n = kvc.snapkv_workspace_bytes(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k.dtype)
+    off = kvc.snapkv_status_offset(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k.dtype)
+    assert 0 < off and off + 12 <= n and off % 4 == 0
+    ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        print(f"[snapkv] status word {name} B{B} H{H} L{L} call {rep}", flush=True)
+        res = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", kvc.SNAPKV_SINGLE_PASS, workspace=ws)
+        assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
+        words = ws[off:off + 12].view(torch.int32).cpu().tolist()
+        assert words[0] == 0 and words[2] == 1, f"status word {words[0]}, gate {words[1:]}"
+    if L < 20000:
+        _report(f"waits-{L}", _compare(qn, kn, vn, res, wl.window, wl.budget, wl.pool_kernel, "bf16",
+                                       heads=[(0, 0), (B - 1, H - 1)]), 2)
+
+
 def test_single_pass_many_heads_unaligned():
     """Heads whose units straddle device-wide rounds (B*H*units not a multiple of the grid)."""
     wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=3, H=7, L=70001, budget=1500)
