@@ -258,6 +258,17 @@ int kvc_snapkv_force_split_select(int on);
  * string, "" if none. For reports and tests. */
 const char* kvc_snapkv_last_select_kernel(void);
 
+/* Name of the kernel that pooled the votes (max or average) and counted the
+ * histogram of pooled scores in the last kvc_snapkv_compress call on the
+ * calling thread:
+ * "snap_votes_bf16" or "snap_votes_f32" (two passes: the vote pass pools),
+ * "snap_pool" or "snap_pool_lds" (single pass: a pooling kernel after the
+ * score kernel), "snap_select_head" (single pass, max-pool of radius at most
+ * 4 over heads of at most 16384 prefix positions: the per-head selection
+ * kernel pools, counts and recomputes flagged heads itself, and no pooling
+ * kernel is launched); a static string, "" if none. For reports and tests. */
+const char* kvc_snapkv_last_pool_kernel(void);
+
 /* Instrumentation (not part of the method): while set, every
  * kvc_snapkv_compress call on the calling thread records events[i] on its
  * stream at phase boundary i, for i < n_events (at most 7) and events[i] not

@@ -25,6 +25,7 @@ __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
     "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS", "KVC_POOL_MAX",
     "KVC_POOL_AVG", "snapkv_workspace_bytes_ex", "snapkv_compress_ex", "snapkv_status_offset",
+    "snapkv_last_pool_kernel",
     "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
     "decode_attention_workspace_bytes", "decode_attention", "decode_attention_noalloc",
 ]
@@ -44,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "kvc_snapkv_force_split_select", "kvc_snapkv_last_select_kernel",
     "kvc_decode_attention_workspace_bytes", "kvc_decode_attention", "kvc_measure_stream_read",
     "kvc_decode_attention_noalloc", "kvc_snapkv_workspace_bytes_ex", "kvc_snapkv_compress_ex",
-    "kvc_sink_cache_positions", "kvc_snapkv_status_offset",
+    "kvc_sink_cache_positions", "kvc_snapkv_status_offset", "kvc_snapkv_last_pool_kernel",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -125,6 +126,8 @@ def library():
     L.kvc_snapkv_last_select_kernel.restype = ctypes.c_char_p
     L.kvc_snapkv_last_select_kernel.argtypes = []
     L.kvc_snapkv_status_offset.restype = i64
+    L.kvc_snapkv_last_pool_kernel.restype = ctypes.c_char_p
+    L.kvc_snapkv_last_pool_kernel.argtypes = []
     L.kvc_snapkv_status_offset.argtypes = [i32] * 7 + [i32]
     L.kvc_decode_attention_noalloc.restype = i32
     L.kvc_decode_attention_noalloc.argtypes = [vp, Strides, vp, vp, Strides, i32, i32, i32, i32, i32, vp, vp]
@@ -225,6 +228,11 @@ def snapkv_last_score_kernel():
 def snapkv_last_select_kernel():
     """Selection kernel the last snapkv_compress call launched."""
     return library().kvc_snapkv_last_select_kernel().decode()
+
+
+def snapkv_last_pool_kernel():
+    """Kernel that pooled the votes and counted their histogram in the last snapkv_compress call."""
+    return library().kvc_snapkv_last_pool_kernel().decode()
 
 
 def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,

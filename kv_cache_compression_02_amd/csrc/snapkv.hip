@@ -2694,12 +2694,21 @@ __device__ __forceinline__ void sel_piece_lds(SelShared& s, unsigned* ctr_head, 
 // so that no workgroup waits for another's results through device memory.
 // Longer heads go to snap_select: one workgroup walking them range by range
 // would wait for each range's loads in turn.
+//
+// With self_hist (single pass, raw votes max-pooled here) the workgroup also
+// does the pooling kernel's work for its head, which is then not launched:
+// the exact votes of a flagged head (ea, as the pooling kernel), the head's
+// 12-bit histogram of pooled scores (in LDS, from the pooled pieces the
+// classification uses) and, if pooled_out is not NULL, the pooled scores.
+// `hist` is not read then.
 __global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __restrict__ src, int rad, int skip,
                                                                 const unsigned* __restrict__ hist, int N, int kk,
                                                                 unsigned* __restrict__ ctr,
                                                                 uint2* __restrict__ cand_ws,
-                                                                int* __restrict__ idx_out) {
+                                                                int* __restrict__ idx_out, int self_hist,
+                                                                float* __restrict__ pooled_out, const ExactArgs ea) {
   __shared__ SelShared s;
+  __shared__ ExactShared es;
   const int bh = blockIdx.x, tid = threadIdx.x, lane = lane_id();
   const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(bh) * N);
   const int nf = N >> 2;
@@ -2708,27 +2717,74 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __r
   unsigned* ctr_head = ctr + bh * kSelCtrWords;
   const unsigned* hb = hist + static_cast<int64_t>(bh) * kHistBins;
 
-  // the histogram row and the head's pieces in flight together
+  // the histogram row (or the head's flag) and the head's pieces in flight together
   constexpr int kHistPer = kHistBins / kSelThreads;
   unsigned hv[kHistPer];
+  if (!self_hist) {
 #pragma unroll
-  for (int r = 0; r < kHistPer; ++r) hv[r] = hb[tid + r * kSelThreads];
-  f32x4_t xb[kSelPer], xe[kSelPer];
-#pragma unroll
-  for (int k = 0; k < kSelPer; ++k) {
-    const int f = tid + k * kSelThreads;
-    xb[k] = pv[min(f, nf - 1)];
-    // the piece just beyond the wave, for lanes 0 and 63 (a clamped copy for the others)
-    xe[k] = pv[min(max(lane == 0 ? f - 1 : f + 1, 0), nf - 1)];
+    for (int r = 0; r < kHistPer; ++r) hv[r] = hb[tid + r * kSelThreads];
   }
+  f32x4_t xb[kSelPer], xe[kSelPer];
+  auto load_pieces = [&]() {
 #pragma unroll
-  for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = hv[r];
+    for (int k = 0; k < kSelPer; ++k) {
+      const int f = tid + k * kSelThreads;
+      xb[k] = pv[min(f, nf - 1)];
+      // the piece just beyond the wave, for lanes 0 and 63 (a clamped copy for the others)
+      xe[k] = pv[min(max(lane == 0 ? f - 1 : f + 1, 0), nf - 1)];
+    }
+  };
+  load_pieces();
+  if (self_hist && exact_flagged(ea, bh)) {
+    // the head's exact votes (the pieces just loaded are discarded), written
+    // back where the caller reads them, then read again from L2
+    float* vb = const_cast<float*>(src) + static_cast<int64_t>(bh) * N;
+    exact_prepare(es, ea, bh);
+    for (int j = tid; j < N; j += kSelThreads) vb[j] = exact_vote(es, ea, bh, j);
+    __threadfence();
+    __syncthreads();
+    __threadfence();
+    load_pieces();
+  }
+  f32x4_t pp[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) pp[k] = sel_pool_piece(xb[k], xe[k], tid + k * kSelThreads, nf, rad);
+  if (self_hist) {
+#pragma unroll
+    for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = 0;
+  } else {
+#pragma unroll
+    for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = hv[r];
+  }
   if (tid == 0) {
     s.bin = 0;
     s.above = 0;
     s.nloc = 0;
   }
   __syncthreads();
+  if (self_hist) {
+    // each piece's four pooled scores, a run of equal bins one LDS add
+#pragma unroll
+    for (int k = 0; k < kSelPer; ++k) {
+      const int f = tid + k * kSelThreads;
+      if (f < nf) {
+        unsigned run_bin = (__float_as_uint(pp[k][0]) >> kHistShift) & (kHistBins - 1), run = 1;
+#pragma unroll
+        for (int e = 1; e < 4; ++e) {
+          const unsigned bin = (__float_as_uint(pp[k][e]) >> kHistShift) & (kHistBins - 1);
+          if (bin != run_bin) {
+            atomicAdd(&s.sh[run_bin], run);
+            run_bin = bin;
+            run = 0;
+          }
+          ++run;
+        }
+        atomicAdd(&s.sh[run_bin], run);
+        if (pooled_out) *reinterpret_cast<f32x4_t*>(pooled_out + static_cast<int64_t>(bh) * N + 4 * f) = pp[k];
+      }
+    }
+    __syncthreads();
+  }
   sel_find_bin(s.sh, static_cast<unsigned>(kk), s.wsum, &s.bin, &s.above);
   const unsigned bstar = s.bin;
   const unsigned rem = static_cast<unsigned>(kk) - s.above;
@@ -2736,7 +2792,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __r
   for (int k = 0; k < kSelPer; ++k) {
     const int f = tid + k * kSelThreads;
     if (!skip || sel_wave_reaches(xb[k], xe[k], bstar))
-      sel_piece_lds(s, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+      sel_piece_lds(s, ctr_head, cand_g, N, pp[k], f, f < nf, bstar);
     else if (f < nf && (lane & 7) == 0)
       s.bm[f >> 3] = 0u;
   }
@@ -3017,6 +3073,7 @@ thread_local bool g_force_residency_fail = false;
 thread_local bool g_force_wait_timeout = false;
 thread_local bool g_force_split_select = false;
 thread_local const char* g_last_select = "";
+thread_local const char* g_last_pool = "";
 
 template <int R>
 void launch_pool_r(float* vote, float* pooled, unsigned* hist, int BH, int N, int avg, const ExactArgs& ea,
@@ -3067,7 +3124,7 @@ void launch_pool(float* vote, float* pooled, unsigned* hist, int BH, int N, int 
 template <int D>
 kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint16_t* q, kvc_strides qs, int qrow0,
                               const uint16_t* k, kvc_strides kvs, int H, int L, int w, int r, int avg,
-                              float scale_log2, char* ws, float* vote, float* pooled, hipStream_t stream) {
+                              float scale_log2, char* ws, float* vote, float* pooled, ExactArgs* fused, hipStream_t stream) {
   float* ref = reinterpret_cast<float*>(ws + lay.cref);
   unsigned long long* acc = reinterpret_cast<unsigned long long*>(ws + lay.cacc);
   unsigned* cnt = reinterpret_cast<unsigned*>(ws + lay.ccnt);
@@ -3124,7 +3181,10 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   }
   if (e != hipSuccess) return fail(KVC_ERR_HIP, "snapkv single pass launch: %s", hipGetErrorString(e));
   mark_phase(3, stream);
-  launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, avg, ea, stream);
+  if (fused)
+    *fused = ea;  // the per-head selection pools, counts and recomputes flagged heads itself
+  else
+    launch_pool(vote, pooled, hist, static_cast<int>(lay.BH), lay.N, r, avg, ea, stream);
   mark_phase(4, stream);
   return KVC_OK;
 }
@@ -3165,6 +3225,8 @@ extern "C" int kvc_snapkv_force_split_select(int on) {
 }
 
 extern "C" const char* kvc_snapkv_last_select_kernel(void) { return g_last_select; }
+
+extern "C" const char* kvc_snapkv_last_pool_kernel(void) { return g_last_pool; }
 
 extern "C" size_t kvc_snapkv_workspace_bytes(int B, int H, int L, int D, int window, int budget,
                                              int pool_kernel, kvc_dtype dt) {
@@ -3248,6 +3310,8 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
   // a small radius) the raw votes, which it then pools itself
   const float* sel_src = pooled;
   int sel_rad = 0;
+  bool self_hist = false;
+  ExactArgs fused_ea{};
   if (Gw > 0 || Gc > 0) {
     // Raw votes go to the caller's buffer, else to the pooled-score area when
     // the selection pools them (nothing else is stored there then), else to
@@ -3262,12 +3326,20 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
     float* pooled_dst = pooled_out ? pooled_out : sel_pools ? nullptr : pooled;
     const uint16_t* qb = static_cast<const uint16_t*>(q);
     const uint16_t* kb = static_cast<const uint16_t*>(k);
+    // heads of at most one selection workgroup's range: that workgroup also
+    // does the pooling kernel's work (histogram, pooled output, exact votes of
+    // flagged heads), which is then not launched
+    const bool fuse = sel_pools && lay.N <= kSelChunk && lay.N % 4 == 0 && aligned16(vraw) &&
+                      (!pooled_out || aligned16(pooled_out)) && !g_force_split_select;
+    ExactArgs* fused_arg = fuse ? &fused_ea : nullptr;
     kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r, avg,
-                                                       scale_log2, ws, vraw, pooled_dst, stream)
+                                                       scale_log2, ws, vraw, pooled_dst, fused_arg, stream)
                              : launch_single_pass<64>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r, avg,
-                                                      scale_log2, ws, vraw, pooled_dst, stream);
+                                                      scale_log2, ws, vraw, pooled_dst, fused_arg, stream);
     if (st == KVC_OK) {
       schedule = KVC_SNAPKV_SINGLE_PASS;
+      self_hist = fuse;
+      g_last_pool = fuse ? "snap_select_head" : r <= kPoolRegRadius ? "snap_pool" : "snap_pool_lds";
       if (sel_pools) {
         sel_src = vraw;
         sel_rad = r;
@@ -3282,6 +3354,7 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
   if (schedule == KVC_SNAPKV_TWO_PASS) {
     mark_phase(1, stream);  // counters and histograms are cleared by the statistics pass
     g_last_kernel = dt == KVC_BF16 ? "snap_stats_bf16+snap_votes_bf16" : "snap_stats_f32+snap_votes_f32";
+    g_last_pool = dt == KVC_BF16 ? "snap_votes_bf16" : "snap_votes_f32";
     if (dt == KVC_BF16)
       launch_score_passes<uint16_t>(lay, static_cast<const uint16_t*>(q), qs, qrow0,
                                     static_cast<const uint16_t*>(k), kvs, H, L, D, window, pool_kernel / 2, avg,
@@ -3303,7 +3376,8 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
     // exchange between workgroups
     snap_select_head<<<static_cast<unsigned>(lay.BH), kSelThreads, 0, stream>>>(
         sel_src, sel_rad, skip, hist, lay.N, lay.kk, reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
-        reinterpret_cast<uint2*>(ws + lay.cand), idx_out);
+        reinterpret_cast<uint2*>(ws + lay.cand), idx_out, self_hist ? 1 : 0, self_hist ? pooled_out : nullptr,
+        fused_ea);
     g_last_select = "snap_select_head";
   } else {
     const dim3 gs((lay.N + kSelChunk - 1) / kSelChunk, static_cast<unsigned>(lay.BH));

@@ -228,6 +228,21 @@ def test_single_pass_residency_fallback(pool):
         lib.kvc_snapkv_force_residency_fallback(prev)
 
 
+def test_single_pass_residency_fallback_fused_select():
+    """The same at the 16K layer's shape, where the per-head selection kernel also does the pooling
+    kernel's work (no pooling kernel is launched): each selection workgroup recomputes its flagged
+    head's votes exactly before pooling and counting them."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"]
+    lib = kvc.library()
+    prev = lib.kvc_snapkv_force_residency_fallback(1)
+    try:
+        _workload(wl, heads=[(0, 0), (0, 17), (1, 31)], schedule=kvc.SNAPKV_SINGLE_PASS)
+        assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
+        assert kvc.snapkv_last_select_kernel() == "snap_select_head"
+    finally:
+        lib.kvc_snapkv_force_residency_fallback(prev)
+
+
 @pytest.mark.parametrize("pool", [7, 17])
 def test_single_pass_wait_timeout(pool):
     """The independent-wave kernel's cross-worker waits given a limit of zero polls from the host: a
@@ -352,7 +367,9 @@ def test_select_forms_agree(name, L, pool):
     """One workgroup per head (heads of at most 16384 prefix positions) and several per head keep
     the same positions, bit for bit, on the same votes (both schedules' votes: the selection reads
     raw votes and pools them itself for a max-pool of radius <= 4, else the pooling kernel's
-    stored scores)."""
+    stored scores). Under the single pass with a max-pool of radius <= 4 the per-head form also
+    does the pooling kernel's work (pooled output and histogram), which is then not launched: its
+    pooled scores equal the pooling kernel's bit for bit."""
     wl = syn.SNAPKV_WORKLOADS[name].with_(pool_kernel=pool)
     if L is not None:
         wl = wl.with_(L=L, name=f"{name}-L{L}")
@@ -360,11 +377,15 @@ def test_select_forms_agree(name, L, pool):
     qn, kn, vn = _batch(wl.with_(pool_kernel=syn.SNAPKV_WORKLOADS[name].pool_kernel))
     q, k, v = (par.to_device(x, wl.dtype) for x in (qn, kn, vn))
     for schedule in (kvc.SNAPKV_SINGLE_PASS, kvc.SNAPKV_TWO_PASS):
+        single = schedule == kvc.SNAPKV_SINGLE_PASS
         a = _run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True, want_pooled=True)
         assert kvc.snapkv_last_select_kernel() == "snap_select_head"
+        assert kvc.snapkv_last_pool_kernel() == (("snap_select_head" if pool <= 9 else "snap_pool") if single
+                                                 else "snap_votes_bf16")
         with _SplitSelect():
             b = _run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True, want_pooled=True)
             assert kvc.snapkv_last_select_kernel() == "snap_select"
+            assert kvc.snapkv_last_pool_kernel() == ("snap_pool" if single else "snap_votes_bf16")
         assert torch.equal(a.vote, b.vote) and torch.equal(a.pooled, b.pooled)  # deterministic votes
         assert torch.equal(a.idx, b.idx)
         assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
