@@ -10,6 +10,9 @@ Default run (N = 1 GPU):
     way and reported under "workloads", each with its own roofline.
   * Consecutive steps rotate over enough device copies of K and V that a step
     never finds the previous step's K in the 256 MB infinity cache (MALL).
+  * The timed steps of a layer come after its warmup steps and its untimed
+    instrumented passes (kernel and phase events), so that they run at the
+    clocks the GPU holds under sustained load.
   * The H2O + StreamingLLM decode loop of an OPT-6.7B-shaped layer (B64 H32
     D128, 2048-token prompt then 2048 decode steps, budget len//10 heavy +
     len//10 recent, sink 4 + recent 1020 ring) is measured as a second object.
@@ -148,9 +151,10 @@ def put_host(x, dtype):
 
 
 def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
-    """Time kvc_snapkv_compress on one layer: `steps` calls back to back with no events in the stream
-    (the step time), the same calls again with events around the score kernel(s) only (the dominant
-    kernel's launch time) and, with `detail`, once more with every phase boundary marked."""
+    """Time kvc_snapkv_compress on one layer: after `warmup` calls, `steps` calls with events around
+    the score kernel(s) only (the dominant kernel's launch time), with `detail` the same calls again
+    with every phase boundary marked (both untimed for the step), then `steps` calls back to back
+    with no events in the stream (the step time)."""
     import torch
 
     import kv_cache_compression_02_amd as kvc
@@ -195,20 +199,20 @@ def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
     torch.cuda.synchronize()
     single = kvc.snapkv_last_schedule() == kvc.SNAPKV_SINGLE_PASS
     score_kernel = kvc.snapkv_last_score_kernel()
+    pool_kernel = kvc.snapkv_last_pool_kernel()
+    # the per-head selection kernel pools and counts itself: no pooling kernel between marks 3 and 4
+    fused_pool = single and pool_kernel == "snap_select_head"
     phases = PHASES_SINGLE if single else PHASES
+    if fused_pool:
+        phases = [("none_pool" if p == "pool" else p) for p in phases]
     passes = ("score", "pool") if single else ("stats", "votes")
-    log(f"schedule: {'single pass' if single else 'two passes'} ({score_kernel})")
-    # Timed region: the steps back to back with no events in the stream (a
-    # recorded event between two kernels costs the GPU several microseconds).
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        call(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # The same steps again with events around the score passes only
-    # (boundaries 1 to 4): 1 -> 2 is the statistics pass or the single score
-    # kernel, 3 -> 4 the vote pass or the pooling kernel.
+    log(f"schedule: {'single pass' if single else 'two passes'} ({score_kernel}; pooling in {pool_kernel})")
+    # Untimed instrumented passes first (the timed steps then start with the
+    # GPU at the clocks it holds under sustained load, as in a serving loop:
+    # the first ~10 ms of work after an idle period run a few percent slower).
+    # The steps with events around the score passes only (boundaries 1 to 4):
+    # 1 -> 2 is the statistics pass or the single score kernel, 3 -> 4 the
+    # vote pass or the pooling kernel.
     timed = [ev.create(4) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -220,9 +224,11 @@ def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
     set_events(None)
     kern_ms = {passes[0]: sum(ev.ms(e[0], e[1]) for e in timed) / steps,
                passes[1]: sum(ev.ms(e[2], e[3]) for e in timed) / steps}
+    if fused_pool:
+        del kern_ms["pool"]
     phase_ms = None
     if detail:
-        # Untimed instrumented pass: every phase boundary, for the breakdown only.
+        # every phase boundary, for the breakdown only
         events = [ev.create(n_ev) for _ in range(steps)]
         for i in range(steps):
             set_events(events[i])
@@ -230,8 +236,18 @@ def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
         torch.cuda.synchronize()
         set_events(None)
         phase_ms = {p: sum(ev.ms(e[j], e[j + 1]) for e in events) / steps for j, p in enumerate(phases)}
-        # (single pass: nothing runs between marks 2 and 3; that interval is the events' own cost)
+        # (single pass: nothing runs between marks 2 and 3, nor between 3 and 4 where the
+        # selection pools; such an interval is the events' own cost)
         phase_ms.pop("none", None)
+        phase_ms.pop("none_pool", None)
+    # Timed region: the steps back to back with no events in the stream (a
+    # recorded event between two kernels costs the GPU several microseconds).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     lib.kvc_snapkv_set_schedule(0)
     step_ms = elapsed / steps * 1e3
     nbytes = snapkv_bytes(wl)
@@ -253,6 +269,7 @@ def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
                   "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": kern_ms[dominant],
                   "score_pass_ms": kern_ms},
         phase_ms=phase_ms, alg_bytes=nbytes["total"], schedule="single-pass" if single else "two-pass",
+        pool_kernel=pool_kernel,
         host=(qn, kn, vn) if keep_host else None)
     if detail:
         # decode attention over the compressed cache, rotated over enough copies of it (K' and V')
@@ -276,6 +293,7 @@ def workload_line(res):
         "kv_copies_rotated": res["copies"],
         "hbm_gbps_path": res["path_gbps"], "hbm_frac_path": res["path_gbps"] * 1e9 / PEAK_HBM,
         "algorithmic_bytes_per_step": res["alg_bytes"], "roofline": res["roofline"],
+        "pooling_kernel": res["pool_kernel"],
     }
 
 
@@ -587,6 +605,7 @@ def main():
         "kv_copies_rotated": res["copies"],
         "roofline": res["roofline"],
         "phase_ms": res["phase_ms"],
+        "pooling_kernel": res["pool_kernel"],
         "decode_attention_compressed": res["decode_attention"],
     }
     sp = stream_peak(ev)
