@@ -225,6 +225,8 @@ int kvc_snapkv_force_residency_fallback(int on);
  * round): every wait that
  * would have to wait gives up at once and records a failure code in the
  * status word, exactly as a wait whose normal limit (2^18 polls) runs out.
+ * The split selection's wait for its head's histogram also gives up at once
+ * (each workgroup then counts the whole head's pooled scores itself).
  * The kernel still exits normally. The pooling kernel reads the status word
  * and recomputes every head's votes exactly, so the results are the same as
  * without the knob (the votes may differ in the last bits). Returns the
@@ -248,9 +250,11 @@ int64_t kvc_snapkv_status_offset(int B, int H, int L, int D, int window, int bud
  * thread's kvc_snapkv_compress calls run the top-k selection as several
  * workgroups per head that classify ranges of the head's positions and leave
  * the ranking and compaction to the head's last workgroup (the form used for
- * heads of more than 16384 prefix positions or rows that are not 16-byte aligned),
- * instead of one workgroup per head. The kept positions are the same either
- * way. Returns the previous setting. */
+ * heads of more than 16384 prefix positions or rows that are not 16-byte
+ * aligned), instead of one workgroup per head. With `on` = 2 the single pass
+ * also launches its separate pooling kernel where the split selection would
+ * otherwise pool and count the votes itself. The kept positions are the same
+ * either way. Returns the previous setting (0, 1 or 2). */
 int kvc_snapkv_force_split_select(int on);
 
 /* Name of the selection kernel the last kvc_snapkv_compress call on the
@@ -263,10 +267,12 @@ const char* kvc_snapkv_last_select_kernel(void);
  * calling thread:
  * "snap_votes_bf16" or "snap_votes_f32" (two passes: the vote pass pools),
  * "snap_pool" or "snap_pool_lds" (single pass: a pooling kernel after the
- * score kernel), "snap_select_head" (single pass, max-pool of radius at most
- * 4 over heads of at most 16384 prefix positions: the per-head selection
- * kernel pools, counts and recomputes flagged heads itself, and no pooling
- * kernel is launched); a static string, "" if none. For reports and tests. */
+ * score kernel), "snap_select_head" or "snap_select" (single pass, max-pool
+ * of radius at most 4: the selection kernel pools, counts and recomputes
+ * flagged heads itself and no pooling kernel is launched; one workgroup per
+ * head for heads of at most 16384 prefix positions, else the head's
+ * workgroups together where the whole selection grid fits on the GPU at
+ * once); a static string, "" if none. For reports and tests. */
 const char* kvc_snapkv_last_pool_kernel(void);
 
 /* Instrumentation (not part of the method): while set, every

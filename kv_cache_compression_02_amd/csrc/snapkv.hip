@@ -67,7 +67,8 @@ constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 19;       // pooled >= 0: bits 30..19 = exponent + 4 mantissa bits
 constexpr int kMaxPoolRadius = 32;
-constexpr int kSelCtrWords = 2;     // per head: candidates listed, selection workgroups finished
+constexpr int kSelCtrWords = 3;     // per head: candidates listed, selection workgroups finished,
+                                    // selection workgroups whose histogram is in (single pass)
 constexpr float kNegBig = -1.0e30f;  // "no score" sentinel: 2^(kNegBig - m) == 0
 
 // ------------------------------------------------------------------ loaders
@@ -2181,6 +2182,7 @@ constexpr int kCandLds = 4096;                        // candidates a workgroup 
 constexpr int kBitmapLds = 16384;                     // bitmap words kept in LDS (N <= 524288)
 constexpr int kKeyFixed = 51;                         // key bits 63..51: the sign (clear) and the bin
 constexpr int kSelMaxRad = 4;                         // pooling radius the selection applies to raw votes
+constexpr unsigned kSelHistSpin = 1u << 14;           // polls for a head's histogram before counting it alone
 
 __device__ __forceinline__ unsigned long long sel_key(unsigned u, unsigned j) {
   return (static_cast<unsigned long long>(u & 0x7FFFFFFFu) << 32) | static_cast<unsigned long long>(~j);
@@ -2258,7 +2260,7 @@ struct SelShared {
   alignas(16) unsigned long long mem[kWave];
   unsigned wsum[kSelWaves];
   unsigned long long thr;
-  unsigned bin, above, nloc, base, last, nmem;
+  unsigned bin, above, nloc, base, last, nmem, hist_in;
 };
 
 // A candidate found by this workgroup: held in LDS while there is room, else
@@ -2363,6 +2365,32 @@ __device__ __forceinline__ f32x4_t sel_pool_piece(f32x4_t cur, f32x4_t edge, int
     out[e] = m;
   }
   return out;
+}
+
+// A piece's four pooled scores counted in the LDS histogram `sh` (a run of
+// equal bins one add) and, if out is not NULL, stored there.
+__device__ __forceinline__ void sel_count_piece(unsigned* sh, f32x4_t p, float* out) {
+  unsigned run_bin = (__float_as_uint(p[0]) >> kHistShift) & (kHistBins - 1), run = 1;
+#pragma unroll
+  for (int e = 1; e < 4; ++e) {
+    const unsigned bin = (__float_as_uint(p[e]) >> kHistShift) & (kHistBins - 1);
+    if (bin != run_bin) {
+      atomicAdd(&sh[run_bin], run);
+      run_bin = bin;
+      run = 0;
+    }
+    ++run;
+  }
+  atomicAdd(&sh[run_bin], run);
+  if (out) *reinterpret_cast<f32x4_t*>(out) = p;
+}
+
+// The exact votes of piece f (positions 4f .. 4f + 3) of head bh.
+__device__ f32x4_t sel_exact_piece(const ExactShared& e, const ExactArgs& a, int bh, int f) {
+  f32x4_t x;
+#pragma unroll 1
+  for (int i = 0; i < 4; ++i) x[i] = exact_vote(e, a, bh, 4 * f + i);
+  return x;
 }
 
 // The max-pool (radius rad) of position j of a row of N raw votes, one by one.
@@ -2568,26 +2596,31 @@ __device__ void sel_rank_compact(SelShared& s, unsigned bstar, unsigned rem, uns
 
 // src: per head N pooled scores (rad = 0) or raw votes (pooled here with radius rad)
 __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restrict__ src, int vec, int rad, int skip,
-                                                           const unsigned* __restrict__ hist, int N, int kk,
+                                                           unsigned* __restrict__ hist, int N, int kk,
                                                            unsigned* __restrict__ ctr, uint2* __restrict__ cand_ws,
                                                            unsigned* __restrict__ bitmap_ws,
-                                                           int* __restrict__ idx_out) {
+                                                           int* __restrict__ idx_out, int self_hist,
+                                                           float* __restrict__ pooled_out, const ExactArgs ea,
+                                                           unsigned spin) {
   __shared__ SelShared s;
-  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  __shared__ ExactShared es;
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = lane_id();
   const float* pb = src + static_cast<int64_t>(bh) * N;
   const int words = (N + 31) >> 5;
   unsigned* bm_g = bitmap_ws + static_cast<int64_t>(bh) * words;
   uint2* cand_g = cand_ws + static_cast<int64_t>(bh) * N;
   unsigned* ctr_head = ctr + bh * kSelCtrWords;
-  const unsigned* hb = hist + static_cast<int64_t>(bh) * kHistBins;
+  unsigned* hb = hist + static_cast<int64_t>(bh) * kHistBins;
   const int c0 = blk * kSelChunk, c1 = min(N, c0 + kSelChunk);
 
   // 1. the range's scores on their way (off the 16-byte path the loads read,
   // and ignore, the histogram row), then the threshold bin
   constexpr int kHistPer = kHistBins / kSelThreads;
   unsigned hv[kHistPer];
+  if (!self_hist) {
 #pragma unroll
-  for (int r = 0; r < kHistPer; ++r) hv[r] = hb[tid + r * kSelThreads];
+    for (int r = 0; r < kHistPer; ++r) hv[r] = hb[tid + r * kSelThreads];
+  }
   const int nf = vec ? N >> 2 : 1;
   const int fb = vec ? c0 >> 2 : 0;
   const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(vec ? static_cast<const void*>(pb) : static_cast<const void*>(hb));
@@ -2597,16 +2630,83 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
     const int f = fb + tid + k * kSelThreads;
     xb[k] = pv[min(f, nf - 1)];
     // the piece just beyond the wave, for lanes 0 and 63 (a clamped copy for the others)
-    xe[k] = pv[min(max((lane_id() == 0 ? f - 1 : f + 1), 0), nf - 1)];
+    xe[k] = pv[min(max((lane == 0 ? f - 1 : f + 1), 0), nf - 1)];
   }
+  const bool exact = self_hist && exact_flagged(ea, bh);
+  if (exact) {
+    // the exact votes of the range's pieces and of the pieces beyond the
+    // waves' edges (those of a neighbouring range computed here too, so that
+    // no workgroup reads another's); the range's own go back to the vote buffer
+    exact_prepare(es, ea, bh);
+    float* vb = const_cast<float*>(pb);
+#pragma unroll 1
+    for (int k = 0; k < kSelPer; ++k) {
+      const int f = fb + tid + k * kSelThreads;
+      xb[k] = sel_exact_piece(es, ea, bh, min(f, nf - 1));
+      if (lane == 0 || lane == kWave - 1) xe[k] = sel_exact_piece(es, ea, bh, min(max((lane == 0 ? f - 1 : f + 1), 0), nf - 1));
+      if (f < nf) *reinterpret_cast<f32x4_t*>(vb + 4 * f) = xb[k];
+    }
+  }
+  f32x4_t pp[kSelPer];
 #pragma unroll
-  for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = hv[r];
+  for (int k = 0; k < kSelPer; ++k) pp[k] = vec ? sel_pool_piece(xb[k], xe[k], fb + tid + k * kSelThreads, nf, rad) : xb[k];
+#pragma unroll
+  for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = self_hist ? 0u : hv[r];
   if (tid == 0) {
     s.bin = 0;
     s.above = 0;
     s.nloc = 0;
   }
   __syncthreads();
+  if (self_hist) {
+    // the range's histogram into the head's row, then the head's once all its
+    // workgroups have added theirs (bounded wait), else counted here
+#pragma unroll
+    for (int k = 0; k < kSelPer; ++k) {
+      const int f = fb + tid + k * kSelThreads;
+      if (f < nf) sel_count_piece(s.sh, pp[k], pooled_out ? pooled_out + static_cast<int64_t>(bh) * N + 4 * f : nullptr);
+    }
+    __syncthreads();
+    flush_hist(s.sh, hb);
+    // this thread's device-scope adds are complete before the workgroup counts
+    // itself in (a wait, not a fence: an agent-scope release fence would write
+    // back the L2 for every wave)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      atomicAdd(&ctr_head[2], 1u);
+      unsigned n = load_word(&ctr_head[2]);
+      for (unsigned polls = 0; n < gridDim.x && polls < spin; ++polls) {
+        __builtin_amdgcn_s_sleep(2);
+        n = load_word(&ctr_head[2]);
+      }
+      s.hist_in = n >= gridDim.x;
+    }
+    __syncthreads();
+    if (s.hist_in) {
+      // (agent-scope loads: they read the adds where they were made)
+#pragma unroll
+      for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = load_word(&hb[tid + r * kSelThreads]);
+    } else {
+      // some of the head's workgroups were not resident: every piece of the
+      // head pooled and counted here (exact votes again for a flagged head)
+#pragma unroll
+      for (int r = 0; r < kHistPer; ++r) s.sh[tid + r * kSelThreads] = 0;
+      __syncthreads();
+#pragma unroll 1
+      for (int f0 = 0; f0 < nf; f0 += kSelThreads) {
+        const int f = f0 + tid, fe = min(max((lane == 0 ? f - 1 : f + 1), 0), nf - 1);
+        f32x4_t x = pv[min(f, nf - 1)], y = pv[fe];
+        if (exact) {
+          x = sel_exact_piece(es, ea, bh, min(f, nf - 1));
+          if (lane == 0 || lane == kWave - 1) y = sel_exact_piece(es, ea, bh, fe);
+        }
+        const f32x4_t p = sel_pool_piece(x, y, f, nf, rad);
+        if (f < nf) sel_count_piece(s.sh, p, nullptr);
+      }
+    }
+    __syncthreads();
+  }
   sel_find_bin(s.sh, static_cast<unsigned>(kk), s.wsum, &s.bin, &s.above);
   const unsigned bstar = s.bin;
   unsigned rem = static_cast<unsigned>(kk) - s.above;
@@ -2617,7 +2717,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
     for (int k = 0; k < kSelPer; ++k) {
       const int f = fb + tid + k * kSelThreads;
       if (!skip || sel_wave_reaches(xb[k], xe[k], bstar))
-        sel_piece(s, bm_g, ctr_head, cand_g, N, sel_pool_piece(xb[k], xe[k], f, nf, rad), f, f < nf, bstar);
+        sel_piece(s, bm_g, ctr_head, cand_g, N, pp[k], f, f < nf, bstar);
       else if (f < nf && (lane_id() & 7) == 0)
         store_word(&bm_g[f >> 3], 0u);
     }
@@ -2763,25 +2863,10 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_head(const float* __r
   }
   __syncthreads();
   if (self_hist) {
-    // each piece's four pooled scores, a run of equal bins one LDS add
 #pragma unroll
     for (int k = 0; k < kSelPer; ++k) {
       const int f = tid + k * kSelThreads;
-      if (f < nf) {
-        unsigned run_bin = (__float_as_uint(pp[k][0]) >> kHistShift) & (kHistBins - 1), run = 1;
-#pragma unroll
-        for (int e = 1; e < 4; ++e) {
-          const unsigned bin = (__float_as_uint(pp[k][e]) >> kHistShift) & (kHistBins - 1);
-          if (bin != run_bin) {
-            atomicAdd(&s.sh[run_bin], run);
-            run_bin = bin;
-            run = 0;
-          }
-          ++run;
-        }
-        atomicAdd(&s.sh[run_bin], run);
-        if (pooled_out) *reinterpret_cast<f32x4_t*>(pooled_out + static_cast<int64_t>(bh) * N + 4 * f) = pp[k];
-      }
+      if (f < nf) sel_count_piece(s.sh, pp[k], pooled_out ? pooled_out + static_cast<int64_t>(bh) * N + 4 * f : nullptr);
     }
     __syncthreads();
   }
@@ -2982,6 +3067,7 @@ thread_local int g_last_schedule = 0;
 struct CoopCaps {
   bool queried = false, coop = false;
   int cus = 0, per_cu[2] = {0, 0}, wv_per_cu[2] = {0, 0};
+  int sel_per_cu = 0;  // split selection workgroups per compute unit
 };
 
 const CoopCaps& coop_caps() {
@@ -2996,19 +3082,21 @@ const CoopCaps& coop_caps() {
   CoopCaps& c = caps[dev];
   if (!c.queried) {
     c.queried = true;
-    int coop = 0, cus = 0, n64 = 0, n128 = 0, w64 = 0, w128 = 0;
+    int coop = 0, cus = 0, n64 = 0, n128 = 0, w64 = 0, w128 = 0, sel = 0;
     if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&n64, snap_coop_bf16<64>, kCoopThreads, 0) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&n128, snap_coop_bf16<128>, kCoopThreads, 0) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&w64, snap_wave_bf16<64, false>, kWvThreads, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w128, snap_wave_bf16<128, false>, kWvThreads, 0) == hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&w128, snap_wave_bf16<128, false>, kWvThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&sel, snap_select, kSelThreads, 0) == hipSuccess) {
       c.coop = coop != 0;
       c.cus = cus;
       c.per_cu[0] = n64;
       c.per_cu[1] = n128;
       c.wv_per_cu[0] = w64;
       c.wv_per_cu[1] = w128;
+      c.sel_per_cu = sel;
     }
     (void)hipGetLastError();
   }
@@ -3071,7 +3159,7 @@ int wave_grid(const SnapLayout& lay, int D, int L, int64_t kst, int64_t qst) {
 thread_local const char* g_last_kernel = "";
 thread_local bool g_force_residency_fail = false;
 thread_local bool g_force_wait_timeout = false;
-thread_local bool g_force_split_select = false;
+thread_local int g_force_split_select = 0;  // 1: split selection, 2: split selection and the pooling kernel
 thread_local const char* g_last_select = "";
 thread_local const char* g_last_pool = "";
 
@@ -3219,8 +3307,8 @@ extern "C" int kvc_snapkv_force_wait_timeout(int on) {
 }
 
 extern "C" int kvc_snapkv_force_split_select(int on) {
-  const int prev = g_force_split_select ? 1 : 0;
-  g_force_split_select = on != 0;
+  const int prev = g_force_split_select;
+  g_force_split_select = on == 2 ? 2 : on != 0 ? 1 : 0;
   return prev;
 }
 
@@ -3326,11 +3414,17 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
     float* pooled_dst = pooled_out ? pooled_out : sel_pools ? nullptr : pooled;
     const uint16_t* qb = static_cast<const uint16_t*>(q);
     const uint16_t* kb = static_cast<const uint16_t*>(k);
-    // heads of at most one selection workgroup's range: that workgroup also
-    // does the pooling kernel's work (histogram, pooled output, exact votes of
-    // flagged heads), which is then not launched
-    const bool fuse = sel_pools && lay.N <= kSelChunk && lay.N % 4 == 0 && aligned16(vraw) &&
-                      (!pooled_out || aligned16(pooled_out)) && !g_force_split_select;
+    // The selection also does the pooling kernel's work (histogram, pooled
+    // output, exact votes of flagged heads), which is then not launched: one
+    // workgroup per head where a head is at most one workgroup's range, else
+    // the head's workgroups together (they meet on the head's histogram)
+    // where the whole selection grid is resident at once.
+    const bool sel_vec = lay.N % 4 == 0 && aligned16(vraw) && (!pooled_out || aligned16(pooled_out));
+    const bool per_head = lay.N <= kSelChunk && !g_force_split_select;
+    const CoopCaps& caps = coop_caps();
+    const int64_t sel_grid = static_cast<int64_t>((lay.N + kSelChunk - 1) / kSelChunk) * lay.BH;
+    const bool fuse = sel_pools && sel_vec &&
+                      (per_head || (g_force_split_select != 2 && sel_grid <= static_cast<int64_t>(caps.sel_per_cu) * caps.cus));
     ExactArgs* fused_arg = fuse ? &fused_ea : nullptr;
     kvc_status st = D == 128 ? launch_single_pass<128>(lay, Gw, Gc, qb, qs, qrow0, kb, kvs, H, L, window, r, avg,
                                                        scale_log2, ws, vraw, pooled_dst, fused_arg, stream)
@@ -3339,7 +3433,8 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
     if (st == KVC_OK) {
       schedule = KVC_SNAPKV_SINGLE_PASS;
       self_hist = fuse;
-      g_last_pool = fuse ? "snap_select_head" : r <= kPoolRegRadius ? "snap_pool" : "snap_pool_lds";
+      g_last_pool = fuse ? (per_head ? "snap_select_head" : "snap_select")
+                         : r <= kPoolRegRadius ? "snap_pool" : "snap_pool_lds";
       if (sel_pools) {
         sel_src = vraw;
         sel_rad = r;
@@ -3384,7 +3479,9 @@ kvc_status snap_core(const void* q, int q_len, kvc_strides qs, const void* k, co
     snap_select<<<gs, kSelThreads, 0, stream>>>(sel_src, vec, sel_rad, skip, hist, lay.N, lay.kk,
                                                 reinterpret_cast<unsigned*>(ws + lay.sel_ctr),
                                                 reinterpret_cast<uint2*>(ws + lay.cand),
-                                                reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out);
+                                                reinterpret_cast<unsigned*>(ws + lay.bitmap), idx_out,
+                                                self_hist ? 1 : 0, self_hist ? pooled_out : nullptr, fused_ea,
+                                                g_force_wait_timeout ? kWvSpinForced : kSelHistSpin);
     g_last_select = "snap_select";
   }
   mark_phase(5, stream);

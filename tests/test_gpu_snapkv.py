@@ -298,6 +298,12 @@ def test_single_pass_waits_end_in_time(name, H, L):
         assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
         words = ws[off:off + 12].view(torch.int32).cpu().tolist()
         assert words[0] == 0 and words[2] == 1, f"status word {words[0]}, gate {words[1:]}"
+        # pooling inside the selection: one workgroup per head, or (131K: 8 workgroups for each of
+        # 32 heads, one per compute unit) the head's workgroups together
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        want = "snap_select_head" if L - wl.window <= 16384 else "snap_select" if cus >= 256 else None
+        if want:
+            assert kvc.snapkv_last_pool_kernel() == want
     if L < 20000:
         _report(f"waits-{L}", _compare(qn, kn, vn, res, wl.window, wl.budget, wl.pool_kernel, "bf16",
                                        heads=[(0, 0), (B - 1, H - 1)]), 2)
@@ -334,10 +340,14 @@ def test_zero_queries_exact_ties(L, C, schedule):
 
 
 class _SplitSelect:
-    """Forces the several-workgroups-per-head selection while active."""
+    """Forces the several-workgroups-per-head selection while active (mode 2: and the single pass's
+    separate pooling kernel)."""
+
+    def __init__(self, mode=1):
+        self.mode = mode
 
     def __enter__(self):
-        self.prev = kvc.library().kvc_snapkv_force_split_select(1)
+        self.prev = kvc.library().kvc_snapkv_force_split_select(self.mode)
 
     def __exit__(self, *exc):
         kvc.library().kvc_snapkv_force_split_select(self.prev)
@@ -362,33 +372,41 @@ def test_zero_queries_exact_ties_split_select(L, C):
 
 
 @pytest.mark.parametrize("name,L,pool", [("16k-bf16", None, 7), ("16k-bf16", None, 13), ("131k-bf16", 16416, 7),
-                                          ("16k-bf16", 9000, 5)])
+                                          ("16k-bf16", 9000, 5), ("131k-bf16", 70000, 7)])
 def test_select_forms_agree(name, L, pool):
     """One workgroup per head (heads of at most 16384 prefix positions) and several per head keep
     the same positions, bit for bit, on the same votes (both schedules' votes: the selection reads
     raw votes and pools them itself for a max-pool of radius <= 4, else the pooling kernel's
-    stored scores). Under the single pass with a max-pool of radius <= 4 the per-head form also
-    does the pooling kernel's work (pooled output and histogram), which is then not launched: its
-    pooled scores equal the pooling kernel's bit for bit."""
+    stored scores). Under the single pass with a max-pool of radius <= 4 the selection also does
+    the pooling kernel's work (pooled output and histogram), which is then not launched: the
+    per-head form alone, the split form with the head's workgroups adding to one histogram and
+    meeting on it; the split form with the separate pooling kernel is the third form compared.
+    Their pooled scores agree bit for bit."""
     wl = syn.SNAPKV_WORKLOADS[name].with_(pool_kernel=pool)
     if L is not None:
         wl = wl.with_(L=L, name=f"{name}-L{L}")
-    print(f"[snapkv] selection forms on {name} p{pool}", flush=True)
+    print(f"[snapkv] selection forms on {wl.name} p{pool}", flush=True)
     qn, kn, vn = _batch(wl.with_(pool_kernel=syn.SNAPKV_WORKLOADS[name].pool_kernel))
     q, k, v = (par.to_device(x, wl.dtype) for x in (qn, kn, vn))
+    short = wl.L - wl.window <= 16384
     for schedule in (kvc.SNAPKV_SINGLE_PASS, kvc.SNAPKV_TWO_PASS):
         single = schedule == kvc.SNAPKV_SINGLE_PASS
-        a = _run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True, want_pooled=True)
-        assert kvc.snapkv_last_select_kernel() == "snap_select_head"
-        assert kvc.snapkv_last_pool_kernel() == (("snap_select_head" if pool <= 9 else "snap_pool") if single
-                                                 else "snap_votes_bf16")
-        with _SplitSelect():
-            b = _run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True, want_pooled=True)
-            assert kvc.snapkv_last_select_kernel() == "snap_select"
-            assert kvc.snapkv_last_pool_kernel() == ("snap_pool" if single else "snap_votes_bf16")
-        assert torch.equal(a.vote, b.vote) and torch.equal(a.pooled, b.pooled)  # deterministic votes
-        assert torch.equal(a.idx, b.idx)
-        assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+        fused = single and pool <= 9
+        runs = []
+        for mode in (0, 1, 2):
+            with _SplitSelect(mode):
+                runs.append(_run(q, k, v, wl.window, wl.budget, pool, wl.dtype, schedule, want_vote=True,
+                                 want_pooled=True))
+                per_head = mode == 0 and short
+                assert kvc.snapkv_last_select_kernel() == ("snap_select_head" if per_head else "snap_select")
+                want_pool = ("snap_select_head" if per_head else "snap_select" if mode < 2 else "snap_pool") \
+                    if fused else "snap_pool" if single else "snap_votes_bf16"
+                assert kvc.snapkv_last_pool_kernel() == want_pool
+        a = runs[0]
+        for b in runs[1:]:
+            assert torch.equal(a.vote, b.vote) and torch.equal(a.pooled, b.pooled)  # deterministic votes
+            assert torch.equal(a.idx, b.idx)
+            assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
         pooled, idx = a.pooled.cpu().numpy(), a.idx.cpu().numpy()
         for bb in range(wl.B):
             for h in range(wl.H):
