@@ -1346,13 +1346,17 @@ __device__ __forceinline__ void wv_stage(const WvCtx& c, int h, int lane) {
   WvFin& f = c.fin[b];
   asm volatile("" ::: "memory");
   if (c.sh->fin_owner[b] != h) {
-    // another head of this workgroup still holds the buffer (only if its
-    // finisher had to retry for rounds); bounded wait
-    for (unsigned polls = 0; c.sh->fin_owner[b] >= 0 && polls < kWvSpin; ++polls) {
+    // taken by compare-and-swap (two finisher waves of a workgroup, heads
+    // G apart, map to the same buffer); while another head holds it (only if
+    // its finisher had to retry for rounds) a bounded wait, then taken anyway
+    int prev = 0;
+    for (unsigned polls = 0; polls < kWvSpin; ++polls) {
+      if (lane == 0) prev = atomicCAS(&c.sh->fin_owner[b], -1, h);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev == -1 || prev == h) break;
       __builtin_amdgcn_s_sleep(1);
-      asm volatile("" ::: "memory");
     }
-    if (lane == 0) c.sh->fin_owner[b] = h;
+    if (prev != -1 && prev != h && lane == 0) c.sh->fin_owner[b] = h;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   const unsigned long long* a = c.acc + static_cast<int64_t>(h) * kCoopHeadWords;
@@ -2753,10 +2757,30 @@ __global__ __launch_bounds__(kSelThreads) void snap_select(const float* __restri
   const unsigned n_cand = min(load_word(&ctr_head[0]), static_cast<unsigned>(N));
   const bool in_lds = n_cand <= static_cast<unsigned>(kCandLds);
   const bool lds_bm = words <= kBitmapLds;
-  if (in_lds)
-    for (unsigned i = tid; i < n_cand; i += kSelThreads) s.cand[i] = ld_agent_u2(&cand_g[i]);
-  if (lds_bm)
-    for (int i = tid; i < words; i += kSelThreads) s.bm[i] = load_word(&bm_g[i]);
+  // every load in flight before the first LDS store (one round trip)
+  constexpr int kCandPer = kCandLds / kSelThreads, kBmPer = kBitmapLds / kSelThreads;
+  uint2 cv[kCandPer];
+  unsigned bv[kBmPer];
+#pragma unroll
+  for (int r = 0; r < kBmPer; ++r) {
+    const int i = tid + r * kSelThreads;
+    if (lds_bm && i < words) bv[r] = load_word(&bm_g[i]);
+  }
+#pragma unroll
+  for (int r = 0; r < kCandPer; ++r) {
+    const unsigned i = static_cast<unsigned>(tid + r * kSelThreads);
+    if (in_lds && i < n_cand) cv[r] = ld_agent_u2(&cand_g[i]);
+  }
+#pragma unroll
+  for (int r = 0; r < kBmPer; ++r) {
+    const int i = tid + r * kSelThreads;
+    if (lds_bm && i < words) s.bm[i] = bv[r];
+  }
+#pragma unroll
+  for (int r = 0; r < kCandPer; ++r) {
+    const unsigned i = static_cast<unsigned>(tid + r * kSelThreads);
+    if (in_lds && i < n_cand) s.cand[i] = cv[r];
+  }
   sel_rank_compact(s, bstar, rem, n_cand, in_lds, cand_g, bm_g, lds_bm, words, N, kk,
                    idx_out + static_cast<int64_t>(bh) * kk);
 }

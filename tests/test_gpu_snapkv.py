@@ -309,6 +309,29 @@ def test_single_pass_waits_end_in_time(name, H, L):
                                        heads=[(0, 0), (B - 1, H - 1)]), 2)
 
 
+def test_single_pass_two_finishers_per_workgroup():
+    """More heads than workgroups (9 x 32 = 288 heads of 16K keys on 256 workgroups): head g is
+    finished by wave 0 of workgroup g and head g + 256 by its wave 1, which share a staging buffer
+    (taken by compare-and-swap). The waits end in time and sampled heads of both finishers match
+    the oracle."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=9)
+    qn, kn, vn = _batch(wl)
+    q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
+    B, H, L, D = k.shape
+    n = kvc.snapkv_workspace_bytes(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k.dtype)
+    off = kvc.snapkv_status_offset(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k.dtype)
+    ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    print(f"[snapkv] two finishers per workgroup B{B} H{H} L{L}", flush=True)
+    res = _run(q, k, v, wl.window, wl.budget, wl.pool_kernel, "bf16", kvc.SNAPKV_SINGLE_PASS, workspace=ws)
+    assert kvc.snapkv_last_score_kernel() == "snap_wave_bf16"
+    words = ws[off:off + 12].view(torch.int32).cpu().tolist()
+    assert words[0] == 0 and words[2] == 1, f"status word {words[0]}, gate {words[1:]}"
+    del q, k, v
+    heads = [(0, 0), (0, 1), (8, 0), (8, 31)]  # heads 0, 1 (wave 0) and 256, 287 (wave 1)
+    _report("two-finishers", _compare(qn, kn, vn, res, wl.window, wl.budget, wl.pool_kernel, "bf16", heads=heads),
+            len(heads))
+
+
 def test_single_pass_many_heads_unaligned():
     """Heads whose units straddle device-wide rounds (B*H*units not a multiple of the grid)."""
     wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=3, H=7, L=70001, budget=1500)
