@@ -201,7 +201,7 @@ def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
     score_kernel = kvc.snapkv_last_score_kernel()
     pool_kernel = kvc.snapkv_last_pool_kernel()
     # the per-head selection kernel pools and counts itself: no pooling kernel between marks 3 and 4
-    fused_pool = single and pool_kernel == "snap_select_head"
+    fused_pool = single and pool_kernel in ("snap_select_head", "snap_select")
     phases = PHASES_SINGLE if single else PHASES
     if fused_pool:
         phases = [("none_pool" if p == "pool" else p) for p in phases]
