@@ -283,9 +283,12 @@ const char* kvc_snapkv_last_pool_kernel(void);
  * preparation kernel under SINGLE_PASS), the row-statistics pass (2; the
  * single score kernel under SINGLE_PASS), the row-statistics merge (3; nothing
  * under SINGLE_PASS), the vote + pooling + histogram pass (4;
- * pooling + histogram under SINGLE_PASS), the per-head selection (5) and the
- * gather (6). The events are created and owned by the caller; pass NULL or 0
- * to stop recording. */
+ * pooling + histogram under SINGLE_PASS, nothing where the selection pools),
+ * the per-head selection (5) and the gather (6). When events 1 and 2 are both
+ * set and the independent-wave score kernel runs, the kernel's own dispatch
+ * records them at its start and end (no separate records around it), so that
+ * their interval is the kernel's duration. The events are created and owned
+ * by the caller; pass NULL or 0 to stop recording. */
 void kvc_snapkv_set_phase_events(hipEvent_t* events, int n_events);
 
 /* ------------------------------------------------------------------------- */

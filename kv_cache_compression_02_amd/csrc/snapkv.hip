@@ -48,8 +48,12 @@
 // arithmetic.
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <mutex>
+#include <tuple>
+#include <utility>
 
 #include "common.hpp"
 
@@ -3021,6 +3025,26 @@ void mark_phase(int i, hipStream_t stream) {
   if (g_phase_events && i < g_phase_count && g_phase_events[i]) (void)hipEventRecord(g_phase_events[i], stream);
 }
 
+hipEvent_t phase_event(int i) { return g_phase_events && i < g_phase_count ? g_phase_events[i] : nullptr; }
+
+template <typename... P, typename... A, size_t... I>
+hipError_t launch_timed_impl(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop, std::index_sequence<I...>, A... a) {
+  std::tuple<P...> args(a...);  // every argument as the kernel's own parameter type
+  void* ptrs[] = {static_cast<void*>(&std::get<I>(args))...};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, 0, stream, start, stop, 0);
+}
+
+// A launch whose start and stop events are recorded by the dispatch itself,
+// at the kernel's start and end, instead of by separate records around it
+// (each of which costs a few microseconds of GPU time between the kernels).
+template <typename... P, typename... A>
+hipError_t launch_timed(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  return launch_timed_impl(kern, grid, block, stream, start, stop, std::index_sequence_for<P...>{}, a...);
+}
+
 template <int D>
 void launch_stats(const SnapLayout& lay, const uint16_t* q, kvc_strides qs, int qrow0, const uint16_t* k,
                   kvc_strides kvs, int H, int L, int w, float scale_log2, char* ws, hipStream_t stream) {
@@ -3248,7 +3272,11 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
   snap_coop_prep<D><<<static_cast<unsigned>(lay.BH), kThreads, 0, stream>>>(
       q, qs.b, qs.h, qs.t, qrow0, k, kvs.b, kvs.h, kvs.t, H, L, w, scale_log2, ref, acc, cnt, stat, hist,
       reinterpret_cast<unsigned*>(ws + lay.sel_ctr), status);
-  mark_phase(1, stream);
+  // phase marks 1 and 2 around the independent-wave kernel come from its own
+  // dispatch when both are set
+  const hipEvent_t ev1 = phase_event(1), ev2 = phase_event(2);
+  const bool timed = Gw > 0 && ev1 && ev2;
+  if (!timed) mark_phase(1, stream);
   int64_t qsb = qs.b, qsh = qs.h, qst = qs.t, ksb = kvs.b, ksh = kvs.h, kst = kvs.t;
   const float* cref = ref;
   hipError_t e = hipErrorInvalidValue;
@@ -3263,18 +3291,23 @@ kvc_status launch_single_pass(const SnapLayout& lay, int Gw, int Gc, const uint1
     const unsigned target = static_cast<unsigned>(Gw) + (g_force_residency_fail ? 1u : 0u);
     const unsigned spin = g_force_residency_fail ? 16u : kWvGateSpin;
     const unsigned wait_spin = g_force_wait_timeout ? kWvSpinForced : kWvSpin;
-    if (nt < Gw * kWvWaves)
-      snap_wave_bf16<D, true><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
-          q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref,
-          acc, cnt, stat, status, vote, gate, target, spin, wait_spin);
-    else
-      snap_wave_bf16<D, false><<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(
-          q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total, static_cast<int>(lay.BH), scale_log2, cref,
-          acc, cnt, stat, status, vote, gate, target, spin, wait_spin);
-    e = hipGetLastError();
+    const int bhi = static_cast<int>(lay.BH);
+    auto kern = nt < Gw * kWvWaves ? snap_wave_bf16<D, true> : snap_wave_bf16<D, false>;
+    if (timed) {
+      e = launch_timed(kern, dim3(Gw), dim3(kWvThreads), stream, ev1, ev2, q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst,
+                       H, L, w, nt, total, bhi, scale_log2, cref, acc, cnt, stat, status, vote, gate, target, spin,
+                       wait_spin);
+    } else {
+      kern<<<dim3(Gw), dim3(kWvThreads), 0, stream>>>(q, qsb, qsh, qst, qrow0, k, ksb, ksh, kst, H, L, w, nt, total,
+                                                      bhi, scale_log2, cref, acc, cnt, stat, status, vote, gate,
+                                                      target, spin, wait_spin);
+      e = hipSuccess;
+    }
+    const hipError_t le = hipGetLastError();
+    if (e == hipSuccess) e = le;
     if (e == hipSuccess) {
       g_last_kernel = "snap_wave_bf16";
-      mark_phase(2, stream);
+      if (!timed) mark_phase(2, stream);
       ea.flags = cnt;  // the pooling kernel recomputes the votes of flagged heads exactly
     } else {
       (void)hipGetLastError();
