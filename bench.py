@@ -185,9 +185,13 @@ def bench_snapkv(wl, args, ev, steps, warmup, detail=True, keep_host=False):
     lib = kvc.library()
     n_ev = len(PHASES) + 1
 
+    # one prepared call per K/V copy: arguments checked and marshalled once, each call enqueues the
+    # whole compression (kvc_snapkv_compress) as snapkv_compress would
+    prepared = [kvc.SnapKVCall(q, ks[c], vs[c], wl.window, wl.budget, wl.pool_kernel, workspace=ws, out=out)
+                for c in range(ncp)]
+
     def call(i):
-        kvc.snapkv_compress(q, ks[i % ncp], vs[i % ncp], wl.window, wl.budget, wl.pool_kernel, workspace=ws,
-                            out=out)
+        prepared[i % ncp]()
 
     def set_events(arr):
         lib.kvc_snapkv_set_phase_events(ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,

@@ -25,7 +25,7 @@ __all__ = [
     "KvcError", "library", "library_path", "snapkv_workspace_bytes", "snapkv_compress",
     "SnapKVResult", "H2OCache", "SinkCache", "KVC_F32", "KVC_BF16", "EXPORTED_SYMBOLS", "KVC_POOL_MAX",
     "KVC_POOL_AVG", "snapkv_workspace_bytes_ex", "snapkv_compress_ex", "snapkv_status_offset",
-    "snapkv_last_pool_kernel",
+    "snapkv_last_pool_kernel", "SnapKVCall",
     "SNAPKV_AUTO", "SNAPKV_TWO_PASS", "SNAPKV_SINGLE_PASS", "snapkv_schedule", "snapkv_last_schedule",
     "decode_attention_workspace_bytes", "decode_attention", "decode_attention_noalloc",
 ]
@@ -235,16 +235,8 @@ def snapkv_last_pool_kernel():
     return library().kvc_snapkv_last_pool_kernel().decode()
 
 
-def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,
-                    workspace=None, out=None):
-    """SnapKV compression of one layer (kvc_snapkv_compress).
-
-    q: [B, H, q_len, D] (last ``window`` rows used); k, v: [B, H, L, D] with the same
-    strides; bf16 or fp32 on the GPU. Returns SnapKVResult(k [B,H,budget,D],
-    v [B,H,budget,D], idx int32 [B,H,budget-window], pooled, vote) where pooled/vote
-    are float32 [B,H,L-window] or None. ``workspace`` (uint8 tensor) and ``out``
-    (a SnapKVResult of preallocated tensors) may be passed to avoid allocations.
-    """
+def _snapkv_args(q, k, v, window, budget, pool_kernel, want_pooled, want_vote, workspace, out):
+    """Checks and marshals one kvc_snapkv_compress call: returns (arguments, SnapKVResult)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
         if t.dim() != 4:
@@ -283,11 +275,47 @@ def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, 
     if workspace is None:
         nbytes = snapkv_workspace_bytes(B, H, L, D, window, budget, pool_kernel, k.dtype)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    _check(library().kvc_snapkv_compress(
-        _ptr(q), q.shape[2], _strides4(q), _ptr(k), _ptr(v), _strides4(k), B, H, L, D,
-        window, budget, pool_kernel, dt, _ptr(k_out), _ptr(v_out), _ptr(idx), _ptr(pooled),
-        _ptr(vote), _ptr(workspace), workspace.numel(), _stream()))
-    return SnapKVResult(k_out, v_out, idx, pooled, vote)
+    args = (_ptr(q), q.shape[2], _strides4(q), _ptr(k), _ptr(v), _strides4(k), B, H, L, D,
+            window, budget, pool_kernel, dt, _ptr(k_out), _ptr(v_out), _ptr(idx), _ptr(pooled),
+            _ptr(vote), _ptr(workspace), workspace.numel(), _stream())
+    # the tensors stay referenced by the result (and the workspace by the caller or the call object)
+    return args, SnapKVResult(k_out, v_out, idx, pooled, vote), workspace
+
+
+def snapkv_compress(q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,
+                    workspace=None, out=None):
+    """SnapKV compression of one layer (kvc_snapkv_compress).
+
+    q: [B, H, q_len, D] (last ``window`` rows used); k, v: [B, H, L, D] with the same
+    strides; bf16 or fp32 on the GPU. Returns SnapKVResult(k [B,H,budget,D],
+    v [B,H,budget,D], idx int32 [B,H,budget-window], pooled, vote) where pooled/vote
+    are float32 [B,H,L-window] or None. ``workspace`` (uint8 tensor) and ``out``
+    (a SnapKVResult of preallocated tensors) may be passed to avoid allocations.
+    """
+    args, res, _ = _snapkv_args(q, k, v, window, budget, pool_kernel, want_pooled, want_vote, workspace, out)
+    _check(library().kvc_snapkv_compress(*args))
+    return res
+
+
+class SnapKVCall:
+    """One kvc_snapkv_compress call with its arguments checked and marshalled once, for loops that
+    compress into the same buffers again and again: calling the object enqueues the compression
+    (the same kernels as snapkv_compress) on the stream that was current when it was made, and
+    returns its SnapKVResult. The tensors must stay where they are between calls; their contents
+    may change."""
+
+    def __init__(self, q, k, v, window, budget, pool_kernel, *, want_pooled=False, want_vote=False,
+                 workspace=None, out=None):
+        self._args, self.result, self._ws = _snapkv_args(q, k, v, window, budget, pool_kernel, want_pooled,
+                                                         want_vote, workspace, out)
+        self._inputs = (q, k, v)
+        self._fn = library().kvc_snapkv_compress
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != KVC_OK:
+            raise KvcError(st, library().kvc_last_error().decode())
+        return self.result
 
 
 def snapkv_workspace_bytes_ex(n_layers, B, H, L, D, window, budget, pool_kernel, dtype, ragged=False):

@@ -483,6 +483,32 @@ def test_deterministic_and_workspace_reuse(schedule):
     _compare(qn2, kn2, vn2, b, wl.window, wl.budget, wl.pool_kernel, "bf16")
 
 
+def test_prepared_call_matches():
+    """A SnapKVCall (arguments checked and marshalled once) gives what snapkv_compress gives, bit for
+    bit, call after call, with the inputs' contents changed between calls."""
+    wl = syn.SNAPKV_WORKLOADS["16k-bf16"].with_(B=1, H=4, L=20000, budget=1500)
+    qn, kn, vn = syn.snapkv_batch(wl)
+    q, k, v = (par.to_device(x, "bf16") for x in (qn, kn, vn))
+    B, H, L, D = k.shape
+    n = kvc.snapkv_workspace_bytes(B, H, L, D, wl.window, wl.budget, wl.pool_kernel, k.dtype)
+    ws = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    call = kvc.SnapKVCall(q, k, v, wl.window, wl.budget, wl.pool_kernel, want_vote=True, want_pooled=True,
+                          workspace=ws)
+    print("[snapkv] prepared call", flush=True)
+    for rep in range(3):
+        if rep == 2:
+            k.mul_(-1.0)  # new contents, same buffers
+        got = call()
+        torch.cuda.synchronize()
+        want = kvc.snapkv_compress(q, k, v, wl.window, wl.budget, wl.pool_kernel, want_vote=True, want_pooled=True)
+        torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)
+    bad = kvc.SnapKVCall(q, k, v, wl.window, wl.budget, wl.pool_kernel, workspace=ws[: n // 2])
+    with pytest.raises(kvc.KvcError):
+        bad()
+
+
 def test_error_statuses():
     B, H, L, D = 1, 2, 512, 128
     k = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device="cuda")
