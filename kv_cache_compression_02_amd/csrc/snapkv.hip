@@ -587,10 +587,23 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
   // ran out: 1 vote weights, 2 merge slot, 3 a head's publication, 4 a head
   // still unfinished after the last round, 5 a head's queries); status[1],
   // status[2]: its residency gate
+  // wave 0's query and key rows first (the kernel's one round trip to
+  // memory), the clearing stores while they are in flight
+  constexpr int KS = D / 16;
+  const int lane = threadIdx.x & (kWave - 1), col = lane & 31, half = lane >> 5;
+  bf16x8_t qf[KS], kf[KS];
+  if (threadIdx.x < kWave) {
+    const int rw = min(col, w - 1);
+    load_half_row<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rw) * qst + half * (D / 2), qf);
+    load_half_row<D>(k + b * ksb + h * ksh + static_cast<int64_t>(L - w + rw) * kst + half * (D / 2), kf);
+  }
   if (bh == 0 && threadIdx.x < 3) status[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < 32 * kCoopFinWords; i += kThreads)
     acc[static_cast<int64_t>(bh) * kCoopHeadWords + (i / kCoopFinWords) * kCoopRowWords + i % kCoopFinWords] = 0;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[static_cast<int64_t>(bh) * kHistBins + i] = 0;
+  {
+    u32x4_t* hv = reinterpret_cast<u32x4_t*>(hist + static_cast<int64_t>(bh) * kHistBins);  // 16 KB, 16-byte aligned
+    for (int i = threadIdx.x; i < kHistBins / 4; i += kThreads) hv[i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
   if (threadIdx.x < kCoopCtrWords) cnt[bh * kCoopCtrWords + threadIdx.x] = 0;
   if (threadIdx.x < 32) stat[bh * 32 + threadIdx.x] = make_uint2(0u, 0u);
   if (threadIdx.x < kSelCtrWords) sel_ctr[bh * kSelCtrWords + threadIdx.x] = 0;
@@ -599,12 +612,6 @@ __global__ __launch_bounds__(kThreads) void snap_coop_prep(
   // scores for query (lane & 31) and the row max takes one exchange between
   // the wave's halves; rows and keys past the window repeat row w - 1
   if (threadIdx.x < kWave) {
-    constexpr int KS = D / 16;
-    const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
-    const int rw = min(col, w - 1);
-    bf16x8_t qf[KS], kf[KS];
-    load_half_row<D>(q + b * qsb + h * qsh + static_cast<int64_t>(qrow0 + rw) * qst + half * (D / 2), qf);
-    load_half_row<D>(k + b * ksb + h * ksh + static_cast<int64_t>(L - w + rw) * kst + half * (D / 2), kf);
     f32x16_t sc = {};
 #pragma unroll
     for (int st = 0; st < KS; ++st) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sc, 0, 0, 0);
