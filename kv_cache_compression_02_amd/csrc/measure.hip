@@ -1,5 +1,5 @@
 // Instrumentation: a plain streaming read of a device buffer, the reference
-// against which the library's HBM-bound kernels are judged (not part of the
+// against which the library's HBM-bound kernels are compared (not part of the
 // method). Each thread reads kReadPer 16-byte pieces per step of a grid-stride
 // loop, all issued before any is used, and folds them into one word; the word
 // is stored only if it equals a value the data never produces in practice, so
